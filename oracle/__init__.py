@@ -1,0 +1,8 @@
+"""fp64 CPU oracle (test infrastructure only; never on the product path).
+
+Importable by the tests, the package entry's ``smoke()`` check and the
+benchmark's CPU-baseline leg, and by nothing else.
+"""
+from .attention import attention_backward, attention_forward, attention_probs
+
+__all__ = ["attention_forward", "attention_backward", "attention_probs"]
