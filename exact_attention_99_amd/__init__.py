@@ -1,0 +1,20 @@
+"""Python binding of libfa355 (exact tiled attention for MI355X / gfx950).
+
+Argument marshalling only: every step of the attention computation runs in
+the library's HIP kernels.  Tensors are PyTorch tensors on a ROCm device;
+PyTorch supplies the device memory and the stream.  If the compiled library
+is missing, importing the ABI raises: there is no fallback path.
+
+Names mirror the C entry points of ``include/fa355.h``:
+
+    fa_fwd(q, k, v, causal, scale, o=None, lse=None, stream=None) -> (o, lse)
+    fa_bwd(q, k, v, o, lse, dout, causal, scale, ...) -> (dq, dk, dv)
+    fa_bwd_workspace_size(B, H_q, H_kv, N, d, dtype) -> int
+    fa_status_string(code) -> str
+    fa_version() -> int
+"""
+from ._abi import (FA_DTYPE, FaError, fa_bwd, fa_bwd_workspace_size, fa_fwd, fa_status_string,
+                   fa_version, lib_path, load_library)
+
+__all__ = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string", "fa_version",
+           "FaError", "FA_DTYPE", "load_library", "lib_path"]

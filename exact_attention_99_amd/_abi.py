@@ -1,0 +1,148 @@
+"""ctypes declarations for libfa355 and torch-tensor marshalling."""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Tuple
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libfa355.so"
+
+# fa_dtype values (include/fa355.h)
+FA_DTYPE = {"fp32": 0, "fp16": 1, "bf16": 2}
+
+STATUS = {0: "FA_OK", 1: "FA_ERR_INVALID_ARG", 2: "FA_ERR_UNSUPPORTED", 3: "FA_ERR_HIP"}
+
+_lock = threading.Lock()
+_lib: Optional[ctypes.CDLL] = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {STATUS.get(code, code)} ({fa_status_string(code)})")
+
+
+def lib_path() -> str:
+    return os.environ.get("FA355_LIB", os.path.join(PKG, _LIB_NAME))
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the compiled library; raise if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build it with `python -m exact_attention_99_amd.build` "
+                "(there is no fallback implementation)")
+        lib = ctypes.CDLL(path)
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+        lib.fa_fwd.restype = i
+        lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                               i, i, i, i, i, i, f, i, vp]
+        lib.fa_bwd.restype = i
+        lib.fa_bwd_workspace_size.argtypes = [i, i, i, i, i, i]
+        lib.fa_bwd_workspace_size.restype = sz
+        lib.fa_status_string.argtypes = [i]
+        lib.fa_status_string.restype = ctypes.c_char_p
+        lib.fa_version.argtypes = []
+        lib.fa_version.restype = i
+        _lib = lib
+        return lib
+
+
+def fa_status_string(code: int) -> str:
+    return load_library().fa_status_string(int(code)).decode()
+
+
+def fa_version() -> int:
+    return int(load_library().fa_version())
+
+
+def fa_bwd_workspace_size(B: int, H_q: int, H_kv: int, N: int, d: int, dtype: str) -> int:
+    return int(load_library().fa_bwd_workspace_size(B, H_q, H_kv, N, d, FA_DTYPE[dtype]))
+
+
+def _dtype_name(t) -> str:
+    import torch
+    m = {torch.float32: "fp32", torch.float16: "fp16", torch.bfloat16: "bf16"}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _shape(q, k, v) -> Tuple[int, int, int, int, int]:
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, N, d]")
+    B, Hq, N, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    return B, Hq, k.shape[1], N, d
+
+
+def _check_same(ref, *ts):
+    for t in ts:
+        if t.device != ref.device:
+            raise ValueError("all tensors must be on the same device")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+
+
+def _stream(ref, stream) -> int:
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(ref.device).cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def fa_fwd(q, k, v, causal: bool, scale: float, o=None, lse=None, stream=None):
+    """O = softmax(scale * q k^T [causal]) v and the row logsumexp; returns (o, lse)."""
+    import torch
+    lib = load_library()
+    B, Hq, Hkv, N, d = _shape(q, k, v)
+    dt = _dtype_name(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _check_same(q, k, v, o, lse)
+    st = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                    B, Hq, Hkv, N, d, int(bool(causal)), float(scale), FA_DTYPE[dt],
+                    _stream(q, stream))
+    if st != 0:
+        raise FaError(st, "fa_fwd")
+    return o, lse
+
+
+def fa_bwd(q, k, v, o, lse, dout, causal: bool, scale: float, dq=None, dk=None, dv=None,
+           workspace=None, stream=None):
+    """Gradients of sum(dout * o) for q, k, v; returns (dq, dk, dv)."""
+    import torch
+    lib = load_library()
+    B, Hq, Hkv, N, d = _shape(q, k, v)
+    dt = _dtype_name(q)
+    if dq is None:
+        dq = torch.empty_like(q)
+    if dk is None:
+        dk = torch.empty_like(k)
+    if dv is None:
+        dv = torch.empty_like(v)
+    need = int(lib.fa_bwd_workspace_size(B, Hq, Hkv, N, d, FA_DTYPE[dt]))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check_same(q, k, v, o, lse, dout, dq, dk, dv, workspace)
+    st = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                    dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                    workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                    B, Hq, Hkv, N, d, int(bool(causal)), float(scale), FA_DTYPE[dt],
+                    _stream(q, stream))
+    if st != 0:
+        raise FaError(st, "fa_bwd")
+    return dq, dk, dv

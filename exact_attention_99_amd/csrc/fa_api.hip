@@ -1,0 +1,116 @@
+// C-ABI entry points of libfa355: argument checks, workspace layout and
+// dispatch to the kernels.  Declared in include/fa355.h.
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "fa355.h"
+#include "fa_launch.h"
+
+namespace {
+
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool sizes_ok(int B, int Hq, int Hkv, int N) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || N < 1) return false;
+    if (Hq % Hkv != 0) return false;
+    // Every element offset is formed in 64-bit; block counts must fit a grid.
+    const long long rows = (long long)B * Hq * ((N + 31) / 32);
+    return rows < (1LL << 31);
+}
+
+bool dtype_ok(fa_dtype t) { return t == FA_DTYPE_FP32 || t == FA_DTYPE_FP16 || t == FA_DTYPE_BF16; }
+
+int fwd_variant() {
+    // Tile variant of the 16-bit forward kernel; FA355_FWD_VARIANT overrides
+    // the default for tile sweeps.
+    static const int v = [] {
+        const char* e = getenv("FA355_FWD_VARIANT");
+        return e ? atoi(e) : 0;
+    }();
+    return v;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H_q,
+                 int H_kv, int N, int d, int causal, float scale, fa_dtype dtype,
+                 hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return FA_ERR_INVALID_ARG;
+    if (!sizes_ok(B, H_q, H_kv, N)) return FA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype)) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+
+    fa355::FwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.B = B; a.Hq = H_q; a.Hkv = H_kv; a.N = N; a.d = d;
+    a.causal = causal;
+    a.cl2 = scale * kLog2eHost;
+    a.dtype = (int)dtype;
+    a.fwd_variant = fwd_variant();
+    a.stream = stream;
+    return fa355::launch_fwd(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_bwd_workspace_size(int B, int H_q, int H_kv, int N, int d, fa_dtype dtype) {
+    if (!sizes_ok(B, H_q, H_kv, N) || !dtype_ok(dtype) || (d != 64 && d != 128)) return 0;
+    const size_t rows = (size_t)B * H_q * N;
+    return round256(rows * d * sizeof(float)) + round256(rows * sizeof(float));
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                 size_t workspace_bytes, int B, int H_q, int H_kv, int N, int d, int causal,
+                 float scale, fa_dtype dtype, hipStream_t stream) {
+    const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv, workspace};
+    for (const void* p : ptrs)
+        if (!p || !aligned16(p)) return FA_ERR_INVALID_ARG;
+    if (!sizes_ok(B, H_q, H_kv, N)) return FA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype)) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    const size_t need = fa_bwd_workspace_size(B, H_q, H_kv, N, d, dtype);
+    if (workspace_bytes < need) return FA_ERR_INVALID_ARG;
+
+    const size_t rows = (size_t)B * H_q * N;
+    fa355::BwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    a.dq_acc = static_cast<float*>(workspace);
+    a.delta = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
+                                       round256(rows * d * sizeof(float)));
+    a.B = B; a.Hq = H_q; a.Hkv = H_kv; a.N = N; a.d = d;
+    a.causal = causal;
+    a.scale = scale;
+    a.cl2 = scale * kLog2eHost;
+    a.dtype = (int)dtype;
+    a.stream = stream;
+    return fa355::launch_bwd(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+const char* fa_status_string(fa_status s) {
+    switch (s) {
+        case FA_OK: return "FA_OK: success";
+        case FA_ERR_INVALID_ARG:
+            return "FA_ERR_INVALID_ARG: null or misaligned pointer, bad size, flag or scale, "
+                   "or workspace too small";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dim or dtype not built";
+        case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime refused a kernel launch";
+    }
+    return "unknown fa_status";
+}
+
+int fa_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,124 @@
+// Device-side helpers shared by the libfa355 kernels (gfx950 / CDNA4 only).
+//
+// Matrix-core conventions used throughout (one 64-lane wavefront; lane l,
+// l32 = l % 32, hi = l / 32):
+//
+//   v_mfma_f32_32x32x16_{bf16,f16}:  D[32x32] += A[32x16] * B[16x32]
+//     A operand: lane l holds A[l32][8*hi .. 8*hi+7]      (8 x 16-bit)
+//     B operand: lane l holds B[8*hi .. 8*hi+7][l32]      (8 x 16-bit)
+//     D / C    : lane l, register r holds D[row(r, hi)][l32] with
+//                row(r, hi) = 8*(r/4) + 4*hi + (r%4)        (16 x fp32)
+//   v_mfma_f32_32x32x2_f32:          D[32x32] += A[32x2] * B[2x32]
+//     A: lane l holds A[l32][hi];  B: lane l holds B[hi][l32];  D as above.
+//
+// Both operands are contiguous along the contraction index inside a lane,
+// which is what decides every LDS layout in the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa355 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Element-type tags for the 16-bit paths.
+struct BF16 {};
+struct FP16 {};
+
+template <typename T>
+struct Mma;
+
+template <>
+struct Mma<BF16> {
+    static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+    // Two fp32 values -> one dword of two round-to-nearest-even bf16 values.
+    static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+        bf16x2 r;
+        r[0] = (__bf16)lo;
+        r[1] = (__bf16)hi;
+        return __builtin_bit_cast(uint32_t, r);
+    }
+    static __device__ __forceinline__ float to_f32(uint16_t x) {
+        return __uint_as_float(((uint32_t)x) << 16);
+    }
+};
+
+template <>
+struct Mma<FP16> {
+    static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+        f16x2 r;
+        r[0] = (_Float16)lo;
+        r[1] = (_Float16)hi;
+        return __builtin_bit_cast(uint32_t, r);
+    }
+    static __device__ __forceinline__ float to_f32(uint16_t x) {
+        return (float)__builtin_bit_cast(_Float16, x);
+    }
+};
+
+__device__ __forceinline__ f32x16 mma_f32(float a, float b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+    f32x16 z;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = 0.f;
+    return z;
+}
+
+// Row (within a 32x32 accumulator block) held by register r of a lane in
+// half `hi` of the wave.
+__device__ __forceinline__ constexpr int acc_row(int r, int hi) {
+    return 8 * (r >> 2) + 4 * hi + (r & 3);
+}
+
+// Value of lane (l ^ 32): exchange between the two halves of the wave.
+__device__ __forceinline__ float swap_halves(float x) {
+    return __shfl_xor(x, 32, 64);
+}
+
+// Native 2^x (v_exp_f32); exp2(-inf) = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Workgroups are handed to the 8 XCDs of the chip round-robin, and each XCD
+// has its own L2.  Renumber so that XCD x runs a contiguous range of logical
+// blocks: neighbouring logical blocks (same head, same K/V) then share an L2.
+__device__ __forceinline__ int xcd_remap(int pid, int total) {
+    constexpr int kXcd = 8;
+    const int xcd = pid % kXcd;
+    const int local = pid / kXcd;
+    const int per = total / kXcd;
+    const int rem = total % kXcd;
+    return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+}
+
+__device__ __forceinline__ u32x4 ld_global16(const void* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ u32x4 zero_u4() {
+    u32x4 z;
+    z[0] = z[1] = z[2] = z[3] = 0u;
+    return z;
+}
+
+}  // namespace fa355

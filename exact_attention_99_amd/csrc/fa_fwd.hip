@@ -1,0 +1,459 @@
+// Forward pass of exact tiled attention with online softmax, gfx950.
+//
+// One workgroup owns BR = 32 * NW query rows of one (batch, query head); each
+// of its NW waves owns 32 of them.  The workgroup walks the key/value tiles of
+// BC keys in ascending order (causal: only up to its last row), staging each
+// tile in LDS while the previous one is being used ("FlashAttention and the
+// Kernel Era", The Breakthrough: load one block of each of Q, K, V into fast
+// on-chip memory and fold the partial result into a running output).
+//
+// Per tile a wave computes S^T = K Q^T on the matrix cores, so that lane l
+// owns query row l % 32 and holds 16 of its scores per 32-key block; the row
+// maximum is then an in-lane reduction plus one exchange between the two
+// halves of the wave.  The running maximum m and running sum l follow the
+// online-softmax update ("FlashAttention and the Kernel Era", The Mathematics,
+// online-softmax equation; "FlashAttention 1, 2, and 3 Explained", section 2:
+// rescale the accumulated output by e^(m_old - m_new)).  P~^T stays in
+// registers and is directly the B operand of O^T += V^T P~^T.  The output is
+// divided by l once at the end and the natural-log logsumexp is written for
+// the backward pass.
+//
+// Exponentials are taken base 2 with scale * log2(e) folded into one FMA.
+// The running maximum is only moved when a tile's maximum exceeds it by more
+// than kTau (in log2 units): the skipped rescales leave every result exact,
+// because O and l always refer to the same m, and P~ stays below 2^kTau.
+#include "fa_common.h"
+#include "fa_launch.h"
+
+namespace fa355 {
+
+namespace {
+
+constexpr float kTau = 8.0f;
+
+// K tile in LDS: row = key (D 16-bit elements), 16-byte chunk c of row r is
+// stored at chunk c ^ (r & 7) so that the 32 lanes reading one chunk column of
+// 32 consecutive rows spread over all banks.
+template <int D>
+__device__ __forceinline__ int k_off(int row, int chunk) {
+    return row * (D * 2) + ((chunk ^ (row & 7)) << 4);
+}
+
+// V^T tile in LDS: row = head-dim index (BC 16-bit elements, keys in
+// "position" order, see v_key_of_pos), chunk c of row r stored at
+// c ^ ((r ^ (r >> 3)) & 7): conflict-free both for the transposing writes
+// (rows 8 apart) and for the operand reads (consecutive rows).
+template <int BC>
+__device__ __forceinline__ int v_off(int row, int chunk) {
+    return row * (BC * 2) + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
+}
+
+// Keys inside a 16-key group are stored in the order in which the S^T
+// accumulator hands them to the PV product: position 8*h + i (h = lane half,
+// i = 0..7) holds key 4*h + (i & 3) + 8*(i >> 2).
+__device__ __forceinline__ int v_key_of_pos(int h, int i) { return 4 * h + (i & 3) + 8 * (i >> 2); }
+
+// 16-bit inputs (bf16 or fp16), head dim D, NW waves, BC keys per tile.  Half
+// of the waves stage K, the other half stage V transposed; every staging
+// thread moves NCH (4 or 8) 16-byte chunks per tile: NCH chunks of K rows, or
+// an NCH-key x 8-dim block of V that it transposes in registers.
+template <typename T, int D, bool CAUSAL, int NW, int BC>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+             const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
+             int B, int Hq, int Hkv, int N, float cl2) {
+    constexpr int BR = 32 * NW;
+    constexpr int KCH = D / 8;                 // 16-byte chunks per K row
+    constexpr int TILE_BYTES = BC * D * 2;     // one of K or V^T
+    constexpr int STAGE = 2 * TILE_BYTES;
+    constexpr int NKB = BC / 32;               // 32-key blocks per tile
+    constexpr int NKG = BC / 16;               // 16-key groups per tile
+    constexpr int NDB = D / 32;                // 32-wide head-dim blocks
+    constexpr int NKS = D / 16;                // k-steps of QK^T
+    constexpr int LOADERS = NW * 32;           // threads per staging half
+    constexpr int NCH = BC * D / 8 / LOADERS;  // chunks per staging thread
+    static_assert(NCH == 4 || NCH == 8, "staging split");
+    static_assert(BC % 32 == 0 && BC >= 64, "tile width");
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+
+    const int nqb = (N + BR - 1) / BR;
+    const int total = nqb * Hq * B;
+    const int logical = xcd_remap((int)blockIdx.x, total);
+    const int qb_raw = logical % nqb;
+    const int bh = logical / nqb;
+    const int qb = CAUSAL ? (nqb - 1 - qb_raw) : qb_raw;  // longest rows first
+    const int h = bh % Hq;
+    const int b = bh / Hq;
+    const int hk = h / (Hq / Hkv);
+
+    const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
+    const size_t koff = ((size_t)b * Hkv + hk) * (size_t)N * D;
+    const uint16_t* Qh = Q + qoff;
+    const uint16_t* Kh = K + koff;
+    const uint16_t* Vh = V + koff;
+
+    const int q0 = qb * BR;
+    const int qw = q0 + 32 * wave;
+    const int q = qw + l32;
+
+    // Q^T as the B operand: lane holds Q[q][16*ks + 8*hi .. +7].
+    u32x4 qf[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+        qf[ks] = (q < N) ? ld_global16(Qh + (size_t)q * D + 16 * ks + 8 * hi) : zero_u4();
+
+    const int kv_len = CAUSAL ? min(N, q0 + BR) : N;
+    const int ntiles = (kv_len + BC - 1) / BC;
+
+    // ---- staging: global -> registers -> LDS --------------------------------
+    const bool stage_v = wave < NW / 2;
+    const int st = stage_v ? tid : tid - LOADERS;
+    u32x4 stg[NCH];
+
+    auto fetch = [&](int k0) {
+        if (stage_v) {
+            // block (c, position group pg): positions NCH*pg .. NCH*pg+NCH-1
+            const int c = st % KCH;
+            const int pg = st / KCH;
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                const int pos = NCH * pg + i;  // position inside the tile
+                const int key = k0 + 16 * (pos >> 4) + v_key_of_pos((pos >> 3) & 1, pos & 7);
+                stg[i] = key < N ? ld_global16(Vh + (size_t)key * D + 8 * c) : zero_u4();
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                const int ci = st + i * LOADERS;
+                const int key = k0 + ci / KCH;
+                stg[i] = key < N ? ld_global16(Kh + (size_t)key * D + 8 * (ci % KCH)) : zero_u4();
+            }
+        }
+    };
+    auto deposit = [&](int buf) {
+        unsigned char* base = smem + buf * STAGE;
+        if (stage_v) {
+            unsigned char* vt = base + TILE_BYTES;
+            const int c = st % KCH;
+            const int pg = st / KCH;
+            const int chunk = (NCH * pg) >> 3;          // 16-byte chunk of the V^T row
+            const int sub = ((NCH * pg) & 7) * 2;       // byte offset inside it
+            // NCH keys x 8 dims -> 8 rows (dims) of NCH keys.
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int sh = 16 * (e & 1);
+                uint32_t w[NCH / 2];
+#pragma unroll
+                for (int jj = 0; jj < NCH / 2; ++jj) {
+                    const uint32_t x0 = (stg[2 * jj][e >> 1] >> sh) & 0xffffu;
+                    const uint32_t x1 = (stg[2 * jj + 1][e >> 1] >> sh) & 0xffffu;
+                    w[jj] = x0 | (x1 << 16);
+                }
+                unsigned char* dst = vt + v_off<BC>(8 * c + e, chunk) + sub;
+                if constexpr (NCH == 8) {
+                    u32x4 x; x[0] = w[0]; x[1] = w[1]; x[2] = w[2]; x[3] = w[3];
+                    *reinterpret_cast<u32x4*>(dst) = x;
+                } else {
+                    u32x2 x; x[0] = w[0]; x[1] = w[1];
+                    *reinterpret_cast<u32x2*>(dst) = x;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                const int ci = st + i * LOADERS;
+                *reinterpret_cast<u32x4*>(base + k_off<D>(ci / KCH, ci % KCH)) = stg[i];
+            }
+        }
+    };
+
+    // ---- running state ---------------------------------------------------------
+    f32x16 o[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[db] = zero16();
+    float m_s = -INFINITY;  // running max of scale*log2(e)*s
+    float l_s = 0.f;        // this lane's share of the running sum
+
+    fetch(0);
+    deposit(0);
+    __syncthreads();
+
+    for (int j = 0; j < ntiles; ++j) {
+        const int k0 = j * BC;
+        if (j + 1 < ntiles) fetch(k0 + BC);
+
+        const bool active = !CAUSAL || (k0 <= qw + 31);
+        if (active) {
+            const unsigned char* ks_base = smem + (j & 1) * STAGE;
+            const unsigned char* vt_base = ks_base + TILE_BYTES;
+
+            f32x16 s[NKB];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                s[kb] = zero16();
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const u32x4 a = *reinterpret_cast<const u32x4*>(
+                        ks_base + k_off<D>(32 * kb + l32, 2 * ks + hi));
+                    s[kb] = Mma<T>::mma(a, qf[ks], s[kb]);
+                }
+            }
+
+            const bool need_mask = (CAUSAL && (k0 + BC - 1 > qw)) || (k0 + BC > N);
+            if (need_mask) {
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = k0 + 32 * kb + acc_row(r, hi);
+                        if ((CAUSAL && key > q) || key >= N) s[kb][r] = -INFINITY;
+                    }
+            }
+
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+            mx = fmaxf(mx, swap_halves(mx));
+            const float mt = mx * cl2;
+
+            if (__any(mt > m_s + kTau)) {
+                const float mn = fmaxf(m_s, mt);
+                const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m_s - mn);
+                l_s *= alpha;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+                m_s = mn;
+            }
+            const float mu = (m_s == -INFINITY) ? 0.f : m_s;
+
+            u32x4 pb[NKG];
+            float ls = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const float p0 = fast_exp2(fmaf(s[kb][8 * t + 2 * jj], cl2, -mu));
+                        const float p1 = fast_exp2(fmaf(s[kb][8 * t + 2 * jj + 1], cl2, -mu));
+                        ls += p0 + p1;
+                        pb[2 * kb + t][jj] = Mma<T>::pack2(p0, p1);
+                    }
+            l_s += ls;
+
+#pragma unroll
+            for (int kg = 0; kg < NKG; ++kg)
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const u32x4 a = *reinterpret_cast<const u32x4*>(
+                        vt_base + v_off<BC>(32 * db + l32, 2 * kg + hi));
+                    o[db] = Mma<T>::mma(a, pb[kg], o[db]);
+                }
+        }
+
+        if (j + 1 < ntiles) deposit((j + 1) & 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue -----------------------------------------------------------------
+    const float l_tot = l_s + swap_halves(l_s);
+    if (q < N) {
+        const float inv = 1.f / l_tot;
+        uint16_t* Orow = O + qoff + (size_t)q * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                u32x2 w;
+                w[0] = Mma<T>::pack2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
+                w[1] = Mma<T>::pack2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+                *reinterpret_cast<u32x2*>(Orow + 32 * db + 8 * g + 4 * hi) = w;
+            }
+        if (hi == 0) LSE[(size_t)(b * Hq + h) * N + q] = (m_s + __log2f(l_tot)) * kLn2;
+    }
+}
+
+// fp32 inputs: the same walk with the fp32 matrix-core op (32x32x2), P kept in
+// fp32, single-buffered tiles of 32 keys.  Four waves, 128 rows per workgroup.
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256)
+fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+             float* __restrict__ O, float* __restrict__ LSE, int B, int Hq, int Hkv, int N, float cl2) {
+    constexpr int NW = 4;
+    constexpr int BR = 32 * NW;
+    constexpr int BC = 32;
+    constexpr int KS = D + 1;  // padded K row (column reads)
+    constexpr int NDB = D / 32;
+    __shared__ float Ks[BC * KS];
+    __shared__ float Vs[BC * D];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+
+    const int nqb = (N + BR - 1) / BR;
+    const int total = nqb * Hq * B;
+    const int logical = xcd_remap((int)blockIdx.x, total);
+    const int qb_raw = logical % nqb;
+    const int bh = logical / nqb;
+    const int qb = CAUSAL ? (nqb - 1 - qb_raw) : qb_raw;
+    const int h = bh % Hq;
+    const int b = bh / Hq;
+    const int hk = h / (Hq / Hkv);
+    const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
+    const size_t koff = ((size_t)b * Hkv + hk) * (size_t)N * D;
+
+    const int q0 = qb * BR;
+    const int qw = q0 + 32 * wave;
+    const int q = qw + l32;
+
+    float qf[D / 2];
+#pragma unroll
+    for (int ks = 0; ks < D / 2; ++ks) qf[ks] = (q < N) ? Q[qoff + (size_t)q * D + 2 * ks + hi] : 0.f;
+
+    f32x16 o[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[db] = zero16();
+    float m_s = -INFINITY, l_s = 0.f;
+
+    const int kv_len = CAUSAL ? min(N, q0 + BR) : N;
+    for (int k0 = 0; k0 < kv_len; k0 += BC) {
+        __syncthreads();
+        for (int i = tid; i < BC * D; i += 256) {
+            const int r = i / D, c = i % D;
+            const int key = k0 + r;
+            const float kv = key < N ? K[koff + (size_t)key * D + c] : 0.f;
+            const float vv = key < N ? V[koff + (size_t)key * D + c] : 0.f;
+            Ks[r * KS + c] = kv;
+            Vs[r * D + c] = vv;
+        }
+        __syncthreads();
+        if (CAUSAL && k0 > qw + 31) continue;
+
+        f32x16 s = zero16();
+#pragma unroll 8
+        for (int ks = 0; ks < D / 2; ++ks) s = mma_f32(Ks[l32 * KS + 2 * ks + hi], qf[ks], s);
+
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = k0 + acc_row(r, hi);
+            if ((CAUSAL && key > q) || key >= N) s[r] = -INFINITY;
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+        mx = fmaxf(mx, swap_halves(mx));
+        const float mt = mx * cl2;
+        if (__any(mt > m_s + kTau)) {
+            const float mn = fmaxf(m_s, mt);
+            const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m_s - mn);
+            l_s *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+            m_s = mn;
+        }
+        const float mu = (m_s == -INFINITY) ? 0.f : m_s;
+        float p[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            p[r] = fast_exp2(fmaf(s[r], cl2, -mu));
+            l_s += p[r];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                o[db] = mma_f32(Vs[acc_row(r, hi) * D + 32 * db + l32], p[r], o[db]);
+    }
+
+    const float l_tot = l_s + swap_halves(l_s);
+    if (q < N) {
+        const float inv = 1.f / l_tot;
+        float* Orow = O + qoff + (size_t)q * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                f32x4 w;
+                for (int i = 0; i < 4; ++i) w[i] = o[db][4 * g + i] * inv;
+                *reinterpret_cast<f32x4*>(Orow + 32 * db + 8 * g + 4 * hi) = w;
+            }
+        if (hi == 0) LSE[(size_t)(b * Hq + h) * N + q] = (m_s + __log2f(l_tot)) * kLn2;
+    }
+}
+
+template <typename T, int D, bool CAUSAL, int NW, int BC>
+hipError_t launch16(const FwdArgs& a) {
+    constexpr int BR = 32 * NW;
+    const int nqb = (a.N + BR - 1) / BR;
+    const long long total = (long long)nqb * a.Hq * a.B;
+    hipLaunchKernelGGL((fwd16_kernel<T, D, CAUSAL, NW, BC>), dim3((unsigned)total), dim3(NW * 64), 0,
+                       a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.N, a.cl2);
+    return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch32(const FwdArgs& a) {
+    const int nqb = (a.N + 127) / 128;
+    const long long total = (long long)nqb * a.Hq * a.B;
+    hipLaunchKernelGGL((fwd32_kernel<D, CAUSAL>), dim3((unsigned)total), dim3(256), 0, a.stream,
+                       (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse,
+                       a.B, a.Hq, a.Hkv, a.N, a.cl2);
+    return hipGetLastError();
+}
+
+// Tile variants (waves per workgroup, keys per tile); variant 0 is the default.
+template <typename T, int D, bool CAUSAL>
+hipError_t dispatch16c(const FwdArgs& a) {
+    if constexpr (D == 128) {
+        switch (a.fwd_variant) {
+            case 1: return launch16<T, D, CAUSAL, 4, 64>(a);
+            case 2: return launch16<T, D, CAUSAL, 8, 128>(a);
+            default: return launch16<T, D, CAUSAL, 8, 64>(a);
+        }
+    } else {
+        switch (a.fwd_variant) {
+            case 1: return launch16<T, D, CAUSAL, 4, 64>(a);
+            case 2: return launch16<T, D, CAUSAL, 4, 128>(a);
+            default: return launch16<T, D, CAUSAL, 8, 128>(a);
+        }
+    }
+}
+
+template <typename T, int D>
+hipError_t dispatch16(const FwdArgs& a) {
+    return a.causal ? dispatch16c<T, D, true>(a) : dispatch16c<T, D, false>(a);
+}
+
+template <int D>
+hipError_t dispatch32(const FwdArgs& a) {
+    return a.causal ? launch32<D, true>(a) : launch32<D, false>(a);
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdArgs& a) {
+    switch (a.dtype) {
+        case 2: return a.d == 64 ? dispatch16<BF16, 64>(a) : dispatch16<BF16, 128>(a);
+        case 1: return a.d == 64 ? dispatch16<FP16, 64>(a) : dispatch16<FP16, 128>(a);
+        default: return a.d == 64 ? dispatch32<64>(a) : dispatch32<128>(a);
+    }
+}
+
+}  // namespace fa355

@@ -1,0 +1,46 @@
+// Internal launch interface between the C-ABI entry points and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa355 {
+
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int B, Hq, Hkv, N, d;
+    int causal;
+    float cl2;       // scale * log2(e)
+    int dtype;       // fa_dtype value
+    int fwd_variant; // tile variant of the 16-bit kernel (0 = default)
+    hipStream_t stream;
+};
+
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const float* lse;
+    const void* dout;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dq_acc;   // [B, Hq, N, d] float32 workspace
+    float* delta;    // [B, Hq, N] float32 workspace
+    int B, Hq, Hkv, N, d;
+    int causal;
+    float scale;
+    float cl2;
+    int dtype;
+    hipStream_t stream;
+};
+
+hipError_t launch_fwd(const FwdArgs& a);
+hipError_t launch_bwd(const BwdArgs& a);
+
+}  // namespace fa355

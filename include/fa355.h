@@ -1,0 +1,121 @@
+/*
+ * libfa355 -- exact tiled scaled-dot-product attention with online softmax
+ * (FlashAttention) for AMD Instinct MI355X (gfx950), forward and backward.
+ *
+ * What is computed (all pages agree that the tiled method returns the plain
+ * definition up to rounding: "FlashAttention and the Kernel Era", The
+ * Mathematics, SDPA equation; "FlashAttention 1, 2, and 3 Explained",
+ * section 1):
+ *
+ *     S = scale * Q K^T   (key j hidden from query i when causal and j > i)
+ *     P = softmax(S) row by row,   O = P V,   lse_i = ln sum_j exp(S_ij)
+ *
+ * computed block by block without forming the N x N matrices (running row
+ * max and row sum with rescaling of the output accumulator: "FlashAttention
+ * and the Kernel Era", The Mathematics, online-softmax equation; "FlashAttention
+ * 1, 2, and 3 Explained", section 2), and the backward pass rebuilds P from
+ * Q, K and the saved lse instead of storing it ("FlashAttention Kernel"
+ * glossary, Recomputation bullet).
+ *
+ * Layouts (row-major, densely packed, no strides):
+ *   q, o, dout, dq : [B, H_q,  N, d]
+ *   k, v, dk, dv   : [B, H_kv, N, d]
+ *   lse            : [B, H_q,  N] float32, natural log
+ * Query head h reads K/V head h / (H_q / H_kv) (grouped-query / multi-query
+ * attention, "FlashAttention" glossary, KV-cache paragraph).  All of q, k, v,
+ * o, dout, dq, dk, dv share one element type `dtype`.
+ *
+ * Ownership: every pointer is a device pointer owned by the caller; the
+ * library allocates no device memory and keeps no pointer after a call
+ * returns.  Inputs are only read.  Outputs must not overlap inputs or each
+ * other.  Every buffer must be 16-byte aligned.
+ *
+ * Timing and errors: calls enqueue work on `stream` and return without
+ * synchronising.  Argument errors are reported synchronously and nothing is
+ * enqueued.  A failed launch returns FA_ERR_HIP.  Faults inside a kernel
+ * surface at the caller's next synchronisation.  No C++ exception crosses
+ * this interface.
+ */
+#ifndef FA355_H
+#define FA355_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, bad flag, small workspace */
+    FA_ERR_UNSUPPORTED = 2, /* head dim or dtype this build has no kernel for */
+    FA_ERR_HIP = 3          /* the HIP runtime refused a launch */
+} fa_status;
+
+typedef enum {
+    FA_DTYPE_FP32 = 0,
+    FA_DTYPE_FP16 = 1,
+    FA_DTYPE_BF16 = 2
+} fa_dtype;
+
+/*
+ * Forward pass: O = softmax(scale * Q K^T [causal]) V and lse.
+ *
+ *   q, k, v   in : see layouts above.
+ *   o         out: [B, H_q, N, d], dtype.
+ *   lse       out: [B, H_q, N] float32, ln sum_j exp(scale * q_i . k_j) over
+ *                  the keys visible to row i.
+ *   B, H_q, H_kv, N >= 1; H_q % H_kv == 0; d in {64, 128}.
+ *   causal in {0, 1}: when 1, key j is visible to query i iff j <= i.
+ *   scale: finite; the pages' equation uses 1 / sqrt(d).
+ * Needs no workspace: memory beyond the inputs and outputs is O(1)
+ * ("FlashAttention Kernel" glossary: memory drops from O(N^2) to O(N)).
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v,
+                 void* o, float* lse,
+                 int B, int H_q, int H_kv, int N, int d,
+                 int causal, float scale, fa_dtype dtype, hipStream_t stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for these sizes: a float32 dQ
+ * accumulator [B, H_q, N, d] and the float32 row terms D_i = sum_k dO_ik O_ik
+ * [B, H_q, N], each rounded up to 256 bytes.  Returns 0 for invalid sizes.
+ * Linear in N.
+ */
+size_t fa_bwd_workspace_size(int B, int H_q, int H_kv, int N, int d, fa_dtype dtype);
+
+/*
+ * Backward pass: gradients of sum(dout * O) with respect to q, k, v.
+ *
+ *   q, k, v, o, lse  in : exactly what fa_fwd took and returned.
+ *   dout             in : [B, H_q, N, d], dtype.
+ *   dq               out: [B, H_q, N, d], dtype.
+ *   dk, dv           out: [B, H_kv, N, d], dtype; for grouped heads each is
+ *                         the sum over the H_q / H_kv query heads reading it.
+ *   workspace        scratch of at least fa_bwd_workspace_size() bytes,
+ *                    owned by the caller; contents on entry are ignored and
+ *                    on return are unspecified.
+ * P is rebuilt per tile from q, k and lse ("FlashAttention Kernel" glossary,
+ * Recomputation bullet); dQ is accumulated in float32 across key blocks.
+ * Two calls may differ in the last bits of dq (the order of float32
+ * additions into the accumulator is not fixed).
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v,
+                 const void* o, const float* lse, const void* dout,
+                 void* dq, void* dk, void* dv,
+                 void* workspace, size_t workspace_bytes,
+                 int B, int H_q, int H_kv, int N, int d,
+                 int causal, float scale, fa_dtype dtype, hipStream_t stream);
+
+/* Static, never-NULL description of a status code. */
+const char* fa_status_string(fa_status s);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA355_H */

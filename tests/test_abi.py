@@ -1,0 +1,116 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol,
+and rejects bad arguments before touching the device."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_attention_99_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa355.h")
+
+INVALID, UNSUPPORTED = 1, 2
+FP32, FP16, BF16 = 0, 1, 2
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(fa_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _abi.load_library()
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd",
+                                    "fa_status_string", "fa_version"]
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    raw = ctypes.CDLL(_abi.lib_path())
+    for name in declared_functions():
+        getattr(raw, name)
+
+
+def test_version_and_status_strings(lib):
+    assert _abi.fa_version() == 100
+    for code in range(4):
+        s = _abi.fa_status_string(code)
+        assert s.startswith(_abi.STATUS[code])
+    assert _abi.fa_status_string(99) == "unknown fa_status"
+
+
+def test_workspace_size_is_linear_in_N(lib):
+    def ws(N):
+        return _abi.fa_bwd_workspace_size(2, 8, 2, N, 128, "bf16")
+    rows = 2 * 8 * 4096
+    assert ws(4096) == rows * 128 * 4 + rows * 4
+    assert ws(8192) == 2 * ws(4096)
+    assert _abi.fa_bwd_workspace_size(1, 1, 1, 1, 64, "fp32") == 256 + 256
+    # invalid sizes give 0
+    assert _abi.fa_bwd_workspace_size(1, 3, 2, 16, 64, "bf16") == 0
+    assert _abi.fa_bwd_workspace_size(1, 1, 1, 0, 64, "bf16") == 0
+    assert _abi.fa_bwd_workspace_size(1, 1, 1, 16, 96, "bf16") == 0
+
+
+# Fake device addresses: argument checks run before any device access, and
+# every call below is rejected by them.
+A = 1 << 20          # 16-byte aligned
+MIS = A + 8          # misaligned
+
+
+def fwd(lib, q=A, k=A, v=A, o=A, lse=A, B=1, Hq=2, Hkv=1, N=16, d=64, causal=0, scale=0.125,
+        dtype=BF16):
+    return lib.fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, None)
+
+
+def bwd(lib, ws_bytes=1 << 30, d=64, N=16, causal=0, scale=0.125, dtype=BF16, B=1, Hq=2, Hkv=1,
+        ptrs=None):
+    p = ptrs or [A] * 10
+    return lib.fa_bwd(*p[:9], p[9], ws_bytes, B, Hq, Hkv, N, d, causal, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"q": None}, INVALID), ({"k": None}, INVALID), ({"v": None}, INVALID),
+    ({"o": None}, INVALID), ({"lse": None}, INVALID),
+    ({"q": MIS}, INVALID), ({"o": MIS}, INVALID), ({"lse": MIS}, INVALID),
+    ({"B": 0}, INVALID), ({"Hq": 0}, INVALID), ({"Hkv": 0}, INVALID), ({"N": 0}, INVALID),
+    ({"N": -5}, INVALID), ({"Hq": 3, "Hkv": 2}, INVALID), ({"causal": 2}, INVALID),
+    ({"scale": float("nan")}, INVALID), ({"scale": float("inf")}, INVALID),
+    ({"scale": 0.0}, INVALID), ({"scale": -0.1}, INVALID),
+    ({"dtype": 7}, INVALID), ({"d": 96}, UNSUPPORTED), ({"d": 256}, UNSUPPORTED),
+])
+def test_fwd_rejects(lib, kw, code):
+    assert fwd(lib, **kw) == code
+
+
+def test_bwd_rejects(lib):
+    assert bwd(lib, ptrs=[A] * 9 + [None]) == INVALID
+    for i in range(10):
+        p = [A] * 10
+        p[i] = None
+        assert bwd(lib, ptrs=p) == INVALID
+        p[i] = MIS
+        assert bwd(lib, ptrs=p) == INVALID
+    need = _abi.fa_bwd_workspace_size(1, 2, 1, 16, 64, "bf16")
+    assert bwd(lib, ws_bytes=need - 1) == INVALID
+    assert bwd(lib, d=80) == UNSUPPORTED
+    assert bwd(lib, causal=-1) == INVALID
+    assert bwd(lib, scale=float("nan")) == INVALID
+    assert bwd(lib, Hq=4, Hkv=3) == INVALID
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setenv("FA355_LIB", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_abi, "_lib", None)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        _abi.load_library()
