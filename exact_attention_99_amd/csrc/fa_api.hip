@@ -65,7 +65,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 size_t fa_bwd_workspace_size(int B, int H_q, int H_kv, int N, int d, fa_dtype dtype) {
     if (!sizes_ok(B, H_q, H_kv, N) || !dtype_ok(dtype) || (d != 64 && d != 128)) return 0;
     const size_t rows = (size_t)B * H_q * N;
-    return round256(rows * d * sizeof(float)) + round256(rows * sizeof(float));
+    return round256(rows * sizeof(float));
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -83,13 +83,10 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
     const size_t need = fa_bwd_workspace_size(B, H_q, H_kv, N, d, dtype);
     if (workspace_bytes < need) return FA_ERR_INVALID_ARG;
 
-    const size_t rows = (size_t)B * H_q * N;
     fa355::BwdArgs a;
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
     a.dq = dq; a.dk = dk; a.dv = dv;
-    a.dq_acc = static_cast<float*>(workspace);
-    a.delta = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
-                                       round256(rows * d * sizeof(float)));
+    a.delta = static_cast<float*>(workspace);
     a.B = B; a.Hq = H_q; a.Hkv = H_kv; a.N = N; a.d = d;
     a.causal = causal;
     a.scale = scale;

@@ -1,7 +1,741 @@
-// Backward pass (placeholder until the kernels land).
+// Backward pass of exact tiled attention with recomputation, gfx950.
+//
+// Gradients of sum(dO * O) for O = softmax(scale * Q K^T [causal]) V.  The
+// pages state only that the backward pass rebuilds the attention matrix from
+// Q, K, V and the saved softmax statistics instead of storing it
+// ("FlashAttention Kernel" glossary, Recomputation bullet; "FlashAttention"
+// glossary, recomputation paragraph); the gradient formulas are the chain
+// rule through O = P V and the row-wise softmax:
+//
+//   D_i = sum_k dO_ik O_ik          P = exp(scale * Q K^T - lse)
+//   dP  = dO V^T                    dS = P * (dP - D)
+//   dV  = P^T dO     dK = scale * dS^T Q     dQ = scale * dS K
+//
+// Three launches on the caller's stream:
+//   1. delta:  D_i for every query row (memory bound, one pass over O, dO).
+//   2. dkdv:   one workgroup per block of 128 keys of one K/V head; each wave
+//              owns 32 keys and keeps their dK^T, dV^T in fp32 registers while
+//              it walks all query blocks of every query head of the group
+//              (the key-block-outer order of the "FlashAttention Kernel"
+//              glossary's Tiling bullet).  Scores are formed as S = Q K^T so
+//              that a lane owns one key: P and dS are then directly the B
+//              operands of dV^T += dO^T P and dK^T += Q^T dS.
+//   3. dq:     one workgroup per block of query rows (query-outer, like the
+//              forward pass); S^T = K Q^T and dP^T = V dO^T give a lane one
+//              query, and dS^T is directly the B operand of dQ^T += K^T dS^T.
+// P and dP are thus formed twice (once per pass), which replaces fp32 atomic
+// accumulation of dQ across key blocks; every result is written exactly once.
 #include "fa_common.h"
 #include "fa_launch.h"
 
 namespace fa355 {
-hipError_t launch_bwd(const BwdArgs&) { return hipErrorNotSupported; }
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// D_i = sum_k dO_ik O_ik, fp32 accumulation.  D/8 (16-bit) or D/4 (fp32)
+// lanes share a row and reduce with cross-lane adds.
+template <typename T, int D>
+__global__ void __launch_bounds__(256)
+delta16_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
+               float* __restrict__ Delta, long long rows) {
+    constexpr int LPR = D / 8;
+    constexpr int RPB = 256 / LPR;
+    const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
+    const int c = threadIdx.x % LPR;
+    float acc = 0.f;
+    if (row < rows) {
+        const u32x4 a = ld_global16(O + row * D + 8 * c);
+        const u32x4 g = ld_global16(dO + row * D + 8 * c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc = fmaf(Mma<T>::to_f32(a[i] & 0xffffu), Mma<T>::to_f32(g[i] & 0xffffu), acc);
+            acc = fmaf(Mma<T>::to_f32(a[i] >> 16), Mma<T>::to_f32(g[i] >> 16), acc);
+        }
+    }
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (row < rows && c == 0) Delta[row] = acc;
+}
+
+template <int D>
+__global__ void __launch_bounds__(256)
+delta32_kernel(const float* __restrict__ O, const float* __restrict__ dO, float* __restrict__ Delta,
+               long long rows) {
+    constexpr int LPR = D / 4;
+    constexpr int RPB = 256 / LPR;
+    const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
+    const int c = threadIdx.x % LPR;
+    float acc = 0.f;
+    if (row < rows) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(O + row * D + 4 * c);
+        const f32x4 g = *reinterpret_cast<const f32x4*>(dO + row * D + 4 * c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = fmaf(a[i], g[i], acc);
+    }
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (row < rows && c == 0) Delta[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV for 16-bit inputs.  Four waves, 128 keys per workgroup, BQ query rows
+// per step (32 for D = 128, 64 for D = 64), double-buffered in LDS:
+//   Qs, dOs : row-major, swizzled (A operands of S = Q K^T and dP = dO V^T)
+//   Qt, dOt : transposed, query rows in "position" order, rows padded by 16 B
+//             (A operands of dK^T += Q^T dS and dV^T += dO^T P)
+//   lse2, dl: log2(e) * lse and D of the step's rows.
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(256)
+dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+              const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+              const float* __restrict__ LSE, const float* __restrict__ Delta,
+              uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int B, int Hq, int Hkv, int N,
+              float cl2, float scale) {
+    constexpr int BKV = 128;
+    constexpr int BQ = D == 128 ? 32 : 64;
+    constexpr int NQB = BQ / 32;
+    constexpr int KCH = D / 8;
+    constexpr int QR = BQ * KCH / 256;        // query rows staged per thread (pairs)
+    static_assert(QR == 2, "each staging thread moves one pair of rows");
+    constexpr int TROW = BQ * 2 + 16;         // padded transposed row, bytes
+    constexpr int TRM = BQ * D * 2;
+    constexpr int TT = D * TROW;
+    constexpr int OFF_DOS = TRM;
+    constexpr int OFF_QT = 2 * TRM;
+    constexpr int OFF_DOT = 2 * TRM + TT;
+    constexpr int OFF_LSE = 2 * TRM + 2 * TT;
+    constexpr int OFF_DL = OFF_LSE + BQ * 4;
+    constexpr int STAGE = OFF_DL + BQ * 4;
+    constexpr int NDB = D / 32;
+    constexpr int NKS = D / 16;
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+
+    const int nkb = (N + BKV - 1) / BKV;
+    const int total = nkb * Hkv * B;
+    const int logical = xcd_remap((int)blockIdx.x, total);
+    const int jb = logical % nkb;  // ascending: under a causal mask block 0 is the longest
+    const int bhk = logical / nkb;
+    const int hk = bhk % Hkv;
+    const int b = bhk / Hkv;
+    const int G = Hq / Hkv;
+
+    const int kv0 = jb * BKV;
+    const int kw = kv0 + 32 * wave;
+    const int key = kw + l32;
+    const size_t kvoff = ((size_t)b * Hkv + hk) * (size_t)N * D;
+
+    // K^T, V^T as B operands: lane holds K[key][16*ks + 8*hi .. +7].
+    u32x4 kf[NKS], vf[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        kf[ks] = key < N ? ld_global16(K + kvoff + (size_t)key * D + 16 * ks + 8 * hi) : zero_u4();
+        vf[ks] = key < N ? ld_global16(V + kvoff + (size_t)key * D + 16 * ks + 8 * hi) : zero_u4();
+    }
+
+    f32x16 dkt[NDB], dvt[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        dkt[db] = zero16();
+        dvt[db] = zero16();
+    }
+
+    const int qb_first = CAUSAL ? kv0 / BQ : 0;
+    const int qb_count = (N + BQ - 1) / BQ - qb_first;
+    const int nsteps = G * qb_count;
+
+    // staging: thread -> (chunk c, row pair rp)
+    const int sc = tid % KCH;
+    const int rp = tid / KCH;
+    u32x4 sq[2], sdo[2];
+    float sx = 0.f;
+
+    auto step_rows = [&](int s, int& h, int& q0) {
+        h = hk * G + s / qb_count;
+        q0 = (qb_first + s % qb_count) * BQ;
+    };
+    auto fetch = [&](int s) {
+        int h, q0;
+        step_rows(s, h, q0);
+        const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int q = q0 + 2 * rp + i;
+            sq[i] = q < N ? ld_global16(Q + qoff + (size_t)q * D + 8 * sc) : zero_u4();
+            sdo[i] = q < N ? ld_global16(dO + qoff + (size_t)q * D + 8 * sc) : zero_u4();
+        }
+        const size_t roff = ((size_t)b * Hq + h) * (size_t)N;
+        if (tid < BQ) {
+            const int q = q0 + tid;
+            sx = q < N ? LSE[roff + q] * kLog2e : 0.f;
+        } else if (tid < 2 * BQ) {
+            const int q = q0 + tid - BQ;
+            sx = q < N ? Delta[roff + q] : 0.f;
+        }
+    };
+    auto deposit = [&](int buf) {
+        unsigned char* base = smem + buf * STAGE;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            *reinterpret_cast<u32x4*>(base + k_off<D>(2 * rp + i, sc)) = sq[i];
+            *reinterpret_cast<u32x4*>(base + OFF_DOS + k_off<D>(2 * rp + i, sc)) = sdo[i];
+        }
+        const int r0 = 2 * rp;
+        const int tcol = (16 * (r0 >> 4) + pos_of_elem(r0 & 15)) * 2;  // byte column
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int sh = 16 * (e & 1);
+            const uint32_t wq = ((sq[0][e >> 1] >> sh) & 0xffffu) | (((sq[1][e >> 1] >> sh) & 0xffffu) << 16);
+            const uint32_t wd = ((sdo[0][e >> 1] >> sh) & 0xffffu) | (((sdo[1][e >> 1] >> sh) & 0xffffu) << 16);
+            *reinterpret_cast<uint32_t*>(base + OFF_QT + (8 * sc + e) * TROW + tcol) = wq;
+            *reinterpret_cast<uint32_t*>(base + OFF_DOT + (8 * sc + e) * TROW + tcol) = wd;
+        }
+        if (tid < BQ)
+            reinterpret_cast<float*>(base + OFF_LSE)[tid] = sx;
+        else if (tid < 2 * BQ)
+            reinterpret_cast<float*>(base + OFF_DL)[tid - BQ] = sx;
+    };
+
+    if (nsteps > 0) {
+        fetch(0);
+        deposit(0);
+    }
+    __syncthreads();
+
+    for (int s = 0; s < nsteps; ++s) {
+        if (s + 1 < nsteps) fetch(s + 1);
+        int h, q0;
+        step_rows(s, h, q0);
+        const bool active = !CAUSAL || (q0 + BQ - 1 >= kw);
+        if (active) {
+            const unsigned char* base = smem + (s & 1) * STAGE;
+            const float* lse2s = reinterpret_cast<const float*>(base + OFF_LSE);
+            const float* dls = reinterpret_cast<const float*>(base + OFF_DL);
+#pragma unroll
+            for (int qs = 0; qs < NQB; ++qs) {
+                f32x16 sacc = zero16(), dpacc = zero16();
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const u32x4 aq = *reinterpret_cast<const u32x4*>(base + k_off<D>(32 * qs + l32, 2 * ks + hi));
+                    const u32x4 ad = *reinterpret_cast<const u32x4*>(base + OFF_DOS + k_off<D>(32 * qs + l32, 2 * ks + hi));
+                    sacc = Mma<T>::mma(aq, kf[ks], sacc);
+                    dpacc = Mma<T>::mma(ad, vf[ks], dpacc);
+                }
+                u32x4 pb[2], dsb[2];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + 32 * qs + 8 * g + 4 * hi);
+                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + 32 * qs + 8 * g + 4 * hi);
+                    float pv[4], dv[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = 4 * g + i;
+                        const int q = q0 + 32 * qs + acc_row(r, hi);
+                        const bool vis = (!CAUSAL || key <= q) && q < N && key < N;
+                        const float p = vis ? fast_exp2(fmaf(sacc[r], cl2, -l4[i])) : 0.f;
+                        pv[i] = p;
+                        dv[i] = p * (dpacc[r] - d4[i]);
+                    }
+                    // registers 4g..4g+3 -> dwords (g & 1) * 2 + {0, 1} of operand g >> 1
+                    pb[g >> 1][(g & 1) * 2 + 0] = Mma<T>::pack2(pv[0], pv[1]);
+                    pb[g >> 1][(g & 1) * 2 + 1] = Mma<T>::pack2(pv[2], pv[3]);
+                    dsb[g >> 1][(g & 1) * 2 + 0] = Mma<T>::pack2(dv[0], dv[1]);
+                    dsb[g >> 1][(g & 1) * 2 + 1] = Mma<T>::pack2(dv[2], dv[3]);
+                }
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        const int off = (32 * db + l32) * TROW + (2 * (2 * qs + t) + hi) * 16;
+                        const u32x4 ado = *reinterpret_cast<const u32x4*>(base + OFF_DOT + off);
+                        const u32x4 aqt = *reinterpret_cast<const u32x4*>(base + OFF_QT + off);
+                        dvt[db] = Mma<T>::mma(ado, pb[t], dvt[db]);
+                        dkt[db] = Mma<T>::mma(aqt, dsb[t], dkt[db]);
+                    }
+            }
+        }
+        if (s + 1 < nsteps) deposit((s + 1) & 1);
+        __syncthreads();
+    }
+
+    if (key < N) {
+        uint16_t* dkrow = dK + kvoff + (size_t)key * D;
+        uint16_t* dvrow = dV + kvoff + (size_t)key * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                u32x2 wk, wv;
+                wk[0] = Mma<T>::pack2(dkt[db][4 * g] * scale, dkt[db][4 * g + 1] * scale);
+                wk[1] = Mma<T>::pack2(dkt[db][4 * g + 2] * scale, dkt[db][4 * g + 3] * scale);
+                wv[0] = Mma<T>::pack2(dvt[db][4 * g], dvt[db][4 * g + 1]);
+                wv[1] = Mma<T>::pack2(dvt[db][4 * g + 2], dvt[db][4 * g + 3]);
+                *reinterpret_cast<u32x2*>(dkrow + 32 * db + 8 * g + 4 * hi) = wk;
+                *reinterpret_cast<u32x2*>(dvrow + 32 * db + 8 * g + 4 * hi) = wv;
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ for 16-bit inputs.  Four waves, 128 query rows per workgroup (32 per
+// wave, one per lane), BC keys per tile staged three ways: K and V row-major
+// (A operands of S^T = K Q^T, dP^T = V dO^T) and K transposed in position
+// order (A operand of dQ^T += K^T dS^T).
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(256)
+dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+            const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+            const float* __restrict__ LSE, const float* __restrict__ Delta,
+            uint16_t* __restrict__ dQ, int B, int Hq, int Hkv, int N, float cl2, float scale) {
+    constexpr int NW = 4;
+    constexpr int BR = 32 * NW;
+    constexpr int BC = D == 128 ? 64 : 128;
+    constexpr int KCH = D / 8;
+    constexpr int TB = BC * D * 2;
+    constexpr int STAGE = 3 * TB;
+    constexpr int NKB = BC / 32;
+    constexpr int NKG = BC / 16;
+    constexpr int NDB = D / 32;
+    constexpr int NKS = D / 16;
+    constexpr int ROWS = BC * KCH / 256;      // key rows staged per thread, at one chunk
+    static_assert(ROWS == 4, "staging split");
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+
+    const int nqb = (N + BR - 1) / BR;
+    const int total = nqb * Hq * B;
+    const int logical = xcd_remap((int)blockIdx.x, total);
+    const int qb_raw = logical % nqb;
+    const int bh = logical / nqb;
+    const int qb = CAUSAL ? (nqb - 1 - qb_raw) : qb_raw;
+    const int h = bh % Hq;
+    const int b = bh / Hq;
+    const int hk = h / (Hq / Hkv);
+
+    const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
+    const size_t koff = ((size_t)b * Hkv + hk) * (size_t)N * D;
+    const uint16_t* Kh = K + koff;
+    const uint16_t* Vh = V + koff;
+
+    const int q0 = qb * BR;
+    const int qw = q0 + 32 * wave;
+    const int q = qw + l32;
+
+    u32x4 qf[NKS], dof[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        qf[ks] = q < N ? ld_global16(Q + qoff + (size_t)q * D + 16 * ks + 8 * hi) : zero_u4();
+        dof[ks] = q < N ? ld_global16(dO + qoff + (size_t)q * D + 16 * ks + 8 * hi) : zero_u4();
+    }
+    const size_t roff = ((size_t)b * Hq + h) * (size_t)N;
+    const float lse2 = q < N ? LSE[roff + q] * kLog2e : 0.f;
+    const float dlt = q < N ? Delta[roff + q] : 0.f;
+
+    const int kv_len = CAUSAL ? min(N, q0 + BR) : N;
+    const int ntiles = (kv_len + BC - 1) / BC;
+
+    const int sc = tid % KCH;
+    const int pg = tid / KCH;  // positions ROWS*pg .. ROWS*pg + ROWS - 1
+    u32x4 sk[ROWS], sv[ROWS];
+
+    auto key_of = [&](int i) {
+        const int pos = ROWS * pg + i;
+        return 16 * (pos >> 4) + v_key_of_pos((pos >> 3) & 1, pos & 7);
+    };
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < ROWS; ++i) {
+            const int kk = k0 + key_of(i);
+            sk[i] = kk < N ? ld_global16(Kh + (size_t)kk * D + 8 * sc) : zero_u4();
+            sv[i] = kk < N ? ld_global16(Vh + (size_t)kk * D + 8 * sc) : zero_u4();
+        }
+    };
+    auto deposit = [&](int buf) {
+        unsigned char* base = smem + buf * STAGE;
+#pragma unroll
+        for (int i = 0; i < ROWS; ++i) {
+            *reinterpret_cast<u32x4*>(base + k_off<D>(key_of(i), sc)) = sk[i];
+            *reinterpret_cast<u32x4*>(base + TB + k_off<D>(key_of(i), sc)) = sv[i];
+        }
+        unsigned char* kt = base + 2 * TB;
+        const int chunk = (ROWS * pg) >> 3;
+        const int sub = ((ROWS * pg) & 7) * 2;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int sh = 16 * (e & 1);
+            u32x2 w;
+            w[0] = ((sk[0][e >> 1] >> sh) & 0xffffu) | (((sk[1][e >> 1] >> sh) & 0xffffu) << 16);
+            w[1] = ((sk[2][e >> 1] >> sh) & 0xffffu) | (((sk[3][e >> 1] >> sh) & 0xffffu) << 16);
+            *reinterpret_cast<u32x2*>(kt + v_off<BC>(8 * sc + e, chunk) + sub) = w;
+        }
+    };
+
+    f32x16 dq[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) dq[db] = zero16();
+
+    fetch(0);
+    deposit(0);
+    __syncthreads();
+
+    for (int j = 0; j < ntiles; ++j) {
+        const int k0 = j * BC;
+        if (j + 1 < ntiles) fetch(k0 + BC);
+        const bool active = !CAUSAL || (k0 <= qw + 31);
+        if (active) {
+            const unsigned char* base = smem + (j & 1) * STAGE;
+            f32x16 st[NKB], dpt[NKB];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                st[kb] = zero16();
+                dpt[kb] = zero16();
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const int off = k_off<D>(32 * kb + l32, 2 * ks + hi);
+                    const u32x4 ak = *reinterpret_cast<const u32x4*>(base + off);
+                    const u32x4 av = *reinterpret_cast<const u32x4*>(base + TB + off);
+                    st[kb] = Mma<T>::mma(ak, qf[ks], st[kb]);
+                    dpt[kb] = Mma<T>::mma(av, dof[ks], dpt[kb]);
+                }
+            }
+            u32x4 dsb[NKG];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        float dsv[2];
+#pragma unroll
+                        for (int u = 0; u < 2; ++u) {
+                            const int r = 8 * t + 2 * jj + u;
+                            const int kk = k0 + 32 * kb + acc_row(r, hi);
+                            const bool vis = (!CAUSAL || kk <= q) && kk < N;
+                            const float p = vis ? fast_exp2(fmaf(st[kb][r], cl2, -lse2)) : 0.f;
+                            dsv[u] = p * (dpt[kb][r] - dlt);
+                        }
+                        dsb[2 * kb + t][jj] = Mma<T>::pack2(dsv[0], dsv[1]);
+                    }
+#pragma unroll
+            for (int kg = 0; kg < NKG; ++kg)
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const u32x4 a = *reinterpret_cast<const u32x4*>(
+                        base + 2 * TB + v_off<BC>(32 * db + l32, 2 * kg + hi));
+                    dq[db] = Mma<T>::mma(a, dsb[kg], dq[db]);
+                }
+        }
+        if (j + 1 < ntiles) deposit((j + 1) & 1);
+        __syncthreads();
+    }
+
+    if (q < N) {
+        uint16_t* row = dQ + qoff + (size_t)q * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                u32x2 w;
+                w[0] = Mma<T>::pack2(dq[db][4 * g] * scale, dq[db][4 * g + 1] * scale);
+                w[1] = Mma<T>::pack2(dq[db][4 * g + 2] * scale, dq[db][4 * g + 3] * scale);
+                *reinterpret_cast<u32x2*>(row + 32 * db + 8 * g + 4 * hi) = w;
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 inputs: the same two passes with the fp32 matrix-core op (32x32x2), P
+// and dS kept in fp32, single-buffered LDS tiles with padded rows.
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256)
+dkdv32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+              const float* __restrict__ dO, const float* __restrict__ LSE,
+              const float* __restrict__ Delta, float* __restrict__ dK, float* __restrict__ dV,
+              int B, int Hq, int Hkv, int N, float cl2, float scale) {
+    constexpr int BKV = 128;
+    constexpr int BQ = 32;
+    constexpr int RS = D + 1;
+    constexpr int NDB = D / 32;
+    __shared__ float Qs[BQ * RS];
+    __shared__ float dOs[BQ * RS];
+    __shared__ float lse2s[BQ];
+    __shared__ float dls[BQ];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+
+    const int nkb = (N + BKV - 1) / BKV;
+    const int total = nkb * Hkv * B;
+    const int logical = xcd_remap((int)blockIdx.x, total);
+    const int jb = logical % nkb;
+    const int bhk = logical / nkb;
+    const int hk = bhk % Hkv;
+    const int b = bhk / Hkv;
+    const int G = Hq / Hkv;
+    const int kv0 = jb * BKV;
+    const int kw = kv0 + 32 * wave;
+    const int key = kw + l32;
+    const size_t kvoff = ((size_t)b * Hkv + hk) * (size_t)N * D;
+
+    float kf[D / 2], vf[D / 2];
+#pragma unroll
+    for (int ks = 0; ks < D / 2; ++ks) {
+        kf[ks] = key < N ? K[kvoff + (size_t)key * D + 2 * ks + hi] : 0.f;
+        vf[ks] = key < N ? V[kvoff + (size_t)key * D + 2 * ks + hi] : 0.f;
+    }
+    f32x16 dkt[NDB], dvt[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        dkt[db] = zero16();
+        dvt[db] = zero16();
+    }
+
+    const int qb_first = CAUSAL ? kv0 / BQ : 0;
+    const int nqb = (N + BQ - 1) / BQ;
+    for (int g = 0; g < G; ++g) {
+        const int h = hk * G + g;
+        const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
+        const size_t roff = ((size_t)b * Hq + h) * (size_t)N;
+        for (int qb = qb_first; qb < nqb; ++qb) {
+            const int q0 = qb * BQ;
+            __syncthreads();
+            for (int i = tid; i < BQ * D; i += 256) {
+                const int r = i / D, c = i % D;
+                const int q = q0 + r;
+                Qs[r * RS + c] = q < N ? Q[qoff + (size_t)q * D + c] : 0.f;
+                dOs[r * RS + c] = q < N ? dO[qoff + (size_t)q * D + c] : 0.f;
+            }
+            if (tid < BQ) {
+                const int q = q0 + tid;
+                lse2s[tid] = q < N ? LSE[roff + q] * kLog2e : 0.f;
+                dls[tid] = q < N ? Delta[roff + q] : 0.f;
+            }
+            __syncthreads();
+            if (CAUSAL && q0 + BQ - 1 < kw) continue;
+
+            f32x16 sacc = zero16(), dpacc = zero16();
+#pragma unroll 8
+            for (int ks = 0; ks < D / 2; ++ks) {
+                sacc = mma_f32(Qs[l32 * RS + 2 * ks + hi], kf[ks], sacc);
+                dpacc = mma_f32(dOs[l32 * RS + 2 * ks + hi], vf[ks], dpacc);
+            }
+            float p[16], ds[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int qr = acc_row(r, hi);
+                const int q = q0 + qr;
+                const bool vis = (!CAUSAL || key <= q) && q < N && key < N;
+                p[r] = vis ? fast_exp2(fmaf(sacc[r], cl2, -lse2s[qr])) : 0.f;
+                ds[r] = p[r] * (dpacc[r] - dls[qr]);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int qr = acc_row(r, hi);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    dvt[db] = mma_f32(dOs[qr * RS + 32 * db + l32], p[r], dvt[db]);
+                    dkt[db] = mma_f32(Qs[qr * RS + 32 * db + l32], ds[r], dkt[db]);
+                }
+            }
+        }
+    }
+
+    if (key < N) {
+        float* dkrow = dK + kvoff + (size_t)key * D;
+        float* dvrow = dV + kvoff + (size_t)key * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                f32x4 wk, wv;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    wk[i] = dkt[db][4 * g + i] * scale;
+                    wv[i] = dvt[db][4 * g + i];
+                }
+                *reinterpret_cast<f32x4*>(dkrow + 32 * db + 8 * g + 4 * hi) = wk;
+                *reinterpret_cast<f32x4*>(dvrow + 32 * db + 8 * g + 4 * hi) = wv;
+            }
+    }
+}
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256)
+dq32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+            const float* __restrict__ dO, const float* __restrict__ LSE,
+            const float* __restrict__ Delta, float* __restrict__ dQ, int B, int Hq, int Hkv, int N,
+            float cl2, float scale) {
+    constexpr int NW = 4;
+    constexpr int BR = 32 * NW;
+    constexpr int BC = 32;
+    constexpr int RS = D + 1;
+    constexpr int NDB = D / 32;
+    __shared__ float Ks[BC * RS];
+    __shared__ float Vs[BC * RS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+
+    const int nqb = (N + BR - 1) / BR;
+    const int total = nqb * Hq * B;
+    const int logical = xcd_remap((int)blockIdx.x, total);
+    const int qb_raw = logical % nqb;
+    const int bh = logical / nqb;
+    const int qb = CAUSAL ? (nqb - 1 - qb_raw) : qb_raw;
+    const int h = bh % Hq;
+    const int b = bh / Hq;
+    const int hk = h / (Hq / Hkv);
+    const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
+    const size_t koff = ((size_t)b * Hkv + hk) * (size_t)N * D;
+    const int q0 = qb * BR;
+    const int qw = q0 + 32 * wave;
+    const int q = qw + l32;
+
+    float qf[D / 2], dof[D / 2];
+#pragma unroll
+    for (int ks = 0; ks < D / 2; ++ks) {
+        qf[ks] = q < N ? Q[qoff + (size_t)q * D + 2 * ks + hi] : 0.f;
+        dof[ks] = q < N ? dO[qoff + (size_t)q * D + 2 * ks + hi] : 0.f;
+    }
+    const size_t roff = ((size_t)b * Hq + h) * (size_t)N;
+    const float lse2 = q < N ? LSE[roff + q] * kLog2e : 0.f;
+    const float dlt = q < N ? Delta[roff + q] : 0.f;
+
+    f32x16 dq[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) dq[db] = zero16();
+
+    const int kv_len = CAUSAL ? min(N, q0 + BR) : N;
+    for (int k0 = 0; k0 < kv_len; k0 += BC) {
+        __syncthreads();
+        for (int i = tid; i < BC * D; i += 256) {
+            const int r = i / D, c = i % D;
+            const int kk = k0 + r;
+            Ks[r * RS + c] = kk < N ? K[koff + (size_t)kk * D + c] : 0.f;
+            Vs[r * RS + c] = kk < N ? V[koff + (size_t)kk * D + c] : 0.f;
+        }
+        __syncthreads();
+        if (CAUSAL && k0 > qw + 31) continue;
+
+        f32x16 st = zero16(), dpt = zero16();
+#pragma unroll 8
+        for (int ks = 0; ks < D / 2; ++ks) {
+            st = mma_f32(Ks[l32 * RS + 2 * ks + hi], qf[ks], st);
+            dpt = mma_f32(Vs[l32 * RS + 2 * ks + hi], dof[ks], dpt);
+        }
+        float ds[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int kk = k0 + acc_row(r, hi);
+            const bool vis = (!CAUSAL || kk <= q) && kk < N;
+            const float p = vis ? fast_exp2(fmaf(st[r], cl2, -lse2)) : 0.f;
+            ds[r] = p * (dpt[r] - dlt);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                dq[db] = mma_f32(Ks[acc_row(r, hi) * RS + 32 * db + l32], ds[r], dq[db]);
+    }
+
+    if (q < N) {
+        float* row = dQ + qoff + (size_t)q * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                f32x4 w;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[i] = dq[db][4 * g + i] * scale;
+                *reinterpret_cast<f32x4*>(row + 32 * db + 8 * g + 4 * hi) = w;
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+template <typename T, int D, bool CAUSAL>
+hipError_t run16(const BwdArgs& a) {
+    const long long rows = (long long)a.B * a.Hq * a.N;
+    constexpr int RPB = 256 / (D / 8);
+    hipLaunchKernelGGL((delta16_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
+                       a.stream, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.delta, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nkb = (a.N + 127) / 128;
+    hipLaunchKernelGGL((dkdv16_kernel<T, D, CAUSAL>), dim3((unsigned)(nkb * a.Hkv * a.B)), dim3(256), 0,
+                       a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv,
+                       a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nqb = (a.N + 127) / 128;
+    hipLaunchKernelGGL((dq16_kernel<T, D, CAUSAL>), dim3((unsigned)(nqb * a.Hq * a.B)), dim3(256), 0,
+                       a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, a.B, a.Hq, a.Hkv,
+                       a.N, a.cl2, a.scale);
+    return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t run32(const BwdArgs& a) {
+    const long long rows = (long long)a.B * a.Hq * a.N;
+    constexpr int RPB = 256 / (D / 4);
+    hipLaunchKernelGGL((delta32_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
+                       a.stream, (const float*)a.o, (const float*)a.dout, a.delta, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nkb = (a.N + 127) / 128;
+    hipLaunchKernelGGL((dkdv32_kernel<D, CAUSAL>), dim3((unsigned)(nkb * a.Hkv * a.B)), dim3(256), 0,
+                       a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
+                       (const float*)a.dout, a.lse, a.delta, (float*)a.dk, (float*)a.dv, a.B, a.Hq,
+                       a.Hkv, a.N, a.cl2, a.scale);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nqb = (a.N + 127) / 128;
+    hipLaunchKernelGGL((dq32_kernel<D, CAUSAL>), dim3((unsigned)(nqb * a.Hq * a.B)), dim3(256), 0,
+                       a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
+                       (const float*)a.dout, a.lse, a.delta, (float*)a.dq, a.B, a.Hq, a.Hkv, a.N,
+                       a.cl2, a.scale);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t run16d(const BwdArgs& a) {
+    return a.causal ? run16<T, D, true>(a) : run16<T, D, false>(a);
+}
+
+template <int D>
+hipError_t run32d(const BwdArgs& a) {
+    return a.causal ? run32<D, true>(a) : run32<D, false>(a);
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs& a) {
+    switch (a.dtype) {
+        case 2: return a.d == 64 ? run16d<BF16, 64>(a) : run16d<BF16, 128>(a);
+        case 1: return a.d == 64 ? run16d<FP16, 64>(a) : run16d<FP16, 128>(a);
+        default: return a.d == 64 ? run32d<64>(a) : run32d<128>(a);
+    }
+}
+
 }  // namespace fa355

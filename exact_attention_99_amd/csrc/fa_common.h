@@ -121,4 +121,32 @@ __device__ __forceinline__ u32x4 zero_u4() {
     return z;
 }
 
+// Row-major tile in LDS (row = key or query, D 16-bit elements): 16-byte chunk
+// c of row r is stored at chunk c ^ (r & 7) so that the 32 lanes reading one chunk column of
+// 32 consecutive rows spread over all banks.
+template <int D>
+__device__ __forceinline__ int k_off(int row, int chunk) {
+    return row * (D * 2) + ((chunk ^ (row & 7)) << 4);
+}
+
+// Transposed tile in LDS (row = head-dim index, BC 16-bit elements in
+// "position" order, see v_key_of_pos), chunk c of row r stored at
+// c ^ ((r ^ (r >> 3)) & 7): conflict-free both for the transposing writes
+// (rows 8 apart) and for the operand reads (consecutive rows).
+template <int BC>
+__device__ __forceinline__ int v_off(int row, int chunk) {
+    return row * (BC * 2) + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
+}
+
+// Inside a 16-element group of a transposed tile, elements are stored in the
+// order in which a 32x32 accumulator hands them to the next product as its B
+// operand: position 8*h + i (h = lane half, i = 0..7) holds element
+// 4*h + (i & 3) + 8*(i >> 2) of the group.
+__device__ __forceinline__ int v_key_of_pos(int h, int i) { return 4 * h + (i & 3) + 8 * (i >> 2); }
+
+// Inverse: position of element x (0..15) of a group.
+__device__ __forceinline__ int pos_of_elem(int x) {
+    return 8 * ((x >> 2) & 1) + 4 * ((x >> 3) & 1) + (x & 3);
+}
+
 }  // namespace fa355

@@ -31,28 +31,6 @@ namespace {
 
 constexpr float kTau = 8.0f;
 
-// K tile in LDS: row = key (D 16-bit elements), 16-byte chunk c of row r is
-// stored at chunk c ^ (r & 7) so that the 32 lanes reading one chunk column of
-// 32 consecutive rows spread over all banks.
-template <int D>
-__device__ __forceinline__ int k_off(int row, int chunk) {
-    return row * (D * 2) + ((chunk ^ (row & 7)) << 4);
-}
-
-// V^T tile in LDS: row = head-dim index (BC 16-bit elements, keys in
-// "position" order, see v_key_of_pos), chunk c of row r stored at
-// c ^ ((r ^ (r >> 3)) & 7): conflict-free both for the transposing writes
-// (rows 8 apart) and for the operand reads (consecutive rows).
-template <int BC>
-__device__ __forceinline__ int v_off(int row, int chunk) {
-    return row * (BC * 2) + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
-}
-
-// Keys inside a 16-key group are stored in the order in which the S^T
-// accumulator hands them to the PV product: position 8*h + i (h = lane half,
-// i = 0..7) holds key 4*h + (i & 3) + 8*(i >> 2).
-__device__ __forceinline__ int v_key_of_pos(int h, int i) { return 4 * h + (i & 3) + 8 * (i >> 2); }
-
 // 16-bit inputs (bf16 or fp16), head dim D, NW waves, BC keys per tile.  Half
 // of the waves stage K, the other half stage V transposed; every staging
 // thread moves NCH (4 or 8) 16-byte chunks per tile: NCH chunks of K rows, or

@@ -30,8 +30,7 @@ struct BwdArgs {
     void* dq;
     void* dk;
     void* dv;
-    float* dq_acc;   // [B, Hq, N, d] float32 workspace
-    float* delta;    // [B, Hq, N] float32 workspace
+    float* delta;    // [B, Hq, N] float32 workspace: D_i = sum_k dO_ik O_ik
     int B, Hq, Hkv, N, d;
     int causal;
     float scale;

@@ -68,7 +68,8 @@ typedef enum {
  *                  the keys visible to row i.
  *   B, H_q, H_kv, N >= 1; H_q % H_kv == 0; d in {64, 128}.
  *   causal in {0, 1}: when 1, key j is visible to query i iff j <= i.
- *   scale: finite; the pages' equation uses 1 / sqrt(d).
+ *   scale: finite and > 0 (the pages' equation uses 1 / sqrt(d)); any other
+ *          value is rejected with FA_ERR_INVALID_ARG.
  * Needs no workspace: memory beyond the inputs and outputs is O(1)
  * ("FlashAttention Kernel" glossary: memory drops from O(N^2) to O(N)).
  */
@@ -78,15 +79,17 @@ fa_status fa_fwd(const void* q, const void* k, const void* v,
                  int causal, float scale, fa_dtype dtype, hipStream_t stream);
 
 /*
- * Bytes of device workspace fa_bwd needs for these sizes: a float32 dQ
- * accumulator [B, H_q, N, d] and the float32 row terms D_i = sum_k dO_ik O_ik
- * [B, H_q, N], each rounded up to 256 bytes.  Returns 0 for invalid sizes.
- * Linear in N.
+ * Bytes of device workspace fa_bwd needs for these sizes: the float32 row
+ * terms D_i = sum_k dO_ik O_ik, [B, H_q, N], rounded up to 256 bytes.
+ * Returns 0 for invalid sizes.  Linear in N.
  */
 size_t fa_bwd_workspace_size(int B, int H_q, int H_kv, int N, int d, fa_dtype dtype);
 
 /*
- * Backward pass: gradients of sum(dout * O) with respect to q, k, v.
+ * Backward pass: gradients of sum(dout * O) with respect to q, k, v
+ * (the pages give no gradient formulas; these are the chain rule through
+ * O = P V and the row-wise softmax: D_i = sum_k dO_ik O_ik, dP = dO V^T,
+ * dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO).
  *
  *   q, k, v, o, lse  in : exactly what fa_fwd took and returned.
  *   dout             in : [B, H_q, N, d], dtype.
@@ -97,9 +100,10 @@ size_t fa_bwd_workspace_size(int B, int H_q, int H_kv, int N, int d, fa_dtype dt
  *                    owned by the caller; contents on entry are ignored and
  *                    on return are unspecified.
  * P is rebuilt per tile from q, k and lse ("FlashAttention Kernel" glossary,
- * Recomputation bullet); dQ is accumulated in float32 across key blocks.
- * Two calls may differ in the last bits of dq (the order of float32
- * additions into the accumulator is not fixed).
+ * Recomputation bullet), once in a pass over key blocks that accumulates dK
+ * and dV, and once in a pass over query blocks that accumulates dQ; every
+ * accumulator is float32 until the final rounding to dtype.  Results are
+ * deterministic (no atomics).
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v,
                  const void* o, const float* lse, const void* dout,
