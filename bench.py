@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Throughput of exact tiled attention (forward + backward) on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic input:
+the forward kernel (O and the row logsumexp) followed by the three backward
+phases (row terms D, dK/dV, dQ), on the Llama-style causal workload
+B = 4, H = 32, N = 8192, d = 128, bf16 (Q, K, V, dO ~ N(0, 1), seeded).
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+Prints one JSON line.  `value` is the whole-step rate in TFLOP/s with the
+conventional count: forward 4*B*H*N^2*d (halved under the causal mask) plus
+backward 2.5x that.  Inputs are resident in HBM before the timed region.
+Per-kernel durations come from HIP events recorded on the stream the kernels
+run on, around every launch inside the timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd/bwd TFLOPS (bf16, causal, d=128) and % of MI355X MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+COPY_BYTES = 1 << 30        # size of the counter-calibration copy
+
+
+def source_sha() -> str:
+    """Hash of the kernel sources: ties stored counter readings to a kernel version."""
+    csrc = os.path.join(ROOT, "exact_attention_99_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        k = rec["kernels"][kernel]
+        if rec.get("source_sha") != source_sha():
+            return None
+        return float(k["hbm_bytes_per_launch"])
+    except (KeyError, ValueError, TypeError):
+        return None
+
+
+def cpu_baseline(w, q, k, v, do, budget_s: float = 12.0, max_heads: int = 32):
+    """The fp64 oracle (as it stands) on whole heads of the same workload,
+    head after head until ~budget_s of CPU time; rate scaled to TFLOP/s."""
+    import numpy as np
+    import oracle
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:
+        threads = os.cpu_count() or 1
+    heads = []
+    t_total = 0.0
+    for h in range(min(max_heads, w.H_q)):
+        hk = h // (w.H_q // w.H_kv)
+        sl = lambda x, hh: x[0:1, hh:hh + 1].to("cpu").to(dtype=__import__("torch").float64).numpy()
+        Q, K, V, dO = sl(q, h), sl(k, hk), sl(v, hk), sl(do, h)
+        t0 = time.perf_counter()
+        oracle.attention_backward(Q, K, V, dO, w.scale, True)  # computes O, lse, dQ, dK, dV
+        t_total += time.perf_counter() - t0
+        heads.append(h)
+        if t_total >= budget_s:
+            break
+    per_head = w.flops_fwd(True) / (w.B * w.H_q) * 3.5
+    value = per_head * len(heads) / t_total / 1e12
+    return {"value": value, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": (f"fp64 NumPy oracle, forward+backward of {len(heads)} whole head(s) "
+                       f"(b=0, h=0..{len(heads) - 1}) of the same workload, causal, "
+                       f"{t_total:.1f} s; rate = conventional FLOPs of those heads / time"),
+            "seconds": t_total}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama_mha_8k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for HBM counter calibration)")
+    ap.add_argument("--print-sha", action="store_true", help="print the kernel source hash and exit")
+    args = ap.parse_args()
+    if args.print_sha:
+        print(source_sha())
+        return 0
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "the attention path here has no multi-GPU mode; run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import workloads
+    from exact_attention_99_amd import fa_bwd_dkdv, fa_bwd_dq, fa_bwd_prepare, fa_fwd
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        return 2
+    if args.copy_calibration:
+        n = COPY_BYTES // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": COPY_BYTES}))
+        return 0
+    w = workloads.WORKLOADS[args.workload]
+    causal = True in w.causal_modes
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    q, k, v, do = workloads.workload_inputs(w, with_dout=True, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H_q, w.N), dtype=torch.float32, device=dev)
+    delta = torch.empty_like(lse)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    stream = torch.cuda.current_stream()
+    names = ["fwd", "bwd_prepare", "bwd_dkdv", "bwd_dq"]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa_fwd(q, k, v, causal, w.scale, o=o, lse=lse, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        fa_bwd_prepare(o, do, delta, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        fa_bwd_dkdv(q, k, v, lse, do, delta, causal, w.scale, dk=dk, dv=dv, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+        fa_bwd_dq(q, k, v, lse, do, delta, causal, w.scale, dq=dq, stream=stream)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per = {n: 0.0 for n in names}
+    for ev in events:
+        for j, n in enumerate(names):
+            per[n] += ev[j].elapsed_time(ev[j + 1])
+    per = {n: t / args.steps for n, t in per.items()}  # ms per launch
+
+    F = w.flops_fwd(causal)
+    step_flops = F + w.flops_bwd(causal)
+    ms_step = wall / args.steps * 1e3
+    value = step_flops / (ms_step * 1e-3) / 1e12
+    # FLOPs each kernel performs by design (matrix products of N x N x d):
+    # forward 2 (QK^T, PV), dK/dV pass 4 (QK^T, dO V^T, P^T dO, dS^T Q),
+    # dQ pass 3 (K Q^T, V dO^T, dS K); the row-term pass moves bytes only.
+    kflops = {"fwd": F, "bwd_dkdv": 2.0 * F, "bwd_dq": 1.5 * F, "bwd_prepare": 0.0}
+    elem = 2
+    kbytes = {"bwd_prepare": 2.0 * w.B * w.H_q * w.N * w.d * elem + 4.0 * w.B * w.H_q * w.N}
+    dominant = max(per, key=per.get)
+    if kflops[dominant] > 0:
+        achieved = kflops[dominant] / (per[dominant] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS}
+    else:
+        achieved = kbytes[dominant] / (per[dominant] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS}
+    roof["kernel"] = dominant
+    roof["traffic"] = stored_traffic(dominant)
+
+    kernels = {}
+    for n in names:
+        rec = {"ms": per[n]}
+        if kflops[n] > 0:
+            rec["tflops"] = kflops[n] / (per[n] * 1e-3) / 1e12
+        else:
+            rec["gbs"] = kbytes[n] / (per[n] * 1e-3) / 1e9
+        kernels[n] = rec
+    fwd_ms = per["fwd"]
+    bwd_ms = per["bwd_prepare"] + per["bwd_dkdv"] + per["bwd_dq"]
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H_q": w.H_q, "H_kv": w.H_kv, "N": w.N, "d": w.d,
+                   "causal": causal, "step": "forward + backward"},
+        "pct_of_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "fwd_tflops": F / (fwd_ms * 1e-3) / 1e12,
+        "bwd_tflops": w.flops_bwd(causal) / (bwd_ms * 1e-3) / 1e12,
+        "kernels": kernels,
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, do)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -9,12 +9,17 @@ Names mirror the C entry points of ``include/fa355.h``:
 
     fa_fwd(q, k, v, causal, scale, o=None, lse=None, stream=None) -> (o, lse)
     fa_bwd(q, k, v, o, lse, dout, causal, scale, ...) -> (dq, dk, dv)
+    fa_bwd_prepare(o, dout) -> delta
+    fa_bwd_dkdv(q, k, v, lse, dout, delta, causal, scale) -> (dk, dv)
+    fa_bwd_dq(q, k, v, lse, dout, delta, causal, scale) -> dq
     fa_bwd_workspace_size(B, H_q, H_kv, N, d, dtype) -> int
     fa_status_string(code) -> str
     fa_version() -> int
 """
-from ._abi import (FA_DTYPE, FaError, fa_bwd, fa_bwd_workspace_size, fa_fwd, fa_status_string,
-                   fa_version, lib_path, load_library)
+from ._abi import (FA_DTYPE, FaError, fa_bwd, fa_bwd_dkdv, fa_bwd_dq, fa_bwd_prepare,
+                   fa_bwd_workspace_size, fa_fwd, fa_status_string, fa_version, lib_path,
+                   load_library)
 
-__all__ = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string", "fa_version",
-           "FaError", "FA_DTYPE", "load_library", "lib_path"]
+__all__ = ["fa_fwd", "fa_bwd", "fa_bwd_prepare", "fa_bwd_dkdv", "fa_bwd_dq",
+           "fa_bwd_workspace_size", "fa_status_string", "fa_version", "FaError", "FA_DTYPE",
+           "load_library", "lib_path"]

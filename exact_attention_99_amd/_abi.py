@@ -46,6 +46,12 @@ def load_library() -> ctypes.CDLL:
         lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                i, i, i, i, i, i, f, i, vp]
         lib.fa_bwd.restype = i
+        lib.fa_bwd_prepare.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
+        lib.fa_bwd_prepare.restype = i
+        lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+        lib.fa_bwd_dkdv.restype = i
+        lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+        lib.fa_bwd_dq.restype = i
         lib.fa_bwd_workspace_size.argtypes = [i, i, i, i, i, i]
         lib.fa_bwd_workspace_size.restype = sz
         lib.fa_status_string.argtypes = [i]
@@ -146,3 +152,54 @@ def fa_bwd(q, k, v, o, lse, dout, causal: bool, scale: float, dq=None, dk=None, 
     if st != 0:
         raise FaError(st, "fa_bwd")
     return dq, dk, dv
+
+
+def fa_bwd_prepare(o, dout, delta=None, stream=None):
+    """delta_i = sum_k dout_ik o_ik (float32 [B, H_q, N]); returns delta."""
+    import torch
+    lib = load_library()
+    B, Hq, N, d = o.shape
+    if delta is None:
+        delta = torch.empty((B, Hq, N), dtype=torch.float32, device=o.device)
+    _check_same(o, dout, delta)
+    st = lib.fa_bwd_prepare(o.data_ptr(), dout.data_ptr(), delta.data_ptr(), B, Hq, N, d,
+                            FA_DTYPE[_dtype_name(o)], _stream(o, stream))
+    if st != 0:
+        raise FaError(st, "fa_bwd_prepare")
+    return delta
+
+
+def fa_bwd_dkdv(q, k, v, lse, dout, delta, causal: bool, scale: float, dk=None, dv=None,
+                stream=None):
+    """dk, dv from the forward's lse and the prepared delta; returns (dk, dv)."""
+    import torch
+    lib = load_library()
+    B, Hq, Hkv, N, d = _shape(q, k, v)
+    if dk is None:
+        dk = torch.empty_like(k)
+    if dv is None:
+        dv = torch.empty_like(v)
+    _check_same(q, k, v, lse, dout, delta, dk, dv)
+    st = lib.fa_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                         delta.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, N, d,
+                         int(bool(causal)), float(scale), FA_DTYPE[_dtype_name(q)],
+                         _stream(q, stream))
+    if st != 0:
+        raise FaError(st, "fa_bwd_dkdv")
+    return dk, dv
+
+
+def fa_bwd_dq(q, k, v, lse, dout, delta, causal: bool, scale: float, dq=None, stream=None):
+    """dq from the forward's lse and the prepared delta; returns dq."""
+    import torch
+    lib = load_library()
+    B, Hq, Hkv, N, d = _shape(q, k, v)
+    if dq is None:
+        dq = torch.empty_like(q)
+    _check_same(q, k, v, lse, dout, delta, dq)
+    st = lib.fa_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                       delta.data_ptr(), dq.data_ptr(), B, Hq, Hkv, N, d, int(bool(causal)),
+                       float(scale), FA_DTYPE[_dtype_name(q)], _stream(q, stream))
+    if st != 0:
+        raise FaError(st, "fa_bwd_dq")
+    return dq

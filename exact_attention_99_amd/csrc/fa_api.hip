@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <initializer_list>
+
 #include "fa355.h"
 #include "fa_launch.h"
 
@@ -68,32 +70,93 @@ size_t fa_bwd_workspace_size(int B, int H_q, int H_kv, int N, int d, fa_dtype dt
     return round256(rows * sizeof(float));
 }
 
-fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                 const void* dout, void* dq, void* dk, void* dv, void* workspace,
-                 size_t workspace_bytes, int B, int H_q, int H_kv, int N, int d, int causal,
-                 float scale, fa_dtype dtype, hipStream_t stream) {
-    const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv, workspace};
-    for (const void* p : ptrs)
-        if (!p || !aligned16(p)) return FA_ERR_INVALID_ARG;
+namespace {
+
+fa_status check_common(int B, int H_q, int H_kv, int N, int d, int causal, float scale,
+                       fa_dtype dtype) {
     if (!sizes_ok(B, H_q, H_kv, N)) return FA_ERR_INVALID_ARG;
     if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
     if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
     if (!dtype_ok(dtype)) return FA_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-    const size_t need = fa_bwd_workspace_size(B, H_q, H_kv, N, d, dtype);
-    if (workspace_bytes < need) return FA_ERR_INVALID_ARG;
+    return FA_OK;
+}
 
+bool ptrs_ok(std::initializer_list<const void*> ps) {
+    for (const void* p : ps)
+        if (!p || !aligned16(p)) return false;
+    return true;
+}
+
+fa355::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                        float* delta, int B, int H_q, int H_kv, int N, int d, int causal,
+                        float scale, fa_dtype dtype, hipStream_t stream) {
     fa355::BwdArgs a;
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
     a.dq = dq; a.dk = dk; a.dv = dv;
-    a.delta = static_cast<float*>(workspace);
+    a.delta = delta;
     a.B = B; a.Hq = H_q; a.Hkv = H_kv; a.N = N; a.d = d;
     a.causal = causal;
     a.scale = scale;
     a.cl2 = scale * kLog2eHost;
     a.dtype = (int)dtype;
     a.stream = stream;
-    return fa355::launch_bwd(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+    return a;
+}
+
+fa_status hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+}  // namespace
+
+fa_status fa_bwd_prepare(const void* o, const void* dout, float* delta, int B, int H_q, int N,
+                         int d, fa_dtype dtype, hipStream_t stream) {
+    if (!ptrs_ok({o, dout, delta})) return FA_ERR_INVALID_ARG;
+    const fa_status st = check_common(B, H_q, H_q, N, d, 0, 1.f, dtype);
+    if (st != FA_OK) return st;
+    const auto a = bwd_args(nullptr, nullptr, nullptr, o, nullptr, dout, nullptr, nullptr, nullptr,
+                            delta, B, H_q, H_q, N, d, 0, 1.f, dtype, stream);
+    return hip_status(fa355::launch_bwd_prepare(a));
+}
+
+fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
+                      const void* dout, const float* delta, void* dk, void* dv, int B, int H_q,
+                      int H_kv, int N, int d, int causal, float scale, fa_dtype dtype,
+                      hipStream_t stream) {
+    if (!ptrs_ok({q, k, v, lse, dout, delta, dk, dv})) return FA_ERR_INVALID_ARG;
+    const fa_status st = check_common(B, H_q, H_kv, N, d, causal, scale, dtype);
+    if (st != FA_OK) return st;
+    const auto a = bwd_args(q, k, v, nullptr, lse, dout, nullptr, dk, dv, const_cast<float*>(delta),
+                            B, H_q, H_kv, N, d, causal, scale, dtype, stream);
+    return hip_status(fa355::launch_bwd_dkdv(a));
+}
+
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
+                    const void* dout, const float* delta, void* dq, int B, int H_q, int H_kv,
+                    int N, int d, int causal, float scale, fa_dtype dtype, hipStream_t stream) {
+    if (!ptrs_ok({q, k, v, lse, dout, delta, dq})) return FA_ERR_INVALID_ARG;
+    const fa_status st = check_common(B, H_q, H_kv, N, d, causal, scale, dtype);
+    if (st != FA_OK) return st;
+    const auto a = bwd_args(q, k, v, nullptr, lse, dout, dq, nullptr, nullptr,
+                            const_cast<float*>(delta), B, H_q, H_kv, N, d, causal, scale, dtype,
+                            stream);
+    return hip_status(fa355::launch_bwd_dq(a));
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                 size_t workspace_bytes, int B, int H_q, int H_kv, int N, int d, int causal,
+                 float scale, fa_dtype dtype, hipStream_t stream) {
+    if (!ptrs_ok({q, k, v, o, lse, dout, dq, dk, dv, workspace})) return FA_ERR_INVALID_ARG;
+    const fa_status st = check_common(B, H_q, H_kv, N, d, causal, scale, dtype);
+    if (st != FA_OK) return st;
+    if (workspace_bytes < fa_bwd_workspace_size(B, H_q, H_kv, N, d, dtype)) return FA_ERR_INVALID_ARG;
+    const auto a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace), B,
+                            H_q, H_kv, N, d, causal, scale, dtype, stream);
+    hipError_t e = fa355::launch_bwd_prepare(a);
+    if (e == hipSuccess) e = fa355::launch_bwd_dkdv(a);
+    if (e == hipSuccess) e = fa355::launch_bwd_dq(a);
+    return hip_status(e);
 }
 
 const char* fa_status_string(fa_status s) {

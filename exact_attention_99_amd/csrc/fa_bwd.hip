@@ -672,21 +672,36 @@ dq32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const floa
 }
 
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool CAUSAL>
-hipError_t run16(const BwdArgs& a) {
+template <typename T, int D>
+hipError_t prepare16(const BwdArgs& a) {
     const long long rows = (long long)a.B * a.Hq * a.N;
     constexpr int RPB = 256 / (D / 8);
     hipLaunchKernelGGL((delta16_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
                        a.stream, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.delta, rows);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t prepare32(const BwdArgs& a) {
+    const long long rows = (long long)a.B * a.Hq * a.N;
+    constexpr int RPB = 256 / (D / 4);
+    hipLaunchKernelGGL((delta32_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
+                       a.stream, (const float*)a.o, (const float*)a.dout, a.delta, rows);
+    return hipGetLastError();
+}
+
+template <typename T, int D, bool CAUSAL>
+hipError_t dkdv16(const BwdArgs& a) {
     const int nkb = (a.N + 127) / 128;
     hipLaunchKernelGGL((dkdv16_kernel<T, D, CAUSAL>), dim3((unsigned)(nkb * a.Hkv * a.B)), dim3(256), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv,
                        a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    return hipGetLastError();
+}
+
+template <typename T, int D, bool CAUSAL>
+hipError_t dq16(const BwdArgs& a) {
     const int nqb = (a.N + 127) / 128;
     hipLaunchKernelGGL((dq16_kernel<T, D, CAUSAL>), dim3((unsigned)(nqb * a.Hq * a.B)), dim3(256), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
@@ -696,20 +711,17 @@ hipError_t run16(const BwdArgs& a) {
 }
 
 template <int D, bool CAUSAL>
-hipError_t run32(const BwdArgs& a) {
-    const long long rows = (long long)a.B * a.Hq * a.N;
-    constexpr int RPB = 256 / (D / 4);
-    hipLaunchKernelGGL((delta32_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
-                       a.stream, (const float*)a.o, (const float*)a.dout, a.delta, rows);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+hipError_t dkdv32(const BwdArgs& a) {
     const int nkb = (a.N + 127) / 128;
     hipLaunchKernelGGL((dkdv32_kernel<D, CAUSAL>), dim3((unsigned)(nkb * a.Hkv * a.B)), dim3(256), 0,
                        a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
                        (const float*)a.dout, a.lse, a.delta, (float*)a.dk, (float*)a.dv, a.B, a.Hq,
                        a.Hkv, a.N, a.cl2, a.scale);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t dq32(const BwdArgs& a) {
     const int nqb = (a.N + 127) / 128;
     hipLaunchKernelGGL((dq32_kernel<D, CAUSAL>), dim3((unsigned)(nqb * a.Hq * a.B)), dim3(256), 0,
                        a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
@@ -718,24 +730,40 @@ hipError_t run32(const BwdArgs& a) {
     return hipGetLastError();
 }
 
-template <typename T, int D>
-hipError_t run16d(const BwdArgs& a) {
-    return a.causal ? run16<T, D, true>(a) : run16<T, D, false>(a);
+// dtype x head dim x mask -> instance.
+template <template <typename, int, bool> class F16, template <int, bool> class F32>
+hipError_t pick(const BwdArgs& a) {
+    const bool c = a.causal != 0;
+    switch (a.dtype) {
+        case 2:
+            return a.d == 64 ? (c ? F16<BF16, 64, true>::run(a) : F16<BF16, 64, false>::run(a))
+                             : (c ? F16<BF16, 128, true>::run(a) : F16<BF16, 128, false>::run(a));
+        case 1:
+            return a.d == 64 ? (c ? F16<FP16, 64, true>::run(a) : F16<FP16, 64, false>::run(a))
+                             : (c ? F16<FP16, 128, true>::run(a) : F16<FP16, 128, false>::run(a));
+        default:
+            return a.d == 64 ? (c ? F32<64, true>::run(a) : F32<64, false>::run(a))
+                             : (c ? F32<128, true>::run(a) : F32<128, false>::run(a));
+    }
 }
 
-template <int D>
-hipError_t run32d(const BwdArgs& a) {
-    return a.causal ? run32<D, true>(a) : run32<D, false>(a);
-}
+template <typename T, int D, bool C> struct Dkdv16 { static hipError_t run(const BwdArgs& a) { return dkdv16<T, D, C>(a); } };
+template <int D, bool C> struct Dkdv32 { static hipError_t run(const BwdArgs& a) { return dkdv32<D, C>(a); } };
+template <typename T, int D, bool C> struct Dq16 { static hipError_t run(const BwdArgs& a) { return dq16<T, D, C>(a); } };
+template <int D, bool C> struct Dq32 { static hipError_t run(const BwdArgs& a) { return dq32<D, C>(a); } };
 
 }  // namespace
 
-hipError_t launch_bwd(const BwdArgs& a) {
+hipError_t launch_bwd_prepare(const BwdArgs& a) {
     switch (a.dtype) {
-        case 2: return a.d == 64 ? run16d<BF16, 64>(a) : run16d<BF16, 128>(a);
-        case 1: return a.d == 64 ? run16d<FP16, 64>(a) : run16d<FP16, 128>(a);
-        default: return a.d == 64 ? run32d<64>(a) : run32d<128>(a);
+        case 2: return a.d == 64 ? prepare16<BF16, 64>(a) : prepare16<BF16, 128>(a);
+        case 1: return a.d == 64 ? prepare16<FP16, 64>(a) : prepare16<FP16, 128>(a);
+        default: return a.d == 64 ? prepare32<64>(a) : prepare32<128>(a);
     }
 }
+
+hipError_t launch_bwd_dkdv(const BwdArgs& a) { return pick<Dkdv16, Dkdv32>(a); }
+
+hipError_t launch_bwd_dq(const BwdArgs& a) { return pick<Dq16, Dq32>(a); }
 
 }  // namespace fa355

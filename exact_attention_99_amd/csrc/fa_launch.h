@@ -40,6 +40,9 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a);
-hipError_t launch_bwd(const BwdArgs& a);
+// Backward phases; each reads only the BwdArgs fields it needs.
+hipError_t launch_bwd_prepare(const BwdArgs& a);
+hipError_t launch_bwd_dkdv(const BwdArgs& a);
+hipError_t launch_bwd_dq(const BwdArgs& a);
 
 }  // namespace fa355

@@ -112,6 +112,35 @@ fa_status fa_bwd(const void* q, const void* k, const void* v,
                  int B, int H_q, int H_kv, int N, int d,
                  int causal, float scale, fa_dtype dtype, hipStream_t stream);
 
+/*
+ * The three phases fa_bwd runs, for callers that schedule them themselves
+ * (for example dK/dV and dQ on two streams once the row terms are ready).
+ * Arguments mean what they mean for fa_bwd; `delta` is a float32
+ * [B, H_q, N] buffer (16-byte aligned), owned by the caller.
+ *
+ * fa_bwd_prepare: delta_i = sum_k dout_ik o_ik for every query row.
+ * fa_bwd_dkdv:    dk, dv from q, k, v, lse, dout and delta (rebuilds P and
+ *                 dP per key block; sums grouped query heads).
+ * fa_bwd_dq:      dq from q, k, v, lse, dout and delta (rebuilds P and dP per
+ *                 query block).
+ * fa_bwd_dkdv and fa_bwd_dq only read delta and may run concurrently once
+ * fa_bwd_prepare has completed.
+ */
+fa_status fa_bwd_prepare(const void* o, const void* dout, float* delta,
+                         int B, int H_q, int N, int d, fa_dtype dtype, hipStream_t stream);
+
+fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v,
+                      const float* lse, const void* dout, const float* delta,
+                      void* dk, void* dv,
+                      int B, int H_q, int H_kv, int N, int d,
+                      int causal, float scale, fa_dtype dtype, hipStream_t stream);
+
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v,
+                    const float* lse, const void* dout, const float* delta,
+                    void* dq,
+                    int B, int H_q, int H_kv, int N, int d,
+                    int causal, float scale, fa_dtype dtype, hipStream_t stream);
+
 /* Static, never-NULL description of a status code. */
 const char* fa_status_string(fa_status s);
 

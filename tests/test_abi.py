@@ -29,8 +29,9 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd",
-                                    "fa_status_string", "fa_version"]
+    assert declared_functions() == ["fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_prepare",
+                                    "fa_bwd_workspace_size", "fa_fwd", "fa_status_string",
+                                    "fa_version"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -114,3 +115,24 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_abi, "_lib", None)
     with pytest.raises(RuntimeError, match="no fallback"):
         _abi.load_library()
+
+
+def test_phase_entry_points_reject(lib):
+    assert lib.fa_bwd_prepare(None, A, A, 1, 2, 16, 64, BF16, None) == INVALID
+    assert lib.fa_bwd_prepare(A, A, MIS, 1, 2, 16, 64, BF16, None) == INVALID
+    assert lib.fa_bwd_prepare(A, A, A, 1, 2, 16, 80, BF16, None) == UNSUPPORTED
+    assert lib.fa_bwd_prepare(A, A, A, 0, 2, 16, 64, BF16, None) == INVALID
+    args = [A] * 8
+    for i in range(8):
+        p = list(args)
+        p[i] = None
+        assert lib.fa_bwd_dkdv(*p, 1, 2, 1, 16, 64, 0, 0.1, BF16, None) == INVALID
+    assert lib.fa_bwd_dkdv(*args, 1, 3, 2, 16, 64, 0, 0.1, BF16, None) == INVALID
+    assert lib.fa_bwd_dkdv(*args, 1, 2, 1, 16, 64, 0, -1.0, BF16, None) == INVALID
+    assert lib.fa_bwd_dkdv(*args, 1, 2, 1, 16, 32, 0, 0.1, BF16, None) == UNSUPPORTED
+    for i in range(7):
+        p = [A] * 7
+        p[i] = MIS
+        assert lib.fa_bwd_dq(*p, 1, 2, 1, 16, 64, 1, 0.1, FP16, None) == INVALID
+    assert lib.fa_bwd_dq(*([A] * 7), 1, 2, 1, 16, 64, 3, 0.1, FP16, None) == INVALID
+    assert lib.fa_bwd_dq(*([A] * 7), 1, 2, 1, 16, 64, 1, 0.1, 9, None) == INVALID

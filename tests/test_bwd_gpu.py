@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import workloads
-from exact_attention_99_amd import fa_bwd, fa_fwd
+from exact_attention_99_amd import fa_bwd, fa_bwd_dkdv, fa_bwd_dq, fa_bwd_prepare, fa_fwd
 
 from .parity import TOL, check_grads, errs
 
@@ -122,3 +122,24 @@ def test_workspace_too_small_is_rejected():
     ws = torch.empty(16, dtype=torch.uint8, device=DEV)
     with pytest.raises(FaError):
         fa_bwd(q, k, v, o, lse, do, False, 0.125, workspace=ws)
+
+
+def test_phases_on_two_streams_match_fa_bwd():
+    """prepare, then dK/dV and dQ on two streams concurrently: bitwise equal to fa_bwd."""
+    q, k, v, do = workloads.make_inputs(2, 8, 2, 1500, 128, "bf16", 41, with_dout=True)
+    q, k, v, do = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    for causal in (False, True):
+        o, lse = fa_fwd(q, k, v, causal, 0.1)
+        dq, dk, dv = fa_bwd(q, k, v, o, lse, do, causal, 0.1)
+        delta = fa_bwd_prepare(o, do)
+        ev = torch.cuda.Event()
+        ev.record()
+        s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+        s1.wait_event(ev)
+        s2.wait_event(ev)
+        with torch.cuda.stream(s1):
+            dk2, dv2 = fa_bwd_dkdv(q, k, v, lse, do, delta, causal, 0.1, stream=s1)
+        with torch.cuda.stream(s2):
+            dq2 = fa_bwd_dq(q, k, v, lse, do, delta, causal, 0.1, stream=s2)
+        torch.cuda.synchronize()
+        assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
