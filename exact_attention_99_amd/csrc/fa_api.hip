@@ -20,9 +20,10 @@ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 bool sizes_ok(int B, int Hq, int Hkv, int N) {
     if (B < 1 || Hq < 1 || Hkv < 1 || N < 1) return false;
     if (Hq % Hkv != 0) return false;
-    // Every element offset is formed in 64-bit; block counts must fit a grid.
+    // Block counts must fit a grid, and one head's rows (at 4 bytes per
+    // element, d <= 128) must be addressable with 32-bit byte offsets.
     const long long rows = (long long)B * Hq * ((N + 31) / 32);
-    return rows < (1LL << 31);
+    return rows < (1LL << 31) && (long long)N * 128 * 4 < (1LL << 31);
 }
 
 bool dtype_ok(fa_dtype t) { return t == FA_DTYPE_FP32 || t == FA_DTYPE_FP16 || t == FA_DTYPE_BF16; }

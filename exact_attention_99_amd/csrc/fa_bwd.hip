@@ -79,12 +79,17 @@ delta32_kernel(const float* __restrict__ O, const float* __restrict__ dO, float*
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV for 16-bit inputs.  Four waves, 128 keys per workgroup, BQ query rows
-// per step (32 for D = 128, 64 for D = 64), double-buffered in LDS:
+// dK, dV for 16-bit inputs.  Four waves, 128 keys per workgroup (32 per wave,
+// one per lane), BQ query rows per step (16 KB per tile: 64 rows for D = 128,
+// 128 for D = 64), double-buffered in LDS:
 //   Qs, dOs : row-major, swizzled (A operands of S = Q K^T and dP = dO V^T)
-//   Qt, dOt : transposed, query rows in "position" order, rows padded by 16 B
+//   Qt, dOt : transposed, query rows in "position" order, swizzled
 //             (A operands of dK^T += Q^T dS and dV^T += dO^T P)
 //   lse2, dl: log2(e) * lse and D of the step's rows.
+// Threads 0..127 stage Q, 128..255 stage dO: each loads an 8-row x 8-column
+// block, stores it row-major and, transposed in registers, column-major.
+// No branch encloses the accumulating products (a wave with no visible key in
+// a step runs it with P = dS = 0), so the dK^T/dV^T accumulators stay in place.
 template <typename T, int D, bool CAUSAL>
 __global__ void __launch_bounds__(256)
 dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -93,28 +98,25 @@ dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int B, int Hq, int Hkv, int N,
               float cl2, float scale) {
     constexpr int BKV = 128;
-    constexpr int BQ = D == 128 ? 32 : 64;
+    constexpr int BQ = 8192 / D;
     constexpr int NQB = BQ / 32;
     constexpr int KCH = D / 8;
-    constexpr int QR = BQ * KCH / 256;        // query rows staged per thread (pairs)
-    static_assert(QR == 2, "each staging thread moves one pair of rows");
-    constexpr int TROW = BQ * 2 + 16;         // padded transposed row, bytes
-    constexpr int TRM = BQ * D * 2;
-    constexpr int TT = D * TROW;
-    constexpr int OFF_DOS = TRM;
-    constexpr int OFF_QT = 2 * TRM;
-    constexpr int OFF_DOT = 2 * TRM + TT;
-    constexpr int OFF_LSE = 2 * TRM + 2 * TT;
+    constexpr int TB = BQ * D * 2;            // one tile, bytes
+    constexpr int OFF_DOS = TB;
+    constexpr int OFF_QT = 2 * TB;
+    constexpr int OFF_DOT = 3 * TB;
+    constexpr int OFF_LSE = 4 * TB;
     constexpr int OFF_DL = OFF_LSE + BQ * 4;
     constexpr int STAGE = OFF_DL + BQ * 4;
     constexpr int NDB = D / 32;
     constexpr int NKS = D / 16;
+    static_assert((BQ / 8) * KCH == 128, "one 8x8 block per staging thread");
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // provably wave-uniform
     const int l32 = lane & 31;
     const int hi = lane >> 5;
 
@@ -131,13 +133,17 @@ dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int kw = kv0 + 32 * wave;
     const int key = kw + l32;
     const size_t kvoff = ((size_t)b * Hkv + hk) * (size_t)N * D;
+    const uint32_t head_bytes = (uint32_t)N * D * 2;
 
     // K^T, V^T as B operands: lane holds K[key][16*ks + 8*hi .. +7].
     u32x4 kf[NKS], vf[NKS];
+    {
+        const Buf Kb(K + kvoff, head_bytes), Vb(V + kvoff, head_bytes);
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-        kf[ks] = key < N ? ld_global16(K + kvoff + (size_t)key * D + 16 * ks + 8 * hi) : zero_u4();
-        vf[ks] = key < N ? ld_global16(V + kvoff + (size_t)key * D + 16 * ks + 8 * hi) : zero_u4();
+        for (int ks = 0; ks < NKS; ++ks) {
+            kf[ks] = Kb.load16((uint32_t)(key * D + 16 * ks + 8 * hi) * 2);
+            vf[ks] = Vb.load16((uint32_t)(key * D + 16 * ks + 8 * hi) * 2);
+        }
     }
 
     f32x16 dkt[NDB], dvt[NDB];
@@ -151,12 +157,19 @@ dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int qb_count = (N + BQ - 1) / BQ - qb_first;
     const int nsteps = G * qb_count;
 
-    // staging: thread -> (chunk c, row pair rp)
-    const int sc = tid % KCH;
-    const int rp = tid / KCH;
-    u32x4 sq[2], sdo[2];
+    // staging: thread -> tensor (Q or dO), chunk column sc, 8-position group pg
+    const bool st_do = wave >= 2;
+    const int st = tid & 127;
+    const int sc = st % KCH;
+    const int pg = st / KCH;
+    const uint16_t* src = st_do ? dO : Q;
+    u32x4 stg[8];
     float sx = 0.f;
 
+    auto row_of = [&](int i) {  // query row (within the step) of position 8*pg + i
+        const int pos = 8 * pg + i;
+        return 16 * (pos >> 4) + v_key_of_pos((pos >> 3) & 1, pos & 7);
+    };
     auto step_rows = [&](int s, int& h, int& q0) {
         h = hk * G + s / qb_count;
         q0 = (qb_first + s % qb_count) * BQ;
@@ -165,42 +178,37 @@ dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         int h, q0;
         step_rows(s, h, q0);
         const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
+        const Buf Sb(src + qoff, head_bytes);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int q = q0 + 2 * rp + i;
-            sq[i] = q < N ? ld_global16(Q + qoff + (size_t)q * D + 8 * sc) : zero_u4();
-            sdo[i] = q < N ? ld_global16(dO + qoff + (size_t)q * D + 8 * sc) : zero_u4();
-        }
+        for (int i = 0; i < 8; ++i)
+            stg[i] = Sb.load16((uint32_t)((q0 + row_of(i)) * D + 8 * sc) * 2);
         const size_t roff = ((size_t)b * Hq + h) * (size_t)N;
-        if (tid < BQ) {
-            const int q = q0 + tid;
-            sx = q < N ? LSE[roff + q] * kLog2e : 0.f;
-        } else if (tid < 2 * BQ) {
-            const int q = q0 + tid - BQ;
-            sx = q < N ? Delta[roff + q] : 0.f;
-        }
+        if (tid < BQ)
+            sx = Buf(LSE + roff, (uint32_t)N * 4).load_f32((uint32_t)(q0 + tid) * 4) * kLog2e;
+        else if (tid >= 128 && tid < 128 + BQ)
+            sx = Buf(Delta + roff, (uint32_t)N * 4).load_f32((uint32_t)(q0 + tid - 128) * 4);
     };
     auto deposit = [&](int buf) {
         unsigned char* base = smem + buf * STAGE;
+        unsigned char* rm = base + (st_do ? OFF_DOS : 0);
+        unsigned char* tr = base + (st_do ? OFF_DOT : OFF_QT);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            *reinterpret_cast<u32x4*>(base + k_off<D>(2 * rp + i, sc)) = sq[i];
-            *reinterpret_cast<u32x4*>(base + OFF_DOS + k_off<D>(2 * rp + i, sc)) = sdo[i];
-        }
-        const int r0 = 2 * rp;
-        const int tcol = (16 * (r0 >> 4) + pos_of_elem(r0 & 15)) * 2;  // byte column
+        for (int i = 0; i < 8; ++i)
+            *reinterpret_cast<u32x4*>(rm + k_off<D>(row_of(i), sc)) = stg[i];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int sh = 16 * (e & 1);
-            const uint32_t wq = ((sq[0][e >> 1] >> sh) & 0xffffu) | (((sq[1][e >> 1] >> sh) & 0xffffu) << 16);
-            const uint32_t wd = ((sdo[0][e >> 1] >> sh) & 0xffffu) | (((sdo[1][e >> 1] >> sh) & 0xffffu) << 16);
-            *reinterpret_cast<uint32_t*>(base + OFF_QT + (8 * sc + e) * TROW + tcol) = wq;
-            *reinterpret_cast<uint32_t*>(base + OFF_DOT + (8 * sc + e) * TROW + tcol) = wd;
+            u32x4 w;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                w[jj] = ((stg[2 * jj][e >> 1] >> sh) & 0xffffu) |
+                        (((stg[2 * jj + 1][e >> 1] >> sh) & 0xffffu) << 16);
+            *reinterpret_cast<u32x4*>(tr + v_off<BQ>(8 * sc + e, pg)) = w;
         }
         if (tid < BQ)
             reinterpret_cast<float*>(base + OFF_LSE)[tid] = sx;
-        else if (tid < 2 * BQ)
-            reinterpret_cast<float*>(base + OFF_DL)[tid - BQ] = sx;
+        else if (tid >= 128 && tid < 128 + BQ)
+            reinterpret_cast<float*>(base + OFF_DL)[tid - 128] = sx;
     };
 
     if (nsteps > 0) {
@@ -213,53 +221,61 @@ dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         if (s + 1 < nsteps) fetch(s + 1);
         int h, q0;
         step_rows(s, h, q0);
-        const bool active = !CAUSAL || (q0 + BQ - 1 >= kw);
-        if (active) {
-            const unsigned char* base = smem + (s & 1) * STAGE;
-            const float* lse2s = reinterpret_cast<const float*>(base + OFF_LSE);
-            const float* dls = reinterpret_cast<const float*>(base + OFF_DL);
+        // rows of this step that see only some of the wave's keys, or lie past N
+        const bool need_mask = (CAUSAL && q0 < kw + 32) || (q0 + BQ > N) || (kw + 32 > N);
+        const unsigned char* base = smem + (s & 1) * STAGE;
+        const float* lse2s = reinterpret_cast<const float*>(base + OFF_LSE);
+        const float* dls = reinterpret_cast<const float*>(base + OFF_DL);
+        // one 32-row sub-block at a time keeps a single S / dP pair live
+#pragma unroll 1
+        for (int qs = 0; qs < NQB; ++qs) {
+            f32x16 sacc = zero16(), dpacc = zero16();
 #pragma unroll
-            for (int qs = 0; qs < NQB; ++qs) {
-                f32x16 sacc = zero16(), dpacc = zero16();
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    const u32x4 aq = *reinterpret_cast<const u32x4*>(base + k_off<D>(32 * qs + l32, 2 * ks + hi));
-                    const u32x4 ad = *reinterpret_cast<const u32x4*>(base + OFF_DOS + k_off<D>(32 * qs + l32, 2 * ks + hi));
-                    sacc = Mma<T>::mma(aq, kf[ks], sacc);
-                    dpacc = Mma<T>::mma(ad, vf[ks], dpacc);
-                }
-                u32x4 pb[2], dsb[2];
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + 32 * qs + 8 * g + 4 * hi);
-                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + 32 * qs + 8 * g + 4 * hi);
-                    float pv[4], dv[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int r = 4 * g + i;
-                        const int q = q0 + 32 * qs + acc_row(r, hi);
-                        const bool vis = (!CAUSAL || key <= q) && q < N && key < N;
-                        const float p = vis ? fast_exp2(fmaf(sacc[r], cl2, -l4[i])) : 0.f;
-                        pv[i] = p;
-                        dv[i] = p * (dpacc[r] - d4[i]);
-                    }
-                    // registers 4g..4g+3 -> dwords (g & 1) * 2 + {0, 1} of operand g >> 1
-                    pb[g >> 1][(g & 1) * 2 + 0] = Mma<T>::pack2(pv[0], pv[1]);
-                    pb[g >> 1][(g & 1) * 2 + 1] = Mma<T>::pack2(pv[2], pv[3]);
-                    dsb[g >> 1][(g & 1) * 2 + 0] = Mma<T>::pack2(dv[0], dv[1]);
-                    dsb[g >> 1][(g & 1) * 2 + 1] = Mma<T>::pack2(dv[2], dv[3]);
-                }
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
-                        const int off = (32 * db + l32) * TROW + (2 * (2 * qs + t) + hi) * 16;
-                        const u32x4 ado = *reinterpret_cast<const u32x4*>(base + OFF_DOT + off);
-                        const u32x4 aqt = *reinterpret_cast<const u32x4*>(base + OFF_QT + off);
-                        dvt[db] = Mma<T>::mma(ado, pb[t], dvt[db]);
-                        dkt[db] = Mma<T>::mma(aqt, dsb[t], dkt[db]);
-                    }
+            for (int ks = 0; ks < NKS; ++ks) {
+                const u32x4 aq = *reinterpret_cast<const u32x4*>(base + k_off<D>(32 * qs + l32, 2 * ks + hi));
+                const u32x4 ad = *reinterpret_cast<const u32x4*>(base + OFF_DOS + k_off<D>(32 * qs + l32, 2 * ks + hi));
+                sacc = Mma<T>::mma(aq, kf[ks], sacc);
+                dpacc = Mma<T>::mma(ad, vf[ks], dpacc);
             }
+            float pv[16], dv[16];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + 32 * qs + 8 * g + 4 * hi);
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + 32 * qs + 8 * g + 4 * hi);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 4 * g + i;
+                    pv[r] = fast_exp2(fmaf(sacc[r], cl2, -l4[i]));
+                    dv[r] = dpacc[r] - d4[i];
+                }
+            }
+            if (need_mask) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int q = q0 + 32 * qs + acc_row(r, hi);
+                    const bool vis = (!CAUSAL || key <= q) && q < N && key < N;
+                    pv[r] = vis ? pv[r] : 0.f;
+                }
+            }
+            u32x4 pb[2], dsb[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int r = 8 * t + 2 * jj;
+                    pb[t][jj] = Mma<T>::pack2(pv[r], pv[r + 1]);
+                    dsb[t][jj] = Mma<T>::pack2(pv[r] * dv[r], pv[r + 1] * dv[r + 1]);
+                }
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const int off = v_off<BQ>(32 * db + l32, 2 * (2 * qs + t) + hi);
+                    const u32x4 ado = *reinterpret_cast<const u32x4*>(base + OFF_DOT + off);
+                    const u32x4 aqt = *reinterpret_cast<const u32x4*>(base + OFF_QT + off);
+                    dvt[db] = Mma<T>::mma(ado, pb[t], dvt[db]);
+                    dkt[db] = Mma<T>::mma(aqt, dsb[t], dkt[db]);
+                }
         }
         if (s + 1 < nsteps) deposit((s + 1) & 1);
         __syncthreads();
@@ -311,7 +327,7 @@ dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // provably wave-uniform
     const int l32 = lane & 31;
     const int hi = lane >> 5;
 
@@ -327,18 +343,21 @@ dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
     const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
     const size_t koff = ((size_t)b * Hkv + hk) * (size_t)N * D;
-    const uint16_t* Kh = K + koff;
-    const uint16_t* Vh = V + koff;
+    const uint32_t head_bytes = (uint32_t)N * D * 2;
+    const Buf Kb(K + koff, head_bytes), Vb(V + koff, head_bytes);
 
     const int q0 = qb * BR;
     const int qw = q0 + 32 * wave;
     const int q = qw + l32;
 
     u32x4 qf[NKS], dof[NKS];
+    {
+        const Buf Qb(Q + qoff, head_bytes), Db(dO + qoff, head_bytes);
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-        qf[ks] = q < N ? ld_global16(Q + qoff + (size_t)q * D + 16 * ks + 8 * hi) : zero_u4();
-        dof[ks] = q < N ? ld_global16(dO + qoff + (size_t)q * D + 16 * ks + 8 * hi) : zero_u4();
+        for (int ks = 0; ks < NKS; ++ks) {
+            qf[ks] = Qb.load16((uint32_t)(q * D + 16 * ks + 8 * hi) * 2);
+            dof[ks] = Db.load16((uint32_t)(q * D + 16 * ks + 8 * hi) * 2);
+        }
     }
     const size_t roff = ((size_t)b * Hq + h) * (size_t)N;
     const float lse2 = q < N ? LSE[roff + q] * kLog2e : 0.f;
@@ -358,9 +377,9 @@ dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     auto fetch = [&](int k0) {
 #pragma unroll
         for (int i = 0; i < ROWS; ++i) {
-            const int kk = k0 + key_of(i);
-            sk[i] = kk < N ? ld_global16(Kh + (size_t)kk * D + 8 * sc) : zero_u4();
-            sv[i] = kk < N ? ld_global16(Vh + (size_t)kk * D + 8 * sc) : zero_u4();
+            const uint32_t off = (uint32_t)((k0 + key_of(i)) * D + 8 * sc) * 2;
+            sk[i] = Kb.load16(off);
+            sv[i] = Vb.load16(off);
         }
     };
     auto deposit = [&](int buf) {
@@ -394,48 +413,47 @@ dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     for (int j = 0; j < ntiles; ++j) {
         const int k0 = j * BC;
         if (j + 1 < ntiles) fetch(k0 + BC);
-        const bool active = !CAUSAL || (k0 <= qw + 31);
-        if (active) {
-            const unsigned char* base = smem + (j & 1) * STAGE;
-            f32x16 st[NKB], dpt[NKB];
+        // No branch encloses the accumulating products: a wave whose rows see
+        // no key of this tile runs it with dS = 0.  One 32-key block at a time
+        // keeps a single S^T / dP^T pair live.
+        const unsigned char* base = smem + (j & 1) * STAGE;
+        const bool need_mask = (CAUSAL && k0 + BC - 1 > qw) || (k0 + BC > N);
+#pragma unroll 1
+        for (int kb = 0; kb < NKB; ++kb) {
+            f32x16 st = zero16(), dpt = zero16();
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                st[kb] = zero16();
-                dpt[kb] = zero16();
+            for (int ks = 0; ks < NKS; ++ks) {
+                const int off = k_off<D>(32 * kb + l32, 2 * ks + hi);
+                const u32x4 ak = *reinterpret_cast<const u32x4*>(base + off);
+                const u32x4 av = *reinterpret_cast<const u32x4*>(base + TB + off);
+                st = Mma<T>::mma(ak, qf[ks], st);
+                dpt = Mma<T>::mma(av, dof[ks], dpt);
+            }
+            float p[16];
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    const int off = k_off<D>(32 * kb + l32, 2 * ks + hi);
-                    const u32x4 ak = *reinterpret_cast<const u32x4*>(base + off);
-                    const u32x4 av = *reinterpret_cast<const u32x4*>(base + TB + off);
-                    st[kb] = Mma<T>::mma(ak, qf[ks], st[kb]);
-                    dpt[kb] = Mma<T>::mma(av, dof[ks], dpt[kb]);
+            for (int r = 0; r < 16; ++r) p[r] = fast_exp2(fmaf(st[r], cl2, -lse2));
+            if (need_mask) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int kk = k0 + 32 * kb + acc_row(r, hi);
+                    p[r] = ((!CAUSAL || kk <= q) && kk < N) ? p[r] : 0.f;
                 }
             }
-            u32x4 dsb[NKG];
+            u32x4 dsb[2];
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int r = 8 * t + 2 * jj;
+                    dsb[t][jj] = Mma<T>::pack2(p[r] * (dpt[r] - dlt), p[r + 1] * (dpt[r + 1] - dlt));
+                }
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        float dsv[2];
-#pragma unroll
-                        for (int u = 0; u < 2; ++u) {
-                            const int r = 8 * t + 2 * jj + u;
-                            const int kk = k0 + 32 * kb + acc_row(r, hi);
-                            const bool vis = (!CAUSAL || kk <= q) && kk < N;
-                            const float p = vis ? fast_exp2(fmaf(st[kb][r], cl2, -lse2)) : 0.f;
-                            dsv[u] = p * (dpt[kb][r] - dlt);
-                        }
-                        dsb[2 * kb + t][jj] = Mma<T>::pack2(dsv[0], dsv[1]);
-                    }
-#pragma unroll
-            for (int kg = 0; kg < NKG; ++kg)
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
                     const u32x4 a = *reinterpret_cast<const u32x4*>(
-                        base + 2 * TB + v_off<BC>(32 * db + l32, 2 * kg + hi));
-                    dq[db] = Mma<T>::mma(a, dsb[kg], dq[db]);
+                        base + 2 * TB + v_off<BC>(32 * db + l32, 2 * (2 * kb + t) + hi));
+                    dq[db] = Mma<T>::mma(a, dsb[t], dq[db]);
                 }
         }
         if (j + 1 < ntiles) deposit((j + 1) & 1);
@@ -476,7 +494,7 @@ dkdv32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const fl
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // provably wave-uniform
     const int l32 = lane & 31;
     const int hi = lane >> 5;
 
@@ -591,7 +609,7 @@ dq32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const floa
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // provably wave-uniform
     const int l32 = lane & 31;
     const int hi = lane >> 5;
 

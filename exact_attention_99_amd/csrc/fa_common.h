@@ -111,6 +111,22 @@ __device__ __forceinline__ int xcd_remap(int pid, int total) {
     return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
 }
 
+// Raw buffer resource over one tensor region of `bytes` bytes.  Loads whose
+// byte offset lies at or past `bytes` return zeros (hardware range check), so
+// rows past the end of a sequence need no branch.  The offset is always passed
+// in the per-lane operand, which the range check covers.
+struct Buf {
+    __amdgpu_buffer_rsrc_t r;
+    __device__ __forceinline__ Buf(const void* base, uint32_t bytes)
+        : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000)) {}
+    __device__ __forceinline__ u32x4 load16(uint32_t off) const {
+        return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    }
+    __device__ __forceinline__ float load_f32(uint32_t off) const {
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+    }
+};
+
 __device__ __forceinline__ u32x4 ld_global16(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }

@@ -57,7 +57,7 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // provably wave-uniform
     const int l32 = lane & 31;
     const int hi = lane >> 5;
 
@@ -73,9 +73,8 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
     const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
     const size_t koff = ((size_t)b * Hkv + hk) * (size_t)N * D;
-    const uint16_t* Qh = Q + qoff;
-    const uint16_t* Kh = K + koff;
-    const uint16_t* Vh = V + koff;
+    const uint32_t head_bytes = (uint32_t)N * D * 2;
+    const Buf Qb(Q + qoff, head_bytes), Kb(K + koff, head_bytes), Vb(V + koff, head_bytes);
 
     const int q0 = qb * BR;
     const int qw = q0 + 32 * wave;
@@ -85,7 +84,7 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     u32x4 qf[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
-        qf[ks] = (q < N) ? ld_global16(Qh + (size_t)q * D + 16 * ks + 8 * hi) : zero_u4();
+        qf[ks] = Qb.load16((uint32_t)(q * D + 16 * ks + 8 * hi) * 2);
 
     const int kv_len = CAUSAL ? min(N, q0 + BR) : N;
     const int ntiles = (kv_len + BC - 1) / BC;
@@ -104,14 +103,14 @@ fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             for (int i = 0; i < NCH; ++i) {
                 const int pos = NCH * pg + i;  // position inside the tile
                 const int key = k0 + 16 * (pos >> 4) + v_key_of_pos((pos >> 3) & 1, pos & 7);
-                stg[i] = key < N ? ld_global16(Vh + (size_t)key * D + 8 * c) : zero_u4();
+                stg[i] = Vb.load16((uint32_t)(key * D + 8 * c) * 2);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < NCH; ++i) {
                 const int ci = st + i * LOADERS;
                 const int key = k0 + ci / KCH;
-                stg[i] = key < N ? ld_global16(Kh + (size_t)key * D + 8 * (ci % KCH)) : zero_u4();
+                stg[i] = Kb.load16((uint32_t)(key * D + 8 * (ci % KCH)) * 2);
             }
         }
     };
@@ -278,7 +277,7 @@ fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const flo
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // provably wave-uniform
     const int l32 = lane & 31;
     const int hi = lane >> 5;
 
