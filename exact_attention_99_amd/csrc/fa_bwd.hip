@@ -217,8 +217,11 @@ dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
     __syncthreads();
 
+    // Prefetch and deposit run on every iteration (the last one re-fetches the
+    // last step into the buffer nobody reads again), so the compiler sees every
+    // prefetch consumed and places no wait for it ahead of the products.
     for (int s = 0; s < nsteps; ++s) {
-        if (s + 1 < nsteps) fetch(s + 1);
+        fetch(min(s + 1, nsteps - 1));
         int h, q0;
         step_rows(s, h, q0);
         // rows of this step that see only some of the wave's keys, or lie past N
@@ -277,7 +280,7 @@ dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                     dkt[db] = Mma<T>::mma(aqt, dsb[t], dkt[db]);
                 }
         }
-        if (s + 1 < nsteps) deposit((s + 1) & 1);
+        deposit((s + 1) & 1);
         __syncthreads();
     }
 
@@ -410,9 +413,11 @@ dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     deposit(0);
     __syncthreads();
 
+    // Unconditional prefetch / deposit, as in the forward pass: the extra tile
+    // is inside this head's range (rows past N read as zeros).
     for (int j = 0; j < ntiles; ++j) {
         const int k0 = j * BC;
-        if (j + 1 < ntiles) fetch(k0 + BC);
+        fetch(k0 + BC);
         // No branch encloses the accumulating products: a wave whose rows see
         // no key of this tile runs it with dS = 0.  One 32-key block at a time
         // keeps a single S^T / dP^T pair live.
@@ -456,7 +461,7 @@ dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                     dq[db] = Mma<T>::mma(a, dsb[t], dq[db]);
                 }
         }
-        if (j + 1 < ntiles) deposit((j + 1) & 1);
+        deposit((j + 1) & 1);
         __syncthreads();
     }
 

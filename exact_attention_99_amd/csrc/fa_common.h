@@ -127,6 +127,31 @@ struct Buf {
     }
 };
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Asynchronous copy of 16 bytes per lane from a buffer (byte offset `off`,
+// zeros past the range) into LDS at `lds + 16 * lane`; `lds` must be
+// wave-uniform.  Completion is tracked by the vector-memory counter.
+__device__ __forceinline__ void buf_to_lds16(const Buf& b, void* lds, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(b.r, (lds_ptr_t)lds, 16, (int)off, 0, 0, 0);
+}
+
+// Wait until this wave's outstanding vector-memory operations (including
+// buffer-to-LDS copies) have completed.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i receives element (i % 4) of the 8-byte chunk addressed by lane
+// 4*k + i/4, for k = 0..3: when lane s addresses row r0 + s/4, columns
+// c0 + 4*(s % 4) .. +3 of a row-major 16-bit tile, lane i gets
+// column c0 + i of rows r0 .. r0 + 3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+
 __device__ __forceinline__ u32x4 ld_global16(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
@@ -152,6 +177,34 @@ __device__ __forceinline__ int k_off(int row, int chunk) {
 template <int BC>
 __device__ __forceinline__ int v_off(int row, int chunk) {
     return row * (BC * 2) + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
+}
+
+// LDS on gfx950 serves a 128-bit read for 16 lanes per cycle across 64 banks
+// (256 bytes), and a 64-bit read for 32 lanes.  The layouts below keep every
+// such group of lanes on distinct banks (and also every 8-lane group within a
+// 128-byte window).
+//
+// Row-major tile read as an MFMA A operand (lane l32 reads row l32, one
+// 16-byte chunk): chunk c of row r is stored at c ^ (r & 15) for 16 chunks
+// per row, c ^ ((r ^ (r >> 3)) & 7) for 8.
+template <int D>
+__device__ __forceinline__ int kq_off(int row, int chunk) {
+    const int sw = (D == 128) ? (row & 15) : ((row ^ (row >> 3)) & 7);
+    return row * (D * 2) + ((chunk ^ sw) << 4);
+}
+
+// Row-major tile read with the transposing read (four rows of 32 bytes per
+// 16-lane group, 64 bytes per 32-lane group): chunk c of row r is stored at
+// c ^ s(r & 3) with s = {0, 6, 12, 10} for 16 chunks per row (distinct in
+// chunk bits 1-2 and 2-3), s = {0, 2, 4, 6} for 8.
+template <int D>
+__device__ __forceinline__ int tr_swz(int row) {
+    if (D == 128) return ((row & 1) * 6) ^ (((row >> 1) & 1) * 12);
+    return 2 * (row & 3);
+}
+template <int D>
+__device__ __forceinline__ int vt_off(int row, int byte_in_row) {
+    return row * (D * 2) + ((((byte_in_row >> 4) ^ tr_swz<D>(row)) << 4) | (byte_in_row & 15));
 }
 
 // Inside a 16-element group of a transposed tile, elements are stored in the
