@@ -38,6 +38,16 @@ int fwd_variant() {
     return v;
 }
 
+int bwd_variant() {
+    // Kernel generation of the 16-bit backward passes; FA355_BWD_VARIANT
+    // overrides the default for comparisons.
+    static const int v = [] {
+        const char* e = getenv("FA355_BWD_VARIANT");
+        return e ? atoi(e) : 0;
+    }();
+    return v;
+}
+
 }  // namespace
 
 extern "C" {
@@ -102,6 +112,7 @@ fa355::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void*
     a.scale = scale;
     a.cl2 = scale * kLog2eHost;
     a.dtype = (int)dtype;
+    a.variant = bwd_variant();
     a.stream = stream;
     return a;
 }

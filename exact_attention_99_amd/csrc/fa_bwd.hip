@@ -480,6 +480,388 @@ dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 }
 
 // ---------------------------------------------------------------------------
+// Second-generation dK / dV kernel.  Same work split as dkdv16_kernel, but the
+// Q and dO tiles arrive in LDS through buffer-to-LDS copies (no staging
+// registers, rows past N read as zeros) and are stored row-major only, with a
+// swizzle that suits both ways they are read: 128-bit reads of 16 consecutive
+// rows for the A operands of S = Q K^T and dP = dO V^T, and transposing reads
+// for the A operands of dV^T += dO^T P and dK^T += Q^T dS.
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(256)
+dkdv16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                const float* __restrict__ LSE, const float* __restrict__ Delta,
+                uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int B, int Hq, int Hkv, int N,
+                float cl2, float scale) {
+    constexpr int NW = 4;
+    constexpr int BKV = 128;
+    constexpr int BQ = 8192 / D;
+    constexpr int NQB = BQ / 32;
+    constexpr int KCH = D / 8;
+    constexpr int TB = BQ * D * 2;            // one tile, bytes
+    constexpr int OFF_DOS = TB;
+    constexpr int OFF_LSE = 2 * TB;
+    constexpr int OFF_DL = OFF_LSE + BQ * 4;
+    constexpr int STAGE = OFF_DL + BQ * 4;
+    constexpr int NDB = D / 32;
+    constexpr int NKS = D / 16;
+    constexpr int WI = TB / 1024;             // 1 KB wave copies per tile
+    static_assert(WI % NW == 0, "tile copies split evenly over the waves");
+    constexpr int IPW = WI / NW;
+    static_assert(BQ <= 128, "row terms staged by the first 2*BQ threads");
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+
+    const int nkb = (N + BKV - 1) / BKV;
+    const int total = nkb * Hkv * B;
+    const int logical = xcd_remap((int)blockIdx.x, total);
+    const int jb = logical % nkb;  // ascending: under a causal mask block 0 is the longest
+    const int bhk = logical / nkb;
+    const int hk = bhk % Hkv;
+    const int b = bhk / Hkv;
+    const int G = Hq / Hkv;
+
+    const int kv0 = jb * BKV;
+    const int kw = kv0 + 32 * wave;
+    const int key = kw + l32;
+    const size_t kvoff = ((size_t)b * Hkv + hk) * (size_t)N * D;
+    const uint32_t head_bytes = (uint32_t)N * D * 2;
+
+    u32x4 kf[NKS], vf[NKS];
+    {
+        const Buf Kb(K + kvoff, head_bytes), Vb(V + kvoff, head_bytes);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            kf[ks] = Kb.load16((uint32_t)(key * D + 16 * ks + 8 * hi) * 2);
+            vf[ks] = Vb.load16((uint32_t)(key * D + 16 * ks + 8 * hi) * 2);
+        }
+    }
+
+    f32x16 dkt[NDB], dvt[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        dkt[db] = zero16();
+        dvt[db] = zero16();
+    }
+
+    const int qb_first = CAUSAL ? kv0 / BQ : 0;
+    const int qb_count = (N + BQ - 1) / BQ - qb_first;
+    const int nsteps = G * qb_count;
+
+    // copy slots: this wave's copy i fills bytes [1024*bi, 1024*bi + 1024) of
+    // the Q and dO tiles; cp[i] is the lane's source offset relative to the
+    // step's first row
+    uint32_t cp[IPW];
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+        const int p = (wave + NW * i) * 64 + lane;
+        const int row = p / KCH, pc = p % KCH;
+        cp[i] = (uint32_t)(row * D * 2 + 16 * (pc ^ dual_swz<D>(row)));
+    }
+    float sx = 0.f;
+
+    auto step_rows = [&](int s, int& h, int& q0) {
+        h = hk * G + s / qb_count;
+        q0 = (qb_first + s % qb_count) * BQ;
+    };
+    auto issue = [&](int s, int buf) {
+        int h, q0;
+        step_rows(s, h, q0);
+        const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
+        const Buf Qb(Q + qoff, head_bytes), Db(dO + qoff, head_bytes);
+        unsigned char* base = smem + buf * STAGE;
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            const uint32_t off = (uint32_t)q0 * D * 2 + cp[i];
+            buf_to_lds16(Qb, base + (wave + NW * i) * 1024, off);
+            buf_to_lds16(Db, base + OFF_DOS + (wave + NW * i) * 1024, off);
+        }
+        const size_t roff = ((size_t)b * Hq + h) * (size_t)N;
+        if (tid < BQ)
+            sx = Buf(LSE + roff, (uint32_t)N * 4).load_f32((uint32_t)(q0 + tid) * 4) * kLog2e;
+        else if (tid >= 128 && tid < 128 + BQ)
+            sx = Buf(Delta + roff, (uint32_t)N * 4).load_f32((uint32_t)(q0 + tid - 128) * 4);
+    };
+    auto put_rows = [&](int buf) {
+        unsigned char* base = smem + buf * STAGE;
+        if (tid < BQ)
+            reinterpret_cast<float*>(base + OFF_LSE)[tid] = sx;
+        else if (tid >= 128 && tid < 128 + BQ)
+            reinterpret_cast<float*>(base + OFF_DL)[tid - 128] = sx;
+    };
+
+    // transposing-read coordinates of this lane inside a (16-row, 32-dim) block
+    const int g16 = lane >> 4;
+    const int j16 = lane & 15;
+    const int tr_row = 4 * hi + (j16 >> 2);
+    const int tr_col = 2 * (16 * (g16 & 1) + 4 * (j16 & 3));
+
+    if (nsteps > 0) {
+        issue(0, 0);
+        put_rows(0);
+        wait_vmem();
+    }
+    __syncthreads();
+
+    for (int s = 0; s < nsteps; ++s) {
+        // The copy of the next step runs on every iteration (the last one
+        // re-copies the last step into the buffer nobody reads again).
+        issue(min(s + 1, nsteps - 1), (s + 1) & 1);
+        int h, q0;
+        step_rows(s, h, q0);
+        const bool need_mask = (CAUSAL && q0 < kw + 32) || (q0 + BQ > N) || (kw + 32 > N);
+        const unsigned char* base = smem + (s & 1) * STAGE;
+        const float* lse2s = reinterpret_cast<const float*>(base + OFF_LSE);
+        const float* dls = reinterpret_cast<const float*>(base + OFF_DL);
+#pragma unroll 1
+        for (int qs = 0; qs < NQB; ++qs) {
+            f32x16 sacc = zero16(), dpacc = zero16();
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const int off = dual_off<D>(32 * qs + l32, 16 * (2 * ks + hi));
+                const u32x4 aq = *reinterpret_cast<const u32x4*>(base + off);
+                const u32x4 ad = *reinterpret_cast<const u32x4*>(base + OFF_DOS + off);
+                sacc = Mma<T>::mma(aq, kf[ks], sacc);
+                dpacc = Mma<T>::mma(ad, vf[ks], dpacc);
+            }
+            float pv[16], dv[16];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + 32 * qs + 8 * g + 4 * hi);
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + 32 * qs + 8 * g + 4 * hi);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 4 * g + i;
+                    pv[r] = fast_exp2(fmaf(sacc[r], cl2, -l4[i]));
+                    dv[r] = dpacc[r] - d4[i];
+                }
+            }
+            if (need_mask) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int q = q0 + 32 * qs + acc_row(r, hi);
+                    const bool vis = (!CAUSAL || key <= q) && q < N && key < N;
+                    pv[r] = vis ? pv[r] : 0.f;
+                }
+            }
+            u32x4 pb[2], dsb[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int r = 8 * t + 2 * jj;
+                    pb[t][jj] = Mma<T>::pack2(pv[r], pv[r + 1]);
+                    dsb[t][jj] = Mma<T>::pack2(pv[r] * dv[r], pv[r + 1] * dv[r + 1]);
+                }
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const int row = 32 * qs + 16 * t + tr_row;
+                    const int col = 64 * db + tr_col;
+                    const int o_lo = dual_off<D>(row, col), o_up = dual_off<D>(row + 8, col);
+                    const u32x2 d_lo = lds_read_tr16(base + OFF_DOS + o_lo);
+                    const u32x2 d_up = lds_read_tr16(base + OFF_DOS + o_up);
+                    const u32x2 q_lo = lds_read_tr16(base + o_lo);
+                    const u32x2 q_up = lds_read_tr16(base + o_up);
+                    u32x4 ado, aqt;
+                    ado[0] = d_lo[0]; ado[1] = d_lo[1]; ado[2] = d_up[0]; ado[3] = d_up[1];
+                    aqt[0] = q_lo[0]; aqt[1] = q_lo[1]; aqt[2] = q_up[0]; aqt[3] = q_up[1];
+                    dvt[db] = Mma<T>::mma(ado, pb[t], dvt[db]);
+                    dkt[db] = Mma<T>::mma(aqt, dsb[t], dkt[db]);
+                }
+        }
+        put_rows((s + 1) & 1);
+        wait_vmem();
+        __syncthreads();
+    }
+
+    if (key < N) {
+        uint16_t* dkrow = dK + kvoff + (size_t)key * D;
+        uint16_t* dvrow = dV + kvoff + (size_t)key * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                u32x2 wk, wv;
+                wk[0] = Mma<T>::pack2(dkt[db][4 * g] * scale, dkt[db][4 * g + 1] * scale);
+                wk[1] = Mma<T>::pack2(dkt[db][4 * g + 2] * scale, dkt[db][4 * g + 3] * scale);
+                wv[0] = Mma<T>::pack2(dvt[db][4 * g], dvt[db][4 * g + 1]);
+                wv[1] = Mma<T>::pack2(dvt[db][4 * g + 2], dvt[db][4 * g + 3]);
+                *reinterpret_cast<u32x2*>(dkrow + 32 * db + 8 * g + 4 * hi) = wk;
+                *reinterpret_cast<u32x2*>(dvrow + 32 * db + 8 * g + 4 * hi) = wv;
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Second-generation dQ kernel: K and V tiles arrive by buffer-to-LDS copies,
+// row-major only; K^T operands of dQ^T += K^T dS^T come from transposing reads
+// of the same K tile (dual swizzle), so no transposed copy is built.
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(256)
+dq16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+              const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+              const float* __restrict__ LSE, const float* __restrict__ Delta,
+              uint16_t* __restrict__ dQ, int B, int Hq, int Hkv, int N, float cl2, float scale) {
+    constexpr int NW = 4;
+    constexpr int BR = 32 * NW;
+    constexpr int BC = D == 128 ? 64 : 128;
+    constexpr int KCH = D / 8;
+    constexpr int TB = BC * D * 2;
+    constexpr int STAGE = 2 * TB;
+    constexpr int NKB = BC / 32;
+    constexpr int NDB = D / 32;
+    constexpr int NKS = D / 16;
+    constexpr int WI = TB / 1024;
+    static_assert(WI % NW == 0, "tile copies split evenly over the waves");
+    constexpr int IPW = WI / NW;
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+
+    const int nqb = (N + BR - 1) / BR;
+    const int total = nqb * Hq * B;
+    const int logical = xcd_remap((int)blockIdx.x, total);
+    const int qb_raw = logical % nqb;
+    const int bh = logical / nqb;
+    const int qb = CAUSAL ? (nqb - 1 - qb_raw) : qb_raw;
+    const int h = bh % Hq;
+    const int b = bh / Hq;
+    const int hk = h / (Hq / Hkv);
+
+    const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
+    const size_t koff = ((size_t)b * Hkv + hk) * (size_t)N * D;
+    const uint32_t head_bytes = (uint32_t)N * D * 2;
+    const Buf Kb(K + koff, head_bytes), Vb(V + koff, head_bytes);
+
+    const int q0 = qb * BR;
+    const int qw = q0 + 32 * wave;
+    const int q = qw + l32;
+
+    u32x4 qf[NKS], dof[NKS];
+    {
+        const Buf Qb(Q + qoff, head_bytes), Db(dO + qoff, head_bytes);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            qf[ks] = Qb.load16((uint32_t)(q * D + 16 * ks + 8 * hi) * 2);
+            dof[ks] = Db.load16((uint32_t)(q * D + 16 * ks + 8 * hi) * 2);
+        }
+    }
+    const size_t roff = ((size_t)b * Hq + h) * (size_t)N;
+    const float lse2 = Buf(LSE + roff, (uint32_t)N * 4).load_f32((uint32_t)q * 4) * kLog2e;
+    const float dlt = Buf(Delta + roff, (uint32_t)N * 4).load_f32((uint32_t)q * 4);
+
+    const int kv_len = CAUSAL ? min(N, q0 + BR) : N;
+    const int ntiles = (kv_len + BC - 1) / BC;
+
+    uint32_t cp[IPW];
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+        const int p = (wave + NW * i) * 64 + lane;
+        const int row = p / KCH, pc = p % KCH;
+        cp[i] = (uint32_t)(row * D * 2 + 16 * (pc ^ dual_swz<D>(row)));
+    }
+    auto issue = [&](int k0, int buf) {
+        unsigned char* base = smem + buf * STAGE;
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            const uint32_t off = (uint32_t)k0 * D * 2 + cp[i];
+            buf_to_lds16(Kb, base + (wave + NW * i) * 1024, off);
+            buf_to_lds16(Vb, base + TB + (wave + NW * i) * 1024, off);
+        }
+    };
+
+    const int g16 = lane >> 4;
+    const int j16 = lane & 15;
+    const int tr_row = 4 * hi + (j16 >> 2);
+    const int tr_col = 2 * (16 * (g16 & 1) + 4 * (j16 & 3));
+
+    f32x16 dq[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) dq[db] = zero16();
+
+    issue(0, 0);
+    wait_vmem();
+    __syncthreads();
+
+    for (int j = 0; j < ntiles; ++j) {
+        const int k0 = j * BC;
+        issue(k0 + BC, (j + 1) & 1);
+        const unsigned char* base = smem + (j & 1) * STAGE;
+        const bool need_mask = (CAUSAL && k0 + BC - 1 > qw) || (k0 + BC > N);
+#pragma unroll 1
+        for (int kb = 0; kb < NKB; ++kb) {
+            f32x16 st = zero16(), dpt = zero16();
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const int off = dual_off<D>(32 * kb + l32, 16 * (2 * ks + hi));
+                const u32x4 ak = *reinterpret_cast<const u32x4*>(base + off);
+                const u32x4 av = *reinterpret_cast<const u32x4*>(base + TB + off);
+                st = Mma<T>::mma(ak, qf[ks], st);
+                dpt = Mma<T>::mma(av, dof[ks], dpt);
+            }
+            float p[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) p[r] = fast_exp2(fmaf(st[r], cl2, -lse2));
+            if (need_mask) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int kk = k0 + 32 * kb + acc_row(r, hi);
+                    p[r] = ((!CAUSAL || kk <= q) && kk < N) ? p[r] : 0.f;
+                }
+            }
+            u32x4 dsb[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int r = 8 * t + 2 * jj;
+                    dsb[t][jj] = Mma<T>::pack2(p[r] * (dpt[r] - dlt), p[r + 1] * (dpt[r + 1] - dlt));
+                }
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const int row = 32 * kb + 16 * t + tr_row;
+                    const int col = 64 * db + tr_col;
+                    const u32x2 lo = lds_read_tr16(base + dual_off<D>(row, col));
+                    const u32x2 up = lds_read_tr16(base + dual_off<D>(row + 8, col));
+                    u32x4 a;
+                    a[0] = lo[0]; a[1] = lo[1]; a[2] = up[0]; a[3] = up[1];
+                    dq[db] = Mma<T>::mma(a, dsb[t], dq[db]);
+                }
+        }
+        wait_vmem();
+        __syncthreads();
+    }
+
+    if (q < N) {
+        uint16_t* row = dQ + qoff + (size_t)q * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                u32x2 w;
+                w[0] = Mma<T>::pack2(dq[db][4 * g] * scale, dq[db][4 * g + 1] * scale);
+                w[1] = Mma<T>::pack2(dq[db][4 * g + 2] * scale, dq[db][4 * g + 3] * scale);
+                *reinterpret_cast<u32x2*>(row + 32 * db + 8 * g + 4 * hi) = w;
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 inputs: the same two passes with the fp32 matrix-core op (32x32x2), P
 // and dS kept in fp32, single-buffered LDS tiles with padded rows.
 template <int D, bool CAUSAL>
@@ -716,6 +1098,13 @@ hipError_t prepare32(const BwdArgs& a) {
 template <typename T, int D, bool CAUSAL>
 hipError_t dkdv16(const BwdArgs& a) {
     const int nkb = (a.N + 127) / 128;
+    if (a.variant == 0) {
+        hipLaunchKernelGGL((dkdv16v2_kernel<T, D, CAUSAL>), dim3((unsigned)(nkb * a.Hkv * a.B)),
+                           dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                           (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
+                           (uint16_t*)a.dk, (uint16_t*)a.dv, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL((dkdv16_kernel<T, D, CAUSAL>), dim3((unsigned)(nkb * a.Hkv * a.B)), dim3(256), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv,
@@ -726,6 +1115,13 @@ hipError_t dkdv16(const BwdArgs& a) {
 template <typename T, int D, bool CAUSAL>
 hipError_t dq16(const BwdArgs& a) {
     const int nqb = (a.N + 127) / 128;
+    if (a.variant == 0) {
+        hipLaunchKernelGGL((dq16v2_kernel<T, D, CAUSAL>), dim3((unsigned)(nqb * a.Hq * a.B)),
+                           dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                           (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
+                           (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL((dq16_kernel<T, D, CAUSAL>), dim3((unsigned)(nqb * a.Hq * a.B)), dim3(256), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, a.B, a.Hq, a.Hkv,

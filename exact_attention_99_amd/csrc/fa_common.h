@@ -207,6 +207,23 @@ __device__ __forceinline__ int vt_off(int row, int byte_in_row) {
     return row * (D * 2) + ((((byte_in_row >> 4) ^ tr_swz<D>(row)) << 4) | (byte_in_row & 15));
 }
 
+// Row-major tile read both ways: as MFMA A operands (16 consecutive rows per
+// 128-bit read) and through the transposing read (4-row groups).  Chunk c of
+// row r is stored at c ^ sw(r) with sw(r) = f[r & 3] ^ ((r >> 2) & 3),
+// f = {0, 4, 10, 14} for 16 chunks per row and {0, 2, 4, 6} for 8: distinct
+// for 16 consecutive rows, and within each aligned 4-row group distinct in
+// chunk bits 1-2 and 2-3 (64-bank and 32-bank conflict-free for both reads).
+template <int D>
+__device__ __forceinline__ int dual_swz(int row) {
+    const int r3 = row & 3;
+    const int f = (D == 128) ? ((r3 & 1) * 4 + (r3 >> 1) * 10) : 2 * r3;
+    return f ^ ((row >> 2) & 3);
+}
+template <int D>
+__device__ __forceinline__ int dual_off(int row, int byte_in_row) {
+    return row * (D * 2) + ((((byte_in_row >> 4) ^ dual_swz<D>(row)) << 4) | (byte_in_row & 15));
+}
+
 // Inside a 16-element group of a transposed tile, elements are stored in the
 // order in which a 32x32 accumulator hands them to the next product as its B
 // operand: position 8*h + i (h = lane half, i = 0..7) holds element

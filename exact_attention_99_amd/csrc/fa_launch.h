@@ -36,6 +36,7 @@ struct BwdArgs {
     float scale;
     float cl2;
     int dtype;
+    int variant;     // kernel generation of the 16-bit passes (0 = default)
     hipStream_t stream;
 };
 
