@@ -700,6 +700,293 @@ dkdv16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
 }
 
+// Segment seg of a dK/dV query tile of NQB blocks: 0 and the odd segments
+// before the last hold the S/dP products of block (seg + 1) / 2; the others the
+// dV/dK products of block seg / 2 - 1, and the last one those of block NQB - 1.
+template <int NQB>
+__host__ __device__ constexpr bool dkdv_seg_is_s(int seg) {
+    return seg == 0 || ((seg & 1) && seg < 2 * NQB - 1);
+}
+template <int NQB>
+__host__ __device__ constexpr int dkdv_seg_block(int seg) {
+    return dkdv_seg_is_s<NQB>(seg) ? (seg + 1) / 2 : (seg == 2 * NQB - 1 ? NQB - 1 : seg / 2 - 1);
+}
+
+// ---------------------------------------------------------------------------
+// Software-pipelined dK / dV kernel.  One wave per SIMD (the dK/dV
+// accumulators and the K/V operands fill most of the register file), so the
+// overlap of matrix work, softmax arithmetic and LDS traffic has to come from
+// the instruction order of a single wave.  A query tile of NQB 32-row blocks
+// is one fixed sequence of MFMA slots:
+//   S/dP(0) | S/dP(1) | dV,dK(0) | S/dP(2) | dV,dK(1) | ... | dV,dK(NQB-1)
+// Every slot's A operand (a Q or dO row chunk for S/dP, a pair of transposing
+// dO^T or Q^T reads for dV/dK) is read from LDS a fixed number of slots ahead,
+// so only a small window of operands is live.  The softmax and dS arithmetic
+// of block b runs in the slots of the dV/dK products of block b-1 (block 0's
+// runs between the first two segments), and block b's row terms are read
+// during its S/dP segment.  Query tiles (Q, dO) of 16384/D rows are
+// double-buffered in LDS and filled by buffer-to-LDS copies.  Rows past N read
+// as zeros (Q, dO, the logsumexp and D row terms alike), which makes their
+// P * (dP - D) and P^T dO contributions exactly zero, and keys past N are never
+// written back, so only the causal condition needs a mask.
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(256)
+dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                const float* __restrict__ LSE, const float* __restrict__ Delta,
+                uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int B, int Hq, int Hkv, int N,
+                float cl2, float scale) {
+    constexpr int NW = 4;
+    constexpr int BKV = 128;
+    constexpr int BQ = 16384 / D;
+    constexpr int NQB = BQ / 32;
+    constexpr int KCH = D / 8;
+    constexpr int TB = BQ * D * 2;
+    constexpr int OFF_DOS = TB;
+    constexpr int OFF_LSE = 2 * TB;
+    constexpr int OFF_DL = OFF_LSE + BQ * 4;
+    constexpr int STAGE = OFF_DL + BQ * 4;
+    constexpr int NDB = D / 32;
+    constexpr int NKS = D / 16;
+    constexpr int WI = TB / 1024;
+    static_assert(WI % NW == 0, "tile copies split evenly over the waves");
+    constexpr int IPW = WI / NW;
+    static_assert(BQ <= 256, "row terms staged one per thread");
+    constexpr int NSLOT = 2 * NKS;          // MFMAs per segment (== 4 * NDB)
+    static_assert(NSLOT == 4 * NDB, "S/dP and dV/dK segments hold the same MFMA count");
+    constexpr int EPS = 16 / NSLOT;         // softmax elements per slot
+    constexpr int NSEG = 2 * NQB;
+    constexpr int TSLOT = NSEG * NSLOT;
+    constexpr int AHEAD = 4;                // operand read distance, in slots
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+
+    const int nkb = (N + BKV - 1) / BKV;
+    const int total = nkb * Hkv * B;
+    const int logical = xcd_remap((int)blockIdx.x, total);
+    const int jb = logical % nkb;
+    const int bhk = logical / nkb;
+    const int hk = bhk % Hkv;
+    const int b = bhk / Hkv;
+    const int G = Hq / Hkv;
+
+    const int kv0 = jb * BKV;
+    const int kw = kv0 + 32 * wave;
+    const int key = kw + l32;
+    const size_t kvoff = ((size_t)b * Hkv + hk) * (size_t)N * D;
+    const uint32_t head_bytes = (uint32_t)N * D * 2;
+
+    u32x4 kf[NKS], vf[NKS];
+    {
+        const Buf Kb(K + kvoff, head_bytes), Vb(V + kvoff, head_bytes);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            kf[ks] = Kb.load16((uint32_t)(key * D + 16 * ks + 8 * hi) * 2);
+            vf[ks] = Vb.load16((uint32_t)(key * D + 16 * ks + 8 * hi) * 2);
+        }
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            // keep the B operands in the accumulation registers, leaving the
+            // vector registers to the pipeline
+            asm volatile("" : "+a"(kf[ks]));
+            asm volatile("" : "+a"(vf[ks]));
+        }
+    }
+
+    f32x16 dkt[NDB], dvt[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        dkt[db] = zero16();
+        dvt[db] = zero16();
+    }
+
+    const int qb_first = CAUSAL ? kv0 / BQ : 0;
+    const int qb_count = (N + BQ - 1) / BQ - qb_first;
+    const int nsteps = G * qb_count;
+
+    uint32_t cp[IPW];
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+        const int p = (wave + NW * i) * 64 + lane;
+        const int row = p / KCH, pc = p % KCH;
+        cp[i] = (uint32_t)(row * D * 2 + 16 * (pc ^ dual_swz<D>(row)));
+    }
+    float sl = 0.f, sd = 0.f;
+
+    auto step_rows = [&](int s, int& h, int& q0) {
+        h = hk * G + s / qb_count;
+        q0 = (qb_first + s % qb_count) * BQ;
+    };
+    auto issue = [&](int s, int buf) {
+        int h, q0;
+        step_rows(s, h, q0);
+        const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
+        const Buf Qb(Q + qoff, head_bytes), Db(dO + qoff, head_bytes);
+        unsigned char* base = smem + buf * STAGE;
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            const uint32_t off = (uint32_t)q0 * D * 2 + cp[i];
+            buf_to_lds16(Qb, base + (wave + NW * i) * 1024, off);
+            buf_to_lds16(Db, base + OFF_DOS + (wave + NW * i) * 1024, off);
+        }
+        const size_t roff = ((size_t)b * Hq + h) * (size_t)N;
+        if (tid < BQ) {
+            sl = Buf(LSE + roff, (uint32_t)N * 4).load_f32((uint32_t)(q0 + tid) * 4) * kLog2e;
+            sd = Buf(Delta + roff, (uint32_t)N * 4).load_f32((uint32_t)(q0 + tid) * 4);
+        }
+    };
+    auto put_rows = [&](int buf) {
+        unsigned char* base = smem + buf * STAGE;
+        if (tid < BQ) {
+            reinterpret_cast<float*>(base + OFF_LSE)[tid] = sl;
+            reinterpret_cast<float*>(base + OFF_DL)[tid] = sd;
+        }
+    };
+
+    const int g16 = lane >> 4;
+    const int j16 = lane & 15;
+    const int tr_row = 4 * hi + (j16 >> 2);
+    const int tr_col = 2 * (16 * (g16 & 1) + 4 * (j16 & 3));
+
+    // Segment seg of a tile: 0 and odd segments before the last hold the S/dP
+    // products of block (seg + 1) / 2; the others the dV/dK products of block
+    // seg / 2 - 1, and the last one those of block NQB - 1.
+    // mlim: element (block blk, row offset o) of this lane is visible when
+    // 32 blk + o >= mlim (causal: the query row is at or after the key)
+    auto run_step = [&](const unsigned char* base, int mlim) {
+        u32x4 op[TSLOT];
+        f32x16 sacc = zero16(), dpacc = zero16();
+        u32x4 pb[2][2], dsb[2][2];
+        f32x4 lc[4], dc[4];
+
+        auto load_op = [&](auto nc) {
+            constexpr int n = decltype(nc)::value;
+            constexpr int seg = n / NSLOT, j = n % NSLOT;
+            constexpr int blk = dkdv_seg_block<NQB>(seg);
+            if constexpr (dkdv_seg_is_s<NQB>(seg)) {
+                constexpr int ks = j >> 1;
+                const int off = dual_off<D>(32 * blk + l32, 16 * (2 * ks + hi));
+                op[n] = *reinterpret_cast<const u32x4*>(base + ((j & 1) ? OFF_DOS : 0) + off);
+            } else {
+                constexpr int t = j / (2 * NDB), db = (j >> 1) % NDB;
+                const int row = 32 * blk + 16 * t + tr_row;
+                const unsigned char* tb = base + ((j & 1) ? 0 : OFF_DOS);
+                const u32x2 lo = lds_read_tr16(tb + dual_off<D>(row, 64 * db + tr_col));
+                const u32x2 up = lds_read_tr16(tb + dual_off<D>(row + 8, 64 * db + tr_col));
+                op[n] = u32x4{lo[0], lo[1], up[0], up[1]};
+            }
+        };
+        auto load_rows = [&](int blk, int k) {
+            const int g = k >> 1;
+            const int ro = 32 * blk + 8 * g + 4 * hi;
+            if (k & 1)
+                dc[g] = *reinterpret_cast<const f32x4*>(base + OFF_DL + 4 * ro);
+            else
+                lc[g] = *reinterpret_cast<const f32x4*>(base + OFF_LSE + 4 * ro);
+        };
+        // softmax and dS of element r of block blk (row 32 blk + acc_row(r, hi))
+        float pv[16], dsv[16];
+        auto soft = [&](int blk, int r) {
+            const int g = r >> 2, i = r & 3;
+            float p = fast_exp2(fmaf(sacc[r], cl2, -lc[g][i]));
+            if (CAUSAL) p = (32 * blk + 8 * g + i >= mlim) ? p : 0.f;
+            pv[r] = p;
+            dsv[r] = p * (dpacc[r] - dc[g][i]);
+            if (r & 1) {
+                const int par = blk & 1;
+                pb[par][r >> 3][(r & 7) >> 1] = Mma<T>::pack2(pv[r - 1], pv[r]);
+                dsb[par][r >> 3][(r & 7) >> 1] = Mma<T>::pack2(dsv[r - 1], dsv[r]);
+            }
+        };
+
+#pragma unroll
+        for (int k = 0; k < 8; ++k) load_rows(0, k);
+        static_for<AHEAD>([&](auto nc) { load_op(nc); });
+        static_for<TSLOT>([&](auto nc) {
+            constexpr int n = decltype(nc)::value;
+            constexpr int seg = n / NSLOT, j = n % NSLOT;
+            constexpr bool is_s = dkdv_seg_is_s<NQB>(seg);
+            constexpr int blk = dkdv_seg_block<NQB>(seg);
+            if constexpr (n == NSLOT) {
+                // block 0's softmax has no matrix work to overlap with
+#pragma unroll
+                for (int r = 0; r < 16; ++r) soft(0, r);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (n + AHEAD < TSLOT) load_op(std::integral_constant<int, n + AHEAD>{});
+            if constexpr (is_s) {
+                constexpr int ks = j >> 1;
+                if constexpr (j & 1)
+                    dpacc = Mma<T>::mma(op[n], vf[ks], ks == 0 ? zero16() : dpacc);
+                else
+                    sacc = Mma<T>::mma(op[n], kf[ks], ks == 0 ? zero16() : sacc);
+                // the softmax reads S and dP with vector instructions
+                if constexpr (j == NSLOT - 2) asm volatile("" : "+v"(sacc));
+                if constexpr (j == NSLOT - 1) asm volatile("" : "+v"(dpacc));
+            } else {
+                constexpr int t = j / (2 * NDB), db = (j >> 1) % NDB;
+                constexpr int par = blk & 1;
+                if constexpr (j & 1)
+                    dkt[db] = Mma<T>::mma(op[n], dsb[par][t], dkt[db]);
+                else
+                    dvt[db] = Mma<T>::mma(op[n], pb[par][t], dvt[db]);
+            }
+            if constexpr (!is_s && seg < NSEG - 1) {
+                // a dV/dK segment of block seg/2 - 1 carries the softmax of block seg/2
+#pragma unroll
+                for (int e = 0; e < EPS; ++e) soft(seg / 2, j * EPS + e);
+            } else if constexpr (is_s && seg > 0 && j >= NSLOT - 8) {
+                // row terms of the block whose S/dP this segment computes
+                load_rows(blk, j - (NSLOT - 8));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+
+    if (nsteps > 0) {
+        issue(0, 0);
+        put_rows(0);
+        wait_vmem();
+    }
+    __syncthreads();
+
+    for (int s = 0; s < nsteps; ++s) {
+        issue(min(s + 1, nsteps - 1), (s + 1) & 1);
+        int h, q0;
+        step_rows(s, h, q0);
+        (void)h;
+        const unsigned char* base = smem + (s & 1) * STAGE;
+        // rows q0 + 4 hi + (32 blk + 8 g + i); visible when that row >= key
+        run_step(base, (CAUSAL && q0 < kw + 31) ? key - q0 - 4 * hi : INT_MIN);
+        put_rows((s + 1) & 1);
+        wait_vmem();
+        __syncthreads();
+    }
+
+    if (key < N) {
+        uint16_t* dkrow = dK + kvoff + (size_t)key * D;
+        uint16_t* dvrow = dV + kvoff + (size_t)key * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                u32x2 wk, wv;
+                wk[0] = Mma<T>::pack2(dkt[db][4 * g] * scale, dkt[db][4 * g + 1] * scale);
+                wk[1] = Mma<T>::pack2(dkt[db][4 * g + 2] * scale, dkt[db][4 * g + 3] * scale);
+                wv[0] = Mma<T>::pack2(dvt[db][4 * g], dvt[db][4 * g + 1]);
+                wv[1] = Mma<T>::pack2(dvt[db][4 * g + 2], dvt[db][4 * g + 3]);
+                *reinterpret_cast<u32x2*>(dkrow + 32 * db + 8 * g + 4 * hi) = wk;
+                *reinterpret_cast<u32x2*>(dvrow + 32 * db + 8 * g + 4 * hi) = wv;
+            }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Second-generation dQ kernel: K and V tiles arrive by buffer-to-LDS copies,
 // row-major only; K^T operands of dQ^T += K^T dS^T come from transposing reads
@@ -1099,6 +1386,13 @@ template <typename T, int D, bool CAUSAL>
 hipError_t dkdv16(const BwdArgs& a) {
     const int nkb = (a.N + 127) / 128;
     if (a.variant == 0) {
+        hipLaunchKernelGGL((dkdv16v3_kernel<T, D, CAUSAL>), dim3((unsigned)(nkb * a.Hkv * a.B)),
+                           dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                           (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
+                           (uint16_t*)a.dk, (uint16_t*)a.dv, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale);
+        return hipGetLastError();
+    }
+    if (a.variant == 2) {
         hipLaunchKernelGGL((dkdv16v2_kernel<T, D, CAUSAL>), dim3((unsigned)(nkb * a.Hkv * a.B)),
                            dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                            (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
@@ -1115,7 +1409,7 @@ hipError_t dkdv16(const BwdArgs& a) {
 template <typename T, int D, bool CAUSAL>
 hipError_t dq16(const BwdArgs& a) {
     const int nqb = (a.N + 127) / 128;
-    if (a.variant == 0) {
+    if (a.variant != 1) {
         hipLaunchKernelGGL((dq16v2_kernel<T, D, CAUSAL>), dim3((unsigned)(nqb * a.Hq * a.B)),
                            dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                            (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,

@@ -16,6 +16,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <utility>
 #include <stdint.h>
 
 namespace fa355 {
@@ -213,6 +215,17 @@ __device__ __forceinline__ int vt_off(int row, int byte_in_row) {
 // f = {0, 4, 10, 14} for 16 chunks per row and {0, 2, 4, 6} for 8: distinct
 // for 16 consecutive rows, and within each aligned 4-row group distinct in
 // chunk bits 1-2 and 2-3 (64-bank and 32-bank conflict-free for both reads).
+// Compile-time loop: calls f(std::integral_constant<int, i>) for i = 0..N-1,
+// so every index inside f is a constant expression (unrolling guaranteed).
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 template <int D>
 __device__ __forceinline__ int dual_swz(int row) {
     const int r3 = row & 3;
