@@ -819,10 +819,24 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
     float sl = 0.f, sd = 0.f;
 
+    // Tile order: under a causal mask the G diagonal tiles (the first query
+    // tile of each head, the only ones that need the mask) come first, then
+    // the remaining tiles head by head.
+    const int ndiag = CAUSAL ? G : 0;
+    const int nrest = qb_count - (CAUSAL ? 1 : 0);
     auto step_rows = [&](int s, int& h, int& q0) {
-        h = hk * G + s / qb_count;
-        q0 = (qb_first + s % qb_count) * BQ;
+        if (CAUSAL && s < ndiag) {
+            h = hk * G + s;
+            q0 = qb_first * BQ;
+        } else {
+            const int m = s - ndiag;
+            h = hk * G + m / nrest;
+            q0 = (qb_first + (CAUSAL ? 1 : 0) + m % nrest) * BQ;
+        }
     };
+    // LDS buffer of tile s: the last diagonal tile uses buffer 1, so that the
+    // remaining tiles alternate 0, 1, 0, ... from their first one
+    auto buf_of = [&](int s) { return (s < ndiag ? ndiag - s : s - ndiag) & 1; };
     auto issue = [&](int s, int buf) {
         int h, q0;
         step_rows(s, h, q0);
@@ -859,7 +873,12 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     // seg / 2 - 1, and the last one those of block NQB - 1.
     // mlim: element (block blk, row offset o) of this lane is visible when
     // 32 blk + o >= mlim (causal: the query row is at or after the key)
-    auto run_step = [&](const unsigned char* base, int mlim) {
+    auto run_step = [&](auto mask_tag, auto buf_tag, const unsigned char* rt_base, int mlim) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        constexpr int BUFC = decltype(buf_tag)::value;
+        // a compile-time buffer turns every LDS address into a lane offset
+        // plus an immediate
+        const unsigned char* base = BUFC >= 0 ? smem + BUFC * STAGE : rt_base;
         u32x4 op[TSLOT];
         f32x16 sacc = zero16(), dpacc = zero16();
         u32x4 pb[2][2], dsb[2][2];
@@ -895,7 +914,7 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         auto soft = [&](int blk, int r) {
             const int g = r >> 2, i = r & 3;
             float p = fast_exp2(fmaf(sacc[r], cl2, -lc[g][i]));
-            if (CAUSAL) p = (32 * blk + 8 * g + i >= mlim) ? p : 0.f;
+            if (MASK) p = (32 * blk + 8 * g + i >= mlim) ? p : 0.f;
             pv[r] = p;
             dsv[r] = p * (dpacc[r] - dc[g][i]);
             if (r & 1) {
@@ -950,23 +969,30 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     };
 
     if (nsteps > 0) {
-        issue(0, 0);
-        put_rows(0);
+        issue(0, buf_of(0));
+        put_rows(buf_of(0));
         wait_vmem();
     }
     __syncthreads();
 
-    for (int s = 0; s < nsteps; ++s) {
-        issue(min(s + 1, nsteps - 1), (s + 1) & 1);
+    // one tile: prefetch the next one into the other buffer, compute, publish
+    auto tile = [&](int s, auto mask_tag, auto buf_tag) {
+        const int nb = buf_of(s) ^ 1;
+        issue(min(s + 1, nsteps - 1), nb);
         int h, q0;
         step_rows(s, h, q0);
         (void)h;
-        const unsigned char* base = smem + (s & 1) * STAGE;
-        // rows q0 + 4 hi + (32 blk + 8 g + i); visible when that row >= key
-        run_step(base, (CAUSAL && q0 < kw + 31) ? key - q0 - 4 * hi : INT_MIN);
-        put_rows((s + 1) & 1);
+        // rows q0 + 4 hi + (32 blk + 8 g + i) are visible when at or after the key
+        run_step(mask_tag, buf_tag, smem + buf_of(s) * STAGE, key - q0 - 4 * hi);
+        put_rows(nb);
         wait_vmem();
         __syncthreads();
+    };
+    for (int s = 0; s < ndiag; ++s)
+        tile(s, std::true_type{}, std::integral_constant<int, -1>{});
+    for (int s = ndiag; s < nsteps; s += 2) {
+        tile(s, std::false_type{}, std::integral_constant<int, 0>{});
+        if (s + 1 < nsteps) tile(s + 1, std::false_type{}, std::integral_constant<int, 1>{});
     }
 
     if (key < N) {
