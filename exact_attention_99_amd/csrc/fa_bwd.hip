@@ -876,9 +876,21 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     auto run_step = [&](auto mask_tag, auto buf_tag, const unsigned char* rt_base, int mlim) {
         constexpr bool MASK = decltype(mask_tag)::value;
         constexpr int BUFC = decltype(buf_tag)::value;
-        // a compile-time buffer turns every LDS address into a lane offset
-        // plus an immediate
-        const unsigned char* base = BUFC >= 0 ? smem + BUFC * STAGE : rt_base;
+        // The lane-dependent parts of every LDS address, with the buffer's base
+        // folded in, are formed once per tile; each read then adds only an
+        // immediate (block, half and tensor offsets), which stays within the
+        // 16-bit offset field of the LDS instructions.
+        const uint32_t bb = BUFC >= 0 ? (uint32_t)(BUFC * STAGE) : (uint32_t)(rt_base - smem);
+        uint32_t ao[NKS], to[2][NDB];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) ao[ks] = lds_lane_off(bb + dual_off<D>(l32, 16 * (2 * ks + hi)));
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                to[u][db] = lds_lane_off(bb + dual_off<D>(8 * u + tr_row, 64 * db + tr_col));
+        const uint32_t ro = lds_lane_off(bb + OFF_LSE + 16 * hi);
+
         u32x4 op[TSLOT];
         f32x16 sacc = zero16(), dpacc = zero16();
         u32x4 pb[2][2], dsb[2][2];
@@ -890,24 +902,23 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             constexpr int blk = dkdv_seg_block<NQB>(seg);
             if constexpr (dkdv_seg_is_s<NQB>(seg)) {
                 constexpr int ks = j >> 1;
-                const int off = dual_off<D>(32 * blk + l32, 16 * (2 * ks + hi));
-                op[n] = *reinterpret_cast<const u32x4*>(base + ((j & 1) ? OFF_DOS : 0) + off);
+                constexpr int imm = ((j & 1) ? OFF_DOS : 0) + 32 * blk * D * 2;
+                op[n] = *reinterpret_cast<const u32x4*>(smem + ao[ks] + imm);
             } else {
                 constexpr int t = j / (2 * NDB), db = (j >> 1) % NDB;
-                const int row = 32 * blk + 16 * t + tr_row;
-                const unsigned char* tb = base + ((j & 1) ? 0 : OFF_DOS);
-                const u32x2 lo = lds_read_tr16(tb + dual_off<D>(row, 64 * db + tr_col));
-                const u32x2 up = lds_read_tr16(tb + dual_off<D>(row + 8, 64 * db + tr_col));
+                constexpr int imm = ((j & 1) ? 0 : OFF_DOS) + (32 * blk + 16 * t) * D * 2;
+                const u32x2 lo = lds_read_tr16(smem + to[0][db] + imm);
+                const u32x2 up = lds_read_tr16(smem + to[1][db] + imm);
                 op[n] = u32x4{lo[0], lo[1], up[0], up[1]};
             }
         };
         auto load_rows = [&](int blk, int k) {
             const int g = k >> 1;
-            const int ro = 32 * blk + 8 * g + 4 * hi;
+            const int imm = 4 * (32 * blk + 8 * g);
             if (k & 1)
-                dc[g] = *reinterpret_cast<const f32x4*>(base + OFF_DL + 4 * ro);
+                dc[g] = *reinterpret_cast<const f32x4*>(smem + ro + (OFF_DL - OFF_LSE) + imm);
             else
-                lc[g] = *reinterpret_cast<const f32x4*>(base + OFF_LSE + 4 * ro);
+                lc[g] = *reinterpret_cast<const f32x4*>(smem + ro + imm);
         };
         // softmax and dS of element r of block blk (row 32 blk + acc_row(r, hi))
         float pv[16], dsv[16];

@@ -98,6 +98,14 @@ __device__ __forceinline__ float swap_halves(float x) {
     return __shfl_xor(x, 32, 64);
 }
 
+// max(x[l], x[l ^ 32]) for every lane l, on the vector unit: one
+// v_permlane32_swap exchanges the upper half of one copy with the lower half
+// of the other, so the two results hold both values of each lane pair.
+__device__ __forceinline__ float halves_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Native 2^x (v_exp_f32); exp2(-inf) = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -215,6 +223,14 @@ __device__ __forceinline__ int vt_off(int row, int byte_in_row) {
 // f = {0, 4, 10, 14} for 16 chunks per row and {0, 2, 4, 6} for 8: distinct
 // for 16 consecutive rows, and within each aligned 4-row group distinct in
 // chunk bits 1-2 and 2-3 (64-bank and 32-bank conflict-free for both reads).
+// An LDS byte offset made opaque to the optimiser (so that it stays in one
+// register instead of being re-derived at every use) and then bounded, so the
+// constant parts of later addresses still fold into the instruction offset.
+__device__ __forceinline__ uint32_t lds_lane_off(uint32_t x) {
+    asm volatile("" : "+v"(x));
+    return x & 0x3FFFFu;
+}
+
 // Compile-time loop: calls f(std::integral_constant<int, i>) for i = 0..N-1,
 // so every index inside f is a constant expression (unrolling guaranteed).
 template <typename F, int... Is>

@@ -462,6 +462,232 @@ fwd16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
 }
 
+// Fifth-generation 16-bit forward kernel: the v2 data path (buffer-to-LDS
+// copies, transposing V reads) with the key tiles split in two loops.  Tiles
+// that lie wholly at or below every row of the block and inside the sequence
+// run a body with no mask code at all; the LDS buffer of each is a
+// compile-time constant (the loop handles tiles in pairs), so every LDS
+// address is a per-lane register plus an immediate offset.  The remaining
+// tiles (the causal diagonal of each wave, the ragged end of the sequence)
+// run the masked body.
+template <typename T, int D, bool CAUSAL, int NW, int BC>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+fwd16v5_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+               const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
+               int B, int Hq, int Hkv, int N, float cl2) {
+    constexpr int BR = 32 * NW;
+    constexpr int KCH = D / 8;
+    constexpr int TILE = BC * D * 2;
+    constexpr int STAGE = 2 * TILE;
+    constexpr int NKB = BC / 32;
+    constexpr int NKG = BC / 16;
+    constexpr int NDB = D / 32;
+    constexpr int NKS = D / 16;
+    constexpr int WI = TILE / 1024;
+    static_assert(WI % NW == 0, "tile copies split evenly over the waves");
+    constexpr int IPW = WI / NW;
+    static_assert(2 * STAGE <= 65536, "both buffers addressable by immediate offsets");
+    static_assert(BR % BC == 0, "row blocks start on a key-tile boundary");
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+
+    const int nqb = (N + BR - 1) / BR;
+    const int total = nqb * Hq * B;
+    const int logical = xcd_remap((int)blockIdx.x, total);
+    const int qb_raw = logical % nqb;
+    const int bh = logical / nqb;
+    const int qb = CAUSAL ? (nqb - 1 - qb_raw) : qb_raw;  // longest rows first
+    const int h = bh % Hq;
+    const int b = bh / Hq;
+    const int hk = h / (Hq / Hkv);
+
+    const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
+    const size_t koff = ((size_t)b * Hkv + hk) * (size_t)N * D;
+    const uint32_t head_bytes = (uint32_t)N * D * 2;
+    const Buf Qb(Q + qoff, head_bytes), Kb(K + koff, head_bytes), Vb(V + koff, head_bytes);
+
+    const int q0 = qb * BR;
+    const int qw = q0 + 32 * wave;
+    const int q = qw + l32;
+
+    u32x4 qf[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = Qb.load16((uint32_t)(q * D + 16 * ks + 8 * hi) * 2);
+
+    const int kv_len = CAUSAL ? min(N, q0 + BR) : N;
+    const int ntiles = (kv_len + BC - 1) / BC;
+    // tiles below the whole row block (causal) and inside the sequence
+    const int nfull = min(CAUSAL ? q0 / BC : ntiles, N / BC);
+
+    uint32_t cpk[IPW], cpv[IPW];
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+        const int p = (wave + NW * i) * 64 + lane;
+        const int row = p / KCH, pc = p % KCH;
+        cpk[i] = (uint32_t)kq_off<D>(row, pc);
+        cpv[i] = (uint32_t)(row * D * 2 + 16 * (pc ^ tr_swz<D>(row)));
+    }
+    auto issue = [&](int k0, int buf) {
+        unsigned char* base = smem + buf * STAGE;
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            const int bi = wave + NW * i;
+            const uint32_t rowb = (uint32_t)k0 * D * 2;
+            buf_to_lds16(Kb, base + bi * 1024, rowb + cpk[i]);
+            buf_to_lds16(Vb, base + TILE + bi * 1024, rowb + cpv[i]);
+        }
+    };
+
+    const int g16 = lane >> 4;
+    const int j16 = lane & 15;
+    const int tr_row = 4 * hi + (j16 >> 2);
+    const int tr_col = 2 * (16 * (g16 & 1) + 4 * (j16 & 3));
+
+    // lane parts of the LDS addresses (block, group and buffer offsets are
+    // immediates): K rows 32 kb + l32, chunk 2 ks + hi; V^T rows 16 kg +
+    // tr_row (+ 8), bytes 64 db + tr_col
+    uint32_t ko[2][NKS], vo[NDB];
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) ko[par][ks] = lds_lane_off((uint32_t)kq_off<D>(32 * par + l32, 2 * ks + hi) - 32 * par * D * 2);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) vo[db] = lds_lane_off((uint32_t)vt_off<D>(tr_row, 64 * db + tr_col));
+
+    f32x16 o[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[db] = zero16();
+    float m_s = -INFINITY;
+    float l_s = 0.f;
+
+    auto body = [&](int j, auto mask_tag, auto buf_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        constexpr int BUFC = decltype(buf_tag)::value;
+        const int k0 = j * BC;
+        const uint32_t bb = BUFC >= 0 ? (uint32_t)(BUFC * STAGE) : (uint32_t)((j & 1) * STAGE);
+        const unsigned char* kbase = smem + bb;
+        const unsigned char* vbase = smem + bb + TILE;
+
+        f32x16 s[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) s[kb] = zero16();
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const u32x4 a = *reinterpret_cast<const u32x4*>(kbase + ko[kb & 1][ks] + 32 * kb * D * 2);
+                s[kb] = Mma<T>::mma(a, qf[ks], s[kb]);
+            }
+        if (MASK) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + 32 * kb + acc_row(r, hi);
+                    if ((CAUSAL && key > q) || key >= N) s[kb][r] = -INFINITY;
+                }
+        }
+
+        // V^T operands of this tile: read now, so their latency hides under
+        // the softmax
+        u32x4 va[NKG][NDB];
+#pragma unroll
+        for (int kg = 0; kg < NKG; ++kg)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const u32x2 lo = lds_read_tr16(vbase + vo[db] + 16 * kg * D * 2);
+                const u32x2 up = lds_read_tr16(vbase + vo[db] + (16 * kg + 8) * D * 2);
+                va[kg][db] = u32x4{lo[0], lo[1], up[0], up[1]};
+            }
+
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        const float mt = halves_max(mx) * cl2;
+
+        if (__any(mt > m_s + kTau)) {
+            const float mn = fmaxf(m_s, mt);
+            const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m_s - mn);
+            l_s *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+            m_s = mn;
+        }
+        const float mu = (m_s == -INFINITY) ? 0.f : m_s;
+
+        u32x4 pb[NKG];
+        float ls = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const float p0 = fast_exp2(fmaf(s[kb][8 * t + 2 * jj], cl2, -mu));
+                    const float p1 = fast_exp2(fmaf(s[kb][8 * t + 2 * jj + 1], cl2, -mu));
+                    ls += p0 + p1;
+                    pb[2 * kb + t][jj] = Mma<T>::pack2(p0, p1);
+                }
+        l_s += ls;
+
+#pragma unroll
+        for (int kg = 0; kg < NKG; ++kg)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) o[db] = Mma<T>::mma(va[kg][db], pb[kg], o[db]);
+    };
+
+    issue(0, 0);
+    wait_vmem();
+    __syncthreads();
+
+    // The copy of the next tile is issued at the start of every tile, also
+    // the last (the extra tile lies in this head's range or past its end,
+    // reads as zeros, and lands in the buffer no later tile reads).
+    int j = 0;
+    for (; j + 1 < nfull; j += 2) {
+        issue((j + 1) * BC, 1);
+        body(j, std::false_type{}, std::integral_constant<int, 0>{});
+        wait_vmem();
+        __syncthreads();
+        issue((j + 2) * BC, 0);
+        body(j + 1, std::false_type{}, std::integral_constant<int, 1>{});
+        wait_vmem();
+        __syncthreads();
+    }
+    for (; j < ntiles; ++j) {
+        issue((j + 1) * BC, (j + 1) & 1);
+        if (!CAUSAL || j * BC <= qw + 31) body(j, std::true_type{}, std::integral_constant<int, -1>{});
+        wait_vmem();
+        __syncthreads();
+    }
+
+    const float l_tot = l_s + swap_halves(l_s);
+    if (q < N) {
+        const float inv = 1.f / l_tot;
+        uint16_t* Orow = O + qoff + (size_t)q * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                u32x2 w;
+                w[0] = Mma<T>::pack2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
+                w[1] = Mma<T>::pack2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+                *reinterpret_cast<u32x2*>(Orow + 32 * db + 8 * g + 4 * hi) = w;
+            }
+        if (hi == 0) LSE[(size_t)(b * Hq + h) * N + q] = (m_s + __log2f(l_tot)) * kLn2;
+    }
+}
+
 // Third-generation 16-bit forward kernel: the v2 data path (buffer-to-LDS
 // copies, transposing V reads) with a software pipeline across key tiles.
 // K runs one tile ahead of V: while a wave exponentiates the scores S_j of
@@ -1133,6 +1359,17 @@ hipError_t launch16v2(const FwdArgs& a) {
 }
 
 template <typename T, int D, bool CAUSAL, int NW, int BC>
+hipError_t launch16v5(const FwdArgs& a) {
+    constexpr int BR = 32 * NW;
+    const int nqb = (a.N + BR - 1) / BR;
+    const long long total = (long long)nqb * a.Hq * a.B;
+    hipLaunchKernelGGL((fwd16v5_kernel<T, D, CAUSAL, NW, BC>), dim3((unsigned)total), dim3(NW * 64),
+                       0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                       (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.N, a.cl2);
+    return hipGetLastError();
+}
+
+template <typename T, int D, bool CAUSAL, int NW, int BC>
 hipError_t launch16v3(const FwdArgs& a) {
     constexpr int BR = 32 * NW;
     const int nqb = (a.N + BR - 1) / BR;
@@ -1179,7 +1416,10 @@ hipError_t dispatch16c(const FwdArgs& a) {
             case 7: return launch16v4<T, D, CAUSAL, 32>(a);
             case 8: return launch16v4<T, D, CAUSAL, 64>(a);
             case 9: return launch16<T, D, CAUSAL, 8, 64>(a);
-            default: return launch16v2<T, D, CAUSAL, 8, 64>(a);
+            case 10: return launch16v5<T, D, CAUSAL, 8, 64>(a);
+            case 11: return launch16v5<T, D, CAUSAL, 4, 64>(a);
+            case 12: return launch16v2<T, D, CAUSAL, 8, 64>(a);
+            default: return launch16v5<T, D, CAUSAL, 8, 64>(a);
         }
     } else {
         switch (a.fwd_variant) {
@@ -1192,7 +1432,10 @@ hipError_t dispatch16c(const FwdArgs& a) {
             case 7: return launch16v4<T, D, CAUSAL, 32>(a);
             case 8: return launch16v4<T, D, CAUSAL, 64>(a);
             case 9: return launch16<T, D, CAUSAL, 8, 128>(a);
-            default: return launch16v2<T, D, CAUSAL, 8, 128>(a);
+            case 10: return launch16v5<T, D, CAUSAL, 8, 128>(a);
+            case 11: return launch16v5<T, D, CAUSAL, 4, 128>(a);
+            case 12: return launch16v2<T, D, CAUSAL, 8, 128>(a);
+            default: return launch16v5<T, D, CAUSAL, 4, 128>(a);
         }
     }
 }

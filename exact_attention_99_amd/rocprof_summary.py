@@ -76,8 +76,9 @@ def cmd_traffic(a):
     out = {"command": a.cmd, "source_sha": a.sha, "copy_bytes": a.copy_bytes,
            "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,
            "fetch_factor": f_factor, "write_factor": w_factor, "kernels": {}}
-    for pat, key in (("fwd16", "fwd"), ("delta16_kernel", "bwd_prepare"),
-                     ("dkdv16_kernel", "bwd_dkdv"), ("dq16_kernel", "bwd_dq")):
+    # every kernel generation of a pass matches its prefix
+    for pat, key in (("fwd16", "fwd"), ("delta16", "bwd_prepare"),
+                     ("dkdv16", "bwd_dkdv"), ("dq16", "bwd_dq")):
         fk = [v for n, vals in fetch.items() if pat in n for v in vals]
         wk = [v for n, vals in write.items() if pat in n for v in vals]
         if not fk or not wk:
