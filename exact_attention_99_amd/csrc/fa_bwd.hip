@@ -1185,6 +1185,187 @@ dq16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
 }
 
+// Third-generation dQ kernel: the data path of the second generation with the
+// key tiles split in two loops.  Tiles wholly below every row of the block
+// (and inside the sequence) run a body with no mask code, two at a time so
+// that both LDS buffers have compile-time offsets; the diagonal and ragged-end
+// tiles run the masked body.
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+dq16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+              const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+              const float* __restrict__ LSE, const float* __restrict__ Delta,
+              uint16_t* __restrict__ dQ, int B, int Hq, int Hkv, int N, float cl2, float scale) {
+    constexpr int NW = 4;
+    constexpr int BR = 32 * NW;
+    constexpr int BC = D == 128 ? 64 : 128;
+    constexpr int KCH = D / 8;
+    constexpr int TB = BC * D * 2;
+    constexpr int STAGE = 2 * TB;
+    constexpr int NKB = BC / 32;
+    constexpr int NDB = D / 32;
+    constexpr int NKS = D / 16;
+    constexpr int WI = TB / 1024;
+    static_assert(WI % NW == 0, "tile copies split evenly over the waves");
+    constexpr int IPW = WI / NW;
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+
+    const int nqb = (N + BR - 1) / BR;
+    const int total = nqb * Hq * B;
+    const int logical = xcd_remap((int)blockIdx.x, total);
+    const int qb_raw = logical % nqb;
+    const int bh = logical / nqb;
+    const int qb = CAUSAL ? (nqb - 1 - qb_raw) : qb_raw;
+    const int h = bh % Hq;
+    const int b = bh / Hq;
+    const int hk = h / (Hq / Hkv);
+
+    const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
+    const size_t koff = ((size_t)b * Hkv + hk) * (size_t)N * D;
+    const uint32_t head_bytes = (uint32_t)N * D * 2;
+    const Buf Kb(K + koff, head_bytes), Vb(V + koff, head_bytes);
+
+    const int q0 = qb * BR;
+    const int qw = q0 + 32 * wave;
+    const int q = qw + l32;
+
+    u32x4 qf[NKS], dof[NKS];
+    {
+        const Buf Qb(Q + qoff, head_bytes), Db(dO + qoff, head_bytes);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            qf[ks] = Qb.load16((uint32_t)(q * D + 16 * ks + 8 * hi) * 2);
+            dof[ks] = Db.load16((uint32_t)(q * D + 16 * ks + 8 * hi) * 2);
+        }
+    }
+    const size_t roff = ((size_t)b * Hq + h) * (size_t)N;
+    const float lse2 = Buf(LSE + roff, (uint32_t)N * 4).load_f32((uint32_t)q * 4) * kLog2e;
+    const float dlt = Buf(Delta + roff, (uint32_t)N * 4).load_f32((uint32_t)q * 4);
+
+    const int kv_len = CAUSAL ? min(N, q0 + BR) : N;
+    const int ntiles = (kv_len + BC - 1) / BC;
+
+    uint32_t cp[IPW];
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+        const int p = (wave + NW * i) * 64 + lane;
+        const int row = p / KCH, pc = p % KCH;
+        cp[i] = (uint32_t)(row * D * 2 + 16 * (pc ^ dual_swz<D>(row)));
+    }
+    auto issue = [&](int k0, int buf) {
+        unsigned char* base = smem + buf * STAGE;
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            const uint32_t off = (uint32_t)k0 * D * 2 + cp[i];
+            buf_to_lds16(Kb, base + (wave + NW * i) * 1024, off);
+            buf_to_lds16(Vb, base + TB + (wave + NW * i) * 1024, off);
+        }
+    };
+
+    const int g16 = lane >> 4;
+    const int j16 = lane & 15;
+    const int tr_row = 4 * hi + (j16 >> 2);
+    const int tr_col = 2 * (16 * (g16 & 1) + 4 * (j16 & 3));
+
+    f32x16 dq[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) dq[db] = zero16();
+
+    auto body = [&](int j, auto mask_tag, auto buf_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        constexpr int BUFC = decltype(buf_tag)::value;
+        const int k0 = j * BC;
+        const unsigned char* base = smem + (BUFC >= 0 ? BUFC : (j & 1)) * STAGE;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            f32x16 st = zero16(), dpt = zero16();
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const int off = dual_off<D>(32 * kb + l32, 16 * (2 * ks + hi));
+                const u32x4 ak = *reinterpret_cast<const u32x4*>(base + off);
+                const u32x4 av = *reinterpret_cast<const u32x4*>(base + TB + off);
+                st = Mma<T>::mma(ak, qf[ks], st);
+                dpt = Mma<T>::mma(av, dof[ks], dpt);
+            }
+            float p[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) p[r] = fast_exp2(fmaf(st[r], cl2, -lse2));
+            if (MASK) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int kk = k0 + 32 * kb + acc_row(r, hi);
+                    p[r] = ((!CAUSAL || kk <= q) && kk < N) ? p[r] : 0.f;
+                }
+            }
+            u32x4 dsb[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int r = 8 * t + 2 * jj;
+                    dsb[t][jj] = Mma<T>::pack2(p[r] * (dpt[r] - dlt), p[r + 1] * (dpt[r + 1] - dlt));
+                }
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const int row = 32 * kb + 16 * t + tr_row;
+                    const int col = 64 * db + tr_col;
+                    const u32x2 lo = lds_read_tr16(base + dual_off<D>(row, col));
+                    const u32x2 up = lds_read_tr16(base + dual_off<D>(row + 8, col));
+                    u32x4 a;
+                    a[0] = lo[0]; a[1] = lo[1]; a[2] = up[0]; a[3] = up[1];
+                    dq[db] = Mma<T>::mma(a, dsb[t], dq[db]);
+                }
+        }
+    };
+
+    // tiles below every row of the block and inside the sequence
+    const int nfull = min(CAUSAL ? q0 / BC : ntiles, N / BC);
+    issue(0, 0);
+    wait_vmem();
+    __syncthreads();
+    // The copy of the next tile is issued at the start of every tile, also the
+    // last (it lies in this head's range or past its end and reads as zeros).
+    int j = 0;
+    for (; j + 1 < nfull; j += 2) {
+        issue((j + 1) * BC, 1);
+        body(j, std::false_type{}, std::integral_constant<int, 0>{});
+        wait_vmem();
+        __syncthreads();
+        issue((j + 2) * BC, 0);
+        body(j + 1, std::false_type{}, std::integral_constant<int, 1>{});
+        wait_vmem();
+        __syncthreads();
+    }
+    for (; j < ntiles; ++j) {
+        issue((j + 1) * BC, (j + 1) & 1);
+        if (!CAUSAL || j * BC <= qw + 31) body(j, std::true_type{}, std::integral_constant<int, -1>{});
+        wait_vmem();
+        __syncthreads();
+    }
+
+    if (q < N) {
+        uint16_t* row = dQ + qoff + (size_t)q * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                u32x2 w;
+                w[0] = Mma<T>::pack2(dq[db][4 * g] * scale, dq[db][4 * g + 1] * scale);
+                w[1] = Mma<T>::pack2(dq[db][4 * g + 2] * scale, dq[db][4 * g + 3] * scale);
+                *reinterpret_cast<u32x2*>(row + 32 * db + 8 * g + 4 * hi) = w;
+            }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // fp32 inputs: the same two passes with the fp32 matrix-core op (32x32x2), P
 // and dS kept in fp32, single-buffered LDS tiles with padded rows.
@@ -1446,6 +1627,13 @@ hipError_t dkdv16(const BwdArgs& a) {
 template <typename T, int D, bool CAUSAL>
 hipError_t dq16(const BwdArgs& a) {
     const int nqb = (a.N + 127) / 128;
+    if (a.variant == 0) {
+        hipLaunchKernelGGL((dq16v3_kernel<T, D, CAUSAL>), dim3((unsigned)(nqb * a.Hq * a.B)),
+                           dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                           (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
+                           (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale);
+        return hipGetLastError();
+    }
     if (a.variant != 1) {
         hipLaunchKernelGGL((dq16v2_kernel<T, D, CAUSAL>), dim3((unsigned)(nqb * a.Hq * a.B)),
                            dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
