@@ -787,14 +787,21 @@ fwd16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     for (int db = 0; db < NDB; ++db)
         rv[db] = vt_off<D>(tr_row, 2 * (32 * db + 16 * (g16 & 1) + 4 * (j16 & 3)));
 
-    auto kread = [&](const unsigned char* kb_base, int step) {
-        return *reinterpret_cast<const u32x4*>(
-            kb_base + kq_off<D>(32 * (step / NKS) + l32, 2 * (step % NKS) + hi));
+    // lane parts of the K-row read offsets (block and buffer parts are added
+    // per tile, once, through lds_lane_off)
+    int rk[2][NKS];
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) rk[par][ks] = kq_off<D>(32 * par + l32, 2 * ks + hi) - 32 * par * D * 2;
+    auto kread = [&](const uint32_t (&kl)[2][NKS], int step) {
+        const int kb = step / NKS;
+        return *reinterpret_cast<const u32x4*>(smem + kl[kb & 1][step % NKS] + 32 * kb * D * 2);
     };
-    auto vread = [&](const unsigned char* v_base, int pv) {
+    auto vread = [&](const uint32_t (&vl)[NDB], int pv) {
         const int kg = pv / NDB, db = pv % NDB;
-        const u32x2 lo = lds_read_tr16(v_base + rv[db] + 16 * kg * D * 2);
-        const u32x2 up = lds_read_tr16(v_base + rv[db] + (16 * kg + 8) * D * 2);
+        const u32x2 lo = lds_read_tr16(smem + vl[db] + 16 * kg * D * 2);
+        const u32x2 up = lds_read_tr16(smem + vl[db] + (16 * kg + 8) * D * 2);
         u32x4 a;
         a[0] = lo[0]; a[1] = lo[1]; a[2] = up[0]; a[3] = up[1];
         return a;
@@ -803,6 +810,8 @@ fwd16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     auto mask_max = [&](f32x16 (&sc)[NKB], int k0) {
         const bool need_mask = (CAUSAL && (k0 + BC - 1 > qw)) || (k0 + BC > N);
         if (need_mask) {
+            // a real branch: only the diagonal and ragged-end tiles pay for the mask
+            asm volatile("" ::: "memory");
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -816,8 +825,7 @@ fwd16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-        mx = fmaxf(mx, swap_halves(mx));
-        return mx * cl2;
+        return halves_max(mx) * cl2;
     };
 
     f32x16 o[NDB];
@@ -832,12 +840,22 @@ fwd16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     wait_vmem();
     __syncthreads();
 
+    auto klanes = [&](uint32_t (&kl)[2][NKS], int buf) {
+#pragma unroll
+        for (int par = 0; par < 2; ++par)
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) kl[par][ks] = lds_lane_off((uint32_t)(KBUF + buf * TILE + rk[par][ks]));
+    };
     f32x16 s[NKB];
+    {
+        uint32_t kl[2][NKS];
+        klanes(kl, 0);
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-        s[kb] = zero16();
+        for (int kb = 0; kb < NKB; ++kb) {
+            s[kb] = zero16();
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) s[kb] = Mma<T>::mma(kread(smem + KBUF, kb * NKS + ks), qf[ks], s[kb]);
+            for (int ks = 0; ks < NKS; ++ks) s[kb] = Mma<T>::mma(kread(kl, kb * NKS + ks), qf[ks], s[kb]);
+        }
     }
     float mt = mask_max(s, 0);
 
@@ -864,19 +882,20 @@ fwd16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
             // Region 1: score products of tile j+1 (matrix cores), one per
             // step, interleaved with the probabilities of tile j (vector unit).
-            const unsigned char* kn = smem + KBUF + ((j + 1) & 1) * TILE;
+            uint32_t kl[2][NKS];
+            klanes(kl, (j + 1) & 1);
             f32x16 sn[NKB];
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) sn[kb] = zero16();
             u32x4 ak[AHEAD];
 #pragma unroll
-            for (int t = 0; t < AHEAD; ++t) ak[t] = kread(kn, t);
+            for (int t = 0; t < AHEAD; ++t) ak[t] = kread(kl, t);
             u32x4 pb[NKG];
             float ls = 0.f;
 #pragma unroll
             for (int t = 0; t < NSTEP; ++t) {
                 const u32x4 a = ak[t % AHEAD];
-                if (t + AHEAD < NSTEP) ak[t % AHEAD] = kread(kn, t + AHEAD);
+                if (t + AHEAD < NSTEP) ak[t % AHEAD] = kread(kl, t + AHEAD);
                 sn[t / NKS] = Mma<T>::mma(a, qf[t % NKS], sn[t / NKS]);
 #pragma unroll
                 for (int u = 0; u < PPS; ++u) {
@@ -894,14 +913,16 @@ fwd16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
             // Region 2: PV products of tile j, with the mask and row maximum of
             // tile j+1 on the vector unit.
-            const unsigned char* v_base = smem + VBUF + (j & 1) * TILE;
+            uint32_t vl[NDB];
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) vl[db] = lds_lane_off((uint32_t)(VBUF + (j & 1) * TILE + rv[db]));
             u32x4 av[AHEAD_V];
 #pragma unroll
-            for (int t = 0; t < AHEAD_V; ++t) av[t] = vread(v_base, t);
+            for (int t = 0; t < AHEAD_V; ++t) av[t] = vread(vl, t);
 #pragma unroll
             for (int pv = 0; pv < NPV; ++pv) {
                 const u32x4 a = av[pv % AHEAD_V];
-                if (pv + AHEAD_V < NPV) av[pv % AHEAD_V] = vread(v_base, pv + AHEAD_V);
+                if (pv + AHEAD_V < NPV) av[pv % AHEAD_V] = vread(vl, pv + AHEAD_V);
                 o[pv % NDB] = Mma<T>::mma(a, pb[pv / NDB], o[pv % NDB]);
             }
             mt = mask_max(sn, k0 + BC);
