@@ -12,7 +12,9 @@ Prints one JSON line.  `value` is the whole-step rate in TFLOP/s with the
 conventional count: forward 4*B*H*N^2*d (halved under the causal mask) plus
 backward 2.5x that.  Inputs are resident in HBM before the timed region.
 Per-kernel durations come from HIP events recorded on the stream the kernels
-run on, around every launch inside the timed region.
+run on, around every launch inside the timed region.  After it, every kernel
+is also timed cold (each launch preceded by an untimed 512 MB fill that evicts
+L2 and the MALL), reported as median and minimum per kernel.
 """
 from __future__ import annotations
 
@@ -32,6 +34,7 @@ METRIC = "attention fwd/bwd TFLOPS (bf16, causal, d=128) and % of MI355X MFMA pe
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 COPY_BYTES = 1 << 30        # size of the counter-calibration copy
+FLUSH_BYTES = 512 << 20     # cache-evicting fill before each cold-timed launch
 
 
 def source_sha() -> str:
@@ -99,6 +102,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama_mha_8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush-iters", type=int, default=20,
+                    help="cold-cache timed launches per kernel (0 to skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for HBM counter calibration)")
     ap.add_argument("--print-sha", action="store_true", help="print the kernel source hash and exit")
@@ -175,6 +180,27 @@ def main() -> int:
             per[n] += ev[j].elapsed_time(ev[j + 1])
     per = {n: t / args.steps for n, t in per.items()}  # ms per launch
 
+    # Cold-cache timing: each kernel launched after an untimed 512 MB fill that
+    # evicts L2 and the 256 MB MALL; median and minimum over the iterations.
+    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    launches = {
+        "fwd": lambda: fa_fwd(q, k, v, causal, w.scale, o=o, lse=lse, stream=stream),
+        "bwd_prepare": lambda: fa_bwd_prepare(o, do, delta, stream=stream),
+        "bwd_dkdv": lambda: fa_bwd_dkdv(q, k, v, lse, do, delta, causal, w.scale, dk=dk, dv=dv, stream=stream),
+        "bwd_dq": lambda: fa_bwd_dq(q, k, v, lse, do, delta, causal, w.scale, dq=dq, stream=stream),
+    }
+    cold = {n: [] for n in names}
+    for _ in range(args.flush_iters):
+        for n in names:
+            flush_buf.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launches[n]()
+            e1.record(stream)
+            e1.synchronize()
+            cold[n].append(e0.elapsed_time(e1))
+    del flush_buf
+
     F = w.flops_fwd(causal)
     step_flops = F + w.flops_bwd(causal)
     ms_step = wall / args.steps * 1e3
@@ -199,7 +225,11 @@ def main() -> int:
 
     kernels = {}
     for n in names:
+        ts = sorted(cold[n])
         rec = {"ms": per[n]}
+        if ts:
+            rec["cold_median_ms"] = ts[len(ts) // 2]
+            rec["cold_min_ms"] = ts[0]
         if kflops[n] > 0:
             rec["tflops"] = kflops[n] / (per[n] * 1e-3) / 1e12
         else:

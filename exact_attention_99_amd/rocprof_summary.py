@@ -3,9 +3,13 @@
     python -m exact_attention_99_amd.rocprof_summary stats DB --cmd "..." --out FILE.md
     python -m exact_attention_99_amd.rocprof_summary traffic --fetch DB --write DB \
         --copy-fetch DB --copy-write DB --copy-bytes N --cmd "..." --out traffic.json
+    python -m exact_attention_99_amd.rocprof_summary counters --run LABEL=DB[,DB...] ... \
+        --kernel PATTERN --cmd "..." --out FILE.md
 
 `stats` tabulates per-kernel launch counts and durations (from a
-`--kernel-trace --stats` run).  `traffic` turns FETCH_SIZE and WRITE_SIZE
+`--kernel-trace --stats` run).  `counters` tabulates, for the dispatches of
+one kernel family, every counter found in one or more `--pmc` databases per
+labelled run (one row per run, values averaged over dispatches).  `traffic` turns FETCH_SIZE and WRITE_SIZE
 readings (KiB per dispatch, from two `--pmc` runs) into HBM bytes per launch,
 scaled by what the same counters read for a plain copy of known size.
 Measurement tooling only; nothing on the library's compute path uses it.
@@ -92,6 +96,37 @@ def cmd_traffic(a):
     print(json.dumps(out, indent=1))
 
 
+def cmd_counters(a):
+    rows, names = [], []
+    for spec in a.run:
+        label, dbs = spec.split("=", 1)
+        vals = {}
+        kern = None
+        for db in dbs.split(","):
+            c = sqlite3.connect(db)
+            acc = defaultdict(list)
+            for name, cn, val in c.execute(
+                    "select kernel_name, counter_name, value from counters_collection"):
+                n = short_name(name)
+                if a.kernel not in n:
+                    continue
+                kern = n
+                acc[cn].append(float(val))
+            for cn, v in acc.items():
+                vals[cn] = sum(v) / len(v)
+                if cn not in names:
+                    names.append(cn)
+        rows.append((label, kern, vals))
+    lines = [f"# rocprofv3 counters: {a.title}", "", "Commands:", "", "```", a.cmd, "```", "",
+             "| run | kernel | " + " | ".join(names) + " |", "|---|---|" + "---|" * len(names)]
+    for label, kern, vals in rows:
+        cells = [f"{vals[n]:.4g}" if n in vals else "" for n in names]
+        lines.append(f"| {label} | `{kern}` | " + " | ".join(cells) + " |")
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -105,8 +140,14 @@ def main(argv=None):
     for k in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--cmd", "--out", "--sha"):
         t.add_argument(k, required=True)
     t.add_argument("--copy-bytes", type=float, required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("--run", action="append", required=True)
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--cmd", required=True)
+    c.add_argument("--title", default="")
+    c.add_argument("--out", required=True)
     a = ap.parse_args(argv)
-    {"stats": cmd_stats, "traffic": cmd_traffic}[a.what](a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters}[a.what](a)
 
 
 if __name__ == "__main__":
