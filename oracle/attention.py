@@ -49,7 +49,7 @@ from typing import Optional, Tuple
 
 import numpy as np
 
-__all__ = ["attention_forward", "attention_backward", "attention_probs"]
+__all__ = ["attention_forward", "attention_forward_kv", "attention_backward", "attention_probs"]
 
 
 def _check(Q: np.ndarray, K: np.ndarray, V: np.ndarray) -> Tuple[int, int, int, int, int, int]:
@@ -118,6 +118,44 @@ def attention_forward(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
                 P, l = _softmax_rows(_scores(qr, idx, Kh, scale, causal))
                 O[b, h, r0:r0 + len(idx)] = P @ Vh
                 lse[b, h, r0:r0 + len(idx)] = l
+    return O, lse
+
+
+def attention_forward_kv(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
+                         causal: bool) -> Tuple[np.ndarray, np.ndarray]:
+    """Attention of N_q query rows against N_kv keys (the split-KV / decoding
+    case, "FlashAttention" glossary, FlashDecoding paragraph), in float64.
+
+    Q is [B, H_q, N_q, d]; K, V are [B, H_kv, N_kv, d].  Returns O
+    [B, H_q, N_q, d] and the natural-log lse [B, H_q, N_q].
+
+    Reading taken (the pages fix no alignment for N_q != N_kv): the queries
+    are the last N_q positions of the sequence, so under the causal mask query
+    i sees keys j <= i + N_kv - N_q (which requires N_q <= N_kv, so every row
+    sees at least key 0).  With N_q == N_kv this is ``attention_forward``.
+    """
+    if Q.ndim != 4 or K.ndim != 4 or V.ndim != 4 or K.shape != V.shape:
+        raise ValueError("Q must be [B, H_q, N_q, d] and K, V [B, H_kv, N_kv, d]")
+    B, Hq, Nq, d = Q.shape
+    Bk, Hkv, Nkv, dk = K.shape
+    if Bk != B or dk != d or Hq % Hkv != 0:
+        raise ValueError("K and V must match Q's batch and head dimension")
+    shift = Nkv - Nq
+    if causal and shift < 0:
+        raise ValueError("causal attention needs N_q <= N_kv")
+    G = Hq // Hkv
+    pos = np.arange(Nq) + shift          # sequence position of each query
+    O = np.empty((B, Hq, Nq, d), dtype=np.float64)
+    lse = np.empty((B, Hq, Nq), dtype=np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // G
+            Kh = np.asarray(K[b, hk], dtype=np.float64)
+            Vh = np.asarray(V[b, hk], dtype=np.float64)
+            qr = np.asarray(Q[b, h], dtype=np.float64)
+            P, l = _softmax_rows(_scores(qr, pos, Kh, scale, causal))
+            O[b, h] = P @ Vh
+            lse[b, h] = l
     return O, lse
 
 

@@ -287,3 +287,119 @@ def pin_row_subset(fwd, rng):
         O, l = fwd(Q, K, V, 0.5, causal)
         Os, ls = fwd(Q, K, V, 0.5, causal, rows=rows)
         assert np.allclose(O[:, :, rows], Os, atol=1e-14) and np.allclose(l[:, :, rows], ls, atol=1e-14)
+
+
+# ------------------------------------------ N_q != N_kv (split-KV forward) --
+
+def brute_force_attention_kv(q, k, v, scale, causal):
+    """Pure-Python evaluation for one head with N_q queries at the last N_q
+    positions of an N_kv-key sequence (no numpy)."""
+    nq, nk = len(q), len(k)
+    d, dv = len(q[0]), len(v[0])
+    out, lse = [], []
+    for i in range(nq):
+        pos = i + nk - nq
+        scores = []
+        for j in range(nk):
+            if causal and j > pos:
+                continue
+            s = 0.0
+            for t in range(d):
+                s += q[i][t] * k[j][t]
+            scores.append((j, scale * s))
+        mx = max(s for _, s in scores)
+        w = [(j, math.exp(s - mx)) for j, s in scores]
+        tot = sum(x for _, x in w)
+        row = [0.0] * dv
+        for j, x in w:
+            for t in range(dv):
+                row[t] += x / tot * v[j][t]
+        out.append(row)
+        lse.append(mx + math.log(tot))
+    return out, lse
+
+
+def pin_kv_golden(fwd_kv, atol=1e-12):
+    with open(os.path.join(HERE, "golden", "hand_examples.json")) as f:
+        cases = json.load(f)["kv_cases"]
+    for c in cases:
+        scale = parse_exact(c["scale"])
+        O, lse = fwd_kv(_as4(c["Q"]), _as4(c["K"]), _as4(c["V"]), scale, c["causal"])
+        expO = np.vectorize(parse_exact)(np.asarray(c["O"], dtype=object)).astype(np.float64)
+        explse = np.array([parse_exact(x) for x in c["lse"]])
+        assert np.allclose(O[0, 0], expO, atol=atol, rtol=0), (c["name"], O[0, 0], expO)
+        assert np.allclose(lse[0, 0], explse, atol=atol, rtol=0), (c["name"], lse[0, 0], explse)
+
+
+def pin_kv_brute_force(fwd_kv, rng, atol=1e-12):
+    for (Nq, Nk, d, Hq, Hkv, causal) in [(1, 1, 2, 1, 1, True), (1, 7, 3, 2, 1, True),
+                                         (3, 5, 2, 1, 1, True), (4, 9, 3, 4, 2, False),
+                                         (5, 5, 2, 2, 2, True), (6, 2, 3, 1, 1, False)]:
+        Q = rng.standard_normal((1, Hq, Nq, d))
+        K = rng.standard_normal((1, Hkv, Nk, d))
+        V = rng.standard_normal((1, Hkv, Nk, d))
+        O, lse = fwd_kv(Q, K, V, 0.6, causal)
+        G = Hq // Hkv
+        for h in range(Hq):
+            bo, bl = brute_force_attention_kv(Q[0, h].tolist(), K[0, h // G].tolist(),
+                                              V[0, h // G].tolist(), 0.6, causal)
+            assert np.allclose(O[0, h], np.array(bo), atol=atol, rtol=0), (Nq, Nk, h, causal)
+            assert np.allclose(lse[0, h], np.array(bl), atol=atol, rtol=0), (Nq, Nk, h, causal)
+
+
+def pin_kv_suffix(fwd_kv, fwd, rng):
+    """The last N_q rows of square attention over N_kv positions (computed
+    by the pinned square oracle, row subset) equal N_q queries at the end."""
+    B, Hq, Hkv, N, d = 1, 4, 2, 40, 5
+    Qf = rng.standard_normal((B, Hq, N, d))
+    K = rng.standard_normal((B, Hkv, N, d))
+    V = rng.standard_normal((B, Hkv, N, d))
+    for nq in (1, 3, 17, 40):
+        rows = np.arange(N - nq, N)
+        for causal in (False, True):
+            Oref, lref = fwd(Qf, K, V, 0.45, causal, rows=rows)
+            O, l = fwd_kv(Qf[:, :, N - nq:], K, V, 0.45, causal)
+            assert np.allclose(O, Oref, atol=1e-13) and np.allclose(l, lref, atol=1e-13), (nq, causal)
+
+
+def pin_kv_torch_sdpa(fwd_kv, rng):
+    """torch float64 SDPA with the bottom-right causal mask written out."""
+    import torch
+    import torch.nn.functional as F
+    B, Hq, Hkv, Nq, Nk, d = 2, 4, 1, 6, 23, 8
+    G = Hq // Hkv
+    Q = rng.standard_normal((B, Hq, Nq, d))
+    K = rng.standard_normal((B, Hkv, Nk, d))
+    V = rng.standard_normal((B, Hkv, Nk, d))
+    pos = torch.arange(Nq)[:, None] + (Nk - Nq)
+    mask = torch.arange(Nk)[None, :] <= pos      # True = visible
+    for causal in (False, True):
+        ref = F.scaled_dot_product_attention(torch.tensor(Q), torch.tensor(K).repeat_interleave(G, dim=1),
+                                             torch.tensor(V).repeat_interleave(G, dim=1),
+                                             attn_mask=mask if causal else None, scale=0.3)
+        O, _ = fwd_kv(Q, K, V, 0.3, causal)
+        assert np.allclose(O, ref.numpy(), atol=1e-13), causal
+
+
+def merge_partials(parts):
+    """Combine per-chunk (O_s, lse_s) with the online-softmax rescale
+    ("FlashAttention 1, 2, and 3 Explained", section 2): lse = ln sum exp(lse_s),
+    O = sum_s exp(lse_s - lse) O_s."""
+    lses = np.stack([l for _, l in parts])
+    m = lses.max(axis=0)
+    w = np.exp(lses - m)
+    lse = m + np.log(w.sum(axis=0))
+    O = sum(np.exp(l - lse)[..., None] * o for o, l in parts)
+    return O, lse
+
+
+def pin_kv_merge(fwd_kv, rng):
+    """Chunks of the keys processed on their own and merged give the whole."""
+    Q = rng.standard_normal((1, 2, 3, 4))
+    K = rng.standard_normal((1, 2, 29, 4))
+    V = rng.standard_normal((1, 2, 29, 4))
+    O, l = fwd_kv(Q, K, V, 0.8, False)
+    for cuts in ([0, 10, 29], [0, 1, 2, 15, 29], [0, 29]):
+        parts = [fwd_kv(Q, K[:, :, a:b], V[:, :, a:b], 0.8, False) for a, b in zip(cuts[:-1], cuts[1:])]
+        Om, lm = merge_partials(parts)
+        assert np.allclose(Om, O, atol=1e-13) and np.allclose(lm, l, atol=1e-13), cuts

@@ -104,6 +104,32 @@ def test_online_softmax_recurrence_reaches_the_definition():
         assert np.allclose(m + np.log(ell), l_ref[0, 0], atol=1e-13)
 
 
+def test_kv_golden_hand_examples():
+    pins.pin_kv_golden(oracle.attention_forward_kv)
+
+
+def test_kv_brute_force_tiny():
+    pins.pin_kv_brute_force(oracle.attention_forward_kv, _rng(11))
+
+
+def test_kv_suffix_of_square_attention():
+    pins.pin_kv_suffix(oracle.attention_forward_kv, oracle.attention_forward, _rng(12))
+
+
+def test_kv_torch_float64_sdpa_with_explicit_mask():
+    pins.pin_kv_torch_sdpa(oracle.attention_forward_kv, _rng(13))
+
+
+def test_kv_chunk_merge_identity():
+    pins.pin_kv_merge(oracle.attention_forward_kv, _rng(14))
+
+
+def test_kv_rejects_causal_with_more_queries_than_keys():
+    with pytest.raises(ValueError):
+        oracle.attention_forward_kv(np.zeros((1, 1, 3, 2)), np.zeros((1, 1, 2, 2)),
+                                    np.zeros((1, 1, 2, 2)), 1.0, True)
+
+
 # ------------------------------------------------------- planted mistakes --
 
 MUTATIONS = [
@@ -120,6 +146,10 @@ MUTATIONS = [
     ("scale dropped from dK", "dK[b, hk] += scale * (dS.T @ qr)", "dK[b, hk] += (dS.T @ qr)"),
     ("P not transposed in dV", "dV[b, hk] += P.T @ dor", "dV[b, hk] += P[:, :P.shape[0]] @ dor"),
     ("dP contracted over the wrong dimension order", "dP = dor @ Vh.T", "dP = dor @ Vh.T[::-1]"),
+    ("queries aligned to the start of the keys", "shift = Nkv - Nq", "shift = 0"),
+    ("query positions off by one", "pos = np.arange(Nq) + shift", "pos = np.arange(Nq) + shift - 1"),
+    ("split-KV head mapping wrong", "            hk = h // G\n            Kh = np.asarray(K[b, hk], dtype=np.float64)\n            Vh = np.asarray(V[b, hk], dtype=np.float64)\n            qr = np.asarray(Q[b, h], dtype=np.float64)",
+     "            hk = h % G\n            Kh = np.asarray(K[b, hk], dtype=np.float64)\n            Vh = np.asarray(V[b, hk], dtype=np.float64)\n            qr = np.asarray(Q[b, h], dtype=np.float64)"),
 ]
 
 
@@ -140,6 +170,8 @@ def _caught(mod) -> bool:
         lambda: pins.pin_invariants(mod.attention_forward, mod.attention_probs, _rng(2)),
         lambda: pins.pin_gqa(mod.attention_forward, mod.attention_backward, _rng(3)),
         lambda: pins.pin_finite_differences(mod.attention_forward, mod.attention_backward, _rng(4)),
+        lambda: pins.pin_kv_golden(mod.attention_forward_kv),
+        lambda: pins.pin_kv_brute_force(mod.attention_forward_kv, _rng(5)),
     ]
     for chk in checks:
         try:
