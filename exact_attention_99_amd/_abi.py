@@ -54,6 +54,12 @@ def load_library() -> ctypes.CDLL:
         lib.fa_bwd_dq.restype = i
         lib.fa_bwd_workspace_size.argtypes = [i, i, i, i, i, i]
         lib.fa_bwd_workspace_size.restype = sz
+        lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, f, i, i, vp]
+        lib.fa_fwd_splitkv.restype = i
+        lib.fa_fwd_splitkv_workspace_size.argtypes = [i, i, i, i, i]
+        lib.fa_fwd_splitkv_workspace_size.restype = sz
+        lib.fa_fwd_splitkv_default_splits.argtypes = [i, i, i, i, i, i]
+        lib.fa_fwd_splitkv_default_splits.restype = i
         lib.fa_status_string.argtypes = [i]
         lib.fa_status_string.restype = ctypes.c_char_p
         lib.fa_version.argtypes = []
@@ -124,6 +130,48 @@ def fa_fwd(q, k, v, causal: bool, scale: float, o=None, lse=None, stream=None):
                     _stream(q, stream))
     if st != 0:
         raise FaError(st, "fa_fwd")
+    return o, lse
+
+
+def fa_fwd_splitkv_workspace_size(B: int, H_q: int, N_q: int, d: int, num_splits: int) -> int:
+    return int(load_library().fa_fwd_splitkv_workspace_size(B, H_q, N_q, d, num_splits))
+
+
+def fa_fwd_splitkv_default_splits(B: int, H_q: int, H_kv: int, N_q: int, N_kv: int, d: int) -> int:
+    return int(load_library().fa_fwd_splitkv_default_splits(B, H_q, H_kv, N_q, N_kv, d))
+
+
+def fa_fwd_splitkv(q, k, v, causal: bool, scale: float, num_splits: int = 0, o=None, lse=None,
+                   workspace=None, stream=None):
+    """Split-KV forward for q [B, H_q, N_q, d] against k, v [B, H_kv, N_kv, d];
+    num_splits = 0 takes fa_fwd_splitkv_default_splits().  Returns (o, lse)."""
+    import torch
+    lib = load_library()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, N, d]")
+    B, Hq, Nq, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    Hkv, Nkv = k.shape[1], k.shape[2]
+    dt = _dtype_name(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    if num_splits == 0:
+        num_splits = int(lib.fa_fwd_splitkv_default_splits(B, Hq, Hkv, Nq, Nkv, d))
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    need = int(lib.fa_fwd_splitkv_workspace_size(B, Hq, Nq, d, num_splits))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check_same(q, k, v, o, lse, workspace)
+    st = lib.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                            B, Hq, Hkv, Nq, Nkv, d, int(bool(causal)), float(scale), int(num_splits),
+                            FA_DTYPE[dt], _stream(q, stream))
+    if st != 0:
+        raise FaError(st, "fa_fwd_splitkv")
     return o, lse
 
 

@@ -121,6 +121,84 @@ fa_status hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP
 
 }  // namespace
 
+}  // extern "C"
+
+namespace {
+
+bool split_sizes_ok(int B, int H_q, int H_kv, int N_q, int N_kv) {
+    if (B < 1 || H_q < 1 || H_kv < 1 || N_q < 1 || N_kv < 1) return false;
+    if (H_q % H_kv != 0) return false;
+    const long long G = H_q / H_kv;
+    // one K/V head and one group of stacked query rows must be addressable with
+    // 32-bit byte offsets, and the grid must fit
+    return (long long)N_kv * 128 * 2 < (1LL << 31) && G * N_q * 128 * 2 < (1LL << 31) &&
+           (long long)B * H_kv < (1LL << 31) && (long long)B * H_q * N_q < (1LL << 31);
+}
+
+size_t split_parts_bytes(int B, int H_q, int N_q, int d, int num_splits) {
+    const size_t rows = (size_t)B * H_q * N_q;
+    return round256((size_t)num_splits * rows * d * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd_splitkv_default_splits(int B, int H_q, int H_kv, int N_q, int N_kv, int d) {
+    if (!split_sizes_ok(B, H_q, H_kv, N_q, N_kv) || (d != 64 && d != 128)) return 0;
+    const long long G = H_q / H_kv;
+    const long long groups = (long long)B * H_kv * ((G * N_q + 31) / 32);
+    // about eight one-wave workgroups per compute unit, chunks of at least
+    // four key tiles
+    const long long want = (2048 + groups - 1) / groups;
+    const long long tile = fa355::split_tile_keys(d);
+    const long long most = (N_kv + 4 * tile - 1) / (4 * tile);
+    long long n = want < most ? want : most;
+    if (n < 1) n = 1;
+    if (n > 1024) n = 1024;
+    return (int)n;
+}
+
+size_t fa_fwd_splitkv_workspace_size(int B, int H_q, int N_q, int d, int num_splits) {
+    if (B < 1 || H_q < 1 || N_q < 1 || num_splits < 1 || num_splits > 1024 || (d != 64 && d != 128))
+        return 0;
+    const size_t rows = (size_t)B * H_q * N_q;
+    return split_parts_bytes(B, H_q, N_q, d, num_splits) + round256((size_t)num_splits * rows * sizeof(float));
+}
+
+fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                         void* workspace, size_t workspace_bytes, int B, int H_q, int H_kv,
+                         int N_q, int N_kv, int d, int causal, float scale, int num_splits,
+                         fa_dtype dtype, hipStream_t stream) {
+    if (!ptrs_ok({q, k, v, o, lse, workspace})) return FA_ERR_INVALID_ARG;
+    if (!split_sizes_ok(B, H_q, H_kv, N_q, N_kv)) return FA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    if (causal && N_q > N_kv) return FA_ERR_INVALID_ARG;
+    if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype)) return FA_ERR_INVALID_ARG;
+    if (num_splits < 1 || num_splits > 1024) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (dtype == FA_DTYPE_FP32) return FA_ERR_UNSUPPORTED;
+    const size_t need = fa_fwd_splitkv_workspace_size(B, H_q, N_q, d, num_splits);
+    if (workspace_bytes < need) return FA_ERR_INVALID_ARG;
+
+    fa355::SplitArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.opart = static_cast<float*>(workspace);
+    a.lpart = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                       split_parts_bytes(B, H_q, N_q, d, num_splits));
+    a.B = B; a.Hq = H_q; a.Hkv = H_kv; a.Nq = N_q; a.Nkv = N_kv; a.d = d;
+    a.causal = causal;
+    a.nsplit = num_splits;
+    const int tile = fa355::split_tile_keys(d);
+    const int per = (N_kv + num_splits - 1) / num_splits;
+    a.chunk = (per + tile - 1) / tile * tile;
+    a.cl2 = scale * kLog2eHost;
+    a.dtype = (int)dtype;
+    a.stream = stream;
+    return hip_status(fa355::launch_fwd_split(a));
+}
+
 fa_status fa_bwd_prepare(const void* o, const void* dout, float* delta, int B, int H_q, int N,
                          int d, fa_dtype dtype, hipStream_t stream) {
     if (!ptrs_ok({o, dout, delta})) return FA_ERR_INVALID_ARG;

@@ -106,6 +106,12 @@ __device__ __forceinline__ float halves_max(float x) {
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Lazy rescale threshold of the online softmax (log2 units): the running
+// maximum moves only when a tile's maximum exceeds it by more than this, so
+// unnormalised probabilities stay below 2^kTau and the result stays exact
+// (the output and the row sum always refer to the same maximum).
+constexpr float kTau = 8.0f;
+
 // Native 2^x (v_exp_f32); exp2(-inf) = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

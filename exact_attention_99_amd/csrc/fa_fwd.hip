@@ -29,8 +29,6 @@ namespace fa355 {
 
 namespace {
 
-constexpr float kTau = 8.0f;
-
 // 16-bit inputs (bf16 or fp16), head dim D, NW waves, BC keys per tile.  Half
 // of the waves stage K, the other half stage V transposed; every staging
 // thread moves NCH (4 or 8) 16-byte chunks per tile: NCH chunks of K rows, or

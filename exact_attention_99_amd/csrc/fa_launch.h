@@ -40,7 +40,28 @@ struct BwdArgs {
     hipStream_t stream;
 };
 
+struct SplitArgs {
+    const void* q;   // [B, Hq, Nq, d]
+    const void* k;   // [B, Hkv, Nkv, d]
+    const void* v;
+    void* o;         // [B, Hq, Nq, d]
+    float* lse;      // [B, Hq, Nq]
+    float* opart;    // [nsplit, B*Hq*Nq, d] float32 partial outputs (workspace)
+    float* lpart;    // [nsplit, B*Hq*Nq] float32 partial logsumexps (workspace)
+    int B, Hq, Hkv, Nq, Nkv, d;
+    int causal;
+    int nsplit;      // key chunks
+    int chunk;       // keys per chunk (a multiple of the kernel's key tile)
+    float cl2;
+    int dtype;
+    hipStream_t stream;
+};
+
 hipError_t launch_fwd(const FwdArgs& a);
+// Split-KV forward: partials per key chunk, then the merge.
+hipError_t launch_fwd_split(const SplitArgs& a);
+// Keys per tile of the split-KV kernel at head dimension d.
+int split_tile_keys(int d);
 // Backward phases; each reads only the BwdArgs fields it needs.
 hipError_t launch_bwd_prepare(const BwdArgs& a);
 hipError_t launch_bwd_dkdv(const BwdArgs& a);

@@ -141,6 +141,50 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v,
                     int B, int H_q, int H_kv, int N, int d,
                     int causal, float scale, fa_dtype dtype, hipStream_t stream);
 
+/*
+ * Split-KV forward (FlashDecoding: "FlashAttention" glossary, the
+ * FlashDecoding paragraph): the same attention for a few query rows against
+ * a long key/value sequence, parallelised over the key length.  The keys are
+ * cut into num_splits chunks; each chunk yields a float32 partial output
+ * normalised over its own keys and the logsumexp of its scores, and a second
+ * pass merges them with the online-softmax rescale ("FlashAttention 1, 2,
+ * and 3 Explained", section 2): lse = ln sum_s exp(lse_s),
+ * O = sum_s exp(lse_s - lse) O_s.
+ *
+ *   q         in : [B, H_q, N_q, d], dtype.
+ *   k, v      in : [B, H_kv, N_kv, d], dtype.
+ *   o         out: [B, H_q, N_q, d], dtype.
+ *   lse       out: [B, H_q, N_q] float32, natural log, over the visible keys.
+ *   workspace scratch of at least fa_fwd_splitkv_workspace_size() bytes,
+ *             16-byte aligned, owned by the caller; its contents on entry are
+ *             ignored and on return hold the per-chunk partials:
+ *             float32 [num_splits, B * H_q * N_q, d] partial outputs, then
+ *             (at the next 256-byte boundary) float32 [num_splits,
+ *             B * H_q * N_q] partial logsumexps (-inf for a chunk in which a
+ *             row sees no key).
+ *   causal in {0, 1}: when 1 the queries are the last N_q positions of the
+ *          sequence, so query i sees keys j <= i + N_kv - N_q; requires
+ *          N_q <= N_kv.  With N_q == N_kv this is fa_fwd's mask.
+ *   num_splits in [1, 1024]: number of key chunks (keys are dealt in chunks
+ *          of ceil(N_kv / num_splits) rounded up to the kernel's key tile, so
+ *          trailing chunks may be empty); fa_fwd_splitkv_default_splits()
+ *          suggests one.
+ *   d in {64, 128}; dtype bf16 or fp16 (fp32 returns FA_ERR_UNSUPPORTED).
+ *   Other sizes and checks as for fa_fwd.
+ */
+fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v,
+                         void* o, float* lse,
+                         void* workspace, size_t workspace_bytes,
+                         int B, int H_q, int H_kv, int N_q, int N_kv, int d,
+                         int causal, float scale, int num_splits,
+                         fa_dtype dtype, hipStream_t stream);
+
+/* Workspace bytes fa_fwd_splitkv needs for these sizes (0 if invalid). */
+size_t fa_fwd_splitkv_workspace_size(int B, int H_q, int N_q, int d, int num_splits);
+
+/* A chunk count that fills the device for these sizes (0 if invalid). */
+int fa_fwd_splitkv_default_splits(int B, int H_q, int H_kv, int N_q, int N_kv, int d);
+
 /* Static, never-NULL description of a status code. */
 const char* fa_status_string(fa_status s);
 

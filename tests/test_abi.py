@@ -30,7 +30,9 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_prepare",
-                                    "fa_bwd_workspace_size", "fa_fwd", "fa_status_string",
+                                    "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_splitkv",
+                                    "fa_fwd_splitkv_default_splits",
+                                    "fa_fwd_splitkv_workspace_size", "fa_status_string",
                                     "fa_version"]
 
 
@@ -136,3 +138,44 @@ def test_phase_entry_points_reject(lib):
         assert lib.fa_bwd_dq(*p, 1, 2, 1, 16, 64, 1, 0.1, FP16, None) == INVALID
     assert lib.fa_bwd_dq(*([A] * 7), 1, 2, 1, 16, 64, 3, 0.1, FP16, None) == INVALID
     assert lib.fa_bwd_dq(*([A] * 7), 1, 2, 1, 16, 64, 1, 0.1, 9, None) == INVALID
+
+
+def split(lib, ptrs=None, ws_bytes=1 << 30, B=1, Hq=4, Hkv=1, Nq=1, Nkv=1000, d=128, causal=1,
+          scale=0.088, splits=8, dtype=BF16):
+    p = ptrs or [A] * 6
+    return lib.fa_fwd_splitkv(*p[:5], p[5], ws_bytes, B, Hq, Hkv, Nq, Nkv, d, causal, scale, splits,
+                              dtype, None)
+
+
+def test_splitkv_rejects(lib):
+    for i in range(6):
+        p = [A] * 6
+        p[i] = None
+        assert split(lib, ptrs=p) == INVALID
+        p[i] = MIS
+        assert split(lib, ptrs=p) == INVALID
+    need = _abi.fa_fwd_splitkv_workspace_size(1, 4, 1, 128, 8)
+    assert split(lib, ws_bytes=need - 1) == INVALID
+    assert split(lib, Nq=1001, Nkv=1000) == INVALID          # causal needs N_q <= N_kv
+    assert split(lib, Nq=0) == INVALID and split(lib, Nkv=0) == INVALID
+    assert split(lib, Hq=3, Hkv=2) == INVALID
+    assert split(lib, splits=0) == INVALID and split(lib, splits=1025) == INVALID
+    assert split(lib, causal=2) == INVALID
+    assert split(lib, scale=0.0) == INVALID and split(lib, scale=float("nan")) == INVALID
+    assert split(lib, dtype=7) == INVALID
+    assert split(lib, d=96) == UNSUPPORTED
+    assert split(lib, dtype=FP32) == UNSUPPORTED
+
+
+def test_splitkv_sizes(lib):
+    # partial outputs (splits x rows x d floats) then partial logsumexps, each
+    # rounded up to 256 bytes
+    rows = 2 * 8 * 3
+    assert _abi.fa_fwd_splitkv_workspace_size(2, 8, 3, 64, 5) == (
+        (5 * rows * 64 * 4 + 255) // 256 * 256 + (5 * rows * 4 + 255) // 256 * 256)
+    assert _abi.fa_fwd_splitkv_workspace_size(1, 1, 1, 64, 0) == 0
+    assert _abi.fa_fwd_splitkv_workspace_size(1, 1, 1, 80, 1) == 0
+    # the suggested split count fills the device but keeps chunks of >= 4 tiles
+    assert 1 <= _abi.fa_fwd_splitkv_default_splits(1, 32, 8, 1, 65536, 128) <= 512
+    assert _abi.fa_fwd_splitkv_default_splits(1, 1, 1, 1, 64, 128) == 1
+    assert _abi.fa_fwd_splitkv_default_splits(1, 3, 2, 1, 64, 128) == 0

@@ -114,3 +114,55 @@ def workload_inputs(w: Workload, with_dout: bool = False, device: str = "cpu"):
 def to_f64(x: torch.Tensor):
     """Exact upcast of a dtype tensor to a float64 numpy array (for the oracle)."""
     return x.detach().to("cpu").to(torch.float64).numpy()
+
+
+# --------------------------------------------------------------------------
+# Split-KV (decoding) shapes: a few query rows against a long key/value
+# sequence ("FlashAttention" glossary, FlashDecoding paragraph).  The key/value
+# sequences are those of the long-context workloads above; the query counts
+# are one new token per sequence and an eight-token chunk.
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    B: int
+    H_q: int
+    H_kv: int
+    N_q: int
+    N_kv: int
+    d: int
+    dtype: str
+    causal: bool
+    seed: int
+
+    def kv_bytes(self) -> int:
+        """K and V bytes one pass must read."""
+        return 2 * self.B * self.H_kv * self.N_kv * self.d * (4 if self.dtype == "fp32" else 2)
+
+
+DECODE_WORKLOADS: Dict[str, DecodeWorkload] = {
+    w.name: w for w in (
+        DecodeWorkload("genome_gqa_64k_decode", 1, 32, 8, 1, 65536, 128, "bf16", True, 1006),
+        DecodeWorkload("genome_gqa_64k_chunk8", 1, 32, 8, 8, 65536, 128, "bf16", True, 1007),
+        DecodeWorkload("llama_mha_8k_decode", 4, 32, 32, 1, 8192, 128, "bf16", True, 1008),
+    )
+}
+
+
+def make_decode_inputs(B: int, H_q: int, H_kv: int, N_q: int, N_kv: int, d: int, dtype: str,
+                       seed: int, device: str = "cpu"):
+    """Q [B, H_q, N_q, d], then K and V [B, H_kv, N_kv, d]: fp32 N(0, 1) draws
+    from one seeded generator, cast to the dtype (round to nearest even)."""
+    if dtype not in DTYPES:
+        raise ValueError(f"unknown dtype {dtype!r}")
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    t = DTYPES[dtype]
+
+    def draw(h: int, n: int) -> torch.Tensor:
+        return torch.randn((B, h, n, d), generator=g, dtype=torch.float32, device=device).to(t)
+
+    q = draw(H_q, N_q)
+    k = draw(H_kv, N_kv)
+    v = draw(H_kv, N_kv)
+    return q, k, v
