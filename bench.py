@@ -95,6 +95,47 @@ def cpu_baseline(w, q, k, v, do, budget_s: float = 12.0, max_heads: int = 32):
             "seconds": t_total}
 
 
+def measure_splitkv(dw, dev, stream, iters: int = 20, one_chunk: bool = True):
+    """Split-KV forward on a decoding shape: median time of the whole call
+    (chunk kernel + merge) over `iters` launches, K/V bytes per second against
+    the HBM peak, and the same call with a single chunk for comparison."""
+    import torch
+    import workloads
+    from exact_attention_99_amd import fa_fwd_splitkv, fa_fwd_splitkv_default_splits, fa_fwd_splitkv_workspace_size
+    q, k, v = workloads.make_decode_inputs(dw.B, dw.H_q, dw.H_kv, dw.N_q, dw.N_kv, dw.d, dw.dtype,
+                                           dw.seed, device=dev)
+    scale = 1.0 / math.sqrt(dw.d)
+    o = torch.empty_like(q)
+    lse = torch.empty((dw.B, dw.H_q, dw.N_q), dtype=torch.float32, device=dev)
+
+    def timed(splits):
+        ws = torch.empty(fa_fwd_splitkv_workspace_size(dw.B, dw.H_q, dw.N_q, dw.d, splits),
+                         dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            fa_fwd_splitkv(q, k, v, dw.causal, scale, splits, o=o, lse=lse, workspace=ws, stream=stream)
+        ts = []
+        for _ in range(iters):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fa_fwd_splitkv(q, k, v, dw.causal, scale, splits, o=o, lse=lse, workspace=ws, stream=stream)
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ts.sort()
+        return ts[len(ts) // 2], ts[0]
+
+    splits = fa_fwd_splitkv_default_splits(dw.B, dw.H_q, dw.H_kv, dw.N_q, dw.N_kv, dw.d)
+    med, mn = timed(splits)
+    one = timed(1)[0] if one_chunk else None
+    gbs = dw.kv_bytes() / (med * 1e-3) / 1e9
+    return {"workload": dw.name, "B": dw.B, "H_q": dw.H_q, "H_kv": dw.H_kv, "N_q": dw.N_q,
+            "N_kv": dw.N_kv, "d": dw.d, "causal": dw.causal, "splits": splits,
+            "ms_median": med, "ms_min": mn, "kv_bytes": dw.kv_bytes(),
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS},
+            "ms_one_chunk": one}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,6 +143,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama_mha_8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-splitkv", dest="splitkv", action="store_false",
+                    help="skip the split-KV decoding measurements")
+    ap.add_argument("--splitkv-only", default=None, metavar="DECODE_WORKLOAD",
+                    help="only measure the split-KV forward on one decoding shape")
     ap.add_argument("--flush-iters", type=int, default=20,
                     help="cold-cache timed launches per kernel (0 to skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -133,6 +178,13 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": COPY_BYTES}))
+        return 0
+    if args.splitkv_only:
+        torch.cuda.set_device(0)
+        # the default chunk count only, so that a profile of this run sees one configuration
+        rec = measure_splitkv(workloads.DECODE_WORKLOADS[args.splitkv_only], "cuda:0",
+                              torch.cuda.current_stream(), one_chunk=False)
+        print(json.dumps({"splitkv": rec}), flush=True)
         return 0
     w = workloads.WORKLOADS[args.workload]
     causal = True in w.causal_modes
@@ -260,6 +312,9 @@ def main() -> int:
         "roofline": roof,
         "cpu_baseline": None,
     }
+    if args.splitkv:
+        out["splitkv"] = [measure_splitkv(workloads.DECODE_WORKLOADS[n], dev, stream)
+                          for n in ("genome_gqa_64k_decode", "genome_gqa_64k_chunk8", "llama_mha_8k_decode")]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, do)
     print(json.dumps(out), flush=True)

@@ -197,40 +197,63 @@ fwd_split16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     }
 }
 
-// Merge of the partials of one row per wave: lse = log sum_s exp(lse_s),
-// O = sum_s exp(lse_s - lse) O_s, rounded to the output dtype.
+// Merge of the partials of one row per 256-thread workgroup:
+// lse = log sum_s exp(lse_s), O = sum_s exp(lse_s - lse) O_s, rounded to the
+// output dtype.  The chunk weights are formed in parallel (one chunk per
+// thread, at most kMaxSplits chunks) and kept in LDS; then 256 / D groups of
+// D threads each accumulate one output dimension over every (256 / D)-th
+// chunk, and the groups' sums are added in LDS.
+constexpr int kMaxSplits = 1024;
+
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
 merge_split_kernel(const float* __restrict__ Opart, const float* __restrict__ Lpart,
                    uint16_t* __restrict__ O, float* __restrict__ LSE, int nrows, int nsplit) {
-    constexpr int PER = D / 64;  // dims per lane
-    const int lane = threadIdx.x & 63;
-    const int R = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (R >= nrows) return;
+    constexpr int NG = 256 / D;
+    __shared__ float w[kMaxSplits];
+    __shared__ float red[8];
+    __shared__ float part[NG][D];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = tid >> 6;
+    const int R = blockIdx.x;
+
+    // the largest partial logsumexp
     float m = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) m = fmaxf(m, Lpart[(size_t)s * nrows + R]);
-    float acc[PER];
+    for (int s = tid; s < nsplit; s += 256) m = fmaxf(m, Lpart[(size_t)s * nrows + R]);
 #pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-    float wsum = 0.f;
-    if (m != -INFINITY) {
-        for (int s = 0; s < nsplit; ++s) {
-            const float ls = Lpart[(size_t)s * nrows + R];
-            const float w = (ls == -INFINITY) ? 0.f : __expf(ls - m);
-            wsum += w;
-            const float* orow = Opart + ((size_t)s * nrows + R) * D;
-#pragma unroll
-            for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, orow[lane + 64 * i], acc[i]);
-        }
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    if (lane == 0) red[wv] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    // chunk weights relative to it, and their sum
+    float ws = 0.f;
+    for (int s = tid; s < nsplit; s += 256) {
+        const float ls = Lpart[(size_t)s * nrows + R];
+        const float x = (ls == -INFINITY || m == -INFINITY) ? 0.f : __expf(ls - m);
+        w[s] = x;
+        ws += x;
     }
-    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-    uint16_t* orow = O + (size_t)R * D;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const uint32_t packed = Mma<T>::pack2(acc[i] * inv, 0.f);
-        orow[lane + 64 * i] = (uint16_t)(packed & 0xFFFFu);
+    for (int o = 32; o >= 1; o >>= 1) ws += __shfl_xor(ws, o, 64);
+    if (lane == 0) red[4 + wv] = ws;
+    __syncthreads();
+    const float wsum = red[4] + red[5] + red[6] + red[7];
+
+    const int dim = tid % D, grp = tid / D;
+    float acc = 0.f;
+#pragma unroll 8
+    for (int s = grp; s < nsplit; s += NG) acc = fmaf(w[s], Opart[((size_t)s * nrows + R) * D + dim], acc);
+    part[grp][dim] = acc;
+    __syncthreads();
+    if (grp == 0) {
+        float t = 0.f;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) t += part[g][dim];
+        const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+        O[(size_t)R * D + dim] = (uint16_t)(Mma<T>::pack2(t * inv, 0.f) & 0xFFFFu);
+        if (dim == 0) LSE[R] = wsum > 0.f ? m + __logf(wsum) : -INFINITY;
     }
-    if (lane == 0) LSE[R] = wsum > 0.f ? m + __logf(wsum) : -INFINITY;
 }
 
 template <typename T, int D, bool CAUSAL>
@@ -245,7 +268,7 @@ hipError_t split16(const SplitArgs& a) {
     if (e != hipSuccess) return e;
     (void)BC;
     const int nrows = a.B * a.Hq * a.Nq;
-    hipLaunchKernelGGL((merge_split_kernel<T, D>), dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, a.stream,
+    hipLaunchKernelGGL((merge_split_kernel<T, D>), dim3((unsigned)nrows), dim3(256), 0, a.stream,
                        a.opart, a.lpart, (uint16_t*)a.o, a.lse, nrows, a.nsplit);
     return hipGetLastError();
 }
