@@ -166,3 +166,37 @@ def make_decode_inputs(B: int, H_q: int, H_kv: int, N_q: int, N_kv: int, d: int,
     k = draw(H_kv, N_kv)
     v = draw(H_kv, N_kv)
     return q, k, v
+
+
+# --------------------------------------------------------------------------
+# FP8 forward inputs.  Block quantization with an incoherent-processing
+# rotation ("FlashAttention" glossary, FlashAttention-3 paragraph: FP8 with
+# block quantization and incoherent processing) matters most when a few
+# entries are far larger than the rest.  The outlier recipe: i.i.d. N(0, 1)
+# entries, plus, at a Bernoulli(p) subset of positions, an extra N(0, s^2)
+# term; then cast to the dtype.  The rotation's random +-1 signs are drawn
+# here too, so both sides receive them as inputs.
+
+def make_outlier_inputs(B: int, H_q: int, H_kv: int, N: int, d: int, dtype: str, seed: int,
+                        p: float = 1e-3, s: float = 10.0, device: str = "cpu"):
+    """Q, K, V as in ``make_inputs`` with outliers added (draw order: Q, K, V
+    bases, then for each of Q, K, V a uniform mask draw and an N(0, 1) draw)."""
+    if dtype not in DTYPES:
+        raise ValueError(f"unknown dtype {dtype!r}")
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    shapes = [(B, H_q, N, d), (B, H_kv, N, d), (B, H_kv, N, d)]
+    base = [torch.randn(sh, generator=g, dtype=torch.float32, device=device) for sh in shapes]
+    out = []
+    for x, sh in zip(base, shapes):
+        mask = torch.rand(sh, generator=g, dtype=torch.float32, device=device) < p
+        extra = torch.randn(sh, generator=g, dtype=torch.float32, device=device) * s
+        out.append((x + mask * extra).to(DTYPES[dtype]))
+    return tuple(out)
+
+
+def make_signs(d: int, seed: int) -> torch.Tensor:
+    """d random signs (+1.0 / -1.0, float32) for the rotation."""
+    g = torch.Generator()
+    g.manual_seed(seed)
+    return torch.randint(0, 2, (d,), generator=g).to(torch.float32) * 2 - 1
