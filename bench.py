@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 
 METRIC = "attention fwd/bwd TFLOPS (bf16, causal, d=128) and % of MI355X MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 matrix-core peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 COPY_BYTES = 1 << 30        # size of the counter-calibration copy
 FLUSH_BYTES = 512 << 20     # cache-evicting fill before each cold-timed launch
@@ -136,6 +137,61 @@ def measure_splitkv(dw, dev, stream, iters: int = 20, one_chunk: bool = True):
             "ms_one_chunk": one}
 
 
+def measure_fp8(w, q, k, v, stream, iters: int = 20):
+    """FP8 forward on the workload's own Q, K, V: block quantization of Q and K
+    (with the rotation) and of V, then the e4m3 forward.  Median of `iters`
+    event-timed launches of each kernel, warm."""
+    import torch
+    import workloads
+    from exact_attention_99_amd import fa_fp8_quantize, fa_fwd_fp8
+    causal = True in w.causal_modes
+    signs = workloads.make_signs(w.d, w.seed + 1).to(q.device)
+    qc, qs = fa_fp8_quantize(q, signs, stream=stream)
+    kc, ks = fa_fp8_quantize(k, signs, stream=stream)
+    vc, vs = fa_fp8_quantize(v, stream=stream)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H_q, w.N), dtype=torch.float32, device=q.device)
+    launches = {
+        "quant_q": lambda: fa_fp8_quantize(q, signs, codes=qc, scales=qs, stream=stream),
+        "quant_k": lambda: fa_fp8_quantize(k, signs, codes=kc, scales=ks, stream=stream),
+        "quant_v": lambda: fa_fp8_quantize(v, codes=vc, scales=vs, stream=stream),
+        "fwd_fp8": lambda: fa_fwd_fp8(qc, kc, vc, qs, ks, vs, causal, w.scale, o=o, lse=lse, stream=stream),
+    }
+    med = {}
+    for name, fn in launches.items():
+        for _ in range(3):
+            fn()
+        ts = []
+        for _ in range(iters):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ts.sort()
+        med[name] = ts[len(ts) // 2]
+    F = w.flops_fwd(causal)
+    tf = F / (med["fwd_fp8"] * 1e-3) / 1e12
+    # quantizer traffic per tensor: 2-byte reads, 1-byte codes, one float per 64 rows
+    def qbytes(h):
+        n = w.B * h * w.N * w.d
+        return 3.0 * n + 4.0 * w.B * h * ((w.N + 63) // 64)
+    quant_bytes = qbytes(w.H_q) + 2 * qbytes(w.H_kv)
+    quant_ms = med["quant_q"] + med["quant_k"] + med["quant_v"]
+    gbs = quant_bytes / (quant_ms * 1e-3) / 1e9
+    return {"workload": w.name, "causal": causal, "out_dtype": "bf16", "block_rows": 64,
+            "rotation": "Q and K", "kernels_ms": med,
+            "fwd_fp8": {"ms": med["fwd_fp8"], "tflops": tf,
+                        "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP8_TFLOPS,
+                                     "unit": "TFLOP/s", "frac": tf / PEAK_FP8_TFLOPS}},
+            "quantize": {"ms": quant_ms, "bytes": quant_bytes,
+                         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                                      "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS}},
+            "path_ms": quant_ms + med["fwd_fp8"],
+            "path_tflops": F / ((quant_ms + med["fwd_fp8"]) * 1e-3) / 1e12}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,6 +203,10 @@ def main() -> int:
                     help="skip the split-KV decoding measurements")
     ap.add_argument("--splitkv-only", default=None, metavar="DECODE_WORKLOAD",
                     help="only measure the split-KV forward on one decoding shape")
+    ap.add_argument("--no-fp8", dest="fp8", action="store_false",
+                    help="skip the FP8 forward measurement")
+    ap.add_argument("--fp8-only", action="store_true",
+                    help="only measure the FP8 path (quantizer + e4m3 forward)")
     ap.add_argument("--flush-iters", type=int, default=20,
                     help="cold-cache timed launches per kernel (0 to skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -191,6 +251,9 @@ def main() -> int:
     dev = "cuda:0"
     torch.cuda.set_device(0)
     q, k, v, do = workloads.workload_inputs(w, with_dout=True, device=dev)
+    if args.fp8_only:
+        print(json.dumps({"fp8": measure_fp8(w, q, k, v, torch.cuda.current_stream())}), flush=True)
+        return 0
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H_q, w.N), dtype=torch.float32, device=dev)
     delta = torch.empty_like(lse)
@@ -315,6 +378,9 @@ def main() -> int:
     if args.splitkv:
         out["splitkv"] = [measure_splitkv(workloads.DECODE_WORKLOADS[n], dev, stream)
                           for n in ("genome_gqa_64k_decode", "genome_gqa_64k_chunk8", "llama_mha_8k_decode")]
+    if args.fp8:
+        out["fp8"] = measure_fp8(w, q, k, v, stream)
+        out["fp8"]["speedup_vs_16bit_fwd"] = fwd_ms / out["fp8"]["fwd_fp8"]["ms"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, do)
     print(json.dumps(out), flush=True)

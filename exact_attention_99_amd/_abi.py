@@ -60,6 +60,10 @@ def load_library() -> ctypes.CDLL:
         lib.fa_fwd_splitkv_workspace_size.restype = sz
         lib.fa_fwd_splitkv_default_splits.argtypes = [i, i, i, i, i, i]
         lib.fa_fwd_splitkv_default_splits.restype = i
+        lib.fa_fp8_quantize.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
+        lib.fa_fp8_quantize.restype = i
+        lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+        lib.fa_fwd_fp8.restype = i
         lib.fa_status_string.argtypes = [i]
         lib.fa_status_string.restype = ctypes.c_char_p
         lib.fa_version.argtypes = []
@@ -251,3 +255,74 @@ def fa_bwd_dq(q, k, v, lse, dout, delta, causal: bool, scale: float, dq=None, st
     if st != 0:
         raise FaError(st, "fa_bwd_dq")
     return dq
+
+
+FP8_BLOCK_ROWS = 64
+
+
+def fa_fp8_quantize(x, signs=None, codes=None, scales=None, stream=None):
+    """Block-quantize x [B, H, N, d] (bf16 / fp16) to e4m3 codes (uint8, same
+    shape) and float32 scales [B, H, ceil(N / 64)]; ``signs`` (d float32 +-1
+    values) applies the rotation first.  Returns (codes, scales)."""
+    import torch
+    lib = load_library()
+    if x.dim() != 4:
+        raise ValueError("x must be 4-D [B, H, N, d]")
+    B, H, N, d = x.shape
+    dt = _dtype_name(x)
+    nblk = (N + FP8_BLOCK_ROWS - 1) // FP8_BLOCK_ROWS
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((B, H, nblk), dtype=torch.float32, device=x.device)
+    if codes.dtype != torch.uint8 or tuple(codes.shape) != tuple(x.shape):
+        raise ValueError("codes must be uint8 with the shape of x")
+    if scales.dtype != torch.float32 or tuple(scales.shape) != (B, H, nblk):
+        raise ValueError(f"scales must be float32 [{B}, {H}, {nblk}]")
+    tensors = [x, codes, scales]
+    if signs is not None:
+        if signs.dtype != torch.float32 or tuple(signs.shape) != (d,):
+            raise ValueError(f"signs must be float32 [{d}]")
+        tensors.append(signs)
+    _check_same(*tensors)
+    st = lib.fa_fp8_quantize(x.data_ptr(), signs.data_ptr() if signs is not None else None,
+                             codes.data_ptr(), scales.data_ptr(), B, H, N, d, FA_DTYPE[dt],
+                             _stream(x, stream))
+    if st != 0:
+        raise FaError(st, "fa_fp8_quantize")
+    return codes, scales
+
+
+def fa_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, causal: bool, scale: float,
+               out_dtype: str = "bf16", o=None, lse=None, stream=None):
+    """Attention of block-quantized inputs (e4m3 codes q, k, v and their
+    block scales); returns (o, lse) with o in ``out_dtype``."""
+    import torch
+    lib = load_library()
+    B, Hq, Hkv, N, d = _shape(q, k, v)
+    for t in (q, k, v):
+        if t.dtype != torch.uint8:
+            raise TypeError("q, k, v must be uint8 e4m3 codes")
+    nblk = (N + FP8_BLOCK_ROWS - 1) // FP8_BLOCK_ROWS
+    for t, h in ((q_scale, Hq), (k_scale, Hkv), (v_scale, Hkv)):
+        if t.dtype != torch.float32 or tuple(t.shape) != (B, h, nblk):
+            raise ValueError(f"block scales must be float32 [B, H, {nblk}]")
+    if out_dtype not in ("bf16", "fp16"):
+        raise ValueError("out_dtype must be bf16 or fp16")
+    if o is None:
+        o = torch.empty(q.shape, dtype=_OUT_DTYPES()[out_dtype], device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _check_same(q, k, v, q_scale, k_scale, v_scale, o, lse)
+    st = lib.fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_scale.data_ptr(),
+                        k_scale.data_ptr(), v_scale.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                        B, Hq, Hkv, N, d, int(bool(causal)), float(scale), FA_DTYPE[out_dtype],
+                        _stream(q, stream))
+    if st != 0:
+        raise FaError(st, "fa_fwd_fp8")
+    return o, lse
+
+
+def _OUT_DTYPES():
+    import torch
+    return {"bf16": torch.bfloat16, "fp16": torch.float16}

@@ -249,6 +249,44 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
     return hip_status(e);
 }
 
+fa_status fa_fp8_quantize(const void* x, const float* signs, unsigned char* codes, float* scales,
+                          int B, int H, int N, int d, fa_dtype dtype, hipStream_t stream) {
+    if (!ptrs_ok({x, codes}) || !scales || (reinterpret_cast<uintptr_t>(scales) & 3u)) return FA_ERR_INVALID_ARG;
+    if (signs && !aligned16(signs)) return FA_ERR_INVALID_ARG;
+    if (!sizes_ok(B, H, H, N) || !dtype_ok(dtype)) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (dtype == FA_DTYPE_FP32) return FA_ERR_UNSUPPORTED;
+    fa355::Fp8QuantArgs a;
+    a.x = x; a.signs = signs; a.codes = codes; a.scales = scales;
+    a.B = B; a.H = H; a.N = N; a.d = d;
+    a.rs = (float)(1.0 / sqrt((double)d));
+    a.dtype = (int)dtype;
+    a.stream = stream;
+    return hip_status(fa355::launch_fp8_quantize(a));
+}
+
+fa_status fa_fwd_fp8(const unsigned char* q, const unsigned char* k, const unsigned char* v, const float* q_scale,
+                     const float* k_scale, const float* v_scale, void* o, float* lse, int B,
+                     int H_q, int H_kv, int N, int d, int causal, float scale, fa_dtype out_dtype,
+                     hipStream_t stream) {
+    if (!ptrs_ok({q, k, v, o, lse})) return FA_ERR_INVALID_ARG;
+    for (const float* p : {q_scale, k_scale, v_scale})
+        if (!p || (reinterpret_cast<uintptr_t>(p) & 3u)) return FA_ERR_INVALID_ARG;
+    const fa_status st = check_common(B, H_q, H_kv, N, d, causal, scale, out_dtype);
+    if (st != FA_OK) return st;
+    if (out_dtype == FA_DTYPE_FP32) return FA_ERR_UNSUPPORTED;
+    fa355::Fp8FwdArgs a;
+    a.q = q; a.k = k; a.v = v;
+    a.sq = q_scale; a.sk = k_scale; a.sv = v_scale;
+    a.o = o; a.lse = lse;
+    a.B = B; a.Hq = H_q; a.Hkv = H_kv; a.N = N; a.d = d;
+    a.causal = causal;
+    a.cl2 = scale * kLog2eHost;
+    a.out_dtype = (int)out_dtype;
+    a.stream = stream;
+    return hip_status(fa355::launch_fwd_fp8(a));
+}
+
 const char* fa_status_string(fa_status s) {
     switch (s) {
         case FA_OK: return "FA_OK: success";

@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace fa355 {
 
@@ -57,7 +58,37 @@ struct SplitArgs {
     hipStream_t stream;
 };
 
+struct Fp8QuantArgs {
+    const void* x;       // [B, H, N, d] bf16 / fp16
+    const float* signs;  // [d] rotation signs, or null for no rotation
+    uint8_t* codes;      // [B, H, N, d] e4m3
+    float* scales;       // [B, H, ceil(N / 64)]
+    int B, H, N, d;
+    float rs;            // fp32(1 / sqrt(d))
+    int dtype;
+    hipStream_t stream;
+};
+
+struct Fp8FwdArgs {
+    const uint8_t* q;    // [B, Hq, N, d] e4m3
+    const uint8_t* k;    // [B, Hkv, N, d]
+    const uint8_t* v;
+    const float* sq;     // [B, Hq, ceil(N / 64)] block scales
+    const float* sk;     // [B, Hkv, ceil(N / 64)]
+    const float* sv;
+    void* o;             // [B, Hq, N, d] out_dtype
+    float* lse;          // [B, Hq, N]
+    int B, Hq, Hkv, N, d;
+    int causal;
+    float cl2;
+    int out_dtype;
+    hipStream_t stream;
+};
+
 hipError_t launch_fwd(const FwdArgs& a);
+// FP8 path: block quantizer and the e4m3 forward.
+hipError_t launch_fp8_quantize(const Fp8QuantArgs& a);
+hipError_t launch_fwd_fp8(const Fp8FwdArgs& a);
 // Split-KV forward: partials per key chunk, then the merge.
 hipError_t launch_fwd_split(const SplitArgs& a);
 // Keys per tile of the split-KV kernel at head dimension d.

@@ -185,6 +185,69 @@ size_t fa_fwd_splitkv_workspace_size(int B, int H_q, int N_q, int d, int num_spl
 /* A chunk count that fills the device for these sizes (0 if invalid). */
 int fa_fwd_splitkv_default_splits(int B, int H_q, int H_kv, int N_q, int N_kv, int d);
 
+/*
+ * FP8 path ("FlashAttention 1, 2, and 3 Explained", section 4 on
+ * FlashAttention-3: FP8 with block quantization and incoherent processing;
+ * "FlashAttention" glossary, FlashAttention-3 paragraph).  Low precision:
+ * the forward below computes attention of the quantized values, not of the
+ * 16-bit inputs.
+ *
+ * e4m3 codes are the OCP FP8 E4M3 format (1 sign, 4 exponent bits with bias
+ * 7, 3 mantissa bits; largest finite value 448; 0x7f / 0xff are NaN and are
+ * never produced).  A quantized tensor is a pair:
+ *   codes  uint8   [B, H, N, d]          (same layout as the 16-bit tensor)
+ *   scales float32 [B, H, ceil(N / 64)]  one scale per block of 64 rows
+ * and stands for codes * scales[block of the row] (FA_FP8_BLOCK_ROWS).
+ */
+#define FA_FP8_BLOCK_ROWS 64
+
+/*
+ * Block quantizer.  For each head and block of 64 rows of x (the last block
+ * may be shorter):
+ *   y      = x, or (x * signs) H / sqrt(d) when signs != NULL: the
+ *            incoherent-processing rotation, H the d x d Sylvester Hadamard
+ *            matrix, evaluated in float32 as the fast Walsh-Hadamard transform
+ *            (butterflies (a, b) -> (a + b, a - b) with strides 1, 2, 4, ...,
+ *            then one multiplication by float32(1 / sqrt(d)));
+ *   amax   = max |y| over the block;  scale = amax / 448 (1 if amax == 0);
+ *   codes  = e4m3(clamp(y * (448 / amax), -448, 448)), round to nearest even,
+ *            sign bit kept for negative values that round to zero.
+ *   x      in : [B, H, N, d] bf16 or fp16 (`dtype`; fp32 returns
+ *               FA_ERR_UNSUPPORTED), 16-byte aligned.
+ *   signs  in : NULL, or d float32 values (+1 / -1), 16-byte aligned.  Pass
+ *               the same signs for Q and K (the rotation is orthogonal, so
+ *               scores are unchanged) and NULL for V.
+ *   codes  out: [B, H, N, d] uint8, 16-byte aligned.
+ *   scales out: [B, H, ceil(N / 64)] float32, 4-byte aligned.
+ *   B, H, N >= 1 (sizes as for fa_fwd); d in {64, 128}.
+ */
+fa_status fa_fp8_quantize(const void* x, const float* signs,
+                          unsigned char* codes, float* scales,
+                          int B, int H, int N, int d, fa_dtype dtype,
+                          hipStream_t stream);
+
+/*
+ * FP8 forward: O = softmax(scale * Qd Kd^T [causal]) Vd and lse, where Qd,
+ * Kd, Vd are the dequantized values of three fa_fp8_quantize outputs.  Both
+ * products run on the e4m3 matrix cores; the probabilities enter the P V
+ * product rounded to e4m3 (relative error up to 2^-4 each), the row sums and
+ * lse are kept in float32 from the unrounded probabilities.
+ *   q, k, v   in : e4m3 codes [B, H_q, N, d] / [B, H_kv, N, d] / [B, H_kv, N, d],
+ *                  16-byte aligned.
+ *   q_scale, k_scale, v_scale in: their block scales [B, H, ceil(N / 64)],
+ *                  float32, finite and > 0 (as fa_fp8_quantize writes them),
+ *                  4-byte aligned.
+ *   o         out: [B, H_q, N, d] in out_dtype (bf16 or fp16; fp32 returns
+ *                  FA_ERR_UNSUPPORTED).
+ *   lse       out: [B, H_q, N] float32, natural log, of the dequantized scores.
+ *   Other arguments and checks as for fa_fwd.  Needs no workspace.
+ */
+fa_status fa_fwd_fp8(const unsigned char* q, const unsigned char* k, const unsigned char* v,
+                     const float* q_scale, const float* k_scale, const float* v_scale,
+                     void* o, float* lse,
+                     int B, int H_q, int H_kv, int N, int d,
+                     int causal, float scale, fa_dtype out_dtype, hipStream_t stream);
+
 /* Static, never-NULL description of a status code. */
 const char* fa_status_string(fa_status s);
 

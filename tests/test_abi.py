@@ -30,7 +30,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_prepare",
-                                    "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_splitkv",
+                                    "fa_bwd_workspace_size", "fa_fp8_quantize", "fa_fwd",
+                                    "fa_fwd_fp8", "fa_fwd_splitkv",
                                     "fa_fwd_splitkv_default_splits",
                                     "fa_fwd_splitkv_workspace_size", "fa_status_string",
                                     "fa_version"]
@@ -179,3 +180,35 @@ def test_splitkv_sizes(lib):
     assert 1 <= _abi.fa_fwd_splitkv_default_splits(1, 32, 8, 1, 65536, 128) <= 512
     assert _abi.fa_fwd_splitkv_default_splits(1, 1, 1, 1, 64, 128) == 1
     assert _abi.fa_fwd_splitkv_default_splits(1, 3, 2, 1, 64, 128) == 0
+
+
+def test_fp8_entry_points_reject(lib):
+    # fa_fp8_quantize(x, signs, codes, scales, B, H, N, d, dtype, stream)
+    assert lib.fa_fp8_quantize(None, None, A, A, 1, 2, 100, 128, BF16, None) == INVALID
+    assert lib.fa_fp8_quantize(A, None, None, A, 1, 2, 100, 128, BF16, None) == INVALID
+    assert lib.fa_fp8_quantize(A, None, A, None, 1, 2, 100, 128, BF16, None) == INVALID
+    assert lib.fa_fp8_quantize(MIS, None, A, A, 1, 2, 100, 128, BF16, None) == INVALID
+    assert lib.fa_fp8_quantize(A, MIS, A, A, 1, 2, 100, 128, BF16, None) == INVALID
+    assert lib.fa_fp8_quantize(A, None, A, A + 2, 1, 2, 100, 128, BF16, None) == INVALID
+    assert lib.fa_fp8_quantize(A, None, A, A, 0, 2, 100, 128, BF16, None) == INVALID
+    assert lib.fa_fp8_quantize(A, None, A, A, 1, 2, 100, 96, BF16, None) == UNSUPPORTED
+    assert lib.fa_fp8_quantize(A, None, A, A, 1, 2, 100, 128, FP32, None) == UNSUPPORTED
+    assert lib.fa_fp8_quantize(A, None, A, A, 1, 2, 100, 128, 5, None) == INVALID
+    # fa_fwd_fp8(q, k, v, sq, sk, sv, o, lse, B, Hq, Hkv, N, d, causal, scale, out_dtype, stream)
+    for i in range(8):
+        p = [A] * 8
+        p[i] = None
+        assert lib.fa_fwd_fp8(*p, 1, 4, 2, 100, 128, 1, 0.1, BF16, None) == INVALID
+    for i in (0, 1, 2, 6, 7):
+        p = [A] * 8
+        p[i] = MIS
+        assert lib.fa_fwd_fp8(*p, 1, 4, 2, 100, 128, 1, 0.1, BF16, None) == INVALID
+    p = [A] * 8
+    p[4] = A + 2
+    assert lib.fa_fwd_fp8(*p, 1, 4, 2, 100, 128, 1, 0.1, BF16, None) == INVALID
+    q = [A] * 8
+    assert lib.fa_fwd_fp8(*q, 1, 4, 3, 100, 128, 1, 0.1, BF16, None) == INVALID
+    assert lib.fa_fwd_fp8(*q, 1, 4, 2, 100, 128, 2, 0.1, BF16, None) == INVALID
+    assert lib.fa_fwd_fp8(*q, 1, 4, 2, 100, 128, 1, 0.0, BF16, None) == INVALID
+    assert lib.fa_fwd_fp8(*q, 1, 4, 2, 100, 32, 1, 0.1, BF16, None) == UNSUPPORTED
+    assert lib.fa_fwd_fp8(*q, 1, 4, 2, 100, 128, 1, 0.1, FP32, None) == UNSUPPORTED
