@@ -15,6 +15,12 @@ Per-kernel durations come from HIP events recorded on the stream the kernels
 run on, around every launch inside the timed region.  After it, every kernel
 is also timed cold (each launch preceded by an untimed 512 MB fill that evicts
 L2 and the MALL), reported as median and minimum per kernel.
+
+Two further objects in the same line: `splitkv` (the split-KV forward on
+decoding shapes, K/V bytes per second against the HBM peak) and `fp8` (the
+block quantizer and the e4m3 forward on the same workload, against the fp8
+matrix-core peak).  `--splitkv-only NAME` and `--fp8-only` run just those, for
+profiling.
 """
 from __future__ import annotations
 
@@ -184,10 +190,12 @@ def measure_fp8(w, q, k, v, stream, iters: int = 20):
             "rotation": "Q and K", "kernels_ms": med,
             "fwd_fp8": {"ms": med["fwd_fp8"], "tflops": tf,
                         "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP8_TFLOPS,
-                                     "unit": "TFLOP/s", "frac": tf / PEAK_FP8_TFLOPS}},
+                                     "unit": "TFLOP/s", "frac": tf / PEAK_FP8_TFLOPS,
+                                     "traffic": stored_traffic("fwd_fp8")}},
             "quantize": {"ms": quant_ms, "bytes": quant_bytes,
                          "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
-                                      "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS}},
+                                      "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                                      "traffic_per_launch": stored_traffic("fp8_quantize")}},
             "path_ms": quant_ms + med["fwd_fp8"],
             "path_tflops": F / ((quant_ms + med["fwd_fp8"]) * 1e-3) / 1e12}
 

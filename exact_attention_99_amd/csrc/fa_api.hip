@@ -38,6 +38,16 @@ int fwd_variant() {
     return v;
 }
 
+int fp8_variant() {
+    // Tile variant of the FP8 forward; FA355_FP8_VARIANT overrides the default
+    // for tile sweeps.
+    static const int v = [] {
+        const char* e = getenv("FA355_FP8_VARIANT");
+        return e ? atoi(e) : 0;
+    }();
+    return v;
+}
+
 int bwd_variant() {
     // Kernel generation of the 16-bit backward passes; FA355_BWD_VARIANT
     // overrides the default for comparisons.
@@ -283,6 +293,7 @@ fa_status fa_fwd_fp8(const unsigned char* q, const unsigned char* k, const unsig
     a.causal = causal;
     a.cl2 = scale * kLog2eHost;
     a.out_dtype = (int)out_dtype;
+    a.variant = fp8_variant();
     a.stream = stream;
     return hip_status(fa355::launch_fwd_fp8(a));
 }

@@ -82,6 +82,7 @@ struct Fp8FwdArgs {
     int causal;
     float cl2;
     int out_dtype;
+    int variant;         // tile variant (0 = default)
     hipStream_t stream;
 };
 

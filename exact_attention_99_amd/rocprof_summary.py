@@ -82,7 +82,8 @@ def cmd_traffic(a):
            "fetch_factor": f_factor, "write_factor": w_factor, "kernels": {}}
     # every kernel generation of a pass matches its prefix
     for pat, key in (("fwd16", "fwd"), ("delta16", "bwd_prepare"),
-                     ("dkdv16", "bwd_dkdv"), ("dq16", "bwd_dq")):
+                     ("dkdv16", "bwd_dkdv"), ("dq16", "bwd_dq"),
+                     ("fwd8_", "fwd_fp8"), ("quant8_", "fp8_quantize")):
         fk = [v for n, vals in fetch.items() if pat in n for v in vals]
         wk = [v for n, vals in write.items() if pat in n for v in vals]
         if not fk or not wk:
