@@ -16,11 +16,12 @@ run on, around every launch inside the timed region.  After it, every kernel
 is also timed cold (each launch preceded by an untimed 512 MB fill that evicts
 L2 and the MALL), reported as median and minimum per kernel.
 
-Two further objects in the same line: `splitkv` (the split-KV forward on
-decoding shapes, K/V bytes per second against the HBM peak) and `fp8` (the
-block quantizer and the e4m3 forward on the same workload, against the fp8
-matrix-core peak).  `--splitkv-only NAME` and `--fp8-only` run just those, for
-profiling.
+Further objects in the same line: `splitkv` (the split-KV forward on
+decoding shapes, K/V bytes per second against the HBM peak), `dropout` (the
+forward and backward with fused dropout, p = 0.1, on the same workload) and
+`fp8` (the block quantizer and the e4m3 forward on the same workload, against
+the fp8 matrix-core peak).  `--splitkv-only NAME`, `--dropout-only` and
+`--fp8-only` run just those, for profiling.
 """
 from __future__ import annotations
 
@@ -200,6 +201,46 @@ def measure_fp8(w, q, k, v, stream, iters: int = 20):
             "path_tflops": F / ((quant_ms + med["fwd_fp8"]) * 1e-3) / 1e12}
 
 
+def measure_dropout(w, q, k, v, do, stream, p: float = 0.1, iters: int = 10):
+    """Forward and backward with fused dropout (probability p) on the
+    workload's tensors: median event-timed durations of each call, and the
+    rate with the same conventional FLOP count as the step without dropout."""
+    import torch
+    from exact_attention_99_amd import fa_bwd_dropout, fa_bwd_workspace_size, fa_fwd_dropout
+    causal = True in w.causal_modes
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H_q, w.N), dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(fa_bwd_workspace_size(w.B, w.H_q, w.H_kv, w.N, w.d, w.dtype), 256),
+                     dtype=torch.uint8, device=q.device)
+    calls = {
+        "fwd_dropout": lambda: fa_fwd_dropout(q, k, v, causal, w.scale, p, 1234, 0, o=o, lse=lse, stream=stream),
+        "bwd_dropout": lambda: fa_bwd_dropout(q, k, v, o, lse, do, causal, w.scale, p, 1234, 0,
+                                              dq=dq, dk=dk, dv=dv, workspace=ws, stream=stream),
+    }
+    med = {}
+    for name, fn in calls.items():
+        for _ in range(2):
+            fn()
+        ts = []
+        for _ in range(iters):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ts.sort()
+        med[name] = ts[len(ts) // 2]
+    F = w.flops_fwd(causal)
+    Fb = w.flops_bwd(causal)
+    return {"workload": w.name, "dropout_p": p, "causal": causal,
+            "fwd_ms": med["fwd_dropout"], "bwd_ms": med["bwd_dropout"],
+            "fwd_tflops": F / (med["fwd_dropout"] * 1e-3) / 1e12,
+            "bwd_tflops": Fb / (med["bwd_dropout"] * 1e-3) / 1e12,
+            "step_tflops": (F + Fb) / ((med["fwd_dropout"] + med["bwd_dropout"]) * 1e-3) / 1e12}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -215,6 +256,10 @@ def main() -> int:
                     help="skip the FP8 forward measurement")
     ap.add_argument("--fp8-only", action="store_true",
                     help="only measure the FP8 path (quantizer + e4m3 forward)")
+    ap.add_argument("--no-dropout", dest="dropout", action="store_false",
+                    help="skip the fused-dropout measurement")
+    ap.add_argument("--dropout-only", action="store_true",
+                    help="only measure the forward and backward with dropout")
     ap.add_argument("--flush-iters", type=int, default=20,
                     help="cold-cache timed launches per kernel (0 to skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -261,6 +306,10 @@ def main() -> int:
     q, k, v, do = workloads.workload_inputs(w, with_dout=True, device=dev)
     if args.fp8_only:
         print(json.dumps({"fp8": measure_fp8(w, q, k, v, torch.cuda.current_stream())}), flush=True)
+        return 0
+    if args.dropout_only:
+        print(json.dumps({"dropout": measure_dropout(w, q, k, v, do, torch.cuda.current_stream())}),
+              flush=True)
         return 0
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H_q, w.N), dtype=torch.float32, device=dev)
@@ -386,6 +435,8 @@ def main() -> int:
     if args.splitkv:
         out["splitkv"] = [measure_splitkv(workloads.DECODE_WORKLOADS[n], dev, stream)
                           for n in ("genome_gqa_64k_decode", "genome_gqa_64k_chunk8", "llama_mha_8k_decode")]
+    if args.dropout:
+        out["dropout"] = measure_dropout(w, q, k, v, do, stream)
     if args.fp8:
         out["fp8"] = measure_fp8(w, q, k, v, stream)
         out["fp8"]["speedup_vs_16bit_fwd"] = fwd_ms / out["fp8"]["fwd_fp8"]["ms"]

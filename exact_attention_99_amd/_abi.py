@@ -60,6 +60,12 @@ def load_library() -> ctypes.CDLL:
         lib.fa_fwd_splitkv_workspace_size.restype = sz
         lib.fa_fwd_splitkv_default_splits.argtypes = [i, i, i, i, i, i]
         lib.fa_fwd_splitkv_default_splits.restype = i
+        u64 = ctypes.c_ulonglong
+        lib.fa_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, u64, u64, i, vp]
+        lib.fa_fwd_dropout.restype = i
+        lib.fa_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                       i, i, i, i, i, i, f, f, u64, u64, i, vp]
+        lib.fa_bwd_dropout.restype = i
         lib.fa_fp8_quantize.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
         lib.fa_fp8_quantize.restype = i
         lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
@@ -326,3 +332,56 @@ def fa_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, causal: bool, scale: float,
 def _OUT_DTYPES():
     import torch
     return {"bf16": torch.bfloat16, "fp16": torch.float16}
+
+
+def fa_fwd_dropout(q, k, v, causal: bool, scale: float, dropout_p: float, seed: int, offset: int = 0,
+                   o=None, lse=None, stream=None):
+    """Forward with attention dropout (mask drawn from Philox4x64-10 keyed by
+    seed and offset); returns (o, lse)."""
+    import torch
+    lib = load_library()
+    B, Hq, Hkv, N, d = _shape(q, k, v)
+    dt = _dtype_name(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _check_same(q, k, v, o, lse)
+    st = lib.fa_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                            B, Hq, Hkv, N, d, int(bool(causal)), float(scale), float(dropout_p),
+                            int(seed) & (2 ** 64 - 1), int(offset) & (2 ** 64 - 1), FA_DTYPE[dt],
+                            _stream(q, stream))
+    if st != 0:
+        raise FaError(st, "fa_fwd_dropout")
+    return o, lse
+
+
+def fa_bwd_dropout(q, k, v, o, lse, dout, causal: bool, scale: float, dropout_p: float, seed: int,
+                   offset: int = 0, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Backward of fa_fwd_dropout with the same dropout_p, seed and offset;
+    returns (dq, dk, dv)."""
+    import torch
+    lib = load_library()
+    B, Hq, Hkv, N, d = _shape(q, k, v)
+    dt = _dtype_name(q)
+    if dq is None:
+        dq = torch.empty_like(q)
+    if dk is None:
+        dk = torch.empty_like(k)
+    if dv is None:
+        dv = torch.empty_like(v)
+    need = int(lib.fa_bwd_workspace_size(B, Hq, Hkv, N, d, FA_DTYPE[dt]))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check_same(q, k, v, o, lse, dout, dq, dk, dv, workspace)
+    st = lib.fa_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                            dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                            B, Hq, Hkv, N, d, int(bool(causal)), float(scale), float(dropout_p),
+                            int(seed) & (2 ** 64 - 1), int(offset) & (2 ** 64 - 1), FA_DTYPE[dt],
+                            _stream(q, stream))
+    if st != 0:
+        raise FaError(st, "fa_bwd_dropout")
+    return dq, dk, dv

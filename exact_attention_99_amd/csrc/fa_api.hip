@@ -81,6 +81,49 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
     a.cl2 = scale * kLog2eHost;
     a.dtype = (int)dtype;
     a.fwd_variant = fwd_variant();
+    a.drop = 0;
+    a.dp = fa355::DropParams{0, 0, 256, 1.f};
+    a.stream = stream;
+    return fa355::launch_fwd(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+namespace {
+
+// Keep threshold t8 = round((1 - p) 256) of a dropout probability; 0 when p
+// is outside [0, 1) or leaves no byte below the threshold.
+int drop_threshold(float p) {
+    if (!(p >= 0.f) || !(p < 1.f)) return 0;
+    const int t = (int)floor((1.0 - (double)p) * 256.0 + 0.5);
+    return t >= 1 ? t : 0;
+}
+
+}  // namespace
+
+fa_status fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                         int H_q, int H_kv, int N, int d, int causal, float scale, float dropout_p,
+                         unsigned long long seed, unsigned long long offset, fa_dtype dtype,
+                         hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return FA_ERR_INVALID_ARG;
+    if (!sizes_ok(B, H_q, H_kv, N)) return FA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype)) return FA_ERR_INVALID_ARG;
+    const int t8 = drop_threshold(dropout_p);
+    if (t8 == 0) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (dtype == FA_DTYPE_FP32) return FA_ERR_UNSUPPORTED;
+
+    fa355::FwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.B = B; a.Hq = H_q; a.Hkv = H_kv; a.N = N; a.d = d;
+    a.causal = causal;
+    a.cl2 = scale * kLog2eHost;
+    a.dtype = (int)dtype;
+    a.fwd_variant = 0;
+    a.drop = 1;
+    a.dp = fa355::DropParams{seed, offset, t8, 256.f / (float)t8};
     a.stream = stream;
     return fa355::launch_fwd(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -123,6 +166,8 @@ fa355::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void*
     a.cl2 = scale * kLog2eHost;
     a.dtype = (int)dtype;
     a.variant = bwd_variant();
+    a.drop = 0;
+    a.dp = fa355::DropParams{0, 0, 256, 1.f};
     a.stream = stream;
     return a;
 }
@@ -296,6 +341,28 @@ fa_status fa_fwd_fp8(const unsigned char* q, const unsigned char* k, const unsig
     a.variant = fp8_variant();
     a.stream = stream;
     return hip_status(fa355::launch_fwd_fp8(a));
+}
+
+fa_status fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                         void* workspace, size_t workspace_bytes, int B, int H_q, int H_kv, int N,
+                         int d, int causal, float scale, float dropout_p, unsigned long long seed,
+                         unsigned long long offset, fa_dtype dtype, hipStream_t stream) {
+    if (!ptrs_ok({q, k, v, o, lse, dout, dq, dk, dv, workspace})) return FA_ERR_INVALID_ARG;
+    const fa_status st = check_common(B, H_q, H_kv, N, d, causal, scale, dtype);
+    if (st != FA_OK) return st;
+    const int t8 = drop_threshold(dropout_p);
+    if (t8 == 0) return FA_ERR_INVALID_ARG;
+    if (dtype == FA_DTYPE_FP32) return FA_ERR_UNSUPPORTED;
+    if (workspace_bytes < fa_bwd_workspace_size(B, H_q, H_kv, N, d, dtype)) return FA_ERR_INVALID_ARG;
+    auto a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace), B, H_q,
+                      H_kv, N, d, causal, scale, dtype, stream);
+    a.drop = 1;
+    a.dp = fa355::DropParams{seed, offset, t8, 256.f / (float)t8};
+    hipError_t e = fa355::launch_bwd_prepare(a);
+    if (e == hipSuccess) e = fa355::launch_bwd_dkdv(a);
+    if (e == hipSuccess) e = fa355::launch_bwd_dq(a);
+    return hip_status(e);
 }
 
 const char* fa_status_string(fa_status s) {

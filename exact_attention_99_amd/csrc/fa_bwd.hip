@@ -486,13 +486,19 @@ dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 // swizzle that suits both ways they are read: 128-bit reads of 16 consecutive
 // rows for the A operands of S = Q K^T and dP = dO V^T, and transposing reads
 // for the A operands of dV^T += dO^T P and dK^T += Q^T dS.
-template <typename T, int D, bool CAUSAL>
+//
+// DROP: attention dropout (fa_common.h): dV^T += dO^T (Z P 256 / t8) and
+// dS = P * (Z dP 256 / t8 - D).  A wave's 32 keys are one key block, so each
+// query row of a step needs one generator call: lane l draws row q0 + l (and
+// q0 + 64 + l), writes the 32 bytes to its wave's LDS area, and transposing
+// byte reads give every lane the bytes of its key for its 16 rows.
+template <typename T, int D, bool CAUSAL, bool DROP = false>
 __global__ void __launch_bounds__(256)
 dkdv16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                 const float* __restrict__ LSE, const float* __restrict__ Delta,
                 uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int B, int Hq, int Hkv, int N,
-                float cl2, float scale) {
+                float cl2, float scale, DropParams dp) {
     constexpr int NW = 4;
     constexpr int BKV = 128;
     constexpr int BQ = 8192 / D;
@@ -510,7 +516,8 @@ dkdv16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     constexpr int IPW = WI / NW;
     static_assert(BQ <= 128, "row terms staged by the first 2*BQ threads");
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+    constexpr int DROP_BYTES = DROP ? NW * BQ * 32 : 0;   // per wave: BQ rows x 32 keys
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE + DROP_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -619,6 +626,19 @@ dkdv16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         const unsigned char* base = smem + (s & 1) * STAGE;
         const float* lse2s = reinterpret_cast<const float*>(base + OFF_LSE);
         const float* dls = reinterpret_cast<const float*>(base + OFF_DL);
+        unsigned char* dbase = smem + 2 * STAGE + wave * (BQ * 32);
+        if constexpr (DROP) {
+#pragma unroll
+            for (int rr = 0; rr < BQ / 64; ++rr) {
+                uint32_t w[8];
+                drop_bytes(w, (uint32_t)(kw / 32), (uint32_t)(q0 + 64 * rr + lane), (uint32_t)(b * Hq + h), dp);
+                u32x4 lo, up;
+                lo[0] = w[0]; lo[1] = w[1]; lo[2] = w[2]; lo[3] = w[3];
+                up[0] = w[4]; up[1] = w[5]; up[2] = w[6]; up[3] = w[7];
+                *reinterpret_cast<u32x4*>(dbase + (64 * rr + lane) * 32) = lo;
+                *reinterpret_cast<u32x4*>(dbase + (64 * rr + lane) * 32 + 16) = up;
+            }
+        }
 #pragma unroll 1
         for (int qs = 0; qs < NQB; ++qs) {
             f32x16 sacc = zero16(), dpacc = zero16();
@@ -630,7 +650,7 @@ dkdv16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 sacc = Mma<T>::mma(aq, kf[ks], sacc);
                 dpacc = Mma<T>::mma(ad, vf[ks], dpacc);
             }
-            float pv[16], dv[16];
+            float pv[16], dv[16], d4s[16];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + 32 * qs + 8 * g + 4 * hi);
@@ -640,6 +660,7 @@ dkdv16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                     const int r = 4 * g + i;
                     pv[r] = fast_exp2(fmaf(sacc[r], cl2, -l4[i]));
                     dv[r] = dpacc[r] - d4[i];
+                    d4s[r] = d4[i];
                 }
             }
             if (need_mask) {
@@ -650,13 +671,35 @@ dkdv16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                     pv[r] = vis ? pv[r] : 0.f;
                 }
             }
+            float pd[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) pd[r] = pv[r];
+            if constexpr (DROP) {
+                // rows 8 g .. 8 g + 7 of block qs at this lane's key; register
+                // 4 g + i (row 8 g + 4 hi + i) is byte i of dword hi
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int s16 = lane & 15;
+                    const int off = (32 * qs + 8 * g + (s16 >> 1)) * 32 + 16 * ((lane >> 4) & 1) + 8 * (s16 & 1);
+                    const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (__attribute__((address_space(3))) i32x2*)(dbase + off));
+                    const uint32_t m = (uint32_t)(hi ? x[1] : x[0]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = 4 * g + i;
+                        const bool keep = drop_keep(m, i, dp.t8);
+                        pd[r] = keep ? pv[r] * dp.scale : 0.f;
+                        dv[r] = (keep ? dpacc[r] * dp.scale : 0.f) - d4s[r];
+                    }
+                }
+            }
             u32x4 pb[2], dsb[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const int r = 8 * t + 2 * jj;
-                    pb[t][jj] = Mma<T>::pack2(pv[r], pv[r + 1]);
+                    pb[t][jj] = Mma<T>::pack2(pd[r], pd[r + 1]);
                     dsb[t][jj] = Mma<T>::pack2(pv[r] * dv[r], pv[r + 1] * dv[r + 1]);
                 }
 #pragma unroll
@@ -1028,12 +1071,17 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 // Second-generation dQ kernel: K and V tiles arrive by buffer-to-LDS copies,
 // row-major only; K^T operands of dQ^T += K^T dS^T come from transposing reads
 // of the same K tile (dual swizzle), so no transposed copy is built.
-template <typename T, int D, bool CAUSAL>
+//
+// DROP: attention dropout (fa_common.h): dS = P * (Z dP 256 / t8 - D), with
+// the keep bytes of a tile's key blocks drawn as in the forward kernel (lane
+// half hi draws block 2 kp + hi of its row, one exchange per block pair).
+template <typename T, int D, bool CAUSAL, bool DROP = false>
 __global__ void __launch_bounds__(256)
 dq16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
               const float* __restrict__ LSE, const float* __restrict__ Delta,
-              uint16_t* __restrict__ dQ, int B, int Hq, int Hkv, int N, float cl2, float scale) {
+              uint16_t* __restrict__ dQ, int B, int Hq, int Hkv, int N, float cl2, float scale,
+              DropParams dp) {
     constexpr int NW = 4;
     constexpr int BR = 32 * NW;
     constexpr int BC = D == 128 ? 64 : 128;
@@ -1125,8 +1173,16 @@ dq16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         issue(k0 + BC, (j + 1) & 1);
         const unsigned char* base = smem + (j & 1) * STAGE;
         const bool need_mask = (CAUSAL && k0 + BC - 1 > qw) || (k0 + BC > N);
-#pragma unroll 1
-        for (int kb = 0; kb < NKB; ++kb) {
+        uint32_t dm[DROP ? NKB : 1][4];
+        if constexpr (DROP) {
+#pragma unroll
+            for (int kp = 0; kp < NKB / 2; ++kp) {
+                uint32_t w[8];
+                drop_bytes(w, (uint32_t)(k0 / 32 + 2 * kp + hi), (uint32_t)q, (uint32_t)(b * Hq + h), dp);
+                drop_pair_exchange(w, dm[2 * kp], dm[2 * kp + 1]);
+            }
+        }
+        auto kb_body = [&](int kb, const uint32_t* m) __attribute__((always_inline)) {
             f32x16 st = zero16(), dpt = zero16();
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
@@ -1145,6 +1201,11 @@ dq16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                     const int kk = k0 + 32 * kb + acc_row(r, hi);
                     p[r] = ((!CAUSAL || kk <= q) && kk < N) ? p[r] : 0.f;
                 }
+            }
+            if constexpr (DROP) {
+                // register r: byte r % 4 of dword r / 4
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dpt[r] = drop_keep(m[r >> 2], r & 3, dp.t8) ? dpt[r] * dp.scale : 0.f;
             }
             u32x4 dsb[2];
 #pragma unroll
@@ -1166,6 +1227,12 @@ dq16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                     a[0] = lo[0]; a[1] = lo[1]; a[2] = up[0]; a[3] = up[1];
                     dq[db] = Mma<T>::mma(a, dsb[t], dq[db]);
                 }
+        };
+        if constexpr (DROP) {
+            static_for<NKB>([&](auto kbc) { kb_body(kbc.value, dm[kbc.value]); });
+        } else {
+#pragma unroll 1
+            for (int kb = 0; kb < NKB; ++kb) kb_body(kb, nullptr);
         }
         wait_vmem();
         __syncthreads();
@@ -1603,6 +1670,15 @@ hipError_t prepare32(const BwdArgs& a) {
 template <typename T, int D, bool CAUSAL>
 hipError_t dkdv16(const BwdArgs& a) {
     const int nkb = (a.N + 127) / 128;
+    if (a.drop) {
+        // dropout runs on the second-generation kernels
+        hipLaunchKernelGGL((dkdv16v2_kernel<T, D, CAUSAL, true>), dim3((unsigned)(nkb * a.Hkv * a.B)),
+                           dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                           (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
+                           (uint16_t*)a.dk, (uint16_t*)a.dv, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale,
+                           a.dp);
+        return hipGetLastError();
+    }
     if (a.variant == 0) {
         hipLaunchKernelGGL((dkdv16v3_kernel<T, D, CAUSAL>), dim3((unsigned)(nkb * a.Hkv * a.B)),
                            dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
@@ -1614,7 +1690,8 @@ hipError_t dkdv16(const BwdArgs& a) {
         hipLaunchKernelGGL((dkdv16v2_kernel<T, D, CAUSAL>), dim3((unsigned)(nkb * a.Hkv * a.B)),
                            dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                            (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
-                           (uint16_t*)a.dk, (uint16_t*)a.dv, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale);
+                           (uint16_t*)a.dk, (uint16_t*)a.dv, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale,
+                           a.dp);
         return hipGetLastError();
     }
     hipLaunchKernelGGL((dkdv16_kernel<T, D, CAUSAL>), dim3((unsigned)(nkb * a.Hkv * a.B)), dim3(256), 0,
@@ -1627,6 +1704,13 @@ hipError_t dkdv16(const BwdArgs& a) {
 template <typename T, int D, bool CAUSAL>
 hipError_t dq16(const BwdArgs& a) {
     const int nqb = (a.N + 127) / 128;
+    if (a.drop) {
+        hipLaunchKernelGGL((dq16v2_kernel<T, D, CAUSAL, true>), dim3((unsigned)(nqb * a.Hq * a.B)),
+                           dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                           (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
+                           (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale, a.dp);
+        return hipGetLastError();
+    }
     if (a.variant == 0) {
         hipLaunchKernelGGL((dq16v3_kernel<T, D, CAUSAL>), dim3((unsigned)(nqb * a.Hq * a.B)),
                            dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
@@ -1638,7 +1722,7 @@ hipError_t dq16(const BwdArgs& a) {
         hipLaunchKernelGGL((dq16v2_kernel<T, D, CAUSAL>), dim3((unsigned)(nqb * a.Hq * a.B)),
                            dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                            (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
-                           (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale);
+                           (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale, a.dp);
         return hipGetLastError();
     }
     hipLaunchKernelGGL((dq16_kernel<T, D, CAUSAL>), dim3((unsigned)(nqb * a.Hq * a.B)), dim3(256), 0,

@@ -17,6 +17,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "fa_launch.h"
+
 #include <utility>
 #include <stdint.h>
 
@@ -30,6 +32,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -268,6 +271,80 @@ __device__ __forceinline__ int v_key_of_pos(int h, int i) { return 4 * h + (i & 
 // Inverse: position of element x (0..15) of a group.
 __device__ __forceinline__ int pos_of_elem(int x) {
     return 8 * ((x >> 2) & 1) + 4 * ((x >> 3) & 1) + (x & 3);
+}
+
+// ---------------------------------------------------------------- dropout
+//
+// Keep mask of attention dropout.  Element (b, h, i, j) (query head h, row i,
+// key j) is kept iff its random byte is below t8 = round((1 - p) 256); kept
+// probabilities are scaled by 256 / t8.  The bytes come from the
+// counter-based generator Philox4x64-10 (Salmon, Moraes, Dror and Shaw,
+// "Parallel random numbers: as easy as 1, 2, 3", SC 2011) with key
+// (seed, offset) and counter (j / 32, i, b H_q + h, 0): one call gives the
+// 32 bytes of one row and one aligned 32-key block, little-endian, byte
+// j % 32 for key j (dword (j % 32) / 4 of the result).
+__device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64_t k1) {
+    // multipliers and Weyl key increments of Philox4x64 (Salmon et al.)
+    constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+    constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t lo0 = M0 * c[0], hi0 = __umul64hi(M0, c[0]);
+        const uint64_t lo1 = M1 * c[2], hi1 = __umul64hi(M1, c[2]);
+        const uint64_t n0 = hi1 ^ c[1] ^ k0;
+        const uint64_t n2 = hi0 ^ c[3] ^ k1;
+        c[0] = n0;
+        c[1] = lo1;
+        c[2] = n2;
+        c[3] = lo0;
+        k0 += W0;
+        k1 += W1;
+    }
+}
+
+// The 32 random bytes of (row, key block kblk) of head index bh, as 8 dwords.
+__device__ __forceinline__ void drop_bytes(uint32_t w[8], uint32_t kblk, uint32_t row, uint32_t bh,
+                                           const DropParams& dp) {
+    uint64_t c[4] = {kblk, row, bh, 0};
+    philox4x64_10(c, dp.seed, dp.offset);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        w[2 * i] = (uint32_t)c[i];
+        w[2 * i + 1] = (uint32_t)(c[i] >> 32);
+    }
+}
+
+// In the score layouts where a lane owns one query row and, in each 32-key
+// block, keys 8 g + 4 hi + (0..3) for g = 0..3 (register 4 g + i), a lane
+// needs dword 2 g + hi of that block's bytes.  When lane half hi has
+// computed the bytes w of block (pair base + hi), one v_permlane32_swap per g
+// hands every lane its dwords of both blocks of the pair: m0 for the first,
+// m1 for the second.
+__device__ __forceinline__ void drop_pair_exchange(const uint32_t w[8], uint32_t m0[4], uint32_t m1[4]) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const auto r = __builtin_amdgcn_permlane32_swap(w[2 * g], w[2 * g + 1], false, false);
+        m0[g] = r[0];
+        m1[g] = r[1];
+    }
+}
+
+// Byte i of dword m kept?
+__device__ __forceinline__ bool drop_keep(uint32_t m, int i, int t8) {
+    return (int)((m >> (8 * i)) & 0xFFu) < t8;
+}
+
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// Mask for a dword of two 16-bit values built from bytes i0 and i0 + 1 of m:
+// 0xFFFF in each half whose byte is below t8, else 0.
+__device__ __forceinline__ uint32_t drop_mask16x2(uint32_t m, int i0, int t8) {
+    const uint32_t sel = (uint32_t)i0 | (0x0Cu << 8) | ((uint32_t)(i0 + 1) << 16) | (0x0Cu << 24);
+    const uint32_t x = __builtin_amdgcn_perm(0u, m, sel);   // bytes -> 16-bit halves
+    s16x2 v = __builtin_bit_cast(s16x2, x);
+    const s16x2 t = {(short)t8, (short)t8};
+    v = (v - t) >> (short)15;
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 }  // namespace fa355

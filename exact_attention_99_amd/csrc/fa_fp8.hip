@@ -24,7 +24,6 @@ namespace fa355 {
 namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kQBlk = 64;          // rows per quantization block
 constexpr float kE4m3Max = 448.f;  // largest finite e4m3 value

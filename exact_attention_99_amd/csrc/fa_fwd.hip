@@ -468,11 +468,16 @@ fwd16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 // address is a per-lane register plus an immediate offset.  The remaining
 // tiles (the causal diagonal of each wave, the ragged end of the sequence)
 // run the masked body.
-template <typename T, int D, bool CAUSAL, int NW, int BC>
+//
+// DROP: attention dropout (fa_common.h) on the probabilities before the P V
+// product; the row sums and lse stay those of the undropped probabilities.
+// Lane half hi draws the bytes of key block 2 kp + hi of its row, and one
+// exchange between the halves gives each lane its bytes of both blocks.
+template <typename T, int D, bool CAUSAL, int NW, int BC, bool DROP = false>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 fwd16v5_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-               int B, int Hq, int Hkv, int N, float cl2) {
+               int B, int Hq, int Hkv, int N, float cl2, DropParams dp) {
     constexpr int BR = 32 * NW;
     constexpr int KCH = D / 8;
     constexpr int TILE = BC * D * 2;
@@ -637,6 +642,23 @@ fwd16v5_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                     pb[2 * kb + t][jj] = Mma<T>::pack2(p0, p1);
                 }
         l_s += ls;
+        if constexpr (DROP) {
+            // pair (8 t + 2 jj, +1) of block kb: bytes 2 (jj & 1), +1 of dword 2 t + jj / 2
+#pragma unroll
+            for (int kp = 0; kp < NKB / 2; ++kp) {
+                uint32_t w[8], dm[2][4];
+                drop_bytes(w, (uint32_t)(k0 / 32 + 2 * kp + hi), (uint32_t)q, (uint32_t)(b * Hq + h), dp);
+                drop_pair_exchange(w, dm[0], dm[1]);
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj)
+                            pb[2 * (2 * kp + kk) + t][jj] &=
+                                drop_mask16x2(dm[kk][2 * t + (jj >> 1)], 2 * (jj & 1), dp.t8);
+            }
+        }
 
 #pragma unroll
         for (int kg = 0; kg < NKG; ++kg)
@@ -671,7 +693,7 @@ fwd16v5_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
     const float l_tot = l_s + swap_halves(l_s);
     if (q < N) {
-        const float inv = 1.f / l_tot;
+        const float inv = (DROP ? dp.scale : 1.f) / l_tot;
         uint16_t* Orow = O + qoff + (size_t)q * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -1377,14 +1399,15 @@ hipError_t launch16v2(const FwdArgs& a) {
     return hipGetLastError();
 }
 
-template <typename T, int D, bool CAUSAL, int NW, int BC>
+template <typename T, int D, bool CAUSAL, int NW, int BC, bool DROP = false>
 hipError_t launch16v5(const FwdArgs& a) {
     constexpr int BR = 32 * NW;
     const int nqb = (a.N + BR - 1) / BR;
     const long long total = (long long)nqb * a.Hq * a.B;
-    hipLaunchKernelGGL((fwd16v5_kernel<T, D, CAUSAL, NW, BC>), dim3((unsigned)total), dim3(NW * 64),
-                       0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                       (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.N, a.cl2);
+    hipLaunchKernelGGL((fwd16v5_kernel<T, D, CAUSAL, NW, BC, DROP>), dim3((unsigned)total),
+                       dim3(NW * 64), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                       (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.N, a.cl2,
+                       a.dp);
     return hipGetLastError();
 }
 
@@ -1424,6 +1447,11 @@ hipError_t launch32(const FwdArgs& a) {
 // 32-row waves) is the default, the others are kept for tile sweeps.
 template <typename T, int D, bool CAUSAL>
 hipError_t dispatch16c(const FwdArgs& a) {
+    if (a.drop) {
+        // dropout runs on the default tiling only
+        if constexpr (D == 128) return launch16v5<T, D, CAUSAL, 8, 64, true>(a);
+        else return launch16v5<T, D, CAUSAL, 4, 128, true>(a);
+    }
     if constexpr (D == 128) {
         switch (a.fwd_variant) {
             case 1: return launch16<T, D, CAUSAL, 4, 64>(a);

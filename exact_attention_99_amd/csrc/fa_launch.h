@@ -7,6 +7,15 @@
 
 namespace fa355 {
 
+// Attention dropout: keep iff the element's Philox byte < t8; kept values
+// scaled by 256 / t8 (see the device helpers in fa_common.h).
+struct DropParams {
+    uint64_t seed;
+    uint64_t offset;
+    int t8;        // 1..256
+    float scale;   // 256 / t8
+};
+
 struct FwdArgs {
     const void* q;
     const void* k;
@@ -18,6 +27,8 @@ struct FwdArgs {
     float cl2;       // scale * log2(e)
     int dtype;       // fa_dtype value
     int fwd_variant; // tile variant of the 16-bit kernel (0 = default)
+    int drop;        // 1: apply dropout with dp
+    DropParams dp;
     hipStream_t stream;
 };
 
@@ -38,6 +49,8 @@ struct BwdArgs {
     float cl2;
     int dtype;
     int variant;     // kernel generation of the 16-bit passes (0 = default)
+    int drop;        // 1: apply dropout with dp
+    DropParams dp;
     hipStream_t stream;
 };
 

@@ -186,6 +186,49 @@ size_t fa_fwd_splitkv_workspace_size(int B, int H_q, int N_q, int d, int num_spl
 int fa_fwd_splitkv_default_splits(int B, int H_q, int H_kv, int N_q, int N_kv, int d);
 
 /*
+ * Attention dropout, fused into the kernels ("FlashAttention Kernel" glossary,
+ * opening paragraph; "FlashAttention" glossary, kernel-fusion paragraph;
+ * "Flash Attention" (21medien), fusion bullet and the dropout_p argument of
+ * its code example):
+ *
+ *     P = softmax(scale * Q K^T [causal]),   O = (P o Z) V * 256 / t8,
+ *
+ * Z the keep mask: element (b, h, i, j) (query head h, row i, key j) is kept
+ * iff its random byte is below t8 = round((1 - dropout_p) * 256), computed in
+ * double from the float dropout_p.  The bytes come from the counter-based
+ * generator Philox4x64-10 (Salmon et al., SC 2011) with key (seed, offset) and
+ * counter (j / 32, i, b * H_q + h, 0); the four 64-bit outputs are 32 bytes,
+ * little-endian, byte j % 32 for key j.  The mask is never stored: the
+ * backward pass draws the same bytes again.  lse is that of the undropped
+ * scores (as fa_fwd's).
+ *
+ * fa_fwd_dropout: arguments as fa_fwd, plus dropout_p in [0, 1) leaving
+ *   t8 >= 1 (else FA_ERR_INVALID_ARG), seed and offset (any values; change
+ *   offset between calls that must draw different masks).  bf16 / fp16 only
+ *   (fp32 returns FA_ERR_UNSUPPORTED).
+ * fa_bwd_dropout: arguments as fa_bwd, plus the same dropout_p, seed and
+ *   offset as the forward call that produced o; gradients of sum(dout * o)
+ *   with the same mask: dV = (P o Z)^T dO * 256 / t8, dP = (dO V^T) o Z *
+ *   256 / t8, dS = P o (dP - rowsum(dO o O)), dQ = scale dS K,
+ *   dK = scale dS^T Q.
+ */
+fa_status fa_fwd_dropout(const void* q, const void* k, const void* v,
+                         void* o, float* lse,
+                         int B, int H_q, int H_kv, int N, int d,
+                         int causal, float scale, float dropout_p,
+                         unsigned long long seed, unsigned long long offset,
+                         fa_dtype dtype, hipStream_t stream);
+
+fa_status fa_bwd_dropout(const void* q, const void* k, const void* v,
+                         const void* o, const float* lse, const void* dout,
+                         void* dq, void* dk, void* dv,
+                         void* workspace, size_t workspace_bytes,
+                         int B, int H_q, int H_kv, int N, int d,
+                         int causal, float scale, float dropout_p,
+                         unsigned long long seed, unsigned long long offset,
+                         fa_dtype dtype, hipStream_t stream);
+
+/*
  * FP8 path ("FlashAttention 1, 2, and 3 Explained", section 4 on
  * FlashAttention-3: FP8 with block quantization and incoherent processing;
  * "FlashAttention" glossary, FlashAttention-3 paragraph).  Low precision:

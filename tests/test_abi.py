@@ -29,9 +29,9 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_prepare",
-                                    "fa_bwd_workspace_size", "fa_fp8_quantize", "fa_fwd",
-                                    "fa_fwd_fp8", "fa_fwd_splitkv",
+    assert declared_functions() == ["fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_dropout",
+                                    "fa_bwd_prepare", "fa_bwd_workspace_size", "fa_fp8_quantize",
+                                    "fa_fwd", "fa_fwd_dropout", "fa_fwd_fp8", "fa_fwd_splitkv",
                                     "fa_fwd_splitkv_default_splits",
                                     "fa_fwd_splitkv_workspace_size", "fa_status_string",
                                     "fa_version"]
@@ -212,3 +212,29 @@ def test_fp8_entry_points_reject(lib):
     assert lib.fa_fwd_fp8(*q, 1, 4, 2, 100, 128, 1, 0.0, BF16, None) == INVALID
     assert lib.fa_fwd_fp8(*q, 1, 4, 2, 100, 32, 1, 0.1, BF16, None) == UNSUPPORTED
     assert lib.fa_fwd_fp8(*q, 1, 4, 2, 100, 128, 1, 0.1, FP32, None) == UNSUPPORTED
+
+
+def test_dropout_entry_points_reject(lib):
+    # fa_fwd_dropout(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, p, seed, offset, dtype, stream)
+    ok = [A] * 5
+    for i in range(5):
+        p = [A] * 5
+        p[i] = None
+        assert lib.fa_fwd_dropout(*p, 1, 2, 1, 64, 128, 1, 0.1, 0.1, 1, 2, BF16, None) == INVALID
+        p[i] = MIS
+        assert lib.fa_fwd_dropout(*p, 1, 2, 1, 64, 128, 1, 0.1, 0.1, 1, 2, BF16, None) == INVALID
+    for bad_p in (-0.1, 1.0, 0.999, float("nan")):
+        assert lib.fa_fwd_dropout(*ok, 1, 2, 1, 64, 128, 1, 0.1, bad_p, 1, 2, BF16, None) == INVALID
+    assert lib.fa_fwd_dropout(*ok, 1, 2, 1, 64, 96, 1, 0.1, 0.1, 1, 2, BF16, None) == UNSUPPORTED
+    assert lib.fa_fwd_dropout(*ok, 1, 2, 1, 64, 128, 1, 0.1, 0.1, 1, 2, FP32, None) == UNSUPPORTED
+    assert lib.fa_fwd_dropout(*ok, 1, 3, 2, 64, 128, 1, 0.1, 0.1, 1, 2, BF16, None) == INVALID
+    # fa_bwd_dropout(q, k, v, o, lse, dout, dq, dk, dv, ws, ws_bytes, B, Hq, Hkv, N, d, causal,
+    #                scale, p, seed, offset, dtype, stream)
+    for i in range(10):
+        p = [A] * 10
+        p[i] = None
+        assert lib.fa_bwd_dropout(*p, 1 << 20, 1, 2, 1, 64, 128, 0, 0.1, 0.1, 1, 2, BF16, None) == INVALID
+    need = _abi.fa_bwd_workspace_size(1, 2, 1, 64, 128, "bf16")
+    assert lib.fa_bwd_dropout(*([A] * 10), need - 1, 1, 2, 1, 64, 128, 0, 0.1, 0.1, 1, 2, BF16, None) == INVALID
+    assert lib.fa_bwd_dropout(*([A] * 10), need, 1, 2, 1, 64, 128, 0, 0.1, 1.5, 1, 2, BF16, None) == INVALID
+    assert lib.fa_bwd_dropout(*([A] * 10), need, 1, 2, 1, 64, 128, 0, 0.1, 0.1, 1, 2, FP32, None) == UNSUPPORTED
