@@ -18,10 +18,12 @@ L2 and the MALL), reported as median and minimum per kernel.
 
 Further objects in the same line: `splitkv` (the split-KV forward on
 decoding shapes, K/V bytes per second against the HBM peak), `dropout` (the
-forward and backward with fused dropout, p = 0.1, on the same workload) and
+forward and backward with fused dropout, p = 0.1, on the same workload),
+`blocksparse` (the same workload under a band block mask, rates over the
+visible elements) and
 `fp8` (the block quantizer and the e4m3 forward on the same workload, against
-the fp8 matrix-core peak).  `--splitkv-only NAME`, `--dropout-only` and
-`--fp8-only` run just those, for profiling.
+the fp8 matrix-core peak).  `--splitkv-only NAME`, `--dropout-only`,
+`--blocksparse-only` and `--fp8-only` run just those, for profiling.
 """
 from __future__ import annotations
 
@@ -241,6 +243,59 @@ def measure_dropout(w, q, k, v, do, stream, p: float = 0.1, iters: int = 10):
             "step_tflops": (F + Fb) / ((med["fwd_dropout"] + med["bwd_dropout"]) * 1e-3) / 1e12}
 
 
+def measure_blocksparse(w, q, k, v, do, stream, width: int = 4, globals_: int = 1, iters: int = 10):
+    """Forward and backward under a block mask (a local band of `width`
+    128-key blocks plus the first `globals_` key blocks, with the workload's
+    causal mask): median event-timed durations, and rates over the FLOPs of
+    the visible elements only (4 d per visible score forward, 2.5x that
+    backward)."""
+    import torch
+    import workloads
+    from exact_attention_99_amd import fa_bwd_blocksparse, fa_bwd_workspace_size, fa_fwd_blocksparse
+    causal = True in w.causal_modes
+    M = workloads.make_band_mask(w.N, width, globals_).to(q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H_q, w.N), dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(fa_bwd_workspace_size(w.B, w.H_q, w.H_kv, w.N, w.d, w.dtype), 256),
+                     dtype=torch.uint8, device=q.device)
+    calls = {
+        "fwd": lambda: fa_fwd_blocksparse(q, k, v, M, causal, w.scale, o=o, lse=lse, stream=stream),
+        "bwd": lambda: fa_bwd_blocksparse(q, k, v, o, lse, do, M, causal, w.scale, dq=dq, dk=dk, dv=dv,
+                                          workspace=ws, stream=stream),
+    }
+    med = {}
+    for name, fn in calls.items():
+        for _ in range(2):
+            fn()
+        ts = []
+        for _ in range(iters):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ts.sort()
+        med[name] = ts[len(ts) // 2]
+    # visible (row, key) pairs of one head
+    idx = torch.arange(w.N, device="cpu") // 128
+    Mc = M[0].cpu().bool()
+    vis = 0
+    for r0 in range(0, w.N, 1024):
+        rows = torch.arange(r0, min(w.N, r0 + 1024))
+        allowed = Mc[idx[rows]][:, idx]
+        if causal:
+            allowed &= torch.arange(w.N)[None, :] <= rows[:, None]
+        vis += int(allowed.sum())
+    F = 4.0 * w.d * vis * w.B * w.H_q
+    density = vis / (w.N * (w.N + 1) / 2 if causal else w.N * w.N)
+    return {"workload": w.name, "mask": f"band of {width} blocks + {globals_} global key block(s)",
+            "causal": causal, "visible_fraction": density, "fwd_ms": med["fwd"], "bwd_ms": med["bwd"],
+            "fwd_tflops": F / (med["fwd"] * 1e-3) / 1e12,
+            "bwd_tflops": 2.5 * F / (med["bwd"] * 1e-3) / 1e12}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -260,6 +315,10 @@ def main() -> int:
                     help="skip the fused-dropout measurement")
     ap.add_argument("--dropout-only", action="store_true",
                     help="only measure the forward and backward with dropout")
+    ap.add_argument("--no-blocksparse", dest="blocksparse", action="store_false",
+                    help="skip the block-sparse measurement")
+    ap.add_argument("--blocksparse-only", action="store_true",
+                    help="only measure the forward and backward under a band block mask")
     ap.add_argument("--flush-iters", type=int, default=20,
                     help="cold-cache timed launches per kernel (0 to skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -306,6 +365,10 @@ def main() -> int:
     q, k, v, do = workloads.workload_inputs(w, with_dout=True, device=dev)
     if args.fp8_only:
         print(json.dumps({"fp8": measure_fp8(w, q, k, v, torch.cuda.current_stream())}), flush=True)
+        return 0
+    if args.blocksparse_only:
+        print(json.dumps({"blocksparse": measure_blocksparse(w, q, k, v, do, torch.cuda.current_stream())}),
+              flush=True)
         return 0
     if args.dropout_only:
         print(json.dumps({"dropout": measure_dropout(w, q, k, v, do, torch.cuda.current_stream())}),
@@ -437,6 +500,8 @@ def main() -> int:
                           for n in ("genome_gqa_64k_decode", "genome_gqa_64k_chunk8", "llama_mha_8k_decode")]
     if args.dropout:
         out["dropout"] = measure_dropout(w, q, k, v, do, stream)
+    if args.blocksparse:
+        out["blocksparse"] = measure_blocksparse(w, q, k, v, do, stream)
     if args.fp8:
         out["fp8"] = measure_fp8(w, q, k, v, stream)
         out["fp8"]["speedup_vs_16bit_fwd"] = fwd_ms / out["fp8"]["fwd_fp8"]["ms"]

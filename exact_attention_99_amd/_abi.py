@@ -66,6 +66,11 @@ def load_library() -> ctypes.CDLL:
         lib.fa_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                        i, i, i, i, i, i, f, f, u64, u64, i, vp]
         lib.fa_bwd_dropout.restype = i
+        lib.fa_fwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
+        lib.fa_fwd_blocksparse.restype = i
+        lib.fa_bwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, i,
+                                           i, i, i, i, i, i, f, i, vp]
+        lib.fa_bwd_blocksparse.restype = i
         lib.fa_fp8_quantize.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
         lib.fa_fp8_quantize.restype = i
         lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
@@ -384,4 +389,67 @@ def fa_bwd_dropout(q, k, v, o, lse, dout, causal: bool, scale: float, dropout_p:
                             _stream(q, stream))
     if st != 0:
         raise FaError(st, "fa_bwd_dropout")
+    return dq, dk, dv
+
+
+SPARSE_BLOCK = 128
+
+
+def _check_block_mask(block_mask, H_q, N):
+    import torch
+    nb = (N + SPARSE_BLOCK - 1) // SPARSE_BLOCK
+    if block_mask.dtype not in (torch.uint8, torch.bool) or block_mask.dim() != 3 or \
+            tuple(block_mask.shape[1:]) != (nb, nb) or block_mask.shape[0] not in (1, H_q):
+        raise ValueError(f"block_mask must be uint8/bool [1 or {H_q}, {nb}, {nb}]")
+    return block_mask.shape[0]
+
+
+def fa_fwd_blocksparse(q, k, v, block_mask, causal: bool, scale: float, o=None, lse=None, stream=None):
+    """Attention restricted to the 128 x 128 blocks block_mask allows
+    ([1 or H_q, nb, nb], nonzero = visible); returns (o, lse)."""
+    import torch
+    lib = load_library()
+    B, Hq, Hkv, N, d = _shape(q, k, v)
+    dt = _dtype_name(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    mh = _check_block_mask(block_mask, Hq, N)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _check_same(q, k, v, o, lse, block_mask)
+    st = lib.fa_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                block_mask.data_ptr(), mh, B, Hq, Hkv, N, d, int(bool(causal)),
+                                float(scale), FA_DTYPE[dt], _stream(q, stream))
+    if st != 0:
+        raise FaError(st, "fa_fwd_blocksparse")
+    return o, lse
+
+
+def fa_bwd_blocksparse(q, k, v, o, lse, dout, block_mask, causal: bool, scale: float, dq=None,
+                       dk=None, dv=None, workspace=None, stream=None):
+    """Backward of fa_fwd_blocksparse with the same mask; returns (dq, dk, dv)."""
+    import torch
+    lib = load_library()
+    B, Hq, Hkv, N, d = _shape(q, k, v)
+    dt = _dtype_name(q)
+    mh = _check_block_mask(block_mask, Hq, N)
+    if dq is None:
+        dq = torch.empty_like(q)
+    if dk is None:
+        dk = torch.empty_like(k)
+    if dv is None:
+        dv = torch.empty_like(v)
+    need = int(lib.fa_bwd_workspace_size(B, Hq, Hkv, N, d, FA_DTYPE[dt]))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check_same(q, k, v, o, lse, dout, dq, dk, dv, workspace, block_mask)
+    st = lib.fa_bwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                block_mask.data_ptr(), mh, B, Hq, Hkv, N, d, int(bool(causal)),
+                                float(scale), FA_DTYPE[dt], _stream(q, stream))
+    if st != 0:
+        raise FaError(st, "fa_bwd_blocksparse")
     return dq, dk, dv

@@ -492,13 +492,17 @@ dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 // query row of a step needs one generator call: lane l draws row q0 + l (and
 // q0 + 64 + l), writes the 32 bytes to its wave's LDS area, and transposing
 // byte reads give every lane the bytes of its key for its 16 rows.
-template <typename T, int D, bool CAUSAL, bool DROP = false>
+//
+// SPARSE: block-sparse attention (SparseParams): the workgroup's 128 keys are
+// one mask column; it walks only the (query head, query block) steps whose
+// mask block is set.
+template <typename T, int D, bool CAUSAL, bool DROP = false, bool SPARSE = false>
 __global__ void __launch_bounds__(256)
 dkdv16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                 const float* __restrict__ LSE, const float* __restrict__ Delta,
                 uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int B, int Hq, int Hkv, int N,
-                float cl2, float scale, DropParams dp) {
+                float cl2, float scale, DropParams dp, SparseParams sp) {
     constexpr int NW = 4;
     constexpr int BKV = 128;
     constexpr int BQ = 8192 / D;
@@ -609,21 +613,12 @@ dkdv16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int tr_row = 4 * hi + (j16 >> 2);
     const int tr_col = 2 * (16 * (g16 & 1) + 4 * (j16 & 3));
 
-    if (nsteps > 0) {
-        issue(0, 0);
-        put_rows(0);
-        wait_vmem();
-    }
-    __syncthreads();
-
-    for (int s = 0; s < nsteps; ++s) {
-        // The copy of the next step runs on every iteration (the last one
-        // re-copies the last step into the buffer nobody reads again).
-        issue(min(s + 1, nsteps - 1), (s + 1) & 1);
+    // step s from buffer par & 1
+    auto run_step = [&](int s, int par) __attribute__((always_inline)) {
         int h, q0;
         step_rows(s, h, q0);
         const bool need_mask = (CAUSAL && q0 < kw + 32) || (q0 + BQ > N) || (kw + 32 > N);
-        const unsigned char* base = smem + (s & 1) * STAGE;
+        const unsigned char* base = smem + (par & 1) * STAGE;
         const float* lse2s = reinterpret_cast<const float*>(base + OFF_LSE);
         const float* dls = reinterpret_cast<const float*>(base + OFF_DL);
         unsigned char* dbase = smem + 2 * STAGE + wave * (BQ * 32);
@@ -720,9 +715,55 @@ dkdv16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                     dkt[db] = Mma<T>::mma(aqt, dsb[t], dkt[db]);
                 }
         }
-        put_rows((s + 1) & 1);
-        wait_vmem();
+    };
+
+    if constexpr (SPARSE) {
+        const int nb = sp.nb;
+        const int mc = min(kv0 / 128, nb - 1);
+        auto need = [&](int st) {
+            int h, q0;
+            step_rows(st, h, q0);
+            return sp.mask[((size_t)(sp.heads == 1 ? 0 : h) * nb + min(q0 / 128, nb - 1)) * nb + mc] != 0;
+        };
+        int st = 0;
+        while (st < nsteps && !need(st)) ++st;
+        if (st < nsteps) {
+            issue(st, 0);
+            put_rows(0);
+            wait_vmem();
+        }
         __syncthreads();
+        int par = 0;
+        while (st < nsteps) {
+            int sn = st + 1;
+            while (sn < nsteps && !need(sn)) ++sn;
+            // past the last needed step, re-copy a valid step into the buffer
+            // nobody reads again
+            issue(min(sn, nsteps - 1), par ^ 1);
+            run_step(st, par);
+            put_rows(par ^ 1);
+            wait_vmem();
+            __syncthreads();
+            st = sn;
+            par ^= 1;
+        }
+    } else {
+        if (nsteps > 0) {
+            issue(0, 0);
+            put_rows(0);
+            wait_vmem();
+        }
+        __syncthreads();
+
+        for (int s = 0; s < nsteps; ++s) {
+            // The copy of the next step runs on every iteration (the last one
+            // re-copies the last step into the buffer nobody reads again).
+            issue(min(s + 1, nsteps - 1), (s + 1) & 1);
+            run_step(s, s);
+            put_rows((s + 1) & 1);
+            wait_vmem();
+            __syncthreads();
+        }
     }
 
     if (key < N) {
@@ -1075,13 +1116,16 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 // DROP: attention dropout (fa_common.h): dS = P * (Z dP 256 / t8 - D), with
 // the keep bytes of a tile's key blocks drawn as in the forward kernel (lane
 // half hi draws block 2 kp + hi of its row, one exchange per block pair).
-template <typename T, int D, bool CAUSAL, bool DROP = false>
+//
+// SPARSE: block-sparse attention (SparseParams): the workgroup's 128 rows are
+// one mask row; it walks only the key tiles the mask allows for them.
+template <typename T, int D, bool CAUSAL, bool DROP = false, bool SPARSE = false>
 __global__ void __launch_bounds__(256)
 dq16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
               const float* __restrict__ LSE, const float* __restrict__ Delta,
               uint16_t* __restrict__ dQ, int B, int Hq, int Hkv, int N, float cl2, float scale,
-              DropParams dp) {
+              DropParams dp, SparseParams sp) {
     constexpr int NW = 4;
     constexpr int BR = 32 * NW;
     constexpr int BC = D == 128 ? 64 : 128;
@@ -1164,14 +1208,10 @@ dq16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
     for (int db = 0; db < NDB; ++db) dq[db] = zero16();
 
-    issue(0, 0);
-    wait_vmem();
-    __syncthreads();
-
-    for (int j = 0; j < ntiles; ++j) {
+    // tile j from buffer par & 1
+    auto tile = [&](int j, int par) __attribute__((always_inline)) {
         const int k0 = j * BC;
-        issue(k0 + BC, (j + 1) & 1);
-        const unsigned char* base = smem + (j & 1) * STAGE;
+        const unsigned char* base = smem + (par & 1) * STAGE;
         const bool need_mask = (CAUSAL && k0 + BC - 1 > qw) || (k0 + BC > N);
         uint32_t dm[DROP ? NKB : 1][4];
         if constexpr (DROP) {
@@ -1234,8 +1274,38 @@ dq16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll 1
             for (int kb = 0; kb < NKB; ++kb) kb_body(kb, nullptr);
         }
+    };
+
+    if constexpr (SPARSE) {
+        const int nb = sp.nb;
+        const unsigned char* mrow = sp.mask + ((size_t)(sp.heads == 1 ? 0 : h) * nb + min(q0 / 128, nb - 1)) * nb;
+        auto need = [&](int jt) { return mrow[jt * BC / 128] != 0; };
+        int jt = 0;
+        while (jt < ntiles && !need(jt)) ++jt;
+        if (jt < ntiles) issue(jt * BC, 0);
         wait_vmem();
         __syncthreads();
+        int par = 0;
+        while (jt < ntiles) {
+            int jn = jt + 1;
+            while (jn < ntiles && !need(jn)) ++jn;
+            issue(jn * BC, par ^ 1);
+            tile(jt, par);
+            wait_vmem();
+            __syncthreads();
+            jt = jn;
+            par ^= 1;
+        }
+    } else {
+        issue(0, 0);
+        wait_vmem();
+        __syncthreads();
+        for (int j = 0; j < ntiles; ++j) {
+            issue((j + 1) * BC, (j + 1) & 1);
+            tile(j, j);
+            wait_vmem();
+            __syncthreads();
+        }
     }
 
     if (q < N) {
@@ -1670,13 +1740,21 @@ hipError_t prepare32(const BwdArgs& a) {
 template <typename T, int D, bool CAUSAL>
 hipError_t dkdv16(const BwdArgs& a) {
     const int nkb = (a.N + 127) / 128;
+    if (a.sparse) {
+        // dropout and block masks run on the second-generation kernels
+        hipLaunchKernelGGL((dkdv16v2_kernel<T, D, CAUSAL, false, true>), dim3((unsigned)(nkb * a.Hkv * a.B)),
+                           dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                           (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
+                           (uint16_t*)a.dk, (uint16_t*)a.dv, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale,
+                           a.dp, a.sp);
+        return hipGetLastError();
+    }
     if (a.drop) {
-        // dropout runs on the second-generation kernels
         hipLaunchKernelGGL((dkdv16v2_kernel<T, D, CAUSAL, true>), dim3((unsigned)(nkb * a.Hkv * a.B)),
                            dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                            (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
                            (uint16_t*)a.dk, (uint16_t*)a.dv, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale,
-                           a.dp);
+                           a.dp, a.sp);
         return hipGetLastError();
     }
     if (a.variant == 0) {
@@ -1691,7 +1769,7 @@ hipError_t dkdv16(const BwdArgs& a) {
                            dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                            (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
                            (uint16_t*)a.dk, (uint16_t*)a.dv, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale,
-                           a.dp);
+                           a.dp, a.sp);
         return hipGetLastError();
     }
     hipLaunchKernelGGL((dkdv16_kernel<T, D, CAUSAL>), dim3((unsigned)(nkb * a.Hkv * a.B)), dim3(256), 0,
@@ -1704,11 +1782,18 @@ hipError_t dkdv16(const BwdArgs& a) {
 template <typename T, int D, bool CAUSAL>
 hipError_t dq16(const BwdArgs& a) {
     const int nqb = (a.N + 127) / 128;
+    if (a.sparse) {
+        hipLaunchKernelGGL((dq16v2_kernel<T, D, CAUSAL, false, true>), dim3((unsigned)(nqb * a.Hq * a.B)),
+                           dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                           (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
+                           (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale, a.dp, a.sp);
+        return hipGetLastError();
+    }
     if (a.drop) {
         hipLaunchKernelGGL((dq16v2_kernel<T, D, CAUSAL, true>), dim3((unsigned)(nqb * a.Hq * a.B)),
                            dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                            (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
-                           (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale, a.dp);
+                           (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale, a.dp, a.sp);
         return hipGetLastError();
     }
     if (a.variant == 0) {
@@ -1722,7 +1807,7 @@ hipError_t dq16(const BwdArgs& a) {
         hipLaunchKernelGGL((dq16v2_kernel<T, D, CAUSAL>), dim3((unsigned)(nqb * a.Hq * a.B)),
                            dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                            (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
-                           (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale, a.dp);
+                           (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale, a.dp, a.sp);
         return hipGetLastError();
     }
     hipLaunchKernelGGL((dq16_kernel<T, D, CAUSAL>), dim3((unsigned)(nqb * a.Hq * a.B)), dim3(256), 0,

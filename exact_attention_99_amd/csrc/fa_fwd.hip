@@ -473,11 +473,17 @@ fwd16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 // product; the row sums and lse stay those of the undropped probabilities.
 // Lane half hi draws the bytes of key block 2 kp + hi of its row, and one
 // exchange between the halves gives each lane its bytes of both blocks.
-template <typename T, int D, bool CAUSAL, int NW, int BC, bool DROP = false>
+//
+// SPARSE: block-sparse attention (SparseParams): the workgroup walks only the
+// key tiles that the block mask allows for one of its rows (the copy of the
+// next such tile overlaps the current one), and a wave computes a tile only
+// if its own 32 rows may see it.  Rows that see no key get O = 0 and
+// lse = -inf.
+template <typename T, int D, bool CAUSAL, int NW, int BC, bool DROP = false, bool SPARSE = false>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 fwd16v5_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-               int B, int Hq, int Hkv, int N, float cl2, DropParams dp) {
+               int B, int Hq, int Hkv, int N, float cl2, DropParams dp, SparseParams sp) {
     constexpr int BR = 32 * NW;
     constexpr int KCH = D / 8;
     constexpr int TILE = BC * D * 2;
@@ -569,11 +575,12 @@ fwd16v5_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     float m_s = -INFINITY;
     float l_s = 0.f;
 
-    auto body = [&](int j, auto mask_tag, auto buf_tag) {
+    // tile j in buffer BUFC, or (BUFC < 0) in buffer par & 1
+    auto body = [&](int j, auto mask_tag, auto buf_tag, int par) {
         constexpr bool MASK = decltype(mask_tag)::value;
         constexpr int BUFC = decltype(buf_tag)::value;
         const int k0 = j * BC;
-        const uint32_t bb = BUFC >= 0 ? (uint32_t)(BUFC * STAGE) : (uint32_t)((j & 1) * STAGE);
+        const uint32_t bb = BUFC >= 0 ? (uint32_t)(BUFC * STAGE) : (uint32_t)((par & 1) * STAGE);
         const unsigned char* kbase = smem + bb;
         const unsigned char* vbase = smem + bb + TILE;
 
@@ -666,34 +673,69 @@ fwd16v5_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             for (int db = 0; db < NDB; ++db) o[db] = Mma<T>::mma(va[kg][db], pb[kg], o[db]);
     };
 
-    issue(0, 0);
-    wait_vmem();
-    __syncthreads();
+    if constexpr (SPARSE) {
+        const int nb = sp.nb;
+        const unsigned char* mk = sp.mask + (size_t)(sp.heads == 1 ? 0 : h) * nb * nb;
+        const int mr0 = min(q0 / 128, nb - 1);
+        const int mr1 = min((q0 + BR - 1) / 128, nb - 1);
+        const unsigned char* mw = mk + min(qw / 128, nb - 1) * nb;
+        auto wg_need = [&](int jt) {
+            const int c = jt * BC / 128;
+            bool any = false;
+            for (int r = mr0; r <= mr1; ++r) any |= mk[r * nb + c] != 0;
+            return any;
+        };
+        int jt = 0;
+        while (jt < ntiles && !wg_need(jt)) ++jt;
+        if (jt < ntiles) issue(jt * BC, 0);
+        wait_vmem();
+        __syncthreads();
+        int par = 0;
+        while (jt < ntiles) {
+            int jn = jt + 1;
+            while (jn < ntiles && !wg_need(jn)) ++jn;
+            // past the last needed tile the copy reads this head's range or
+            // zeros and lands in the buffer no later tile reads
+            issue(jn * BC, par ^ 1);
+            // one (masked) body keeps the register allocation of the dense loops
+            if (mw[jt * BC / 128] != 0 && (!CAUSAL || jt * BC <= qw + 31))
+                body(jt, std::true_type{}, std::integral_constant<int, -1>{}, par);
+            wait_vmem();
+            __syncthreads();
+            jt = jn;
+            par ^= 1;
+        }
+    } else {
+        issue(0, 0);
+        wait_vmem();
+        __syncthreads();
 
-    // The copy of the next tile is issued at the start of every tile, also
-    // the last (the extra tile lies in this head's range or past its end,
-    // reads as zeros, and lands in the buffer no later tile reads).
-    int j = 0;
-    for (; j + 1 < nfull; j += 2) {
-        issue((j + 1) * BC, 1);
-        body(j, std::false_type{}, std::integral_constant<int, 0>{});
-        wait_vmem();
-        __syncthreads();
-        issue((j + 2) * BC, 0);
-        body(j + 1, std::false_type{}, std::integral_constant<int, 1>{});
-        wait_vmem();
-        __syncthreads();
-    }
-    for (; j < ntiles; ++j) {
-        issue((j + 1) * BC, (j + 1) & 1);
-        if (!CAUSAL || j * BC <= qw + 31) body(j, std::true_type{}, std::integral_constant<int, -1>{});
-        wait_vmem();
-        __syncthreads();
+        // The copy of the next tile is issued at the start of every tile, also
+        // the last (the extra tile lies in this head's range or past its end,
+        // reads as zeros, and lands in the buffer no later tile reads).
+        int j = 0;
+        for (; j + 1 < nfull; j += 2) {
+            issue((j + 1) * BC, 1);
+            body(j, std::false_type{}, std::integral_constant<int, 0>{}, 0);
+            wait_vmem();
+            __syncthreads();
+            issue((j + 2) * BC, 0);
+            body(j + 1, std::false_type{}, std::integral_constant<int, 1>{}, 1);
+            wait_vmem();
+            __syncthreads();
+        }
+        for (; j < ntiles; ++j) {
+            issue((j + 1) * BC, (j + 1) & 1);
+            if (!CAUSAL || j * BC <= qw + 31) body(j, std::true_type{}, std::integral_constant<int, -1>{}, j);
+            wait_vmem();
+            __syncthreads();
+        }
     }
 
     const float l_tot = l_s + swap_halves(l_s);
     if (q < N) {
-        const float inv = (DROP ? dp.scale : 1.f) / l_tot;
+        const bool empty = SPARSE && !(l_tot > 0.f);
+        const float inv = empty ? 0.f : (DROP ? dp.scale : 1.f) / l_tot;
         uint16_t* Orow = O + qoff + (size_t)q * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -704,7 +746,7 @@ fwd16v5_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 w[1] = Mma<T>::pack2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
                 *reinterpret_cast<u32x2*>(Orow + 32 * db + 8 * g + 4 * hi) = w;
             }
-        if (hi == 0) LSE[(size_t)(b * Hq + h) * N + q] = (m_s + __log2f(l_tot)) * kLn2;
+        if (hi == 0) LSE[(size_t)(b * Hq + h) * N + q] = empty ? -INFINITY : (m_s + __log2f(l_tot)) * kLn2;
     }
 }
 
@@ -1399,15 +1441,15 @@ hipError_t launch16v2(const FwdArgs& a) {
     return hipGetLastError();
 }
 
-template <typename T, int D, bool CAUSAL, int NW, int BC, bool DROP = false>
+template <typename T, int D, bool CAUSAL, int NW, int BC, bool DROP = false, bool SPARSE = false>
 hipError_t launch16v5(const FwdArgs& a) {
     constexpr int BR = 32 * NW;
     const int nqb = (a.N + BR - 1) / BR;
     const long long total = (long long)nqb * a.Hq * a.B;
-    hipLaunchKernelGGL((fwd16v5_kernel<T, D, CAUSAL, NW, BC, DROP>), dim3((unsigned)total),
+    hipLaunchKernelGGL((fwd16v5_kernel<T, D, CAUSAL, NW, BC, DROP, SPARSE>), dim3((unsigned)total),
                        dim3(NW * 64), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.N, a.cl2,
-                       a.dp);
+                       a.dp, a.sp);
     return hipGetLastError();
 }
 
@@ -1448,9 +1490,13 @@ hipError_t launch32(const FwdArgs& a) {
 template <typename T, int D, bool CAUSAL>
 hipError_t dispatch16c(const FwdArgs& a) {
     if (a.drop) {
-        // dropout runs on the default tiling only
+        // dropout and block masks run on the default tiling only
         if constexpr (D == 128) return launch16v5<T, D, CAUSAL, 8, 64, true>(a);
         else return launch16v5<T, D, CAUSAL, 4, 128, true>(a);
+    }
+    if (a.sparse) {
+        if constexpr (D == 128) return launch16v5<T, D, CAUSAL, 8, 64, false, true>(a);
+        else return launch16v5<T, D, CAUSAL, 4, 128, false, true>(a);
     }
     if constexpr (D == 128) {
         switch (a.fwd_variant) {

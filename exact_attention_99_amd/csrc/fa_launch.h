@@ -16,6 +16,15 @@ struct DropParams {
     float scale;   // 256 / t8
 };
 
+// Block-sparse attention: query i sees key j only if
+// mask[h_m][i / 128][j / 128] != 0, h_m = 0 when heads == 1, else the query
+// head; nb = ceil(N / 128).
+struct SparseParams {
+    const unsigned char* mask;
+    int heads;
+    int nb;
+};
+
 struct FwdArgs {
     const void* q;
     const void* k;
@@ -29,6 +38,8 @@ struct FwdArgs {
     int fwd_variant; // tile variant of the 16-bit kernel (0 = default)
     int drop;        // 1: apply dropout with dp
     DropParams dp;
+    int sparse;      // 1: apply the block mask sp
+    SparseParams sp;
     hipStream_t stream;
 };
 
@@ -51,6 +62,8 @@ struct BwdArgs {
     int variant;     // kernel generation of the 16-bit passes (0 = default)
     int drop;        // 1: apply dropout with dp
     DropParams dp;
+    int sparse;      // 1: apply the block mask sp
+    SparseParams sp;
     hipStream_t stream;
 };
 

@@ -229,6 +229,40 @@ fa_status fa_bwd_dropout(const void* q, const void* k, const void* v,
                          fa_dtype dtype, hipStream_t stream);
 
 /*
+ * Block-sparse attention: the kernels skip the blocks of the attention matrix
+ * that a block mask zeroes ("FlashAttention and the Kernel Era", The
+ * Breakthrough: the block-sparse extension of the kernel).
+ *
+ *   block_mask in: uint8 [mask_heads, nb, nb], nb = ceil(N / 128)
+ *                  (FA_SPARSE_BLOCK), row-major, device memory, any
+ *                  alignment.  Query i may see key j iff
+ *                  block_mask[h_m][i / 128][j / 128] != 0 (and j <= i when
+ *                  causal), with h_m = 0 when mask_heads == 1 and the query
+ *                  head otherwise.  The same mask serves every batch element.
+ *   mask_heads     1 or H_q (else FA_ERR_INVALID_ARG).
+ * The softmax runs over the visible keys only.  A row that sees no key gets
+ * o = 0 and lse = -inf, and contributes no gradient.  Other arguments, sizes
+ * and errors as for fa_fwd / fa_bwd; bf16 / fp16 only (fp32 returns
+ * FA_ERR_UNSUPPORTED).  The work (and time) falls with the fraction of
+ * blocks set.
+ */
+#define FA_SPARSE_BLOCK 128
+
+fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v,
+                             void* o, float* lse,
+                             const unsigned char* block_mask, int mask_heads,
+                             int B, int H_q, int H_kv, int N, int d,
+                             int causal, float scale, fa_dtype dtype, hipStream_t stream);
+
+fa_status fa_bwd_blocksparse(const void* q, const void* k, const void* v,
+                             const void* o, const float* lse, const void* dout,
+                             void* dq, void* dk, void* dv,
+                             void* workspace, size_t workspace_bytes,
+                             const unsigned char* block_mask, int mask_heads,
+                             int B, int H_q, int H_kv, int N, int d,
+                             int causal, float scale, fa_dtype dtype, hipStream_t stream);
+
+/*
  * FP8 path ("FlashAttention 1, 2, and 3 Explained", section 4 on
  * FlashAttention-3: FP8 with block quantization and incoherent processing;
  * "FlashAttention" glossary, FlashAttention-3 paragraph).  Low precision:

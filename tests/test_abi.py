@@ -29,9 +29,10 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_dropout",
-                                    "fa_bwd_prepare", "fa_bwd_workspace_size", "fa_fp8_quantize",
-                                    "fa_fwd", "fa_fwd_dropout", "fa_fwd_fp8", "fa_fwd_splitkv",
+    assert declared_functions() == ["fa_bwd", "fa_bwd_blocksparse", "fa_bwd_dkdv", "fa_bwd_dq",
+                                    "fa_bwd_dropout", "fa_bwd_prepare", "fa_bwd_workspace_size",
+                                    "fa_fp8_quantize", "fa_fwd", "fa_fwd_blocksparse",
+                                    "fa_fwd_dropout", "fa_fwd_fp8", "fa_fwd_splitkv",
                                     "fa_fwd_splitkv_default_splits",
                                     "fa_fwd_splitkv_workspace_size", "fa_status_string",
                                     "fa_version"]
@@ -238,3 +239,30 @@ def test_dropout_entry_points_reject(lib):
     assert lib.fa_bwd_dropout(*([A] * 10), need - 1, 1, 2, 1, 64, 128, 0, 0.1, 0.1, 1, 2, BF16, None) == INVALID
     assert lib.fa_bwd_dropout(*([A] * 10), need, 1, 2, 1, 64, 128, 0, 0.1, 1.5, 1, 2, BF16, None) == INVALID
     assert lib.fa_bwd_dropout(*([A] * 10), need, 1, 2, 1, 64, 128, 0, 0.1, 0.1, 1, 2, FP32, None) == UNSUPPORTED
+
+
+def test_blocksparse_entry_points_reject(lib):
+    # fa_fwd_blocksparse(q, k, v, o, lse, mask, mask_heads, B, Hq, Hkv, N, d, causal, scale, dtype, stream)
+    for i in range(6):
+        p = [A] * 6
+        p[i] = None
+        assert lib.fa_fwd_blocksparse(*p, 1, 1, 4, 2, 300, 128, 1, 0.1, BF16, None) == INVALID
+    for i in range(5):
+        p = [A] * 6
+        p[i] = MIS
+        assert lib.fa_fwd_blocksparse(*p, 1, 1, 4, 2, 300, 128, 1, 0.1, BF16, None) == INVALID
+    ok = [A] * 5 + [A + 3]     # the mask needs no alignment
+    assert lib.fa_fwd_blocksparse(*ok, 2, 1, 4, 2, 300, 128, 1, 0.1, BF16, None) == INVALID   # mask_heads
+    assert lib.fa_fwd_blocksparse(*ok, 1, 1, 4, 2, 300, 96, 1, 0.1, BF16, None) == UNSUPPORTED
+    assert lib.fa_fwd_blocksparse(*ok, 1, 1, 4, 2, 300, 128, 1, 0.1, FP32, None) == UNSUPPORTED
+    assert lib.fa_fwd_blocksparse(*ok, 1, 1, 4, 2, 300, 128, 3, 0.1, BF16, None) == INVALID
+    # fa_bwd_blocksparse(10 pointers, ws_bytes, mask, mask_heads, B, Hq, Hkv, N, d, causal, scale, dtype, stream)
+    need = _abi.fa_bwd_workspace_size(1, 4, 2, 300, 128, "bf16")
+    for i in range(10):
+        p = [A] * 10
+        p[i] = None
+        assert lib.fa_bwd_blocksparse(*p, need, A, 1, 1, 4, 2, 300, 128, 1, 0.1, BF16, None) == INVALID
+    assert lib.fa_bwd_blocksparse(*([A] * 10), need, None, 1, 1, 4, 2, 300, 128, 1, 0.1, BF16, None) == INVALID
+    assert lib.fa_bwd_blocksparse(*([A] * 10), need - 1, A, 1, 1, 4, 2, 300, 128, 1, 0.1, BF16, None) == INVALID
+    assert lib.fa_bwd_blocksparse(*([A] * 10), need, A, 3, 1, 4, 2, 300, 128, 1, 0.1, BF16, None) == INVALID
+    assert lib.fa_bwd_blocksparse(*([A] * 10), need, A, 4, 1, 4, 2, 300, 128, 1, 0.1, FP32, None) == UNSUPPORTED

@@ -200,3 +200,31 @@ def make_signs(d: int, seed: int) -> torch.Tensor:
     g = torch.Generator()
     g.manual_seed(seed)
     return torch.randint(0, 2, (d,), generator=g).to(torch.float32) * 2 - 1
+
+
+# --------------------------------------------------------------------------
+# Block masks for block-sparse attention ("FlashAttention and the Kernel
+# Era", The Breakthrough: the block-sparse extension), one entry per 128 x 128
+# block.  Random masks: i.i.d. Bernoulli(density) blocks, the diagonal blocks
+# set when `diag` (so that no row is empty under the causal mask).  Band
+# masks: a local window of `width` blocks at and below the diagonal plus the
+# first `globals_` key blocks for every row (a long-context pattern).
+
+def make_block_mask(heads: int, N: int, density: float, seed: int, diag: bool = True,
+                    blk: int = 128) -> torch.Tensor:
+    nb = (N + blk - 1) // blk
+    g = torch.Generator()
+    g.manual_seed(seed)
+    m = (torch.rand((heads, nb, nb), generator=g) < density).to(torch.uint8)
+    if diag:
+        idx = torch.arange(nb)
+        m[:, idx, idx] = 1
+    return m
+
+
+def make_band_mask(N: int, width: int, globals_: int, blk: int = 128) -> torch.Tensor:
+    nb = (N + blk - 1) // blk
+    i = torch.arange(nb)[:, None]
+    j = torch.arange(nb)[None, :]
+    m = ((j <= i) & (j > i - width)) | (j < globals_)
+    return m.to(torch.uint8)[None]
