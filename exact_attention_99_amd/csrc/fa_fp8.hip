@@ -105,13 +105,18 @@ quant8_kernel(const uint16_t* __restrict__ X, const float* __restrict__ signs, f
                     y[i] = a + b;
                     y[i + h] = a - b;
                 }
+        // partner lanes t ^ 1, then t ^ 2, through quad permutes (DPP
+        // quad_perm [1,0,3,2] and [2,3,0,1])
 #pragma unroll
-        for (int m = 1; m <= 2; m *= 2)
+        for (int i = 0; i < E; ++i) {
+            const float o = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y[i]), 0xB1, 0xF, 0xF, true));
+            y[i] = (part & 1) ? (o - y[i]) : (y[i] + o);
+        }
 #pragma unroll
-            for (int i = 0; i < E; ++i) {
-                const float o = __shfl_xor(y[i], m, 64);
-                y[i] = (part & m) ? (o - y[i]) : (y[i] + o);
-            }
+        for (int i = 0; i < E; ++i) {
+            const float o = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y[i]), 0x4E, 0xF, 0xF, true));
+            y[i] = (part & 2) ? (o - y[i]) : (y[i] + o);
+        }
 #pragma unroll
         for (int i = 0; i < E; ++i) y[i] *= rs;
     }

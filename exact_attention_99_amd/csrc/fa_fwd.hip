@@ -1485,8 +1485,11 @@ hipError_t launch32(const FwdArgs& a) {
     return hipGetLastError();
 }
 
-// Kernel / tile variants; variant 0 (the buffer-to-LDS kernel with eight
-// 32-row waves) is the default, the others are kept for tile sweeps.
+// Kernel / tile variants; variant 0 (the buffer-to-LDS kernel with four
+// 32-row waves, two workgroups per compute unit: the two waves that share a
+// SIMD belong to different workgroups, so their barriers do not lock their
+// matrix and softmax phases together) is the default, the others are kept
+// for tile sweeps.
 template <typename T, int D, bool CAUSAL>
 hipError_t dispatch16c(const FwdArgs& a) {
     if (a.drop) {
@@ -1512,7 +1515,7 @@ hipError_t dispatch16c(const FwdArgs& a) {
             case 10: return launch16v5<T, D, CAUSAL, 8, 64>(a);
             case 11: return launch16v5<T, D, CAUSAL, 4, 64>(a);
             case 12: return launch16v2<T, D, CAUSAL, 8, 64>(a);
-            default: return launch16v5<T, D, CAUSAL, 8, 64>(a);
+            default: return launch16v5<T, D, CAUSAL, 4, 64>(a);
         }
     } else {
         switch (a.fwd_variant) {
