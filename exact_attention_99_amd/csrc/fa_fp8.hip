@@ -57,7 +57,9 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const void* p) {
 // Four fp32 values -> one dword of e4m3 codes (round to nearest even; the
 // inputs are within +-448).
 __device__ __forceinline__ int pack4_e4m3(float a, float b, float c, float d) {
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    // the first conversion's upper half is overwritten by the second, so its
+    // "old" operand is a don't-care (a's register; no zeroing move)
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
     return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
@@ -266,14 +268,32 @@ fwd8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
         cpk[i] = (uint32_t)(row * D + 16 * (cs ^ k8_swz<D>(row)));
         cpv[i] = (uint32_t)(row * D + 16 * (cs ^ v8_swz<D>(row)));
     }
+    // Block scales of the tile being copied are loaded with it (vector
+    // loads, so that waits on LDS reads stay fine-grained); they become the
+    // current tile's when the next copy is issued.
+    const Buf SKb(sk_h, (uint32_t)nblk * 4), SVb(sv_h, (uint32_t)nblk * 4);
+    float skc[NH], svc[NH], skn[NH], svn[NH];
+#pragma unroll
+    for (int t = 0; t < NH; ++t) skn[t] = svn[t] = 1.f;
     auto issue = [&](int k0, int buf) {
         unsigned char* base = smem + buf * STAGE;
+#pragma unroll
+        for (int t = 0; t < NH; ++t) {
+            skc[t] = skn[t];
+            svc[t] = svn[t];
+        }
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
             const int bi = wave + NW * i;
             const uint32_t rowb = (uint32_t)k0 * D;
             buf_to_lds16(Kb, base + bi * 1024, rowb + cpk[i]);
             buf_to_lds16(Vb, base + TILE + bi * 1024, rowb + cpv[i]);
+        }
+#pragma unroll
+        for (int t = 0; t < NH; ++t) {
+            const uint32_t blk = (uint32_t)min(k0 / kQBlk + t, nblk - 1);
+            skn[t] = SKb.load_f32(blk * 4);
+            svn[t] = SVb.load_f32(blk * 4);
         }
     };
 
@@ -313,9 +333,8 @@ fwd8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
         float c[NH], e[NH];
 #pragma unroll
         for (int t = 0; t < NH; ++t) {
-            const int blk = min(k0 / kQBlk + t, nblk - 1);
-            c[t] = cq * sk_h[blk];
-            e[t] = __log2f(sv_h[blk]) - lsv;
+            c[t] = cq * skc[t];
+            e[t] = __log2f(svc[t]) - lsv;
         }
 
         f32x16 s[NKB];
