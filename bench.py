@@ -19,8 +19,8 @@ L2 and the MALL), reported as median and minimum per kernel.
 Further objects in the same line: `splitkv` (the split-KV forward on
 decoding shapes, K/V bytes per second against the HBM peak), `dropout` (the
 forward and backward with fused dropout, p = 0.1, on the same workload),
-`blocksparse` (the same workload under a band block mask, rates over the
-visible elements) and
+`blocksparse` and `varlen` (the same workload under a band block mask, and
+with per-sequence lengths N, 3N/4, N/2, N/4; rates over the valid elements) and
 `fp8` (the block quantizer and the e4m3 forward on the same workload, against
 the fp8 matrix-core peak).  `--splitkv-only NAME`, `--dropout-only`,
 `--blocksparse-only` and `--fp8-only` run just those, for profiling.
@@ -296,6 +296,47 @@ def measure_blocksparse(w, q, k, v, do, stream, width: int = 4, globals_: int = 
             "bwd_tflops": 2.5 * F / (med["bwd"] * 1e-3) / 1e12}
 
 
+def measure_varlen(w, q, k, v, do, stream, iters: int = 10):
+    """Forward and backward of the workload's batch with per-sequence lengths
+    N, 3N/4, N/2, N/4 (cycled over the batch): median event-timed durations,
+    and rates over the FLOPs of the valid elements only."""
+    import torch
+    from exact_attention_99_amd import fa_bwd_varlen, fa_bwd_workspace_size, fa_fwd_varlen
+    causal = True in w.causal_modes
+    lens = [w.N * (4 - (b % 4)) // 4 for b in range(w.B)]
+    sl = torch.tensor(lens, dtype=torch.int32, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H_q, w.N), dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(fa_bwd_workspace_size(w.B, w.H_q, w.H_kv, w.N, w.d, w.dtype), 256),
+                     dtype=torch.uint8, device=q.device)
+    calls = {
+        "fwd": lambda: fa_fwd_varlen(q, k, v, sl, causal, w.scale, o=o, lse=lse, stream=stream),
+        "bwd": lambda: fa_bwd_varlen(q, k, v, o, lse, do, sl, causal, w.scale, dq=dq, dk=dk, dv=dv,
+                                     workspace=ws, stream=stream),
+    }
+    med = {}
+    for name, fn in calls.items():
+        for _ in range(2):
+            fn()
+        ts = []
+        for _ in range(iters):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ts.sort()
+        med[name] = ts[len(ts) // 2]
+    pairs = sum((n * (n + 1) / 2 if causal else n * n) for n in lens)
+    F = 4.0 * w.d * pairs * w.H_q
+    return {"workload": w.name, "lengths": lens, "causal": causal,
+            "fwd_ms": med["fwd"], "bwd_ms": med["bwd"],
+            "fwd_tflops": F / (med["fwd"] * 1e-3) / 1e12,
+            "bwd_tflops": 2.5 * F / (med["bwd"] * 1e-3) / 1e12}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -367,8 +408,9 @@ def main() -> int:
         print(json.dumps({"fp8": measure_fp8(w, q, k, v, torch.cuda.current_stream())}), flush=True)
         return 0
     if args.blocksparse_only:
-        print(json.dumps({"blocksparse": measure_blocksparse(w, q, k, v, do, torch.cuda.current_stream())}),
-              flush=True)
+        st = torch.cuda.current_stream()
+        print(json.dumps({"blocksparse": measure_blocksparse(w, q, k, v, do, st),
+                          "varlen": measure_varlen(w, q, k, v, do, st)}), flush=True)
         return 0
     if args.dropout_only:
         print(json.dumps({"dropout": measure_dropout(w, q, k, v, do, torch.cuda.current_stream())}),
@@ -502,6 +544,7 @@ def main() -> int:
         out["dropout"] = measure_dropout(w, q, k, v, do, stream)
     if args.blocksparse:
         out["blocksparse"] = measure_blocksparse(w, q, k, v, do, stream)
+        out["varlen"] = measure_varlen(w, q, k, v, do, stream)
     if args.fp8:
         out["fp8"] = measure_fp8(w, q, k, v, stream)
         out["fp8"]["speedup_vs_16bit_fwd"] = fwd_ms / out["fp8"]["fwd_fp8"]["ms"]

@@ -20,6 +20,8 @@ Names mirror the C entry points of ``include/fa355.h``:
     fa_bwd_dropout(q, k, v, o, lse, dout, causal, scale, dropout_p, seed, offset=0) -> (dq, dk, dv)
     fa_fwd_blocksparse(q, k, v, block_mask, causal, scale) -> (o, lse)
     fa_bwd_blocksparse(q, k, v, o, lse, dout, block_mask, causal, scale) -> (dq, dk, dv)
+    fa_fwd_varlen(q, k, v, seqlens, causal, scale) -> (o, lse)
+    fa_bwd_varlen(q, k, v, o, lse, dout, seqlens, causal, scale) -> (dq, dk, dv)
     fa_fp8_quantize(x, signs=None, ...) -> (codes, scales)
     fa_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal, scale, out_dtype="bf16") -> (o, lse)
     fa_status_string(code) -> str
@@ -27,13 +29,14 @@ Names mirror the C entry points of ``include/fa355.h``:
 """
 from ._abi import (FA_DTYPE, FP8_BLOCK_ROWS, FaError, fa_bwd, fa_bwd_dkdv, fa_bwd_dq,
                    fa_bwd_blocksparse, fa_bwd_dropout, fa_bwd_prepare, fa_bwd_workspace_size,
-                   fa_fp8_quantize, fa_fwd, fa_fwd_blocksparse, fa_fwd_dropout, fa_fwd_fp8,
+                   fa_bwd_varlen, fa_fp8_quantize, fa_fwd, fa_fwd_blocksparse, fa_fwd_dropout,
+                   fa_fwd_fp8, fa_fwd_varlen,
                    fa_fwd_splitkv, fa_fwd_splitkv_default_splits,
                    fa_fwd_splitkv_workspace_size, fa_status_string, fa_version, lib_path,
                    load_library)
 
 __all__ = ["fa_fwd", "fa_bwd", "fa_bwd_prepare", "fa_bwd_dkdv", "fa_bwd_dq",
            "fa_bwd_workspace_size", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
-           "fa_fwd_splitkv_default_splits", "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_blocksparse", "fa_bwd_blocksparse", "fa_fp8_quantize", "fa_fwd_fp8", "FP8_BLOCK_ROWS",
+           "fa_fwd_splitkv_default_splits", "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_blocksparse", "fa_bwd_blocksparse", "fa_fwd_varlen", "fa_bwd_varlen", "fa_fp8_quantize", "fa_fwd_fp8", "FP8_BLOCK_ROWS",
            "fa_status_string", "fa_version", "FaError", "FA_DTYPE",
            "load_library", "lib_path"]

@@ -71,6 +71,11 @@ def load_library() -> ctypes.CDLL:
         lib.fa_bwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, i,
                                            i, i, i, i, i, i, f, i, vp]
         lib.fa_bwd_blocksparse.restype = i
+        lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+        lib.fa_fwd_varlen.restype = i
+        lib.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                      i, i, i, i, i, i, f, i, vp]
+        lib.fa_bwd_varlen.restype = i
         lib.fa_fp8_quantize.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
         lib.fa_fp8_quantize.restype = i
         lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
@@ -452,4 +457,61 @@ def fa_bwd_blocksparse(q, k, v, o, lse, dout, block_mask, causal: bool, scale: f
                                 float(scale), FA_DTYPE[dt], _stream(q, stream))
     if st != 0:
         raise FaError(st, "fa_bwd_blocksparse")
+    return dq, dk, dv
+
+
+def _check_seqlens(seqlens, B):
+    import torch
+    if seqlens.dtype != torch.int32 or tuple(seqlens.shape) != (B,):
+        raise ValueError(f"seqlens must be int32 [{B}]")
+
+
+def fa_fwd_varlen(q, k, v, seqlens, causal: bool, scale: float, o=None, lse=None, stream=None):
+    """Attention of a padded batch whose element b holds seqlens[b] tokens
+    (int32 [B] on the device); returns (o, lse), zero / -inf on padding."""
+    import torch
+    lib = load_library()
+    B, Hq, Hkv, N, d = _shape(q, k, v)
+    dt = _dtype_name(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    _check_seqlens(seqlens, B)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _check_same(q, k, v, o, lse, seqlens)
+    st = lib.fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                           seqlens.data_ptr(), B, Hq, Hkv, N, d, int(bool(causal)), float(scale),
+                           FA_DTYPE[dt], _stream(q, stream))
+    if st != 0:
+        raise FaError(st, "fa_fwd_varlen")
+    return o, lse
+
+
+def fa_bwd_varlen(q, k, v, o, lse, dout, seqlens, causal: bool, scale: float, dq=None, dk=None,
+                  dv=None, workspace=None, stream=None):
+    """Backward of fa_fwd_varlen with the same lengths; returns (dq, dk, dv)."""
+    import torch
+    lib = load_library()
+    B, Hq, Hkv, N, d = _shape(q, k, v)
+    dt = _dtype_name(q)
+    _check_seqlens(seqlens, B)
+    if dq is None:
+        dq = torch.empty_like(q)
+    if dk is None:
+        dk = torch.empty_like(k)
+    if dv is None:
+        dv = torch.empty_like(v)
+    need = int(lib.fa_bwd_workspace_size(B, Hq, Hkv, N, d, FA_DTYPE[dt]))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check_same(q, k, v, o, lse, dout, dq, dk, dv, workspace, seqlens)
+    st = lib.fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                           dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                           seqlens.data_ptr(), B, Hq, Hkv, N, d, int(bool(causal)), float(scale),
+                           FA_DTYPE[dt], _stream(q, stream))
+    if st != 0:
+        raise FaError(st, "fa_bwd_varlen")
     return dq, dk, dv

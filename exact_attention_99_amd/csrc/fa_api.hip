@@ -84,7 +84,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
     a.drop = 0;
     a.dp = fa355::DropParams{0, 0, 256, 1.f};
     a.sparse = 0;
-    a.sp = fa355::SparseParams{nullptr, 1, 0};
+    a.sp = fa355::SparseParams{nullptr, 1, 0, nullptr};
     a.stream = stream;
     return fa355::launch_fwd(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -127,7 +127,7 @@ fa_status fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, f
     a.drop = 1;
     a.dp = fa355::DropParams{seed, offset, t8, 256.f / (float)t8};
     a.sparse = 0;
-    a.sp = fa355::SparseParams{nullptr, 1, 0};
+    a.sp = fa355::SparseParams{nullptr, 1, 0, nullptr};
     a.stream = stream;
     return fa355::launch_fwd(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -157,7 +157,7 @@ fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* 
     a.drop = 0;
     a.dp = fa355::DropParams{0, 0, 256, 1.f};
     a.sparse = 1;
-    a.sp = fa355::SparseParams{block_mask, mask_heads, (N + FA_SPARSE_BLOCK - 1) / FA_SPARSE_BLOCK};
+    a.sp = fa355::SparseParams{block_mask, mask_heads, (N + FA_SPARSE_BLOCK - 1) / FA_SPARSE_BLOCK, nullptr};
     a.stream = stream;
     return fa355::launch_fwd(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -203,7 +203,7 @@ fa355::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void*
     a.drop = 0;
     a.dp = fa355::DropParams{0, 0, 256, 1.f};
     a.sparse = 0;
-    a.sp = fa355::SparseParams{nullptr, 1, 0};
+    a.sp = fa355::SparseParams{nullptr, 1, 0, nullptr};
     a.stream = stream;
     return a;
 }
@@ -417,7 +417,57 @@ fa_status fa_bwd_blocksparse(const void* q, const void* k, const void* v, const 
     auto a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace), B, H_q,
                       H_kv, N, d, causal, scale, dtype, stream);
     a.sparse = 1;
-    a.sp = fa355::SparseParams{block_mask, mask_heads, (N + FA_SPARSE_BLOCK - 1) / FA_SPARSE_BLOCK};
+    a.sp = fa355::SparseParams{block_mask, mask_heads, (N + FA_SPARSE_BLOCK - 1) / FA_SPARSE_BLOCK, nullptr};
+    hipError_t e = fa355::launch_bwd_prepare(a);
+    if (e == hipSuccess) e = fa355::launch_bwd_dkdv(a);
+    if (e == hipSuccess) e = fa355::launch_bwd_dq(a);
+    return hip_status(e);
+}
+
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int* seqlens, int B, int H_q, int H_kv, int N, int d, int causal,
+                        float scale, fa_dtype dtype, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse || !seqlens) return FA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return FA_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(seqlens) & 3u) return FA_ERR_INVALID_ARG;
+    if (!sizes_ok(B, H_q, H_kv, N)) return FA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype)) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (dtype == FA_DTYPE_FP32) return FA_ERR_UNSUPPORTED;
+
+    fa355::FwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.B = B; a.Hq = H_q; a.Hkv = H_kv; a.N = N; a.d = d;
+    a.causal = causal;
+    a.cl2 = scale * kLog2eHost;
+    a.dtype = (int)dtype;
+    a.fwd_variant = 0;
+    a.drop = 0;
+    a.dp = fa355::DropParams{0, 0, 256, 1.f};
+    a.sparse = 1;
+    a.sp = fa355::SparseParams{nullptr, 1, 0, seqlens};
+    a.stream = stream;
+    return fa355::launch_fwd(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, const int* seqlens, int B,
+                        int H_q, int H_kv, int N, int d, int causal, float scale, fa_dtype dtype,
+                        hipStream_t stream) {
+    if (!ptrs_ok({q, k, v, o, lse, dout, dq, dk, dv, workspace}) || !seqlens) return FA_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(seqlens) & 3u) return FA_ERR_INVALID_ARG;
+    const fa_status st = check_common(B, H_q, H_kv, N, d, causal, scale, dtype);
+    if (st != FA_OK) return st;
+    if (dtype == FA_DTYPE_FP32) return FA_ERR_UNSUPPORTED;
+    if (workspace_bytes < fa_bwd_workspace_size(B, H_q, H_kv, N, d, dtype)) return FA_ERR_INVALID_ARG;
+    auto a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace), B, H_q,
+                      H_kv, N, d, causal, scale, dtype, stream);
+    a.sparse = 1;
+    a.sp = fa355::SparseParams{nullptr, 1, 0, seqlens};
     hipError_t e = fa355::launch_bwd_prepare(a);
     if (e == hipSuccess) e = fa355::launch_bwd_dkdv(a);
     if (e == hipSuccess) e = fa355::launch_bwd_dq(a);

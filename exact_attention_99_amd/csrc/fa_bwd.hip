@@ -534,15 +534,19 @@ dkdv16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int logical = xcd_remap((int)blockIdx.x, total);
     const int jb = logical % nkb;  // ascending: under a causal mask block 0 is the longest
     const int bhk = logical / nkb;
-    const int hk = bhk % Hkv;
-    const int b = bhk / Hkv;
+    // the masked path takes the batch index fastest (XCD balance across
+    // sequences of different lengths)
+    const int hk = SPARSE ? bhk / B : bhk % Hkv;
+    const int b = SPARSE ? bhk % B : bhk / Hkv;
     const int G = Hq / Hkv;
 
     const int kv0 = jb * BKV;
     const int kw = kv0 + 32 * wave;
     const int key = kw + l32;
     const size_t kvoff = ((size_t)b * Hkv + hk) * (size_t)N * D;
-    const uint32_t head_bytes = (uint32_t)N * D * 2;
+    // valid positions of this sequence (the masked path's lengths; else N)
+    const int Nk = (SPARSE && sp.seqlens) ? min(max(sp.seqlens[b], 0), N) : N;
+    const uint32_t head_bytes = (uint32_t)Nk * D * 2;
 
     u32x4 kf[NKS], vf[NKS];
     {
@@ -562,7 +566,7 @@ dkdv16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
 
     const int qb_first = CAUSAL ? kv0 / BQ : 0;
-    const int qb_count = (N + BQ - 1) / BQ - qb_first;
+    const int qb_count = max((Nk + BQ - 1) / BQ - qb_first, 0);
     const int nsteps = G * qb_count;
 
     // copy slots: this wave's copy i fills bytes [1024*bi, 1024*bi + 1024) of
@@ -617,7 +621,7 @@ dkdv16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     auto run_step = [&](int s, int par) __attribute__((always_inline)) {
         int h, q0;
         step_rows(s, h, q0);
-        const bool need_mask = (CAUSAL && q0 < kw + 32) || (q0 + BQ > N) || (kw + 32 > N);
+        const bool need_mask = (CAUSAL && q0 < kw + 32) || (q0 + BQ > Nk) || (kw + 32 > Nk);
         const unsigned char* base = smem + (par & 1) * STAGE;
         const float* lse2s = reinterpret_cast<const float*>(base + OFF_LSE);
         const float* dls = reinterpret_cast<const float*>(base + OFF_DL);
@@ -662,7 +666,7 @@ dkdv16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int q = q0 + 32 * qs + acc_row(r, hi);
-                    const bool vis = (!CAUSAL || key <= q) && q < N && key < N;
+                    const bool vis = (!CAUSAL || key <= q) && q < Nk && key < Nk;
                     pv[r] = vis ? pv[r] : 0.f;
                 }
             }
@@ -721,6 +725,7 @@ dkdv16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         const int nb = sp.nb;
         const int mc = min(kv0 / 128, nb - 1);
         auto need = [&](int st) {
+            if (!sp.mask) return true;   // lengths only: every step of the sequence
             int h, q0;
             step_rows(st, h, q0);
             return sp.mask[((size_t)(sp.heads == 1 ? 0 : h) * nb + min(q0 / 128, nb - 1)) * nb + mc] != 0;
@@ -1153,14 +1158,18 @@ dq16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int qb_raw = logical % nqb;
     const int bh = logical / nqb;
     const int qb = CAUSAL ? (nqb - 1 - qb_raw) : qb_raw;
-    const int h = bh % Hq;
-    const int b = bh / Hq;
+    // the masked path takes the batch index fastest (XCD balance across
+    // sequences of different lengths)
+    const int h = SPARSE ? bh / B : bh % Hq;
+    const int b = SPARSE ? bh % B : bh / Hq;
     const int hk = h / (Hq / Hkv);
 
     const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
     const size_t koff = ((size_t)b * Hkv + hk) * (size_t)N * D;
+    // valid positions of this sequence (the masked path's lengths; else N)
+    const int Nk = (SPARSE && sp.seqlens) ? min(max(sp.seqlens[b], 0), N) : N;
     const uint32_t head_bytes = (uint32_t)N * D * 2;
-    const Buf Kb(K + koff, head_bytes), Vb(V + koff, head_bytes);
+    const Buf Kb(K + koff, (uint32_t)Nk * D * 2), Vb(V + koff, (uint32_t)Nk * D * 2);
 
     const int q0 = qb * BR;
     const int qw = q0 + 32 * wave;
@@ -1179,7 +1188,7 @@ dq16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const float lse2 = Buf(LSE + roff, (uint32_t)N * 4).load_f32((uint32_t)q * 4) * kLog2e;
     const float dlt = Buf(Delta + roff, (uint32_t)N * 4).load_f32((uint32_t)q * 4);
 
-    const int kv_len = CAUSAL ? min(N, q0 + BR) : N;
+    const int kv_len = q0 >= Nk ? 0 : (CAUSAL ? min(Nk, q0 + BR) : Nk);
     const int ntiles = (kv_len + BC - 1) / BC;
 
     uint32_t cp[IPW];
@@ -1212,7 +1221,7 @@ dq16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     auto tile = [&](int j, int par) __attribute__((always_inline)) {
         const int k0 = j * BC;
         const unsigned char* base = smem + (par & 1) * STAGE;
-        const bool need_mask = (CAUSAL && k0 + BC - 1 > qw) || (k0 + BC > N);
+        const bool need_mask = (CAUSAL && k0 + BC - 1 > qw) || (k0 + BC > Nk) || (qw + 32 > Nk);
         uint32_t dm[DROP ? NKB : 1][4];
         if constexpr (DROP) {
 #pragma unroll
@@ -1239,7 +1248,7 @@ dq16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int kk = k0 + 32 * kb + acc_row(r, hi);
-                    p[r] = ((!CAUSAL || kk <= q) && kk < N) ? p[r] : 0.f;
+                    p[r] = ((!CAUSAL || kk <= q) && kk < Nk && q < Nk) ? p[r] : 0.f;
                 }
             }
             if constexpr (DROP) {
@@ -1278,8 +1287,8 @@ dq16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
     if constexpr (SPARSE) {
         const int nb = sp.nb;
-        const unsigned char* mrow = sp.mask + ((size_t)(sp.heads == 1 ? 0 : h) * nb + min(q0 / 128, nb - 1)) * nb;
-        auto need = [&](int jt) { return mrow[jt * BC / 128] != 0; };
+        const unsigned char* mrow = sp.mask ? sp.mask + ((size_t)(sp.heads == 1 ? 0 : h) * nb + min(q0 / 128, nb - 1)) * nb : nullptr;
+        auto need = [&](int jt) { return !mrow || mrow[jt * BC / 128] != 0; };
         int jt = 0;
         while (jt < ntiles && !need(jt)) ++jt;
         if (jt < ntiles) issue(jt * BC, 0);
@@ -1309,14 +1318,15 @@ dq16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
 
     if (q < N) {
+        const float sc = q < Nk ? scale : 0.f;   // padded rows get no gradient
         uint16_t* row = dQ + qoff + (size_t)q * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 u32x2 w;
-                w[0] = Mma<T>::pack2(dq[db][4 * g] * scale, dq[db][4 * g + 1] * scale);
-                w[1] = Mma<T>::pack2(dq[db][4 * g + 2] * scale, dq[db][4 * g + 3] * scale);
+                w[0] = Mma<T>::pack2(dq[db][4 * g] * sc, dq[db][4 * g + 1] * sc);
+                w[1] = Mma<T>::pack2(dq[db][4 * g + 2] * sc, dq[db][4 * g + 3] * sc);
                 *reinterpret_cast<u32x2*>(row + 32 * db + 8 * g + 4 * hi) = w;
             }
     }

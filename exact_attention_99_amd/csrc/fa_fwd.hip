@@ -512,14 +512,20 @@ fwd16v5_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int qb_raw = logical % nqb;
     const int bh = logical / nqb;
     const int qb = CAUSAL ? (nqb - 1 - qb_raw) : qb_raw;  // longest rows first
-    const int h = bh % Hq;
-    const int b = bh / Hq;
+    // the masked path takes the batch index fastest, so that the XCDs (each
+    // runs a contiguous range of heads) share sequences of different lengths
+    const int h = SPARSE ? bh / B : bh % Hq;
+    const int b = SPARSE ? bh % B : bh / Hq;
     const int hk = h / (Hq / Hkv);
 
     const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
     const size_t koff = ((size_t)b * Hkv + hk) * (size_t)N * D;
-    const uint32_t head_bytes = (uint32_t)N * D * 2;
-    const Buf Qb(Q + qoff, head_bytes), Kb(K + koff, head_bytes), Vb(V + koff, head_bytes);
+    // valid positions of this sequence (the masked path's lengths; else N)
+    const int Nk = (SPARSE && sp.seqlens) ? min(max(sp.seqlens[b], 0), N) : N;
+    // positions past Nk read as zeros (padded queries then score 0 against
+    // every key and never move the rescale decision of their wave)
+    const uint32_t kv_bytes = (uint32_t)Nk * D * 2;
+    const Buf Qb(Q + qoff, kv_bytes), Kb(K + koff, kv_bytes), Vb(V + koff, kv_bytes);
 
     const int q0 = qb * BR;
     const int qw = q0 + 32 * wave;
@@ -529,10 +535,10 @@ fwd16v5_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qf[ks] = Qb.load16((uint32_t)(q * D + 16 * ks + 8 * hi) * 2);
 
-    const int kv_len = CAUSAL ? min(N, q0 + BR) : N;
+    const int kv_len = q0 >= Nk ? 0 : (CAUSAL ? min(Nk, q0 + BR) : Nk);
     const int ntiles = (kv_len + BC - 1) / BC;
     // tiles below the whole row block (causal) and inside the sequence
-    const int nfull = min(CAUSAL ? q0 / BC : ntiles, N / BC);
+    const int nfull = min(CAUSAL ? q0 / BC : ntiles, Nk / BC);
 
     uint32_t cpk[IPW], cpv[IPW];
 #pragma unroll
@@ -600,7 +606,9 @@ fwd16v5_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = k0 + 32 * kb + acc_row(r, hi);
-                    if ((CAUSAL && key > q) || key >= N) s[kb][r] = -INFINITY;
+                    // (masked path: padded query rows see nothing, so they
+                    // never move the wave's rescale decision)
+                    if ((CAUSAL && key > q) || key >= Nk || (SPARSE && q >= Nk)) s[kb][r] = -INFINITY;
                 }
         }
 
@@ -673,13 +681,16 @@ fwd16v5_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             for (int db = 0; db < NDB; ++db) o[db] = Mma<T>::mma(va[kg][db], pb[kg], o[db]);
     };
 
-    if constexpr (SPARSE) {
+    bool compact = false;   // walk only the tiles a block mask allows
+    if constexpr (SPARSE) compact = sp.mask != nullptr;
+    if (compact) {
         const int nb = sp.nb;
-        const unsigned char* mk = sp.mask + (size_t)(sp.heads == 1 ? 0 : h) * nb * nb;
+        const unsigned char* mk = sp.mask ? sp.mask + (size_t)(sp.heads == 1 ? 0 : h) * nb * nb : nullptr;
         const int mr0 = min(q0 / 128, nb - 1);
         const int mr1 = min((q0 + BR - 1) / 128, nb - 1);
-        const unsigned char* mw = mk + min(qw / 128, nb - 1) * nb;
+        const unsigned char* mw = mk ? mk + min(qw / 128, nb - 1) * nb : nullptr;
         auto wg_need = [&](int jt) {
+            if (!mk) return true;
             const int c = jt * BC / 128;
             bool any = false;
             for (int r = mr0; r <= mr1; ++r) any |= mk[r * nb + c] != 0;
@@ -698,7 +709,7 @@ fwd16v5_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             // zeros and lands in the buffer no later tile reads
             issue(jn * BC, par ^ 1);
             // one (masked) body keeps the register allocation of the dense loops
-            if (mw[jt * BC / 128] != 0 && (!CAUSAL || jt * BC <= qw + 31))
+            if ((!mw || mw[jt * BC / 128] != 0) && (!CAUSAL || jt * BC <= qw + 31))
                 body(jt, std::true_type{}, std::integral_constant<int, -1>{}, par);
             wait_vmem();
             __syncthreads();
@@ -734,7 +745,7 @@ fwd16v5_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
     const float l_tot = l_s + swap_halves(l_s);
     if (q < N) {
-        const bool empty = SPARSE && !(l_tot > 0.f);
+        const bool empty = SPARSE && (!(l_tot > 0.f) || q >= Nk);
         const float inv = empty ? 0.f : (DROP ? dp.scale : 1.f) / l_tot;
         uint16_t* Orow = O + qoff + (size_t)q * D;
 #pragma unroll
@@ -1498,7 +1509,7 @@ hipError_t dispatch16c(const FwdArgs& a) {
         else return launch16v5<T, D, CAUSAL, 4, 128, true>(a);
     }
     if (a.sparse) {
-        if constexpr (D == 128) return launch16v5<T, D, CAUSAL, 8, 64, false, true>(a);
+        if constexpr (D == 128) return launch16v5<T, D, CAUSAL, 4, 64, false, true>(a);
         else return launch16v5<T, D, CAUSAL, 4, 128, false, true>(a);
     }
     if constexpr (D == 128) {

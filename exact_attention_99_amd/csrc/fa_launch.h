@@ -16,13 +16,17 @@ struct DropParams {
     float scale;   // 256 / t8
 };
 
-// Block-sparse attention: query i sees key j only if
-// mask[h_m][i / 128][j / 128] != 0, h_m = 0 when heads == 1, else the query
-// head; nb = ceil(N / 128).
+// General masked path (block-sparse and variable-length attention).  When
+// mask is set, query i sees key j only if mask[h_m][i / 128][j / 128] != 0,
+// h_m = 0 when heads == 1, else the query head; nb = ceil(N / 128).  When
+// seqlens is set, batch element b has seqlens[b] valid positions (clamped to
+// [0, N]); later queries and keys are padding (zero output, lse -inf, no
+// gradient).
 struct SparseParams {
     const unsigned char* mask;
     int heads;
     int nb;
+    const int* seqlens;
 };
 
 struct FwdArgs {

@@ -263,6 +263,30 @@ fa_status fa_bwd_blocksparse(const void* q, const void* k, const void* v,
                              int causal, float scale, fa_dtype dtype, hipStream_t stream);
 
 /*
+ * Variable-length batches in the padded layout: batch element b holds
+ * seqlens[b] valid tokens (the ragged end of one sequence, generalised to a
+ * batch; "Flash Attention" (21medien), the [batch, heads, seq_len, head_dim]
+ * layout of its code example).  Queries and keys at positions >= seqlens[b]
+ * are padding: they take no part in any softmax, their output rows are 0 with
+ * lse -inf, and dq / dk / dv are 0 there.
+ *   seqlens in: int32 [B] in device memory, 4-byte aligned, each in [0, N]
+ *               (values outside are clamped).
+ * Other arguments, sizes and errors as for fa_fwd / fa_bwd; bf16 / fp16 only
+ * (fp32 returns FA_ERR_UNSUPPORTED).  The work falls with the lengths.
+ */
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v,
+                        void* o, float* lse, const int* seqlens,
+                        int B, int H_q, int H_kv, int N, int d,
+                        int causal, float scale, fa_dtype dtype, hipStream_t stream);
+
+fa_status fa_bwd_varlen(const void* q, const void* k, const void* v,
+                        const void* o, const float* lse, const void* dout,
+                        void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, const int* seqlens,
+                        int B, int H_q, int H_kv, int N, int d,
+                        int causal, float scale, fa_dtype dtype, hipStream_t stream);
+
+/*
  * FP8 path ("FlashAttention 1, 2, and 3 Explained", section 4 on
  * FlashAttention-3: FP8 with block quantization and incoherent processing;
  * "FlashAttention" glossary, FlashAttention-3 paragraph).  Low precision:

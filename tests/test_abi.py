@@ -30,12 +30,12 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_blocksparse", "fa_bwd_dkdv", "fa_bwd_dq",
-                                    "fa_bwd_dropout", "fa_bwd_prepare", "fa_bwd_workspace_size",
-                                    "fa_fp8_quantize", "fa_fwd", "fa_fwd_blocksparse",
-                                    "fa_fwd_dropout", "fa_fwd_fp8", "fa_fwd_splitkv",
-                                    "fa_fwd_splitkv_default_splits",
-                                    "fa_fwd_splitkv_workspace_size", "fa_status_string",
-                                    "fa_version"]
+                                    "fa_bwd_dropout", "fa_bwd_prepare", "fa_bwd_varlen",
+                                    "fa_bwd_workspace_size", "fa_fp8_quantize", "fa_fwd",
+                                    "fa_fwd_blocksparse", "fa_fwd_dropout", "fa_fwd_fp8",
+                                    "fa_fwd_splitkv", "fa_fwd_splitkv_default_splits",
+                                    "fa_fwd_splitkv_workspace_size", "fa_fwd_varlen",
+                                    "fa_status_string", "fa_version"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -266,3 +266,25 @@ def test_blocksparse_entry_points_reject(lib):
     assert lib.fa_bwd_blocksparse(*([A] * 10), need - 1, A, 1, 1, 4, 2, 300, 128, 1, 0.1, BF16, None) == INVALID
     assert lib.fa_bwd_blocksparse(*([A] * 10), need, A, 3, 1, 4, 2, 300, 128, 1, 0.1, BF16, None) == INVALID
     assert lib.fa_bwd_blocksparse(*([A] * 10), need, A, 4, 1, 4, 2, 300, 128, 1, 0.1, FP32, None) == UNSUPPORTED
+
+
+def test_varlen_entry_points_reject(lib):
+    # fa_fwd_varlen(q, k, v, o, lse, seqlens, B, Hq, Hkv, N, d, causal, scale, dtype, stream)
+    for i in range(6):
+        p = [A] * 6
+        p[i] = None
+        assert lib.fa_fwd_varlen(*p, 2, 4, 2, 300, 128, 1, 0.1, BF16, None) == INVALID
+    p = [A] * 5 + [A + 2]       # seqlens must be 4-byte aligned
+    assert lib.fa_fwd_varlen(*p, 2, 4, 2, 300, 128, 1, 0.1, BF16, None) == INVALID
+    ok = [A] * 6
+    assert lib.fa_fwd_varlen(*ok, 2, 4, 2, 300, 96, 1, 0.1, BF16, None) == UNSUPPORTED
+    assert lib.fa_fwd_varlen(*ok, 2, 4, 2, 300, 128, 1, 0.1, FP32, None) == UNSUPPORTED
+    assert lib.fa_fwd_varlen(*ok, 2, 4, 3, 300, 128, 1, 0.1, BF16, None) == INVALID
+    need = _abi.fa_bwd_workspace_size(2, 4, 2, 300, 128, "bf16")
+    for i in range(10):
+        p = [A] * 10
+        p[i] = None
+        assert lib.fa_bwd_varlen(*p, need, A, 2, 4, 2, 300, 128, 1, 0.1, BF16, None) == INVALID
+    assert lib.fa_bwd_varlen(*([A] * 10), need, None, 2, 4, 2, 300, 128, 1, 0.1, BF16, None) == INVALID
+    assert lib.fa_bwd_varlen(*([A] * 10), need - 1, A, 2, 4, 2, 300, 128, 1, 0.1, BF16, None) == INVALID
+    assert lib.fa_bwd_varlen(*([A] * 10), need, A, 2, 4, 2, 300, 128, 1, 0.1, FP32, None) == UNSUPPORTED
