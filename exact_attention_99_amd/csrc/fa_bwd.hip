@@ -940,14 +940,16 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         }
         const size_t roff = ((size_t)b * Hq + h) * (size_t)N;
         if (tid < BQ) {
-            sl = Buf(LSE + roff, (uint32_t)N * 4).load_f32((uint32_t)(q0 + tid) * 4) * kLog2e;
+            // scaled to base 2 when it is published (a use here would make the
+            // wave wait for the tile copies issued just before)
+            sl = Buf(LSE + roff, (uint32_t)N * 4).load_f32((uint32_t)(q0 + tid) * 4);
             sd = Buf(Delta + roff, (uint32_t)N * 4).load_f32((uint32_t)(q0 + tid) * 4);
         }
     };
     auto put_rows = [&](int buf) {
         unsigned char* base = smem + buf * STAGE;
         if (tid < BQ) {
-            reinterpret_cast<float*>(base + OFF_LSE)[tid] = sl;
+            reinterpret_cast<float*>(base + OFF_LSE)[tid] = sl * kLog2e;
             reinterpret_cast<float*>(base + OFF_DL)[tid] = sd;
         }
     };
@@ -962,14 +964,21 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     // seg / 2 - 1, and the last one those of block NQB - 1.
     // mlim: element (block blk, row offset o) of this lane is visible when
     // 32 blk + o >= mlim (causal: the query row is at or after the key)
-    auto run_step = [&](auto mask_tag, auto buf_tag, const unsigned char* rt_base, int mlim) {
+    // rt_base: the tile's buffer.  Every LDS read of the step goes through
+    // this restrict-qualified pointer, so the transposing reads carry alias
+    // information and the compiler does not make them wait for the copies of
+    // the next step into the other buffer.
+    // (The buffer is a run-time argument of the step, not a template one: a
+    // step specialised on a constant buffer would lose that information.)
+    auto run_step = [&](auto mask_tag, const unsigned char* __restrict__ rt_base, int mlim)
+                        __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_tag)::value;
-        constexpr int BUFC = decltype(buf_tag)::value;
         // The lane-dependent parts of every LDS address, with the buffer's base
         // folded in, are formed once per tile; each read then adds only an
         // immediate (block, half and tensor offsets), which stays within the
-        // 16-bit offset field of the LDS instructions.
-        const uint32_t bb = BUFC >= 0 ? (uint32_t)(BUFC * STAGE) : (uint32_t)(rt_base - smem);
+        // 16-bit offset field of the LDS instructions (the buffer base is a
+        // constant once the step is inlined into the unmasked loop).
+        const uint32_t bb = (uint32_t)(rt_base - smem);
         uint32_t ao[NKS], to[2][NDB];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) ao[ks] = lds_lane_off(bb + dual_off<D>(l32, 16 * (2 * ks + hi)));
@@ -992,12 +1001,12 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             if constexpr (dkdv_seg_is_s<NQB>(seg)) {
                 constexpr int ks = j >> 1;
                 constexpr int imm = ((j & 1) ? OFF_DOS : 0) + 32 * blk * D * 2;
-                op[n] = *reinterpret_cast<const u32x4*>(smem + ao[ks] + imm);
+                op[n] = *reinterpret_cast<const u32x4*>(rt_base + (ao[ks] - bb) + imm);
             } else {
                 constexpr int t = j / (2 * NDB), db = (j >> 1) % NDB;
                 constexpr int imm = ((j & 1) ? 0 : OFF_DOS) + (32 * blk + 16 * t) * D * 2;
-                const u32x2 lo = lds_read_tr16(smem + to[0][db] + imm);
-                const u32x2 up = lds_read_tr16(smem + to[1][db] + imm);
+                const u32x2 lo = lds_read_tr16(rt_base + (to[0][db] - bb) + imm);
+                const u32x2 up = lds_read_tr16(rt_base + (to[1][db] - bb) + imm);
                 op[n] = u32x4{lo[0], lo[1], up[0], up[1]};
             }
         };
@@ -1005,9 +1014,9 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             const int g = k >> 1;
             const int imm = 4 * (32 * blk + 8 * g);
             if (k & 1)
-                dc[g] = *reinterpret_cast<const f32x4*>(smem + ro + (OFF_DL - OFF_LSE) + imm);
+                dc[g] = *reinterpret_cast<const f32x4*>(rt_base + (ro - bb) + (OFF_DL - OFF_LSE) + imm);
             else
-                lc[g] = *reinterpret_cast<const f32x4*>(smem + ro + imm);
+                lc[g] = *reinterpret_cast<const f32x4*>(rt_base + (ro - bb) + imm);
         };
         // softmax and dS of element r of block blk (row 32 blk + acc_row(r, hi))
         float pv[16], dsv[16];
@@ -1076,14 +1085,15 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     __syncthreads();
 
     // one tile: prefetch the next one into the other buffer, compute, publish
-    auto tile = [&](int s, auto mask_tag, auto buf_tag) {
+    auto tile = [&](int s, auto mask_tag, auto buf_tag) __attribute__((always_inline)) {
+        constexpr int BUFC = decltype(buf_tag)::value;
         const int nb = buf_of(s) ^ 1;
         issue(min(s + 1, nsteps - 1), nb);
         int h, q0;
         step_rows(s, h, q0);
         (void)h;
         // rows q0 + 4 hi + (32 blk + 8 g + i) are visible when at or after the key
-        run_step(mask_tag, buf_tag, smem + buf_of(s) * STAGE, key - q0 - 4 * hi);
+        run_step(mask_tag, smem + (BUFC >= 0 ? BUFC : buf_of(s)) * STAGE, key - q0 - 4 * hi);
         put_rows(nb);
         wait_vmem();
         __syncthreads();
@@ -1406,8 +1416,7 @@ dq16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         const int row = p / KCH, pc = p % KCH;
         cp[i] = (uint32_t)(row * D * 2 + 16 * (pc ^ dual_swz<D>(row)));
     }
-    auto issue = [&](int k0, int buf) {
-        unsigned char* base = smem + buf * STAGE;
+    auto issue_to = [&](unsigned char* base, int k0) {
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
             const uint32_t off = (uint32_t)k0 * D * 2 + cp[i];
@@ -1425,11 +1434,15 @@ dq16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
     for (int db = 0; db < NDB; ++db) dq[db] = zero16();
 
-    auto body = [&](int j, auto mask_tag, auto buf_tag) {
+    // Tile j from the buffer at base.  ISSUE: the copies of key tile kn go to
+    // the buffer at nxt first; the two restrict-qualified buffer pointers let
+    // the compiler see that the transposing reads of this tile never touch
+    // what the copies write, so they do not wait for the copies in flight.
+    auto body = [&](int j, auto mask_tag, auto issue_tag, const unsigned char* __restrict__ base,
+                    unsigned char* __restrict__ nxt, int kn) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_tag)::value;
-        constexpr int BUFC = decltype(buf_tag)::value;
+        if constexpr (decltype(issue_tag)::value) issue_to(nxt, kn);
         const int k0 = j * BC;
-        const unsigned char* base = smem + (BUFC >= 0 ? BUFC : (j & 1)) * STAGE;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             f32x16 st = zero16(), dpt = zero16();
@@ -1476,25 +1489,24 @@ dq16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
     // tiles below every row of the block and inside the sequence
     const int nfull = min(CAUSAL ? q0 / BC : ntiles, N / BC);
-    issue(0, 0);
+    issue_to(smem, 0);
     wait_vmem();
     __syncthreads();
     // The copy of the next tile is issued at the start of every tile, also the
     // last (it lies in this head's range or past its end and reads as zeros).
     int j = 0;
     for (; j + 1 < nfull; j += 2) {
-        issue((j + 1) * BC, 1);
-        body(j, std::false_type{}, std::integral_constant<int, 0>{});
+        body(j, std::false_type{}, std::true_type{}, smem, smem + STAGE, (j + 1) * BC);
         wait_vmem();
         __syncthreads();
-        issue((j + 2) * BC, 0);
-        body(j + 1, std::false_type{}, std::integral_constant<int, 1>{});
+        body(j + 1, std::false_type{}, std::true_type{}, smem + STAGE, smem, (j + 2) * BC);
         wait_vmem();
         __syncthreads();
     }
     for (; j < ntiles; ++j) {
-        issue((j + 1) * BC, (j + 1) & 1);
-        if (!CAUSAL || j * BC <= qw + 31) body(j, std::true_type{}, std::integral_constant<int, -1>{});
+        issue_to(smem + ((j + 1) & 1) * STAGE, (j + 1) * BC);
+        if (!CAUSAL || j * BC <= qw + 31)
+            body(j, std::true_type{}, std::false_type{}, smem + (j & 1) * STAGE, nullptr, 0);
         wait_vmem();
         __syncthreads();
     }

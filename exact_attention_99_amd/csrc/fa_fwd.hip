@@ -479,6 +479,13 @@ fwd16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 // next such tile overlaps the current one), and a wave computes a tile only
 // if its own 32 rows may see it.  Rows that see no key get O = 0 and
 // lse = -inf.
+//
+// A tile's LDS reads go through a restrict-qualified pointer to its buffer.
+// The transposing reads then carry alias information, and the compiler no
+// longer makes them wait for the copies of the next tile into the other
+// buffer, which it must otherwise assume they may overlap (with a plain
+// pointer every tile waited for its successor's copies before its first V^T
+// read).
 template <typename T, int D, bool CAUSAL, int NW, int BC, bool DROP = false, bool SPARSE = false>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 fwd16v5_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -581,14 +588,13 @@ fwd16v5_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     float m_s = -INFINITY;
     float l_s = 0.f;
 
-    // tile j in buffer BUFC, or (BUFC < 0) in buffer par & 1
-    auto body = [&](int j, auto mask_tag, auto buf_tag, int par) {
+    // tile j from the buffer at cur
+    auto body_at = [&](const unsigned char* __restrict__ cur, int j, auto mask_tag)
+                       __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_tag)::value;
-        constexpr int BUFC = decltype(buf_tag)::value;
         const int k0 = j * BC;
-        const uint32_t bb = BUFC >= 0 ? (uint32_t)(BUFC * STAGE) : (uint32_t)((par & 1) * STAGE);
-        const unsigned char* kbase = smem + bb;
-        const unsigned char* vbase = smem + bb + TILE;
+        const unsigned char* kbase = cur;
+        const unsigned char* vbase = cur + TILE;
 
         f32x16 s[NKB];
 #pragma unroll
@@ -680,6 +686,11 @@ fwd16v5_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
             for (int db = 0; db < NDB; ++db) o[db] = Mma<T>::mma(va[kg][db], pb[kg], o[db]);
     };
+    // tile j in buffer BUFC, or (BUFC < 0) in buffer par & 1
+    auto body = [&](int j, auto mask_tag, auto buf_tag, int par) __attribute__((always_inline)) {
+        constexpr int BUFC = decltype(buf_tag)::value;
+        body_at(smem + (BUFC >= 0 ? BUFC * STAGE : (par & 1) * STAGE), j, mask_tag);
+    };
 
     bool compact = false;   // walk only the tiles a block mask allows
     if constexpr (SPARSE) compact = sp.mask != nullptr;
@@ -758,6 +769,287 @@ fwd16v5_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 *reinterpret_cast<u32x2*>(Orow + 32 * db + 8 * g + 4 * hi) = w;
             }
         if (hi == 0) LSE[(size_t)(b * Hq + h) * N + q] = empty ? -INFINITY : (m_s + __log2f(l_tot)) * kLn2;
+    }
+}
+
+// Sixth-generation 16-bit forward kernel (d = 128 tiles of 64 keys): the data
+// path of the fifth generation with two changes to the softmax.
+//
+// 1. The running maximum is not recomputed per tile.  The probabilities of a
+//    32-key half tile are formed against the current maximum m and summed; if
+//    every lane's sum stays at or below 2^kTau (and m is finite), no
+//    probability exceeds 2^kTau either, so the unnormalised values are in
+//    range and the half is accepted as it is: the output and the row sum still
+//    refer to the same m, and the result is exact.  Otherwise (the first tile
+//    of a row, or scores that rose above m) the wave takes the slow path: the
+//    half's true row maximum, the rescale of the output and row sum, and the
+//    probabilities again.
+// 2. PIPE: the two halves of a tile are pipelined inside the wave: the
+//    scores of the second half are formed on the matrix cores while the vector
+//    unit exponentiates the first, and the P V products of the first half run
+//    while the second is exponentiated.  Without PIPE the halves run one after
+//    the other.
+// 3. As in the fifth generation, the tile's LDS reads go through a
+//    restrict-qualified buffer pointer, so they do not wait for the copies of
+//    the next tile.
+template <typename T, int D, bool CAUSAL, int NW, int BC, bool PIPE>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+               const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
+               int B, int Hq, int Hkv, int N, float cl2) {
+    static_assert(BC == 64, "two 32-key halves per tile");
+    constexpr int BR = 32 * NW;
+    constexpr int KCH = D / 8;
+    constexpr int TILE = BC * D * 2;
+    constexpr int STAGE = 2 * TILE;
+    constexpr int NDB = D / 32;
+    constexpr int NKS = D / 16;
+    constexpr int WI = TILE / 1024;
+    static_assert(WI % NW == 0, "tile copies split evenly over the waves");
+    constexpr int IPW = WI / NW;
+    static_assert(2 * STAGE <= 65536, "both buffers addressable by immediate offsets");
+    static_assert(BR % BC == 0, "row blocks start on a key-tile boundary");
+    constexpr float kSumCap = 256.0f;   // 2^kTau
+    static_assert(kTau == 8.0f, "sum cap matches the lazy-rescale threshold");
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+
+    const int nqb = (N + BR - 1) / BR;
+    const int total = nqb * Hq * B;
+    const int logical = xcd_remap((int)blockIdx.x, total);
+    const int qb_raw = logical % nqb;
+    const int bh = logical / nqb;
+    const int qb = CAUSAL ? (nqb - 1 - qb_raw) : qb_raw;  // longest rows first
+    const int h = bh % Hq;
+    const int b = bh / Hq;
+    const int hk = h / (Hq / Hkv);
+
+    const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
+    const size_t koff = ((size_t)b * Hkv + hk) * (size_t)N * D;
+    const uint32_t head_bytes = (uint32_t)N * D * 2;
+    const Buf Qb(Q + qoff, head_bytes), Kb(K + koff, head_bytes), Vb(V + koff, head_bytes);
+
+    const int q0 = qb * BR;
+    const int qw = q0 + 32 * wave;
+    const int q = qw + l32;
+
+    u32x4 qf[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = Qb.load16((uint32_t)(q * D + 16 * ks + 8 * hi) * 2);
+
+    const int kv_len = CAUSAL ? min(N, q0 + BR) : N;
+    const int ntiles = (kv_len + BC - 1) / BC;
+    const int nfull = min(CAUSAL ? q0 / BC : ntiles, N / BC);
+
+    uint32_t cpk[IPW], cpv[IPW];
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+        const int p = (wave + NW * i) * 64 + lane;
+        const int row = p / KCH, pc = p % KCH;
+        cpk[i] = (uint32_t)kq_off<D>(row, pc);
+        cpv[i] = (uint32_t)(row * D * 2 + 16 * (pc ^ tr_swz<D>(row)));
+    }
+    auto issue_to = [&](unsigned char* base, int k0) {
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            const int bi = wave + NW * i;
+            const uint32_t rowb = (uint32_t)k0 * D * 2;
+            buf_to_lds16(Kb, base + bi * 1024, rowb + cpk[i]);
+            buf_to_lds16(Vb, base + TILE + bi * 1024, rowb + cpv[i]);
+        }
+    };
+
+    const int g16 = lane >> 4;
+    const int j16 = lane & 15;
+    const int tr_row = 4 * hi + (j16 >> 2);
+    const int tr_col = 2 * (16 * (g16 & 1) + 4 * (j16 & 3));
+
+    // lane parts of the LDS addresses: K rows 32 kb + l32 (the swizzle
+    // depends on row & 15 only, so both halves share them), chunk 2 ks + hi;
+    // V^T rows 16 kg + tr_row (+ 8), bytes 64 db + tr_col
+    uint32_t ko[NKS], vo[NDB];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) ko[ks] = lds_lane_off((uint32_t)kq_off<D>(l32, 2 * ks + hi));
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) vo[db] = lds_lane_off((uint32_t)vt_off<D>(tr_row, 64 * db + tr_col));
+
+    f32x16 o[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[db] = zero16();
+    float m_s = -INFINITY;
+    float l_s = 0.f;
+
+    // tile j from the buffer at cur
+    auto body = [&](int j, auto mask_tag, const unsigned char* __restrict__ cur)
+                    __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        const int k0 = j * BC;
+        const unsigned char* kbase = cur;
+        const unsigned char* vbase = cur + TILE;
+
+        auto kread = [&](int kb, int ks) {
+            return *reinterpret_cast<const u32x4*>(kbase + ko[ks] + 32 * kb * D * 2);
+        };
+        auto vread = [&](int kg, int db) {
+            const u32x2 lo = lds_read_tr16(vbase + vo[db] + 16 * kg * D * 2);
+            const u32x2 up = lds_read_tr16(vbase + vo[db] + (16 * kg + 8) * D * 2);
+            return u32x4{lo[0], lo[1], up[0], up[1]};
+        };
+        auto mask_half = [&](f32x16& s, int kb) {
+            if (MASK) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + 32 * kb + acc_row(r, hi);
+                    if ((CAUSAL && key > q) || key >= N) s[r] = -INFINITY;
+                }
+            }
+        };
+        // probabilities of pair t (registers 2t, 2t + 1) of a half: dword
+        // t & 3 of operand t >> 2 of that half
+        auto exp_pair = [&](const f32x16& s, int t, float mu, float& ls, u32x4 (&pb)[2]) {
+            const float p0 = fast_exp2(fmaf(s[2 * t], cl2, -mu));
+            const float p1 = fast_exp2(fmaf(s[2 * t + 1], cl2, -mu));
+            ls += p0 + p1;
+            pb[t >> 2][t & 3] = Mma<T>::pack2(p0, p1);
+        };
+        // accept the half's probabilities, or move the maximum and redo them
+        auto settle = [&](const f32x16& s, float& ls, u32x4 (&pb)[2]) {
+            if (__any(!(m_s > -INFINITY && ls <= kSumCap))) {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+                const float mn = fmaxf(m_s, halves_max(mx) * cl2);
+                const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m_s - mn);
+                l_s *= alpha;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+                m_s = mn;
+                const float mu = (m_s == -INFINITY) ? 0.f : m_s;
+                ls = 0.f;
+#pragma unroll
+                for (int t = 0; t < 8; ++t) exp_pair(s, t, mu, ls, pb);
+            }
+            l_s += ls;
+        };
+
+        if constexpr (!PIPE) {
+            static_for<2>([&](auto kc) {
+                constexpr int kb = decltype(kc)::value;
+                f32x16 sc = zero16();
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) sc = Mma<T>::mma(kread(kb, ks), qf[ks], sc);
+                mask_half(sc, kb);
+                const float mu = (m_s == -INFINITY) ? 0.f : m_s;
+                u32x4 pb[2];
+                float ls = 0.f;
+#pragma unroll
+                for (int t = 0; t < 8; ++t) exp_pair(sc, t, mu, ls, pb);
+                settle(sc, ls, pb);
+#pragma unroll
+                for (int t = 0; t < 2 * NDB; ++t)
+                    o[t % NDB] = Mma<T>::mma(vread(2 * kb + t / NDB, t % NDB), pb[t / NDB], o[t % NDB]);
+            });
+            return;
+        }
+
+        const float mu = (m_s == -INFINITY) ? 0.f : m_s;
+
+        // Every LDS operand is read at least one step before its product
+        // (each step below ends in a scheduling fence): K of the first half
+        // up front, K of the second half under the first half's products, the
+        // V^T operands of each half under the step before.
+        u32x4 ka[NKS], kb2[NKS], va[2 * NDB], vb[2 * NDB];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) ka[ks] = kread(0, ks);
+
+        // scores of the first half | K reads of the second
+        f32x16 s0 = zero16(), s1 = zero16();
+        static_for<NKS>([&](auto tc) {
+            constexpr int t = decltype(tc)::value;
+            s0 = Mma<T>::mma(ka[t], qf[t], s0);
+            kb2[t] = kread(1, t);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        mask_half(s0, 0);
+
+        // scores of the second half | probabilities of the first | V^T reads
+        // of the first half
+        u32x4 pb0[2], pb1[2];
+        float ls0 = 0.f, ls1 = 0.f;
+        static_for<NKS>([&](auto tc) {
+            constexpr int t = decltype(tc)::value;
+            s1 = Mma<T>::mma(kb2[t], qf[t], s1);
+            exp_pair(s0, t, mu, ls0, pb0);
+            if (t < 2 * NDB) va[t] = vread(t / NDB, t % NDB);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        mask_half(s1, 1);
+        settle(s0, ls0, pb0);
+
+        // P V of the first half | probabilities of the second | V^T reads of
+        // the second half
+        const float mu1 = (m_s == -INFINITY) ? 0.f : m_s;
+        static_for<2 * NDB>([&](auto tc) {
+            constexpr int t = decltype(tc)::value;
+            o[t % NDB] = Mma<T>::mma(va[t], pb0[t / NDB], o[t % NDB]);
+            exp_pair(s1, t, mu1, ls1, pb1);
+            vb[t] = vread(2 + t / NDB, t % NDB);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        settle(s1, ls1, pb1);
+
+        // P V of the second half
+#pragma unroll
+        for (int t = 0; t < 2 * NDB; ++t) o[t % NDB] = Mma<T>::mma(vb[t], pb1[t / NDB], o[t % NDB]);
+    };
+
+    issue_to(smem, 0);
+    wait_vmem();
+    __syncthreads();
+
+    // The copy of the next tile is issued at the start of every tile, also the
+    // last (the extra tile lies in this head's range or past its end, reads as
+    // zeros, and lands in the buffer no later tile reads).
+    int j = 0;
+    for (; j + 1 < nfull; j += 2) {
+        issue_to(smem + STAGE, (j + 1) * BC);
+        body(j, std::false_type{}, smem);
+        wait_vmem();
+        __syncthreads();
+        issue_to(smem, (j + 2) * BC);
+        body(j + 1, std::false_type{}, smem + STAGE);
+        wait_vmem();
+        __syncthreads();
+    }
+    for (; j < ntiles; ++j) {
+        issue_to(smem + ((j + 1) & 1) * STAGE, (j + 1) * BC);
+        if (!CAUSAL || j * BC <= qw + 31) body(j, std::true_type{}, smem + (j & 1) * STAGE);
+        wait_vmem();
+        __syncthreads();
+    }
+
+    const float l_tot = l_s + swap_halves(l_s);
+    if (q < N) {
+        const float inv = 1.f / l_tot;
+        uint16_t* Orow = O + qoff + (size_t)q * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                u32x2 w;
+                w[0] = Mma<T>::pack2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
+                w[1] = Mma<T>::pack2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+                *reinterpret_cast<u32x2*>(Orow + 32 * db + 8 * g + 4 * hi) = w;
+            }
+        if (hi == 0) LSE[(size_t)(b * Hq + h) * N + q] = (m_s + __log2f(l_tot)) * kLn2;
     }
 }
 
@@ -1464,6 +1756,17 @@ hipError_t launch16v5(const FwdArgs& a) {
     return hipGetLastError();
 }
 
+template <typename T, int D, bool CAUSAL, int NW, int BC, bool PIPE>
+hipError_t launch16v6(const FwdArgs& a) {
+    constexpr int BR = 32 * NW;
+    const int nqb = (a.N + BR - 1) / BR;
+    const long long total = (long long)nqb * a.Hq * a.B;
+    hipLaunchKernelGGL((fwd16v6_kernel<T, D, CAUSAL, NW, BC, PIPE>), dim3((unsigned)total), dim3(NW * 64),
+                       0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                       (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.N, a.cl2);
+    return hipGetLastError();
+}
+
 template <typename T, int D, bool CAUSAL, int NW, int BC>
 hipError_t launch16v3(const FwdArgs& a) {
     constexpr int BR = 32 * NW;
@@ -1526,6 +1829,9 @@ hipError_t dispatch16c(const FwdArgs& a) {
             case 10: return launch16v5<T, D, CAUSAL, 8, 64>(a);
             case 11: return launch16v5<T, D, CAUSAL, 4, 64>(a);
             case 12: return launch16v2<T, D, CAUSAL, 8, 64>(a);
+            case 13: return launch16v6<T, D, CAUSAL, 4, 64, true>(a);
+            case 14: return launch16v6<T, D, CAUSAL, 8, 64, true>(a);
+            case 15: return launch16v6<T, D, CAUSAL, 4, 64, false>(a);
             default: return launch16v5<T, D, CAUSAL, 4, 64>(a);
         }
     } else {
