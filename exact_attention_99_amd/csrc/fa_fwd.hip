@@ -1799,11 +1799,14 @@ hipError_t launch32(const FwdArgs& a) {
     return hipGetLastError();
 }
 
-// Kernel / tile variants; variant 0 (the buffer-to-LDS kernel with four
-// 32-row waves, two workgroups per compute unit: the two waves that share a
-// SIMD belong to different workgroups, so their barriers do not lock their
-// matrix and softmax phases together) is the default, the others are kept
-// for tile sweeps.
+// Kernel / tile variants.  The default at d = 128 is the sixth generation
+// with eight 32-row waves (one workgroup per compute unit, two waves per
+// SIMD; the pipelined halves give each wave its own overlap of matrix and
+// vector work, and eight waves halve the copies per wave and the L2 traffic
+// per query row); dropout and block masks run on the fifth generation with
+// four waves (variant 14: two workgroups per compute unit, so the waves that
+// share a SIMD belong to different workgroups).  The others are kept for tile
+// sweeps.
 template <typename T, int D, bool CAUSAL>
 hipError_t dispatch16c(const FwdArgs& a) {
     if (a.drop) {
@@ -1830,9 +1833,9 @@ hipError_t dispatch16c(const FwdArgs& a) {
             case 11: return launch16v5<T, D, CAUSAL, 4, 64>(a);
             case 12: return launch16v2<T, D, CAUSAL, 8, 64>(a);
             case 13: return launch16v6<T, D, CAUSAL, 4, 64, true>(a);
-            case 14: return launch16v6<T, D, CAUSAL, 8, 64, true>(a);
+            case 14: return launch16v5<T, D, CAUSAL, 4, 64>(a);
             case 15: return launch16v6<T, D, CAUSAL, 4, 64, false>(a);
-            default: return launch16v5<T, D, CAUSAL, 4, 64>(a);
+            default: return launch16v6<T, D, CAUSAL, 8, 64, true>(a);
         }
     } else {
         switch (a.fwd_variant) {

@@ -182,3 +182,29 @@ def test_scale_values(scale):
     omax, _ = errs(o, O)
     lmax, _ = errs(lse, L)
     assert omax <= 2e-2 and lmax <= 1e-3 * max(1.0, scale * 20), (omax, lmax)
+
+
+@pytest.mark.parametrize("pattern", ["rising", "falling", "huge_first"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_running_max_paths(pattern, causal, d):
+    """Score patterns that drive every path of the online softmax's running
+    maximum: scores that rise along the keys (the maximum moves by more than
+    the lazy-rescale threshold in every 32-key block), scores that fall (later
+    probabilities underflow to zero against the first block's maximum), and a
+    first block whose raw scores would overflow exp2 without the maximum."""
+    N, H = 1000, 2
+    g = torch.Generator().manual_seed(7 + d)
+    q = torch.zeros(1, H, N, d)
+    q[..., 0] = 1.0
+    q[..., 1:] = 0.05 * torch.randn(1, H, N, d - 1, generator=g)
+    j = torch.arange(N, dtype=torch.float32)
+    k = 0.05 * torch.randn(1, H, N, d, generator=g)
+    k[..., 0] = {"rising": 0.5 * j, "falling": -0.5 * j, "huge_first": 300.0 - 0.5 * j}[pattern]
+    v = torch.randn(1, H, N, d, generator=g)
+    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    o, lse = fa_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal, 1.0)
+    torch.cuda.synchronize()
+    O, L = oracle.attention_forward(workloads.to_f64(q), workloads.to_f64(k), workloads.to_f64(v),
+                                    1.0, causal)
+    check_fwd(o, lse, O, L, "bf16", f"{pattern} causal={causal} d={d}")
