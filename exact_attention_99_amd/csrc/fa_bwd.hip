@@ -617,15 +617,17 @@ dkdv16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int tr_row = 4 * hi + (j16 >> 2);
     const int tr_col = 2 * (16 * (g16 & 1) + 4 * (j16 & 3));
 
-    // step s from buffer par & 1
-    auto run_step = [&](int s, int par) __attribute__((always_inline)) {
+    // step s from the buffer at base (dbase: this wave's dropout-mask area).
+    // The LDS reads go through these restrict-qualified pointers, so the
+    // compiler does not make the transposing reads wait for the copies of the
+    // next step into the other buffer.
+    auto run_step_at = [&](int s, const unsigned char* __restrict__ base, unsigned char* __restrict__ dbase)
+                           __attribute__((always_inline)) {
         int h, q0;
         step_rows(s, h, q0);
         const bool need_mask = (CAUSAL && q0 < kw + 32) || (q0 + BQ > Nk) || (kw + 32 > Nk);
-        const unsigned char* base = smem + (par & 1) * STAGE;
         const float* lse2s = reinterpret_cast<const float*>(base + OFF_LSE);
         const float* dls = reinterpret_cast<const float*>(base + OFF_DL);
-        unsigned char* dbase = smem + 2 * STAGE + wave * (BQ * 32);
         if constexpr (DROP) {
 #pragma unroll
             for (int rr = 0; rr < BQ / 64; ++rr) {
@@ -719,6 +721,10 @@ dkdv16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                     dkt[db] = Mma<T>::mma(aqt, dsb[t], dkt[db]);
                 }
         }
+    };
+    // step s from buffer par & 1
+    auto run_step = [&](int s, int par) __attribute__((always_inline)) {
+        run_step_at(s, smem + (par & 1) * STAGE, smem + 2 * STAGE + wave * (BQ * 32));
     };
 
     if constexpr (SPARSE) {
@@ -1227,10 +1233,12 @@ dq16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
     for (int db = 0; db < NDB; ++db) dq[db] = zero16();
 
-    // tile j from buffer par & 1
-    auto tile = [&](int j, int par) __attribute__((always_inline)) {
+    // tile j from the buffer at base; the LDS reads go through this
+    // restrict-qualified pointer, so the compiler does not make the
+    // transposing reads wait for the copies of the next tile into the other
+    // buffer
+    auto tile_at = [&](int j, const unsigned char* __restrict__ base) __attribute__((always_inline)) {
         const int k0 = j * BC;
-        const unsigned char* base = smem + (par & 1) * STAGE;
         const bool need_mask = (CAUSAL && k0 + BC - 1 > qw) || (k0 + BC > Nk) || (qw + 32 > Nk);
         uint32_t dm[DROP ? NKB : 1][4];
         if constexpr (DROP) {
@@ -1294,6 +1302,8 @@ dq16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             for (int kb = 0; kb < NKB; ++kb) kb_body(kb, nullptr);
         }
     };
+    // tile j from buffer par & 1
+    auto tile = [&](int j, int par) __attribute__((always_inline)) { tile_at(j, smem + (par & 1) * STAGE); };
 
     if constexpr (SPARSE) {
         const int nb = sp.nb;

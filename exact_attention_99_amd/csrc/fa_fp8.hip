@@ -321,13 +321,16 @@ fwd8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
     float l_s = 0.f;
     const float cq = cl2 * sq;
 
-    auto body = [&](int j, auto mask_tag, auto buf_tag) {
+    // Tile j from the buffer at cur.  The tile's LDS reads go through this
+    // restrict-qualified pointer, so the compiler does not make the
+    // transposing reads wait for the copies of the next tile into the other
+    // buffer.
+    auto body_at = [&](const unsigned char* __restrict__ cur, int j, auto mask_tag)
+                       __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_tag)::value;
-        constexpr int BUFC = decltype(buf_tag)::value;
         const int k0 = j * BC;
-        const uint32_t bb = BUFC >= 0 ? (uint32_t)(BUFC * STAGE) : (uint32_t)((j & 1) * STAGE);
-        const unsigned char* kbase = smem + bb;
-        const unsigned char* vbase = smem + bb + TILE;
+        const unsigned char* kbase = cur;
+        const unsigned char* vbase = cur + TILE;
 
         // exponent multiplier and value-scale offset of each 64-key half
         float c[NH], e[NH];
@@ -425,6 +428,11 @@ fwd8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
 #pragma unroll
             for (int cb = 0; cb < NDB; ++cb)
                 o[cb] = mma8(PRE ? va[PRE ? t : 0][PRE ? cb : 0] : read_v(t, cb), pb[t], o[cb]);
+    };
+    // tile j in buffer BUFC, or (BUFC < 0) in buffer j & 1
+    auto body = [&](int j, auto mask_tag, auto buf_tag) __attribute__((always_inline)) {
+        constexpr int BUFC = decltype(buf_tag)::value;
+        body_at(smem + (BUFC >= 0 ? BUFC : (j & 1)) * STAGE, j, mask_tag);
     };
 
     issue(0, 0);

@@ -96,11 +96,12 @@ fwd_split16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         wait_vmem();
     }
     __syncthreads();
-    for (int j = 0; j < ntiles; ++j) {
-        const int k0 = c0 + j * BC;
-        if (j + 1 < ntiles) issue(k0 + BC, (j + 1) & 1);
-        const unsigned char* ks_base = smem + (j & 1) * STAGE;
-        const unsigned char* vt_base = ks_base + TILE;
+    // One tile from the buffer at cur.  Its LDS reads go through this
+    // restrict-qualified pointer, so the compiler does not make the transposing
+    // reads wait for the copy of the next tile into the other buffer.
+    auto tile = [&](const unsigned char* __restrict__ cur, int k0) __attribute__((always_inline)) {
+        const unsigned char* ks_base = cur;
+        const unsigned char* vt_base = cur + TILE;
 
         f32x16 s[NKB];
 #pragma unroll
@@ -171,6 +172,11 @@ fwd_split16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                 a[0] = lo[0]; a[1] = lo[1]; a[2] = up[0]; a[3] = up[1];
                 o[db] = Mma<T>::mma(a, pb[kg], o[db]);
             }
+    };
+    for (int j = 0; j < ntiles; ++j) {
+        const int k0 = c0 + j * BC;
+        if (j + 1 < ntiles) issue(k0 + BC, (j + 1) & 1);
+        tile(smem + (j & 1) * STAGE, k0);
         wait_vmem();
         __syncthreads();
     }
