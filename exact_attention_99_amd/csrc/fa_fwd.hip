@@ -797,7 +797,8 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)
 fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
                int B, int Hq, int Hkv, int N, float cl2) {
-    static_assert(BC == 64, "two 32-key halves per tile");
+    static_assert(BC == 64 || BC == 128, "tiles of one or two 64-key sub-tiles");
+    constexpr int NSUB = BC / 64;
     constexpr int BR = 32 * NW;
     constexpr int KCH = D / 8;
     constexpr int TILE = BC * D * 2;
@@ -807,7 +808,6 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     constexpr int WI = TILE / 1024;
     static_assert(WI % NW == 0, "tile copies split evenly over the waves");
     constexpr int IPW = WI / NW;
-    static_assert(2 * STAGE <= 65536, "both buffers addressable by immediate offsets");
     static_assert(BR % BC == 0, "row blocks start on a key-tile boundary");
     constexpr float kSumCap = 256.0f;   // 2^kTau
     static_assert(kTau == 8.0f, "sum cap matches the lazy-rescale threshold");
@@ -885,13 +885,13 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     float m_s = -INFINITY;
     float l_s = 0.f;
 
-    // tile j from the buffer at cur
-    auto body = [&](int j, auto mask_tag, const unsigned char* __restrict__ cur)
+    // the 64 keys from k0 (sub-tile SUB of the tile in the buffer at cur)
+    auto body = [&](int k0, auto mask_tag, auto sub_tag, const unsigned char* __restrict__ cur)
                     __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_tag)::value;
-        const int k0 = j * BC;
-        const unsigned char* kbase = cur;
-        const unsigned char* vbase = cur + TILE;
+        constexpr int SUB = decltype(sub_tag)::value;
+        const unsigned char* kbase = cur + SUB * 64 * D * 2;
+        const unsigned char* vbase = cur + TILE + SUB * 64 * D * 2;
 
         auto kread = [&](int kb, int ks) {
             return *reinterpret_cast<const u32x4*>(kbase + ko[ks] + 32 * kb * D * 2);
@@ -1011,6 +1011,15 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         for (int t = 0; t < 2 * NDB; ++t) o[t % NDB] = Mma<T>::mma(vb[t], pb1[t / NDB], o[t % NDB]);
     };
 
+    // tile j (its 64-key sub-tiles in turn; under the mask a wave skips the
+    // sub-tiles above its rows)
+    auto tile = [&](int j, auto mask_tag, const unsigned char* cur) __attribute__((always_inline)) {
+        static_for<NSUB>([&](auto sc) {
+            const int k0 = j * BC + 64 * decltype(sc)::value;
+            if (!decltype(mask_tag)::value || !CAUSAL || k0 <= qw + 31) body(k0, mask_tag, sc, cur);
+        });
+    };
+
     issue_to(smem, 0);
     wait_vmem();
     __syncthreads();
@@ -1021,17 +1030,17 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     int j = 0;
     for (; j + 1 < nfull; j += 2) {
         issue_to(smem + STAGE, (j + 1) * BC);
-        body(j, std::false_type{}, smem);
+        tile(j, std::false_type{}, smem);
         wait_vmem();
         __syncthreads();
         issue_to(smem, (j + 2) * BC);
-        body(j + 1, std::false_type{}, smem + STAGE);
+        tile(j + 1, std::false_type{}, smem + STAGE);
         wait_vmem();
         __syncthreads();
     }
     for (; j < ntiles; ++j) {
         issue_to(smem + ((j + 1) & 1) * STAGE, (j + 1) * BC);
-        if (!CAUSAL || j * BC <= qw + 31) body(j, std::true_type{}, smem + (j & 1) * STAGE);
+        if (!CAUSAL || j * BC <= qw + 31) tile(j, std::true_type{}, smem + (j & 1) * STAGE);
         wait_vmem();
         __syncthreads();
     }
@@ -1835,6 +1844,7 @@ hipError_t dispatch16c(const FwdArgs& a) {
             case 13: return launch16v6<T, D, CAUSAL, 4, 64, true>(a);
             case 14: return launch16v5<T, D, CAUSAL, 4, 64>(a);
             case 15: return launch16v6<T, D, CAUSAL, 4, 64, false>(a);
+            case 16: return launch16v6<T, D, CAUSAL, 8, 128, true>(a);
             default: return launch16v6<T, D, CAUSAL, 8, 64, true>(a);
         }
     } else {
