@@ -798,6 +798,7 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
                int B, int Hq, int Hkv, int N, float cl2) {
     static_assert(BC == 64 || BC == 128, "tiles of one or two 64-key sub-tiles");
+    static_assert(D == 128, "the pipelined steps pair eight score products with eight P V products");
     constexpr int NSUB = BC / 64;
     constexpr int BR = 32 * NW;
     constexpr int KCH = D / 8;
