@@ -902,13 +902,15 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             const u32x2 up = lds_read_tr16(vbase + vo[db] + (16 * kg + 8) * D * 2);
             return u32x4{lo[0], lo[1], up[0], up[1]};
         };
+        // key k0 + 32 kb + acc_row(r, hi) is visible iff it is at most
+        // min(q, N - 1) (without the causal mask: N - 1), i.e. iff the
+        // register's constant part 8 (r / 4) + r % 4 is at most lim
         auto mask_half = [&](f32x16& s, int kb) {
             if (MASK) {
+                const int lim = (CAUSAL ? min(q, N - 1) : N - 1) - (k0 + 32 * kb) - 4 * hi;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + 32 * kb + acc_row(r, hi);
-                    if ((CAUSAL && key > q) || key >= N) s[r] = -INFINITY;
-                }
+                for (int r = 0; r < 16; ++r)
+                    if (8 * (r >> 2) + (r & 3) > lim) s[r] = -INFINITY;
             }
         };
         // probabilities of pair t (registers 2t, 2t + 1) of a half: dword
