@@ -1468,11 +1468,12 @@ dq16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
             for (int r = 0; r < 16; ++r) p[r] = fast_exp2(fmaf(st[r], cl2, -lse2));
             if (MASK) {
+                // key k0 + 32 kb + acc_row(r, hi) is visible iff it is at most
+                // min(q, N - 1) (N - 1 without the causal mask): one compare of
+                // the register's constant part against a per-lane limit
+                const int lim = (CAUSAL ? min(q, N - 1) : N - 1) - (k0 + 32 * kb) - 4 * hi;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int kk = k0 + 32 * kb + acc_row(r, hi);
-                    p[r] = ((!CAUSAL || kk <= q) && kk < N) ? p[r] : 0.f;
-                }
+                for (int r = 0; r < 16; ++r) p[r] = (8 * (r >> 2) + (r & 3) <= lim) ? p[r] : 0.f;
             }
             u32x4 dsb[2];
 #pragma unroll
