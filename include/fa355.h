@@ -49,7 +49,7 @@ extern "C" {
 typedef enum {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, bad flag, small workspace */
-    FA_ERR_UNSUPPORTED = 2, /* head dim or dtype this build has no kernel for */
+    FA_ERR_UNSUPPORTED = 2, /* head dim or dtype the library has no kernel for */
     FA_ERR_HIP = 3          /* the HIP runtime refused a launch */
 } fa_status;
 
