@@ -1357,13 +1357,12 @@ dq16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 // (and inside the sequence) run a body with no mask code, two at a time so
 // that both LDS buffers have compile-time offsets; the diagonal and ragged-end
 // tiles run the masked body.
-template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+template <typename T, int D, bool CAUSAL, int NW = 4>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 dq16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
               const float* __restrict__ LSE, const float* __restrict__ Delta,
               uint16_t* __restrict__ dQ, int B, int Hq, int Hkv, int N, float cl2, float scale) {
-    constexpr int NW = 4;
     constexpr int BR = 32 * NW;
     constexpr int BC = D == 128 ? 64 : 128;
     constexpr int KCH = D / 8;
@@ -1827,6 +1826,15 @@ hipError_t dq16(const BwdArgs& a) {
                            dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                            (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
                            (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale, a.dp, a.sp);
+        return hipGetLastError();
+    }
+    if (a.variant == 3) {
+        // eight-wave tiling (one workgroup per compute unit), kept for sweeps
+        const int nqb8 = (a.N + 255) / 256;
+        hipLaunchKernelGGL((dq16v3_kernel<T, D, CAUSAL, 8>), dim3((unsigned)(nqb8 * a.Hq * a.B)),
+                           dim3(512), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                           (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
+                           (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale);
         return hipGetLastError();
     }
     if (a.variant == 0) {
