@@ -320,7 +320,6 @@ dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     constexpr int TB = BC * D * 2;
     constexpr int STAGE = 3 * TB;
     constexpr int NKB = BC / 32;
-    constexpr int NKG = BC / 16;
     constexpr int NDB = D / 32;
     constexpr int NKS = D / 16;
     constexpr int ROWS = BC * KCH / 256;      // key rows staged per thread, at one chunk

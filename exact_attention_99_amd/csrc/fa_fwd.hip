@@ -798,7 +798,9 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
                int B, int Hq, int Hkv, int N, float cl2) {
     static_assert(BC == 64 || BC == 128, "tiles of one or two 64-key sub-tiles");
-    static_assert(D == 128, "the pipelined steps pair eight score products with eight P V products");
+    static_assert(D == 64 || D == 128, "head dimensions with a K tile swizzle");
+    constexpr int PPB = 8 / (D / 16);    // probability pairs per second-half score product
+    constexpr int PPC = 8 / (2 * (D / 32));  // probability pairs per first-half P V product
     constexpr int NSUB = BC / 64;
     constexpr int BR = 32 * NW;
     constexpr int KCH = D / 8;
@@ -871,12 +873,17 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int tr_row = 4 * hi + (j16 >> 2);
     const int tr_col = 2 * (16 * (g16 & 1) + 4 * (j16 & 3));
 
-    // lane parts of the LDS addresses: K rows 32 kb + l32 (the swizzle
-    // depends on row & 15 only, so both halves share them), chunk 2 ks + hi;
-    // V^T rows 16 kg + tr_row (+ 8), bytes 64 db + tr_col
-    uint32_t ko[NKS], vo[NDB];
+    // lane parts of the LDS addresses: K rows 32 kb + l32, chunk 2 ks + hi
+    // (at d = 128 the swizzle depends on row & 15 only, so both halves share
+    // them; at d = 64 it depends on row bit 5 too); V^T rows 16 kg + tr_row
+    // (+ 8), bytes 64 db + tr_col
+    constexpr int NKO = D == 128 ? 1 : 2;
+    uint32_t ko[NKO][NKS], vo[NDB];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) ko[ks] = lds_lane_off((uint32_t)kq_off<D>(l32, 2 * ks + hi));
+    for (int par = 0; par < NKO; ++par)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+            ko[par][ks] = lds_lane_off((uint32_t)kq_off<D>(32 * par + l32, 2 * ks + hi) - 32 * par * D * 2);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) vo[db] = lds_lane_off((uint32_t)vt_off<D>(tr_row, 64 * db + tr_col));
 
@@ -895,7 +902,7 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         const unsigned char* vbase = cur + TILE + SUB * 64 * D * 2;
 
         auto kread = [&](int kb, int ks) {
-            return *reinterpret_cast<const u32x4*>(kbase + ko[ks] + 32 * kb * D * 2);
+            return *reinterpret_cast<const u32x4*>(kbase + ko[NKO == 1 ? 0 : (kb & 1)][ks] + 32 * kb * D * 2);
         };
         auto vread = [&](int kg, int db) {
             const u32x2 lo = lds_read_tr16(vbase + vo[db] + 16 * kg * D * 2);
@@ -990,7 +997,8 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         static_for<NKS>([&](auto tc) {
             constexpr int t = decltype(tc)::value;
             s1 = Mma<T>::mma(kb2[t], qf[t], s1);
-            exp_pair(s0, t, mu, ls0, pb0);
+#pragma unroll
+            for (int u = 0; u < PPB; ++u) exp_pair(s0, PPB * t + u, mu, ls0, pb0);
             if (t < 2 * NDB) va[t] = vread(t / NDB, t % NDB);
             __builtin_amdgcn_sched_barrier(0);
         });
@@ -1003,7 +1011,8 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         static_for<2 * NDB>([&](auto tc) {
             constexpr int t = decltype(tc)::value;
             o[t % NDB] = Mma<T>::mma(va[t], pb0[t / NDB], o[t % NDB]);
-            exp_pair(s1, t, mu1, ls1, pb1);
+#pragma unroll
+            for (int u = 0; u < PPC; ++u) exp_pair(s1, PPC * t + u, mu1, ls1, pb1);
             vb[t] = vread(2 + t / NDB, t % NDB);
             __builtin_amdgcn_sched_barrier(0);
         });
@@ -1815,10 +1824,11 @@ hipError_t launch32(const FwdArgs& a) {
 // with eight 32-row waves (one workgroup per compute unit, two waves per
 // SIMD; the pipelined halves give each wave its own overlap of matrix and
 // vector work, and eight waves halve the copies per wave and the L2 traffic
-// per query row); dropout and block masks run on the fifth generation with
-// four waves (variant 14: two workgroups per compute unit, so the waves that
-// share a SIMD belong to different workgroups).  The others are kept for tile
-// sweeps.
+// per query row); at d = 64 it is the sixth generation with four waves and
+// 64-key tiles (three waves per SIMD fit in the registers).  Dropout and block
+// masks run on the fifth generation with four waves (variant 14 of both
+// tables: two workgroups per compute unit, so the waves that share a SIMD
+// belong to different workgroups).  The others are kept for tile sweeps.
 template <typename T, int D, bool CAUSAL>
 hipError_t dispatch16c(const FwdArgs& a) {
     if (a.drop) {
@@ -1864,7 +1874,11 @@ hipError_t dispatch16c(const FwdArgs& a) {
             case 10: return launch16v5<T, D, CAUSAL, 8, 128>(a);
             case 11: return launch16v5<T, D, CAUSAL, 4, 128>(a);
             case 12: return launch16v2<T, D, CAUSAL, 8, 128>(a);
-            default: return launch16v5<T, D, CAUSAL, 4, 128>(a);
+            case 13: return launch16v6<T, D, CAUSAL, 4, 128, true>(a);
+            case 14: return launch16v5<T, D, CAUSAL, 4, 128>(a);
+            case 15: return launch16v6<T, D, CAUSAL, 8, 64, true>(a);
+            case 16: return launch16v6<T, D, CAUSAL, 8, 128, true>(a);
+            default: return launch16v6<T, D, CAUSAL, 4, 64, true>(a);
         }
     }
 }

@@ -102,11 +102,10 @@ def test_backward_mask_is_exact():
 
 
 def test_no_dropout_matches_the_plain_forward():
-    """With p = 0 the dropout entry point computes the plain forward.  At
-    d = 128 the two run different kernel generations (their running maxima,
-    and so the rounding of the probabilities, differ), so they agree to the
-    rounding of the 16-bit probabilities and outputs, not bit for bit; at
-    d = 64 they share the kernel and agree exactly."""
+    """With p = 0 the dropout entry point computes the plain forward.  The two
+    run different kernel generations (their running maxima, and so the
+    rounding of the probabilities, differ), so they agree to the rounding of
+    the 16-bit probabilities and outputs, not bit for bit."""
     for d in (128, 64):
         q, k, v, _ = workloads.make_inputs(2, 4, 2, 500, d, "bf16", 61)
         qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
@@ -114,9 +113,6 @@ def test_no_dropout_matches_the_plain_forward():
             o0, l0 = fa_fwd(qd, kd, vd, causal, 0.09)
             o1, l1 = fa_fwd_dropout(qd, kd, vd, causal, 0.09, 0.0, 3, 4)
             torch.cuda.synchronize()
-            if d == 64:
-                assert torch.equal(o0, o1) and torch.equal(l0, l1)
-                continue
             a, b = o0.float(), o1.float()
             assert ((a - b).abs() <= 2e-3 + 2.0 ** -6 * a.abs()).all(), float((a - b).abs().max())
             assert float((l0 - l1).abs().max()) <= 1e-5
