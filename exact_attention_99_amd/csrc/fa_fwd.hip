@@ -772,6 +772,21 @@ fwd16v5_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
 }
 
+// Persistent schedule: XCD x = p % 8 owns the logical blocks that xcd_remap
+// gives it; its G / 8 workgroups (G a multiple of 8), i = p / 8, take the
+// range's k-th block in round r for k = r G/8 + (r even ? i : G/8 - 1 - i),
+// a snake that pairs long and short rows over consecutive rounds.  -1 once
+// the range is exhausted (k only grows with r).
+__device__ __forceinline__ int persist_block(int p, int G, int total, int round) {
+    constexpr int kXcd = 8;
+    const int x = p % kXcd, i = p / kXcd, gx = G / kXcd;
+    const int per = total / kXcd, rem = total % kXcd;
+    const int cnt = per + (x < rem ? 1 : 0);
+    const int start = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+    const int k = round * gx + ((round & 1) ? gx - 1 - i : i);
+    return k < cnt ? start + k : -1;
+}
+
 // Sixth-generation 16-bit forward kernel (d = 128 tiles of 64 keys): the data
 // path of the fifth generation with two changes to the softmax.
 //
@@ -792,7 +807,10 @@ fwd16v5_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 // 3. As in the fifth generation, the tile's LDS reads go through a
 //    restrict-qualified buffer pointer, so they do not wait for the copies of
 //    the next tile.
-template <typename T, int D, bool CAUSAL, int NW, int BC, bool PIPE>
+// 4. PERSIST: the grid holds one workgroup per compute unit, and each walks
+//    the row blocks persist_block() assigns it, which saves a workgroup launch
+//    per block.
+template <typename T, int D, bool CAUSAL, int NW, int BC, bool PIPE, bool PERSIST = false>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
@@ -825,252 +843,263 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
     const int nqb = (N + BR - 1) / BR;
     const int total = nqb * Hq * B;
-    const int logical = xcd_remap((int)blockIdx.x, total);
-    const int qb_raw = logical % nqb;
-    const int bh = logical / nqb;
-    const int qb = CAUSAL ? (nqb - 1 - qb_raw) : qb_raw;  // longest rows first
-    const int h = bh % Hq;
-    const int b = bh / Hq;
-    const int hk = h / (Hq / Hkv);
+    // One block per workgroup, or (PERSIST) a grid of one workgroup per compute
+    // unit that walks its blocks in rounds.
+    for (int round = 0;; ++round) {
+        int logical;
+        if constexpr (PERSIST) {
+            logical = persist_block((int)blockIdx.x, (int)gridDim.x, total, round);
+            if (logical < 0) break;
+        } else {
+            if (round > 0) break;
+            logical = xcd_remap((int)blockIdx.x, total);
+        }
+        const int qb_raw = logical % nqb;
+        const int bh = logical / nqb;
+        const int qb = CAUSAL ? (nqb - 1 - qb_raw) : qb_raw;  // longest rows first
+        const int h = bh % Hq;
+        const int b = bh / Hq;
+        const int hk = h / (Hq / Hkv);
 
-    const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
-    const size_t koff = ((size_t)b * Hkv + hk) * (size_t)N * D;
-    const uint32_t head_bytes = (uint32_t)N * D * 2;
-    const Buf Qb(Q + qoff, head_bytes), Kb(K + koff, head_bytes), Vb(V + koff, head_bytes);
+        const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
+        const size_t koff = ((size_t)b * Hkv + hk) * (size_t)N * D;
+        const uint32_t head_bytes = (uint32_t)N * D * 2;
+        const Buf Qb(Q + qoff, head_bytes), Kb(K + koff, head_bytes), Vb(V + koff, head_bytes);
 
-    const int q0 = qb * BR;
-    const int qw = q0 + 32 * wave;
-    const int q = qw + l32;
+        const int q0 = qb * BR;
+        const int qw = q0 + 32 * wave;
+        const int q = qw + l32;
 
-    u32x4 qf[NKS];
+        u32x4 qf[NKS];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qf[ks] = Qb.load16((uint32_t)(q * D + 16 * ks + 8 * hi) * 2);
+        for (int ks = 0; ks < NKS; ++ks) qf[ks] = Qb.load16((uint32_t)(q * D + 16 * ks + 8 * hi) * 2);
 
-    const int kv_len = CAUSAL ? min(N, q0 + BR) : N;
-    const int ntiles = (kv_len + BC - 1) / BC;
-    const int nfull = min(CAUSAL ? q0 / BC : ntiles, N / BC);
+        const int kv_len = CAUSAL ? min(N, q0 + BR) : N;
+        const int ntiles = (kv_len + BC - 1) / BC;
+        const int nfull = min(CAUSAL ? q0 / BC : ntiles, N / BC);
 
-    uint32_t cpk[IPW], cpv[IPW];
-#pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-        const int p = (wave + NW * i) * 64 + lane;
-        const int row = p / KCH, pc = p % KCH;
-        cpk[i] = (uint32_t)kq_off<D>(row, pc);
-        cpv[i] = (uint32_t)(row * D * 2 + 16 * (pc ^ tr_swz<D>(row)));
-    }
-    auto issue_to = [&](unsigned char* base, int k0) {
+        uint32_t cpk[IPW], cpv[IPW];
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
-            const int bi = wave + NW * i;
-            const uint32_t rowb = (uint32_t)k0 * D * 2;
-            buf_to_lds16(Kb, base + bi * 1024, rowb + cpk[i]);
-            buf_to_lds16(Vb, base + TILE + bi * 1024, rowb + cpv[i]);
+            const int p = (wave + NW * i) * 64 + lane;
+            const int row = p / KCH, pc = p % KCH;
+            cpk[i] = (uint32_t)kq_off<D>(row, pc);
+            cpv[i] = (uint32_t)(row * D * 2 + 16 * (pc ^ tr_swz<D>(row)));
         }
-    };
-
-    const int g16 = lane >> 4;
-    const int j16 = lane & 15;
-    const int tr_row = 4 * hi + (j16 >> 2);
-    const int tr_col = 2 * (16 * (g16 & 1) + 4 * (j16 & 3));
-
-    // lane parts of the LDS addresses: K rows 32 kb + l32, chunk 2 ks + hi
-    // (at d = 128 the swizzle depends on row & 15 only, so both halves share
-    // them; at d = 64 it depends on row bit 5 too); V^T rows 16 kg + tr_row
-    // (+ 8), bytes 64 db + tr_col
-    constexpr int NKO = D == 128 ? 1 : 2;
-    uint32_t ko[NKO][NKS], vo[NDB];
+        auto issue_to = [&](unsigned char* base, int k0) {
 #pragma unroll
-    for (int par = 0; par < NKO; ++par)
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-            ko[par][ks] = lds_lane_off((uint32_t)kq_off<D>(32 * par + l32, 2 * ks + hi) - 32 * par * D * 2);
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) vo[db] = lds_lane_off((uint32_t)vt_off<D>(tr_row, 64 * db + tr_col));
-
-    f32x16 o[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) o[db] = zero16();
-    float m_s = -INFINITY;
-    float l_s = 0.f;
-
-    // the 64 keys from k0 (sub-tile SUB of the tile in the buffer at cur)
-    auto body = [&](int k0, auto mask_tag, auto sub_tag, const unsigned char* __restrict__ cur)
-                    __attribute__((always_inline)) {
-        constexpr bool MASK = decltype(mask_tag)::value;
-        constexpr int SUB = decltype(sub_tag)::value;
-        const unsigned char* kbase = cur + SUB * 64 * D * 2;
-        const unsigned char* vbase = cur + TILE + SUB * 64 * D * 2;
-
-        auto kread = [&](int kb, int ks) {
-            return *reinterpret_cast<const u32x4*>(kbase + ko[NKO == 1 ? 0 : (kb & 1)][ks] + 32 * kb * D * 2);
-        };
-        auto vread = [&](int kg, int db) {
-            const u32x2 lo = lds_read_tr16(vbase + vo[db] + 16 * kg * D * 2);
-            const u32x2 up = lds_read_tr16(vbase + vo[db] + (16 * kg + 8) * D * 2);
-            return u32x4{lo[0], lo[1], up[0], up[1]};
-        };
-        // key k0 + 32 kb + acc_row(r, hi) is visible iff it is at most
-        // min(q, N - 1) (without the causal mask: N - 1), i.e. iff the
-        // register's constant part 8 (r / 4) + r % 4 is at most lim
-        auto mask_half = [&](f32x16& s, int kb) {
-            if (MASK) {
-                const int lim = (CAUSAL ? min(q, N - 1) : N - 1) - (k0 + 32 * kb) - 4 * hi;
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (8 * (r >> 2) + (r & 3) > lim) s[r] = -INFINITY;
+            for (int i = 0; i < IPW; ++i) {
+                const int bi = wave + NW * i;
+                const uint32_t rowb = (uint32_t)k0 * D * 2;
+                buf_to_lds16(Kb, base + bi * 1024, rowb + cpk[i]);
+                buf_to_lds16(Vb, base + TILE + bi * 1024, rowb + cpv[i]);
             }
         };
-        // probabilities of pair t (registers 2t, 2t + 1) of a half: dword
-        // t & 3 of operand t >> 2 of that half
-        auto exp_pair = [&](const f32x16& s, int t, float mu, float& ls, u32x4 (&pb)[2]) {
-            const float p0 = fast_exp2(fmaf(s[2 * t], cl2, -mu));
-            const float p1 = fast_exp2(fmaf(s[2 * t + 1], cl2, -mu));
-            ls += p0 + p1;
-            pb[t >> 2][t & 3] = Mma<T>::pack2(p0, p1);
-        };
-        // accept the half's probabilities, or move the maximum and redo them
-        auto settle = [&](const f32x16& s, float& ls, u32x4 (&pb)[2]) {
-            if (__any(!(m_s > -INFINITY && ls <= kSumCap))) {
-                float mx = -INFINITY;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-                const float mn = fmaxf(m_s, halves_max(mx) * cl2);
-                const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m_s - mn);
-                l_s *= alpha;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-                m_s = mn;
-                const float mu = (m_s == -INFINITY) ? 0.f : m_s;
-                ls = 0.f;
-#pragma unroll
-                for (int t = 0; t < 8; ++t) exp_pair(s, t, mu, ls, pb);
-            }
-            l_s += ls;
-        };
 
-        if constexpr (!PIPE) {
-            static_for<2>([&](auto kc) {
-                constexpr int kb = decltype(kc)::value;
-                f32x16 sc = zero16();
+        const int g16 = lane >> 4;
+        const int j16 = lane & 15;
+        const int tr_row = 4 * hi + (j16 >> 2);
+        const int tr_col = 2 * (16 * (g16 & 1) + 4 * (j16 & 3));
+
+        // lane parts of the LDS addresses: K rows 32 kb + l32, chunk 2 ks + hi
+        // (at d = 128 the swizzle depends on row & 15 only, so both halves share
+        // them; at d = 64 it depends on row bit 5 too); V^T rows 16 kg + tr_row
+        // (+ 8), bytes 64 db + tr_col
+        constexpr int NKO = D == 128 ? 1 : 2;
+        uint32_t ko[NKO][NKS], vo[NDB];
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) sc = Mma<T>::mma(kread(kb, ks), qf[ks], sc);
-                mask_half(sc, kb);
-                const float mu = (m_s == -INFINITY) ? 0.f : m_s;
-                u32x4 pb[2];
-                float ls = 0.f;
+        for (int par = 0; par < NKO; ++par)
 #pragma unroll
-                for (int t = 0; t < 8; ++t) exp_pair(sc, t, mu, ls, pb);
-                settle(sc, ls, pb);
+            for (int ks = 0; ks < NKS; ++ks)
+                ko[par][ks] = lds_lane_off((uint32_t)kq_off<D>(32 * par + l32, 2 * ks + hi) - 32 * par * D * 2);
 #pragma unroll
-                for (int t = 0; t < 2 * NDB; ++t)
-                    o[t % NDB] = Mma<T>::mma(vread(2 * kb + t / NDB, t % NDB), pb[t / NDB], o[t % NDB]);
+        for (int db = 0; db < NDB; ++db) vo[db] = lds_lane_off((uint32_t)vt_off<D>(tr_row, 64 * db + tr_col));
+
+        f32x16 o[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db] = zero16();
+        float m_s = -INFINITY;
+        float l_s = 0.f;
+
+        // the 64 keys from k0 (sub-tile SUB of the tile in the buffer at cur)
+        auto body = [&](int k0, auto mask_tag, auto sub_tag, const unsigned char* __restrict__ cur)
+                        __attribute__((always_inline)) {
+            constexpr bool MASK = decltype(mask_tag)::value;
+            constexpr int SUB = decltype(sub_tag)::value;
+            const unsigned char* kbase = cur + SUB * 64 * D * 2;
+            const unsigned char* vbase = cur + TILE + SUB * 64 * D * 2;
+
+            auto kread = [&](int kb, int ks) {
+                return *reinterpret_cast<const u32x4*>(kbase + ko[NKO == 1 ? 0 : (kb & 1)][ks] + 32 * kb * D * 2);
+            };
+            auto vread = [&](int kg, int db) {
+                const u32x2 lo = lds_read_tr16(vbase + vo[db] + 16 * kg * D * 2);
+                const u32x2 up = lds_read_tr16(vbase + vo[db] + (16 * kg + 8) * D * 2);
+                return u32x4{lo[0], lo[1], up[0], up[1]};
+            };
+            // key k0 + 32 kb + acc_row(r, hi) is visible iff it is at most
+            // min(q, N - 1) (without the causal mask: N - 1), i.e. iff the
+            // register's constant part 8 (r / 4) + r % 4 is at most lim
+            auto mask_half = [&](f32x16& s, int kb) {
+                if (MASK) {
+                    const int lim = (CAUSAL ? min(q, N - 1) : N - 1) - (k0 + 32 * kb) - 4 * hi;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (8 * (r >> 2) + (r & 3) > lim) s[r] = -INFINITY;
+                }
+            };
+            // probabilities of pair t (registers 2t, 2t + 1) of a half: dword
+            // t & 3 of operand t >> 2 of that half
+            auto exp_pair = [&](const f32x16& s, int t, float mu, float& ls, u32x4 (&pb)[2]) {
+                const float p0 = fast_exp2(fmaf(s[2 * t], cl2, -mu));
+                const float p1 = fast_exp2(fmaf(s[2 * t + 1], cl2, -mu));
+                ls += p0 + p1;
+                pb[t >> 2][t & 3] = Mma<T>::pack2(p0, p1);
+            };
+            // accept the half's probabilities, or move the maximum and redo them
+            auto settle = [&](const f32x16& s, float& ls, u32x4 (&pb)[2]) {
+                if (__any(!(m_s > -INFINITY && ls <= kSumCap))) {
+                    float mx = -INFINITY;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+                    const float mn = fmaxf(m_s, halves_max(mx) * cl2);
+                    const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m_s - mn);
+                    l_s *= alpha;
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+                    m_s = mn;
+                    const float mu = (m_s == -INFINITY) ? 0.f : m_s;
+                    ls = 0.f;
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) exp_pair(s, t, mu, ls, pb);
+                }
+                l_s += ls;
+            };
+
+            if constexpr (!PIPE) {
+                static_for<2>([&](auto kc) {
+                    constexpr int kb = decltype(kc)::value;
+                    f32x16 sc = zero16();
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks) sc = Mma<T>::mma(kread(kb, ks), qf[ks], sc);
+                    mask_half(sc, kb);
+                    const float mu = (m_s == -INFINITY) ? 0.f : m_s;
+                    u32x4 pb[2];
+                    float ls = 0.f;
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) exp_pair(sc, t, mu, ls, pb);
+                    settle(sc, ls, pb);
+#pragma unroll
+                    for (int t = 0; t < 2 * NDB; ++t)
+                        o[t % NDB] = Mma<T>::mma(vread(2 * kb + t / NDB, t % NDB), pb[t / NDB], o[t % NDB]);
+                });
+                return;
+            }
+
+            const float mu = (m_s == -INFINITY) ? 0.f : m_s;
+
+            // Every LDS operand is read at least one step before its product
+            // (each step below ends in a scheduling fence): K of the first half
+            // up front, K of the second half under the first half's products, the
+            // V^T operands of each half under the step before.
+            u32x4 ka[NKS], kb2[NKS], va[2 * NDB], vb[2 * NDB];
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) ka[ks] = kread(0, ks);
+
+            // scores of the first half | K reads of the second
+            f32x16 s0 = zero16(), s1 = zero16();
+            static_for<NKS>([&](auto tc) {
+                constexpr int t = decltype(tc)::value;
+                s0 = Mma<T>::mma(ka[t], qf[t], s0);
+                kb2[t] = kread(1, t);
+                __builtin_amdgcn_sched_barrier(0);
             });
-            return;
+            mask_half(s0, 0);
+
+            // scores of the second half | probabilities of the first | V^T reads
+            // of the first half
+            u32x4 pb0[2], pb1[2];
+            float ls0 = 0.f, ls1 = 0.f;
+            static_for<NKS>([&](auto tc) {
+                constexpr int t = decltype(tc)::value;
+                s1 = Mma<T>::mma(kb2[t], qf[t], s1);
+#pragma unroll
+                for (int u = 0; u < PPB; ++u) exp_pair(s0, PPB * t + u, mu, ls0, pb0);
+                if (t < 2 * NDB) va[t] = vread(t / NDB, t % NDB);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            mask_half(s1, 1);
+            settle(s0, ls0, pb0);
+
+            // P V of the first half | probabilities of the second | V^T reads of
+            // the second half
+            const float mu1 = (m_s == -INFINITY) ? 0.f : m_s;
+            static_for<2 * NDB>([&](auto tc) {
+                constexpr int t = decltype(tc)::value;
+                o[t % NDB] = Mma<T>::mma(va[t], pb0[t / NDB], o[t % NDB]);
+#pragma unroll
+                for (int u = 0; u < PPC; ++u) exp_pair(s1, PPC * t + u, mu1, ls1, pb1);
+                vb[t] = vread(2 + t / NDB, t % NDB);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            settle(s1, ls1, pb1);
+
+            // P V of the second half
+#pragma unroll
+            for (int t = 0; t < 2 * NDB; ++t) o[t % NDB] = Mma<T>::mma(vb[t], pb1[t / NDB], o[t % NDB]);
+        };
+
+        // tile j (its 64-key sub-tiles in turn; under the mask a wave skips the
+        // sub-tiles above its rows)
+        auto tile = [&](int j, auto mask_tag, const unsigned char* cur) __attribute__((always_inline)) {
+            static_for<NSUB>([&](auto sc) {
+                const int k0 = j * BC + 64 * decltype(sc)::value;
+                if (!decltype(mask_tag)::value || !CAUSAL || k0 <= qw + 31) body(k0, mask_tag, sc, cur);
+            });
+        };
+
+        issue_to(smem, 0);
+        wait_vmem();
+        __syncthreads();
+
+        // The copy of the next tile is issued at the start of every tile, also the
+        // last (the extra tile lies in this head's range or past its end, reads as
+        // zeros, and lands in the buffer no later tile reads).
+        int j = 0;
+        for (; j + 1 < nfull; j += 2) {
+            issue_to(smem + STAGE, (j + 1) * BC);
+            tile(j, std::false_type{}, smem);
+            wait_vmem();
+            __syncthreads();
+            issue_to(smem, (j + 2) * BC);
+            tile(j + 1, std::false_type{}, smem + STAGE);
+            wait_vmem();
+            __syncthreads();
+        }
+        for (; j < ntiles; ++j) {
+            issue_to(smem + ((j + 1) & 1) * STAGE, (j + 1) * BC);
+            if (!CAUSAL || j * BC <= qw + 31) tile(j, std::true_type{}, smem + (j & 1) * STAGE);
+            wait_vmem();
+            __syncthreads();
         }
 
-        const float mu = (m_s == -INFINITY) ? 0.f : m_s;
-
-        // Every LDS operand is read at least one step before its product
-        // (each step below ends in a scheduling fence): K of the first half
-        // up front, K of the second half under the first half's products, the
-        // V^T operands of each half under the step before.
-        u32x4 ka[NKS], kb2[NKS], va[2 * NDB], vb[2 * NDB];
+        const float l_tot = l_s + swap_halves(l_s);
+        if (q < N) {
+            const float inv = 1.f / l_tot;
+            uint16_t* Orow = O + qoff + (size_t)q * D;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) ka[ks] = kread(0, ks);
-
-        // scores of the first half | K reads of the second
-        f32x16 s0 = zero16(), s1 = zero16();
-        static_for<NKS>([&](auto tc) {
-            constexpr int t = decltype(tc)::value;
-            s0 = Mma<T>::mma(ka[t], qf[t], s0);
-            kb2[t] = kread(1, t);
-            __builtin_amdgcn_sched_barrier(0);
-        });
-        mask_half(s0, 0);
-
-        // scores of the second half | probabilities of the first | V^T reads
-        // of the first half
-        u32x4 pb0[2], pb1[2];
-        float ls0 = 0.f, ls1 = 0.f;
-        static_for<NKS>([&](auto tc) {
-            constexpr int t = decltype(tc)::value;
-            s1 = Mma<T>::mma(kb2[t], qf[t], s1);
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int u = 0; u < PPB; ++u) exp_pair(s0, PPB * t + u, mu, ls0, pb0);
-            if (t < 2 * NDB) va[t] = vread(t / NDB, t % NDB);
-            __builtin_amdgcn_sched_barrier(0);
-        });
-        mask_half(s1, 1);
-        settle(s0, ls0, pb0);
-
-        // P V of the first half | probabilities of the second | V^T reads of
-        // the second half
-        const float mu1 = (m_s == -INFINITY) ? 0.f : m_s;
-        static_for<2 * NDB>([&](auto tc) {
-            constexpr int t = decltype(tc)::value;
-            o[t % NDB] = Mma<T>::mma(va[t], pb0[t / NDB], o[t % NDB]);
-#pragma unroll
-            for (int u = 0; u < PPC; ++u) exp_pair(s1, PPC * t + u, mu1, ls1, pb1);
-            vb[t] = vread(2 + t / NDB, t % NDB);
-            __builtin_amdgcn_sched_barrier(0);
-        });
-        settle(s1, ls1, pb1);
-
-        // P V of the second half
-#pragma unroll
-        for (int t = 0; t < 2 * NDB; ++t) o[t % NDB] = Mma<T>::mma(vb[t], pb1[t / NDB], o[t % NDB]);
-    };
-
-    // tile j (its 64-key sub-tiles in turn; under the mask a wave skips the
-    // sub-tiles above its rows)
-    auto tile = [&](int j, auto mask_tag, const unsigned char* cur) __attribute__((always_inline)) {
-        static_for<NSUB>([&](auto sc) {
-            const int k0 = j * BC + 64 * decltype(sc)::value;
-            if (!decltype(mask_tag)::value || !CAUSAL || k0 <= qw + 31) body(k0, mask_tag, sc, cur);
-        });
-    };
-
-    issue_to(smem, 0);
-    wait_vmem();
-    __syncthreads();
-
-    // The copy of the next tile is issued at the start of every tile, also the
-    // last (the extra tile lies in this head's range or past its end, reads as
-    // zeros, and lands in the buffer no later tile reads).
-    int j = 0;
-    for (; j + 1 < nfull; j += 2) {
-        issue_to(smem + STAGE, (j + 1) * BC);
-        tile(j, std::false_type{}, smem);
-        wait_vmem();
-        __syncthreads();
-        issue_to(smem, (j + 2) * BC);
-        tile(j + 1, std::false_type{}, smem + STAGE);
-        wait_vmem();
-        __syncthreads();
-    }
-    for (; j < ntiles; ++j) {
-        issue_to(smem + ((j + 1) & 1) * STAGE, (j + 1) * BC);
-        if (!CAUSAL || j * BC <= qw + 31) tile(j, std::true_type{}, smem + (j & 1) * STAGE);
-        wait_vmem();
-        __syncthreads();
-    }
-
-    const float l_tot = l_s + swap_halves(l_s);
-    if (q < N) {
-        const float inv = 1.f / l_tot;
-        uint16_t* Orow = O + qoff + (size_t)q * D;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                u32x2 w;
-                w[0] = Mma<T>::pack2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
-                w[1] = Mma<T>::pack2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-                *reinterpret_cast<u32x2*>(Orow + 32 * db + 8 * g + 4 * hi) = w;
-            }
-        if (hi == 0) LSE[(size_t)(b * Hq + h) * N + q] = (m_s + __log2f(l_tot)) * kLn2;
+                for (int g = 0; g < 4; ++g) {
+                    u32x2 w;
+                    w[0] = Mma<T>::pack2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
+                    w[1] = Mma<T>::pack2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+                    *reinterpret_cast<u32x2*>(Orow + 32 * db + 8 * g + 4 * hi) = w;
+                }
+            if (hi == 0) LSE[(size_t)(b * Hq + h) * N + q] = (m_s + __log2f(l_tot)) * kLn2;
+        }
     }
 }
 
@@ -1777,14 +1806,34 @@ hipError_t launch16v5(const FwdArgs& a) {
     return hipGetLastError();
 }
 
-template <typename T, int D, bool CAUSAL, int NW, int BC, bool PIPE>
+// Workgroups in a persistent grid of one workgroup per compute unit of the
+// current device, rounded down to a multiple of the 8 XCDs (0 if unknown).
+int persistent_grid() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    static int cus[64];   // per device; a racing first call stores the same value
+    if (cus[dev] == 0) {
+        int n = 0;
+        cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0
+                       ? n : -1;
+    }
+    return cus[dev] > 0 ? cus[dev] / 8 * 8 : 0;
+}
+
+template <typename T, int D, bool CAUSAL, int NW, int BC, bool PIPE, bool PERSIST = false>
 hipError_t launch16v6(const FwdArgs& a) {
     constexpr int BR = 32 * NW;
     const int nqb = (a.N + BR - 1) / BR;
     const long long total = (long long)nqb * a.Hq * a.B;
-    hipLaunchKernelGGL((fwd16v6_kernel<T, D, CAUSAL, NW, BC, PIPE>), dim3((unsigned)total), dim3(NW * 64),
-                       0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                       (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.N, a.cl2);
+    const int grid = PERSIST ? persistent_grid() : 0;
+    if (grid >= 8 && total > grid)
+        hipLaunchKernelGGL((fwd16v6_kernel<T, D, CAUSAL, NW, BC, PIPE, true>), dim3((unsigned)grid),
+                           dim3(NW * 64), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                           (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.N, a.cl2);
+    else
+        hipLaunchKernelGGL((fwd16v6_kernel<T, D, CAUSAL, NW, BC, PIPE>), dim3((unsigned)total), dim3(NW * 64),
+                           0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                           (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.N, a.cl2);
     return hipGetLastError();
 }
 
@@ -1858,7 +1907,8 @@ hipError_t dispatch16c(const FwdArgs& a) {
             case 14: return launch16v5<T, D, CAUSAL, 4, 64>(a);
             case 15: return launch16v6<T, D, CAUSAL, 4, 64, false>(a);
             case 16: return launch16v6<T, D, CAUSAL, 8, 128, true>(a);
-            default: return launch16v6<T, D, CAUSAL, 8, 64, true>(a);
+            case 17: return launch16v6<T, D, CAUSAL, 8, 64, true>(a);
+            default: return launch16v6<T, D, CAUSAL, 8, 64, true, true>(a);
         }
     } else {
         switch (a.fwd_variant) {
