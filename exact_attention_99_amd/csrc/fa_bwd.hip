@@ -823,7 +823,7 @@ __host__ __device__ constexpr int dkdv_seg_block(int seg) {
 // as zeros (Q, dO, the logsumexp and D row terms alike), which makes their
 // P * (dP - D) and P^T dO contributions exactly zero, and keys past N are never
 // written back, so only the causal condition needs a mask.
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool PERSIST = false>
 __global__ void __launch_bounds__(256)
 dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -863,268 +863,280 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
     const int nkb = (N + BKV - 1) / BKV;
     const int total = nkb * Hkv * B;
-    const int logical = xcd_remap((int)blockIdx.x, total);
-    const int jb = logical % nkb;
-    const int bhk = logical / nkb;
-    const int hk = bhk % Hkv;
-    const int b = bhk / Hkv;
-    const int G = Hq / Hkv;
-
-    const int kv0 = jb * BKV;
-    const int kw = kv0 + 32 * wave;
-    const int key = kw + l32;
-    const size_t kvoff = ((size_t)b * Hkv + hk) * (size_t)N * D;
-    const uint32_t head_bytes = (uint32_t)N * D * 2;
-
-    u32x4 kf[NKS], vf[NKS];
-    {
-        const Buf Kb(K + kvoff, head_bytes), Vb(V + kvoff, head_bytes);
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            kf[ks] = Kb.load16((uint32_t)(key * D + 16 * ks + 8 * hi) * 2);
-            vf[ks] = Vb.load16((uint32_t)(key * D + 16 * ks + 8 * hi) * 2);
-        }
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            // keep the B operands in the accumulation registers, leaving the
-            // vector registers to the pipeline
-            asm volatile("" : "+a"(kf[ks]));
-            asm volatile("" : "+a"(vf[ks]));
-        }
-    }
-
-    f32x16 dkt[NDB], dvt[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-        dkt[db] = zero16();
-        dvt[db] = zero16();
-    }
-
-    const int qb_first = CAUSAL ? kv0 / BQ : 0;
-    const int qb_count = (N + BQ - 1) / BQ - qb_first;
-    const int nsteps = G * qb_count;
-
-    uint32_t cp[IPW];
-#pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-        const int p = (wave + NW * i) * 64 + lane;
-        const int row = p / KCH, pc = p % KCH;
-        cp[i] = (uint32_t)(row * D * 2 + 16 * (pc ^ dual_swz<D>(row)));
-    }
-    float sl = 0.f, sd = 0.f;
-
-    // Tile order: under a causal mask the G diagonal tiles (the first query
-    // tile of each head, the only ones that need the mask) come first, then
-    // the remaining tiles head by head.
-    const int ndiag = CAUSAL ? G : 0;
-    const int nrest = qb_count - (CAUSAL ? 1 : 0);
-    auto step_rows = [&](int s, int& h, int& q0) {
-        if (CAUSAL && s < ndiag) {
-            h = hk * G + s;
-            q0 = qb_first * BQ;
+    // One key block per workgroup, or (PERSIST) a grid of one workgroup per
+    // compute unit that walks its key blocks in rounds.
+    for (int round = 0;; ++round) {
+        int logical;
+        if constexpr (PERSIST) {
+            logical = persist_block((int)blockIdx.x, (int)gridDim.x, total, round);
+            if (logical < 0) break;
         } else {
-            const int m = s - ndiag;
-            h = hk * G + m / nrest;
-            q0 = (qb_first + (CAUSAL ? 1 : 0) + m % nrest) * BQ;
+            if (round > 0) break;
+            logical = xcd_remap((int)blockIdx.x, total);
         }
-    };
-    // LDS buffer of tile s: the last diagonal tile uses buffer 1, so that the
-    // remaining tiles alternate 0, 1, 0, ... from their first one
-    auto buf_of = [&](int s) { return (s < ndiag ? ndiag - s : s - ndiag) & 1; };
-    auto issue = [&](int s, int buf) {
-        int h, q0;
-        step_rows(s, h, q0);
-        const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
-        const Buf Qb(Q + qoff, head_bytes), Db(dO + qoff, head_bytes);
-        unsigned char* base = smem + buf * STAGE;
+        const int jb = logical % nkb;
+        const int bhk = logical / nkb;
+        const int hk = bhk % Hkv;
+        const int b = bhk / Hkv;
+        const int G = Hq / Hkv;
+
+        const int kv0 = jb * BKV;
+        const int kw = kv0 + 32 * wave;
+        const int key = kw + l32;
+        const size_t kvoff = ((size_t)b * Hkv + hk) * (size_t)N * D;
+        const uint32_t head_bytes = (uint32_t)N * D * 2;
+
+        u32x4 kf[NKS], vf[NKS];
+        {
+            const Buf Kb(K + kvoff, head_bytes), Vb(V + kvoff, head_bytes);
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                kf[ks] = Kb.load16((uint32_t)(key * D + 16 * ks + 8 * hi) * 2);
+                vf[ks] = Vb.load16((uint32_t)(key * D + 16 * ks + 8 * hi) * 2);
+            }
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                // keep the B operands in the accumulation registers, leaving the
+                // vector registers to the pipeline
+                asm volatile("" : "+a"(kf[ks]));
+                asm volatile("" : "+a"(vf[ks]));
+            }
+        }
+
+        f32x16 dkt[NDB], dvt[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            dkt[db] = zero16();
+            dvt[db] = zero16();
+        }
+
+        const int qb_first = CAUSAL ? kv0 / BQ : 0;
+        const int qb_count = (N + BQ - 1) / BQ - qb_first;
+        const int nsteps = G * qb_count;
+
+        uint32_t cp[IPW];
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
-            const uint32_t off = (uint32_t)q0 * D * 2 + cp[i];
-            buf_to_lds16(Qb, base + (wave + NW * i) * 1024, off);
-            buf_to_lds16(Db, base + OFF_DOS + (wave + NW * i) * 1024, off);
+            const int p = (wave + NW * i) * 64 + lane;
+            const int row = p / KCH, pc = p % KCH;
+            cp[i] = (uint32_t)(row * D * 2 + 16 * (pc ^ dual_swz<D>(row)));
         }
-        const size_t roff = ((size_t)b * Hq + h) * (size_t)N;
-        if (tid < BQ) {
-            // scaled to base 2 when it is published (a use here would make the
-            // wave wait for the tile copies issued just before)
-            sl = Buf(LSE + roff, (uint32_t)N * 4).load_f32((uint32_t)(q0 + tid) * 4);
-            sd = Buf(Delta + roff, (uint32_t)N * 4).load_f32((uint32_t)(q0 + tid) * 4);
-        }
-    };
-    auto put_rows = [&](int buf) {
-        unsigned char* base = smem + buf * STAGE;
-        if (tid < BQ) {
-            reinterpret_cast<float*>(base + OFF_LSE)[tid] = sl * kLog2e;
-            reinterpret_cast<float*>(base + OFF_DL)[tid] = sd;
-        }
-    };
+        float sl = 0.f, sd = 0.f;
 
-    const int g16 = lane >> 4;
-    const int j16 = lane & 15;
-    const int tr_row = 4 * hi + (j16 >> 2);
-    const int tr_col = 2 * (16 * (g16 & 1) + 4 * (j16 & 3));
+        // Tile order: under a causal mask the G diagonal tiles (the first query
+        // tile of each head, the only ones that need the mask) come first, then
+        // the remaining tiles head by head.
+        const int ndiag = CAUSAL ? G : 0;
+        const int nrest = qb_count - (CAUSAL ? 1 : 0);
+        auto step_rows = [&](int s, int& h, int& q0) {
+            if (CAUSAL && s < ndiag) {
+                h = hk * G + s;
+                q0 = qb_first * BQ;
+            } else {
+                const int m = s - ndiag;
+                h = hk * G + m / nrest;
+                q0 = (qb_first + (CAUSAL ? 1 : 0) + m % nrest) * BQ;
+            }
+        };
+        // LDS buffer of tile s: the last diagonal tile uses buffer 1, so that the
+        // remaining tiles alternate 0, 1, 0, ... from their first one
+        auto buf_of = [&](int s) { return (s < ndiag ? ndiag - s : s - ndiag) & 1; };
+        auto issue = [&](int s, int buf) {
+            int h, q0;
+            step_rows(s, h, q0);
+            const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
+            const Buf Qb(Q + qoff, head_bytes), Db(dO + qoff, head_bytes);
+            unsigned char* base = smem + buf * STAGE;
+#pragma unroll
+            for (int i = 0; i < IPW; ++i) {
+                const uint32_t off = (uint32_t)q0 * D * 2 + cp[i];
+                buf_to_lds16(Qb, base + (wave + NW * i) * 1024, off);
+                buf_to_lds16(Db, base + OFF_DOS + (wave + NW * i) * 1024, off);
+            }
+            const size_t roff = ((size_t)b * Hq + h) * (size_t)N;
+            if (tid < BQ) {
+                // scaled to base 2 when it is published (a use here would make the
+                // wave wait for the tile copies issued just before)
+                sl = Buf(LSE + roff, (uint32_t)N * 4).load_f32((uint32_t)(q0 + tid) * 4);
+                sd = Buf(Delta + roff, (uint32_t)N * 4).load_f32((uint32_t)(q0 + tid) * 4);
+            }
+        };
+        auto put_rows = [&](int buf) {
+            unsigned char* base = smem + buf * STAGE;
+            if (tid < BQ) {
+                reinterpret_cast<float*>(base + OFF_LSE)[tid] = sl * kLog2e;
+                reinterpret_cast<float*>(base + OFF_DL)[tid] = sd;
+            }
+        };
 
-    // Segment seg of a tile: 0 and odd segments before the last hold the S/dP
-    // products of block (seg + 1) / 2; the others the dV/dK products of block
-    // seg / 2 - 1, and the last one those of block NQB - 1.
-    // mlim: element (block blk, row offset o) of this lane is visible when
-    // 32 blk + o >= mlim (causal: the query row is at or after the key)
-    // rt_base: the tile's buffer.  Every LDS read of the step goes through
-    // this restrict-qualified pointer, so the transposing reads carry alias
-    // information and the compiler does not make them wait for the copies of
-    // the next step into the other buffer.
-    // (The buffer is a run-time argument of the step, not a template one: a
-    // step specialised on a constant buffer would lose that information.)
-    auto run_step = [&](auto mask_tag, const unsigned char* __restrict__ rt_base, int mlim)
-                        __attribute__((always_inline)) {
-        constexpr bool MASK = decltype(mask_tag)::value;
-        // The lane-dependent parts of every LDS address, with the buffer's base
-        // folded in, are formed once per tile; each read then adds only an
-        // immediate (block, half and tensor offsets), which stays within the
-        // 16-bit offset field of the LDS instructions (the buffer base is a
-        // constant once the step is inlined into the unmasked loop).
-        const uint32_t bb = (uint32_t)(rt_base - smem);
-        uint32_t ao[NKS], to[2][NDB];
+        const int g16 = lane >> 4;
+        const int j16 = lane & 15;
+        const int tr_row = 4 * hi + (j16 >> 2);
+        const int tr_col = 2 * (16 * (g16 & 1) + 4 * (j16 & 3));
+
+        // Segment seg of a tile: 0 and odd segments before the last hold the S/dP
+        // products of block (seg + 1) / 2; the others the dV/dK products of block
+        // seg / 2 - 1, and the last one those of block NQB - 1.
+        // mlim: element (block blk, row offset o) of this lane is visible when
+        // 32 blk + o >= mlim (causal: the query row is at or after the key)
+        // rt_base: the tile's buffer.  Every LDS read of the step goes through
+        // this restrict-qualified pointer, so the transposing reads carry alias
+        // information and the compiler does not make them wait for the copies of
+        // the next step into the other buffer.
+        // (The buffer is a run-time argument of the step, not a template one: a
+        // step specialised on a constant buffer would lose that information.)
+        auto run_step = [&](auto mask_tag, const unsigned char* __restrict__ rt_base, int mlim)
+                            __attribute__((always_inline)) {
+            constexpr bool MASK = decltype(mask_tag)::value;
+            // The lane-dependent parts of every LDS address, with the buffer's base
+            // folded in, are formed once per tile; each read then adds only an
+            // immediate (block, half and tensor offsets), which stays within the
+            // 16-bit offset field of the LDS instructions (the buffer base is a
+            // constant once the step is inlined into the unmasked loop).
+            const uint32_t bb = (uint32_t)(rt_base - smem);
+            uint32_t ao[NKS], to[2][NDB];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) ao[ks] = lds_lane_off(bb + dual_off<D>(l32, 16 * (2 * ks + hi)));
+            for (int ks = 0; ks < NKS; ++ks) ao[ks] = lds_lane_off(bb + dual_off<D>(l32, 16 * (2 * ks + hi)));
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    to[u][db] = lds_lane_off(bb + dual_off<D>(8 * u + tr_row, 64 * db + tr_col));
+            const uint32_t ro = lds_lane_off(bb + OFF_LSE + 16 * hi);
+
+            u32x4 op[TSLOT];
+            f32x16 sacc = zero16(), dpacc = zero16();
+            u32x4 pb[2][2], dsb[2][2];
+            f32x4 lc[4], dc[4];
+
+            auto load_op = [&](auto nc) {
+                constexpr int n = decltype(nc)::value;
+                constexpr int seg = n / NSLOT, j = n % NSLOT;
+                constexpr int blk = dkdv_seg_block<NQB>(seg);
+                if constexpr (dkdv_seg_is_s<NQB>(seg)) {
+                    constexpr int ks = j >> 1;
+                    constexpr int imm = ((j & 1) ? OFF_DOS : 0) + 32 * blk * D * 2;
+                    op[n] = *reinterpret_cast<const u32x4*>(rt_base + (ao[ks] - bb) + imm);
+                } else {
+                    constexpr int t = j / (2 * NDB), db = (j >> 1) % NDB;
+                    constexpr int imm = ((j & 1) ? 0 : OFF_DOS) + (32 * blk + 16 * t) * D * 2;
+                    const u32x2 lo = lds_read_tr16(rt_base + (to[0][db] - bb) + imm);
+                    const u32x2 up = lds_read_tr16(rt_base + (to[1][db] - bb) + imm);
+                    op[n] = u32x4{lo[0], lo[1], up[0], up[1]};
+                }
+            };
+            auto load_rows = [&](int blk, int k) {
+                const int g = k >> 1;
+                const int imm = 4 * (32 * blk + 8 * g);
+                if (k & 1)
+                    dc[g] = *reinterpret_cast<const f32x4*>(rt_base + (ro - bb) + (OFF_DL - OFF_LSE) + imm);
+                else
+                    lc[g] = *reinterpret_cast<const f32x4*>(rt_base + (ro - bb) + imm);
+            };
+            // softmax and dS of element r of block blk (row 32 blk + acc_row(r, hi))
+            float pv[16], dsv[16];
+            auto soft = [&](int blk, int r) {
+                const int g = r >> 2, i = r & 3;
+                float p = fast_exp2(fmaf(sacc[r], cl2, -lc[g][i]));
+                if (MASK) p = (32 * blk + 8 * g + i >= mlim) ? p : 0.f;
+                pv[r] = p;
+                dsv[r] = p * (dpacc[r] - dc[g][i]);
+                if (r & 1) {
+                    const int par = blk & 1;
+                    pb[par][r >> 3][(r & 7) >> 1] = Mma<T>::pack2(pv[r - 1], pv[r]);
+                    dsb[par][r >> 3][(r & 7) >> 1] = Mma<T>::pack2(dsv[r - 1], dsv[r]);
+                }
+            };
+
+#pragma unroll
+            for (int k = 0; k < 8; ++k) load_rows(0, k);
+            static_for<AHEAD>([&](auto nc) { load_op(nc); });
+            static_for<TSLOT>([&](auto nc) {
+                constexpr int n = decltype(nc)::value;
+                constexpr int seg = n / NSLOT, j = n % NSLOT;
+                constexpr bool is_s = dkdv_seg_is_s<NQB>(seg);
+                constexpr int blk = dkdv_seg_block<NQB>(seg);
+                if constexpr (n == NSLOT) {
+                    // block 0's softmax has no matrix work to overlap with
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) soft(0, r);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if constexpr (n + AHEAD < TSLOT) load_op(std::integral_constant<int, n + AHEAD>{});
+                if constexpr (is_s) {
+                    constexpr int ks = j >> 1;
+                    if constexpr (j & 1)
+                        dpacc = Mma<T>::mma(op[n], vf[ks], ks == 0 ? zero16() : dpacc);
+                    else
+                        sacc = Mma<T>::mma(op[n], kf[ks], ks == 0 ? zero16() : sacc);
+                    // the softmax reads S and dP with vector instructions
+                    if constexpr (j == NSLOT - 2) asm volatile("" : "+v"(sacc));
+                    if constexpr (j == NSLOT - 1) asm volatile("" : "+v"(dpacc));
+                } else {
+                    constexpr int t = j / (2 * NDB), db = (j >> 1) % NDB;
+                    constexpr int par = blk & 1;
+                    if constexpr (j & 1)
+                        dkt[db] = Mma<T>::mma(op[n], dsb[par][t], dkt[db]);
+                    else
+                        dvt[db] = Mma<T>::mma(op[n], pb[par][t], dvt[db]);
+                }
+                if constexpr (!is_s && seg < NSEG - 1) {
+                    // a dV/dK segment of block seg/2 - 1 carries the softmax of block seg/2
+#pragma unroll
+                    for (int e = 0; e < EPS; ++e) soft(seg / 2, j * EPS + e);
+                } else if constexpr (is_s && seg > 0 && j >= NSLOT - 8) {
+                    // row terms of the block whose S/dP this segment computes
+                    load_rows(blk, j - (NSLOT - 8));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        };
+
+        if (nsteps > 0) {
+            issue(0, buf_of(0));
+            put_rows(buf_of(0));
+            wait_vmem();
+        }
+        __syncthreads();
+
+        // one tile: prefetch the next one into the other buffer, compute, publish
+        auto tile = [&](int s, auto mask_tag, auto buf_tag) __attribute__((always_inline)) {
+            constexpr int BUFC = decltype(buf_tag)::value;
+            const int nb = buf_of(s) ^ 1;
+            issue(min(s + 1, nsteps - 1), nb);
+            int h, q0;
+            step_rows(s, h, q0);
+            (void)h;
+            // rows q0 + 4 hi + (32 blk + 8 g + i) are visible when at or after the key
+            run_step(mask_tag, smem + (BUFC >= 0 ? BUFC : buf_of(s)) * STAGE, key - q0 - 4 * hi);
+            put_rows(nb);
+            wait_vmem();
+            __syncthreads();
+        };
+        for (int s = 0; s < ndiag; ++s)
+            tile(s, std::true_type{}, std::integral_constant<int, -1>{});
+        for (int s = ndiag; s < nsteps; s += 2) {
+            tile(s, std::false_type{}, std::integral_constant<int, 0>{});
+            if (s + 1 < nsteps) tile(s + 1, std::false_type{}, std::integral_constant<int, 1>{});
+        }
+
+        if (key < N) {
+            uint16_t* dkrow = dK + kvoff + (size_t)key * D;
+            uint16_t* dvrow = dV + kvoff + (size_t)key * D;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
-                to[u][db] = lds_lane_off(bb + dual_off<D>(8 * u + tr_row, 64 * db + tr_col));
-        const uint32_t ro = lds_lane_off(bb + OFF_LSE + 16 * hi);
-
-        u32x4 op[TSLOT];
-        f32x16 sacc = zero16(), dpacc = zero16();
-        u32x4 pb[2][2], dsb[2][2];
-        f32x4 lc[4], dc[4];
-
-        auto load_op = [&](auto nc) {
-            constexpr int n = decltype(nc)::value;
-            constexpr int seg = n / NSLOT, j = n % NSLOT;
-            constexpr int blk = dkdv_seg_block<NQB>(seg);
-            if constexpr (dkdv_seg_is_s<NQB>(seg)) {
-                constexpr int ks = j >> 1;
-                constexpr int imm = ((j & 1) ? OFF_DOS : 0) + 32 * blk * D * 2;
-                op[n] = *reinterpret_cast<const u32x4*>(rt_base + (ao[ks] - bb) + imm);
-            } else {
-                constexpr int t = j / (2 * NDB), db = (j >> 1) % NDB;
-                constexpr int imm = ((j & 1) ? 0 : OFF_DOS) + (32 * blk + 16 * t) * D * 2;
-                const u32x2 lo = lds_read_tr16(rt_base + (to[0][db] - bb) + imm);
-                const u32x2 up = lds_read_tr16(rt_base + (to[1][db] - bb) + imm);
-                op[n] = u32x4{lo[0], lo[1], up[0], up[1]};
-            }
-        };
-        auto load_rows = [&](int blk, int k) {
-            const int g = k >> 1;
-            const int imm = 4 * (32 * blk + 8 * g);
-            if (k & 1)
-                dc[g] = *reinterpret_cast<const f32x4*>(rt_base + (ro - bb) + (OFF_DL - OFF_LSE) + imm);
-            else
-                lc[g] = *reinterpret_cast<const f32x4*>(rt_base + (ro - bb) + imm);
-        };
-        // softmax and dS of element r of block blk (row 32 blk + acc_row(r, hi))
-        float pv[16], dsv[16];
-        auto soft = [&](int blk, int r) {
-            const int g = r >> 2, i = r & 3;
-            float p = fast_exp2(fmaf(sacc[r], cl2, -lc[g][i]));
-            if (MASK) p = (32 * blk + 8 * g + i >= mlim) ? p : 0.f;
-            pv[r] = p;
-            dsv[r] = p * (dpacc[r] - dc[g][i]);
-            if (r & 1) {
-                const int par = blk & 1;
-                pb[par][r >> 3][(r & 7) >> 1] = Mma<T>::pack2(pv[r - 1], pv[r]);
-                dsb[par][r >> 3][(r & 7) >> 1] = Mma<T>::pack2(dsv[r - 1], dsv[r]);
-            }
-        };
-
 #pragma unroll
-        for (int k = 0; k < 8; ++k) load_rows(0, k);
-        static_for<AHEAD>([&](auto nc) { load_op(nc); });
-        static_for<TSLOT>([&](auto nc) {
-            constexpr int n = decltype(nc)::value;
-            constexpr int seg = n / NSLOT, j = n % NSLOT;
-            constexpr bool is_s = dkdv_seg_is_s<NQB>(seg);
-            constexpr int blk = dkdv_seg_block<NQB>(seg);
-            if constexpr (n == NSLOT) {
-                // block 0's softmax has no matrix work to overlap with
-#pragma unroll
-                for (int r = 0; r < 16; ++r) soft(0, r);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            if constexpr (n + AHEAD < TSLOT) load_op(std::integral_constant<int, n + AHEAD>{});
-            if constexpr (is_s) {
-                constexpr int ks = j >> 1;
-                if constexpr (j & 1)
-                    dpacc = Mma<T>::mma(op[n], vf[ks], ks == 0 ? zero16() : dpacc);
-                else
-                    sacc = Mma<T>::mma(op[n], kf[ks], ks == 0 ? zero16() : sacc);
-                // the softmax reads S and dP with vector instructions
-                if constexpr (j == NSLOT - 2) asm volatile("" : "+v"(sacc));
-                if constexpr (j == NSLOT - 1) asm volatile("" : "+v"(dpacc));
-            } else {
-                constexpr int t = j / (2 * NDB), db = (j >> 1) % NDB;
-                constexpr int par = blk & 1;
-                if constexpr (j & 1)
-                    dkt[db] = Mma<T>::mma(op[n], dsb[par][t], dkt[db]);
-                else
-                    dvt[db] = Mma<T>::mma(op[n], pb[par][t], dvt[db]);
-            }
-            if constexpr (!is_s && seg < NSEG - 1) {
-                // a dV/dK segment of block seg/2 - 1 carries the softmax of block seg/2
-#pragma unroll
-                for (int e = 0; e < EPS; ++e) soft(seg / 2, j * EPS + e);
-            } else if constexpr (is_s && seg > 0 && j >= NSLOT - 8) {
-                // row terms of the block whose S/dP this segment computes
-                load_rows(blk, j - (NSLOT - 8));
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        });
-    };
+                for (int g = 0; g < 4; ++g) {
+                    u32x2 wk, wv;
+                    wk[0] = Mma<T>::pack2(dkt[db][4 * g] * scale, dkt[db][4 * g + 1] * scale);
+                    wk[1] = Mma<T>::pack2(dkt[db][4 * g + 2] * scale, dkt[db][4 * g + 3] * scale);
+                    wv[0] = Mma<T>::pack2(dvt[db][4 * g], dvt[db][4 * g + 1]);
+                    wv[1] = Mma<T>::pack2(dvt[db][4 * g + 2], dvt[db][4 * g + 3]);
+                    *reinterpret_cast<u32x2*>(dkrow + 32 * db + 8 * g + 4 * hi) = wk;
+                    *reinterpret_cast<u32x2*>(dvrow + 32 * db + 8 * g + 4 * hi) = wv;
+                }
+        }
 
-    if (nsteps > 0) {
-        issue(0, buf_of(0));
-        put_rows(buf_of(0));
-        wait_vmem();
-    }
-    __syncthreads();
-
-    // one tile: prefetch the next one into the other buffer, compute, publish
-    auto tile = [&](int s, auto mask_tag, auto buf_tag) __attribute__((always_inline)) {
-        constexpr int BUFC = decltype(buf_tag)::value;
-        const int nb = buf_of(s) ^ 1;
-        issue(min(s + 1, nsteps - 1), nb);
-        int h, q0;
-        step_rows(s, h, q0);
-        (void)h;
-        // rows q0 + 4 hi + (32 blk + 8 g + i) are visible when at or after the key
-        run_step(mask_tag, smem + (BUFC >= 0 ? BUFC : buf_of(s)) * STAGE, key - q0 - 4 * hi);
-        put_rows(nb);
-        wait_vmem();
-        __syncthreads();
-    };
-    for (int s = 0; s < ndiag; ++s)
-        tile(s, std::true_type{}, std::integral_constant<int, -1>{});
-    for (int s = ndiag; s < nsteps; s += 2) {
-        tile(s, std::false_type{}, std::integral_constant<int, 0>{});
-        if (s + 1 < nsteps) tile(s + 1, std::false_type{}, std::integral_constant<int, 1>{});
-    }
-
-    if (key < N) {
-        uint16_t* dkrow = dK + kvoff + (size_t)key * D;
-        uint16_t* dvrow = dV + kvoff + (size_t)key * D;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                u32x2 wk, wv;
-                wk[0] = Mma<T>::pack2(dkt[db][4 * g] * scale, dkt[db][4 * g + 1] * scale);
-                wk[1] = Mma<T>::pack2(dkt[db][4 * g + 2] * scale, dkt[db][4 * g + 3] * scale);
-                wv[0] = Mma<T>::pack2(dvt[db][4 * g], dvt[db][4 * g + 1]);
-                wv[1] = Mma<T>::pack2(dvt[db][4 * g + 2], dvt[db][4 * g + 3]);
-                *reinterpret_cast<u32x2*>(dkrow + 32 * db + 8 * g + 4 * hi) = wk;
-                *reinterpret_cast<u32x2*>(dvrow + 32 * db + 8 * g + 4 * hi) = wv;
-            }
     }
 }
 
@@ -1789,6 +1801,18 @@ hipError_t dkdv16(const BwdArgs& a) {
         return hipGetLastError();
     }
     if (a.variant == 0) {
+        // persistent grid where the key blocks outnumber the compute units
+        const int grid = persistent_grid();
+        const long long total = (long long)nkb * a.Hkv * a.B;
+        if (grid >= 8 && total > grid) {
+            hipLaunchKernelGGL((dkdv16v3_kernel<T, D, CAUSAL, true>), dim3((unsigned)grid), dim3(256), 0,
+                               a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                               (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv,
+                               a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale);
+            return hipGetLastError();
+        }
+    }
+    if (a.variant == 0 || a.variant == 4) {
         hipLaunchKernelGGL((dkdv16v3_kernel<T, D, CAUSAL>), dim3((unsigned)(nkb * a.Hkv * a.B)),
                            dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                            (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
@@ -1836,7 +1860,7 @@ hipError_t dq16(const BwdArgs& a) {
                            (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale);
         return hipGetLastError();
     }
-    if (a.variant == 0) {
+    if (a.variant == 0 || a.variant == 4) {
         hipLaunchKernelGGL((dq16v3_kernel<T, D, CAUSAL>), dim3((unsigned)(nqb * a.Hq * a.B)),
                            dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                            (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,

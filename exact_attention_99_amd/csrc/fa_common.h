@@ -130,6 +130,35 @@ __device__ __forceinline__ int xcd_remap(int pid, int total) {
     return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
 }
 
+// Persistent schedule: XCD x = p % 8 owns the logical blocks that xcd_remap
+// gives it; its G / 8 workgroups (G a multiple of 8), i = p / 8, take the
+// range's k-th block in round r for k = r G/8 + (r even ? i : G/8 - 1 - i),
+// a snake that pairs long and short rows over consecutive rounds.  -1 once
+// the range is exhausted (k only grows with r).
+__device__ __forceinline__ int persist_block(int p, int G, int total, int round) {
+    constexpr int kXcd = 8;
+    const int x = p % kXcd, i = p / kXcd, gx = G / kXcd;
+    const int per = total / kXcd, rem = total % kXcd;
+    const int cnt = per + (x < rem ? 1 : 0);
+    const int start = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+    const int k = round * gx + ((round & 1) ? gx - 1 - i : i);
+    return k < cnt ? start + k : -1;
+}
+
+// Workgroups in a persistent grid of one workgroup per compute unit of the
+// current device, rounded down to a multiple of the 8 XCDs (0 if unknown).
+inline int persistent_grid() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    static int cus[64];   // per device; a racing first call stores the same value
+    if (cus[dev] == 0) {
+        int n = 0;
+        cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0
+                       ? n : -1;
+    }
+    return cus[dev] > 0 ? cus[dev] / 8 * 8 : 0;
+}
+
 // Raw buffer resource over one tensor region of `bytes` bytes.  Loads whose
 // byte offset lies at or past `bytes` return zeros (hardware range check), so
 // rows past the end of a sequence need no branch.  The offset is always passed
