@@ -1796,7 +1796,17 @@ hipError_t launch16v6(const FwdArgs& a) {
     constexpr int BR = 32 * NW;
     const int nqb = (a.N + BR - 1) / BR;
     const long long total = (long long)nqb * a.Hq * a.B;
-    const int grid = PERSIST ? persistent_grid() : 0;
+    int grid = 0;
+    if constexpr (PERSIST) {
+        // workgroups resident per compute unit for this instantiation
+        static const int per_cu = [] {
+            int n = 0;
+            return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                       &n, reinterpret_cast<const void*>(fwd16v6_kernel<T, D, CAUSAL, NW, BC, PIPE, true>), NW * 64,
+                       0) == hipSuccess ? n : 0;
+        }();
+        grid = persistent_grid() * per_cu;
+    }
     if (grid >= 8 && total > grid)
         hipLaunchKernelGGL((fwd16v6_kernel<T, D, CAUSAL, NW, BC, PIPE, true>), dim3((unsigned)grid),
                            dim3(NW * 64), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
@@ -1899,7 +1909,12 @@ hipError_t dispatch16c(const FwdArgs& a) {
             case 14: return launch16v5<T, D, CAUSAL, 4, 128>(a);
             case 15: return launch16v6<T, D, CAUSAL, 8, 64, true>(a);
             case 16: return launch16v6<T, D, CAUSAL, 8, 128, true>(a);
-            default: return launch16v6<T, D, CAUSAL, 4, 64, true>(a);
+            case 17: return launch16v6<T, D, CAUSAL, 4, 64, true>(a);
+            default:
+                // persistent grid under the causal mask only (without it, one row
+                // block per workgroup measures faster at this head dimension)
+                if constexpr (CAUSAL) return launch16v6<T, D, CAUSAL, 4, 64, true, true>(a);
+                else return launch16v6<T, D, CAUSAL, 4, 64, true>(a);
         }
     }
 }
