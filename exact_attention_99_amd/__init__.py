@@ -27,7 +27,8 @@ Names mirror the C entry points of ``include/fa355.h``:
     fa_status_string(code) -> str
     fa_version() -> int
 """
-from ._abi import (FA_DTYPE, FP8_BLOCK_ROWS, FaError, fa_bwd, fa_bwd_dkdv, fa_bwd_dq,
+from ._abi import (FA_DTYPE, FP8_BLOCK_ROWS, FaError, fa_bwd,
+                   fa_bwd_dkdv, fa_bwd_dq,
                    fa_bwd_blocksparse, fa_bwd_dropout, fa_bwd_prepare, fa_bwd_workspace_size,
                    fa_bwd_varlen, fa_fp8_quantize, fa_fwd, fa_fwd_blocksparse, fa_fwd_dropout,
                    fa_fwd_fp8, fa_fwd_varlen,

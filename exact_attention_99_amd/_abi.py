@@ -118,11 +118,46 @@ def _shape(q, k, v) -> Tuple[int, int, int, int, int]:
 
 
 def _check_same(ref, *ts):
+    if ref.device.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
     for t in ts:
         if t.device != ref.device:
             raise ValueError("all tensors must be on the same device")
         if not t.is_contiguous():
             raise ValueError("all tensors must be contiguous")
+
+
+def _expect(t, shape, dtype, name: str):
+    """Shape and dtype of a tensor handed to the library (the layouts of
+    include/fa355.h); a mismatch raises instead of reaching a kernel."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} {list(shape)}, got {t.dtype} {list(t.shape)}")
+
+
+def _check_qkv_dtype(q, k, v):
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
+
+
+def _check_fwd_out(q, o, lse, B, Hq, N):
+    import torch
+    _expect(o, q.shape, q.dtype, "o")
+    _expect(lse, (B, Hq, N), torch.float32, "lse")
+
+
+def _check_bwd_args(q, k, o, lse, dout, dq, dk, dv, B, Hq, N):
+    """Forward results and gradient buffers of the backward entry points."""
+    import torch
+    if o is not None:
+        _expect(o, q.shape, q.dtype, "o")
+    _expect(lse, (B, Hq, N), torch.float32, "lse")
+    _expect(dout, q.shape, q.dtype, "dout")
+    if dq is not None:
+        _expect(dq, q.shape, q.dtype, "dq")
+    if dk is not None:
+        _expect(dk, k.shape, q.dtype, "dk")
+    if dv is not None:
+        _expect(dv, k.shape, q.dtype, "dv")
 
 
 def _stream(ref, stream) -> int:
@@ -138,12 +173,12 @@ def fa_fwd(q, k, v, causal: bool, scale: float, o=None, lse=None, stream=None):
     lib = load_library()
     B, Hq, Hkv, N, d = _shape(q, k, v)
     dt = _dtype_name(q)
-    if k.dtype != q.dtype or v.dtype != q.dtype:
-        raise TypeError("q, k, v must share a dtype")
+    _check_qkv_dtype(q, k, v)
     if o is None:
         o = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _check_fwd_out(q, o, lse, B, Hq, N)
     _check_same(q, k, v, o, lse)
     st = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                     B, Hq, Hkv, N, d, int(bool(causal)), float(scale), FA_DTYPE[dt],
@@ -174,14 +209,14 @@ def fa_fwd_splitkv(q, k, v, causal: bool, scale: float, num_splits: int = 0, o=N
         raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
     Hkv, Nkv = k.shape[1], k.shape[2]
     dt = _dtype_name(q)
-    if k.dtype != q.dtype or v.dtype != q.dtype:
-        raise TypeError("q, k, v must share a dtype")
+    _check_qkv_dtype(q, k, v)
     if num_splits == 0:
         num_splits = int(lib.fa_fwd_splitkv_default_splits(B, Hq, Hkv, Nq, Nkv, d))
     if o is None:
         o = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _check_fwd_out(q, o, lse, B, Hq, Nq)
     need = int(lib.fa_fwd_splitkv_workspace_size(B, Hq, Nq, d, num_splits))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
@@ -202,12 +237,14 @@ def fa_bwd(q, k, v, o, lse, dout, causal: bool, scale: float, dq=None, dk=None, 
     lib = load_library()
     B, Hq, Hkv, N, d = _shape(q, k, v)
     dt = _dtype_name(q)
+    _check_qkv_dtype(q, k, v)
     if dq is None:
         dq = torch.empty_like(q)
     if dk is None:
         dk = torch.empty_like(k)
     if dv is None:
         dv = torch.empty_like(v)
+    _check_bwd_args(q, k, o, lse, dout, dq, dk, dv, B, Hq, N)
     need = int(lib.fa_bwd_workspace_size(B, Hq, Hkv, N, d, FA_DTYPE[dt]))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
@@ -226,9 +263,14 @@ def fa_bwd_prepare(o, dout, delta=None, stream=None):
     """delta_i = sum_k dout_ik o_ik (float32 [B, H_q, N]); returns delta."""
     import torch
     lib = load_library()
+    if o.dim() != 4:
+        raise ValueError("o must be 4-D [B, H_q, N, d]")
     B, Hq, N, d = o.shape
+    _dtype_name(o)
+    _expect(dout, o.shape, o.dtype, "dout")
     if delta is None:
         delta = torch.empty((B, Hq, N), dtype=torch.float32, device=o.device)
+    _expect(delta, (B, Hq, N), torch.float32, "delta")
     _check_same(o, dout, delta)
     st = lib.fa_bwd_prepare(o.data_ptr(), dout.data_ptr(), delta.data_ptr(), B, Hq, N, d,
                             FA_DTYPE[_dtype_name(o)], _stream(o, stream))
@@ -243,10 +285,14 @@ def fa_bwd_dkdv(q, k, v, lse, dout, delta, causal: bool, scale: float, dk=None, 
     import torch
     lib = load_library()
     B, Hq, Hkv, N, d = _shape(q, k, v)
+    _dtype_name(q)
+    _check_qkv_dtype(q, k, v)
     if dk is None:
         dk = torch.empty_like(k)
     if dv is None:
         dv = torch.empty_like(v)
+    _check_bwd_args(q, k, None, lse, dout, None, dk, dv, B, Hq, N)
+    _expect(delta, (B, Hq, N), torch.float32, "delta")
     _check_same(q, k, v, lse, dout, delta, dk, dv)
     st = lib.fa_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), dout.data_ptr(),
                          delta.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, N, d,
@@ -262,8 +308,12 @@ def fa_bwd_dq(q, k, v, lse, dout, delta, causal: bool, scale: float, dq=None, st
     import torch
     lib = load_library()
     B, Hq, Hkv, N, d = _shape(q, k, v)
+    _dtype_name(q)
+    _check_qkv_dtype(q, k, v)
     if dq is None:
         dq = torch.empty_like(q)
+    _check_bwd_args(q, k, None, lse, dout, dq, None, None, B, Hq, N)
+    _expect(delta, (B, Hq, N), torch.float32, "delta")
     _check_same(q, k, v, lse, dout, delta, dq)
     st = lib.fa_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), dout.data_ptr(),
                        delta.data_ptr(), dq.data_ptr(), B, Hq, Hkv, N, d, int(bool(causal)),
@@ -329,6 +379,8 @@ def fa_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, causal: bool, scale: float,
         o = torch.empty(q.shape, dtype=_OUT_DTYPES()[out_dtype], device=q.device)
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _expect(o, q.shape, _OUT_DTYPES()[out_dtype], "o")
+    _expect(lse, (B, Hq, N), torch.float32, "lse")
     _check_same(q, k, v, q_scale, k_scale, v_scale, o, lse)
     st = lib.fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_scale.data_ptr(),
                         k_scale.data_ptr(), v_scale.data_ptr(), o.data_ptr(), lse.data_ptr(),
@@ -352,12 +404,12 @@ def fa_fwd_dropout(q, k, v, causal: bool, scale: float, dropout_p: float, seed: 
     lib = load_library()
     B, Hq, Hkv, N, d = _shape(q, k, v)
     dt = _dtype_name(q)
-    if k.dtype != q.dtype or v.dtype != q.dtype:
-        raise TypeError("q, k, v must share a dtype")
+    _check_qkv_dtype(q, k, v)
     if o is None:
         o = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _check_fwd_out(q, o, lse, B, Hq, N)
     _check_same(q, k, v, o, lse)
     st = lib.fa_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                             B, Hq, Hkv, N, d, int(bool(causal)), float(scale), float(dropout_p),
@@ -376,12 +428,14 @@ def fa_bwd_dropout(q, k, v, o, lse, dout, causal: bool, scale: float, dropout_p:
     lib = load_library()
     B, Hq, Hkv, N, d = _shape(q, k, v)
     dt = _dtype_name(q)
+    _check_qkv_dtype(q, k, v)
     if dq is None:
         dq = torch.empty_like(q)
     if dk is None:
         dk = torch.empty_like(k)
     if dv is None:
         dv = torch.empty_like(v)
+    _check_bwd_args(q, k, o, lse, dout, dq, dk, dv, B, Hq, N)
     need = int(lib.fa_bwd_workspace_size(B, Hq, Hkv, N, d, FA_DTYPE[dt]))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
@@ -416,13 +470,13 @@ def fa_fwd_blocksparse(q, k, v, block_mask, causal: bool, scale: float, o=None, 
     lib = load_library()
     B, Hq, Hkv, N, d = _shape(q, k, v)
     dt = _dtype_name(q)
-    if k.dtype != q.dtype or v.dtype != q.dtype:
-        raise TypeError("q, k, v must share a dtype")
+    _check_qkv_dtype(q, k, v)
     mh = _check_block_mask(block_mask, Hq, N)
     if o is None:
         o = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _check_fwd_out(q, o, lse, B, Hq, N)
     _check_same(q, k, v, o, lse, block_mask)
     st = lib.fa_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                 block_mask.data_ptr(), mh, B, Hq, Hkv, N, d, int(bool(causal)),
@@ -440,12 +494,14 @@ def fa_bwd_blocksparse(q, k, v, o, lse, dout, block_mask, causal: bool, scale: f
     B, Hq, Hkv, N, d = _shape(q, k, v)
     dt = _dtype_name(q)
     mh = _check_block_mask(block_mask, Hq, N)
+    _check_qkv_dtype(q, k, v)
     if dq is None:
         dq = torch.empty_like(q)
     if dk is None:
         dk = torch.empty_like(k)
     if dv is None:
         dv = torch.empty_like(v)
+    _check_bwd_args(q, k, o, lse, dout, dq, dk, dv, B, Hq, N)
     need = int(lib.fa_bwd_workspace_size(B, Hq, Hkv, N, d, FA_DTYPE[dt]))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
@@ -473,13 +529,13 @@ def fa_fwd_varlen(q, k, v, seqlens, causal: bool, scale: float, o=None, lse=None
     lib = load_library()
     B, Hq, Hkv, N, d = _shape(q, k, v)
     dt = _dtype_name(q)
-    if k.dtype != q.dtype or v.dtype != q.dtype:
-        raise TypeError("q, k, v must share a dtype")
+    _check_qkv_dtype(q, k, v)
     _check_seqlens(seqlens, B)
     if o is None:
         o = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _check_fwd_out(q, o, lse, B, Hq, N)
     _check_same(q, k, v, o, lse, seqlens)
     st = lib.fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                            seqlens.data_ptr(), B, Hq, Hkv, N, d, int(bool(causal)), float(scale),
@@ -497,12 +553,14 @@ def fa_bwd_varlen(q, k, v, o, lse, dout, seqlens, causal: bool, scale: float, dq
     B, Hq, Hkv, N, d = _shape(q, k, v)
     dt = _dtype_name(q)
     _check_seqlens(seqlens, B)
+    _check_qkv_dtype(q, k, v)
     if dq is None:
         dq = torch.empty_like(q)
     if dk is None:
         dk = torch.empty_like(k)
     if dv is None:
         dv = torch.empty_like(v)
+    _check_bwd_args(q, k, o, lse, dout, dq, dk, dv, B, Hq, N)
     need = int(lib.fa_bwd_workspace_size(B, Hq, Hkv, N, d, FA_DTYPE[dt]))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)

@@ -28,36 +28,6 @@ bool sizes_ok(int B, int Hq, int Hkv, int N) {
 
 bool dtype_ok(fa_dtype t) { return t == FA_DTYPE_FP32 || t == FA_DTYPE_FP16 || t == FA_DTYPE_BF16; }
 
-int fwd_variant() {
-    // Tile variant of the 16-bit forward kernel; FA355_FWD_VARIANT overrides
-    // the default for tile sweeps.
-    static const int v = [] {
-        const char* e = getenv("FA355_FWD_VARIANT");
-        return e ? atoi(e) : 0;
-    }();
-    return v;
-}
-
-int fp8_variant() {
-    // Tile variant of the FP8 forward; FA355_FP8_VARIANT overrides the default
-    // for tile sweeps.
-    static const int v = [] {
-        const char* e = getenv("FA355_FP8_VARIANT");
-        return e ? atoi(e) : 0;
-    }();
-    return v;
-}
-
-int bwd_variant() {
-    // Kernel generation of the 16-bit backward passes; FA355_BWD_VARIANT
-    // overrides the default for comparisons.
-    static const int v = [] {
-        const char* e = getenv("FA355_BWD_VARIANT");
-        return e ? atoi(e) : 0;
-    }();
-    return v;
-}
-
 }  // namespace
 
 extern "C" {
@@ -80,7 +50,6 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
     a.causal = causal;
     a.cl2 = scale * kLog2eHost;
     a.dtype = (int)dtype;
-    a.fwd_variant = fwd_variant();
     a.drop = 0;
     a.dp = fa355::DropParams{0, 0, 256, 1.f};
     a.sparse = 0;
@@ -123,7 +92,6 @@ fa_status fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, f
     a.causal = causal;
     a.cl2 = scale * kLog2eHost;
     a.dtype = (int)dtype;
-    a.fwd_variant = 0;
     a.drop = 1;
     a.dp = fa355::DropParams{seed, offset, t8, 256.f / (float)t8};
     a.sparse = 0;
@@ -153,7 +121,6 @@ fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* 
     a.causal = causal;
     a.cl2 = scale * kLog2eHost;
     a.dtype = (int)dtype;
-    a.fwd_variant = 0;
     a.drop = 0;
     a.dp = fa355::DropParams{0, 0, 256, 1.f};
     a.sparse = 1;
@@ -199,7 +166,6 @@ fa355::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void*
     a.scale = scale;
     a.cl2 = scale * kLog2eHost;
     a.dtype = (int)dtype;
-    a.variant = bwd_variant();
     a.drop = 0;
     a.dp = fa355::DropParams{0, 0, 256, 1.f};
     a.sparse = 0;
@@ -374,7 +340,6 @@ fa_status fa_fwd_fp8(const unsigned char* q, const unsigned char* k, const unsig
     a.causal = causal;
     a.cl2 = scale * kLog2eHost;
     a.out_dtype = (int)out_dtype;
-    a.variant = fp8_variant();
     a.stream = stream;
     return hip_status(fa355::launch_fwd_fp8(a));
 }
@@ -444,7 +409,6 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
     a.causal = causal;
     a.cl2 = scale * kLog2eHost;
     a.dtype = (int)dtype;
-    a.fwd_variant = 0;
     a.drop = 0;
     a.dp = fa355::DropParams{0, 0, 256, 1.f};
     a.sparse = 1;

@@ -79,409 +79,10 @@ delta32_kernel(const float* __restrict__ O, const float* __restrict__ dO, float*
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV for 16-bit inputs.  Four waves, 128 keys per workgroup (32 per wave,
-// one per lane), BQ query rows per step (16 KB per tile: 64 rows for D = 128,
-// 128 for D = 64), double-buffered in LDS:
-//   Qs, dOs : row-major, swizzled (A operands of S = Q K^T and dP = dO V^T)
-//   Qt, dOt : transposed, query rows in "position" order, swizzled
-//             (A operands of dK^T += Q^T dS and dV^T += dO^T P)
-//   lse2, dl: log2(e) * lse and D of the step's rows.
-// Threads 0..127 stage Q, 128..255 stage dO: each loads an 8-row x 8-column
-// block, stores it row-major and, transposed in registers, column-major.
-// No branch encloses the accumulating products (a wave with no visible key in
-// a step runs it with P = dS = 0), so the dK^T/dV^T accumulators stay in place.
-template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(256)
-dkdv16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-              const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-              const float* __restrict__ LSE, const float* __restrict__ Delta,
-              uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int B, int Hq, int Hkv, int N,
-              float cl2, float scale) {
-    constexpr int BKV = 128;
-    constexpr int BQ = 8192 / D;
-    constexpr int NQB = BQ / 32;
-    constexpr int KCH = D / 8;
-    constexpr int TB = BQ * D * 2;            // one tile, bytes
-    constexpr int OFF_DOS = TB;
-    constexpr int OFF_QT = 2 * TB;
-    constexpr int OFF_DOT = 3 * TB;
-    constexpr int OFF_LSE = 4 * TB;
-    constexpr int OFF_DL = OFF_LSE + BQ * 4;
-    constexpr int STAGE = OFF_DL + BQ * 4;
-    constexpr int NDB = D / 32;
-    constexpr int NKS = D / 16;
-    static_assert((BQ / 8) * KCH == 128, "one 8x8 block per staging thread");
-
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // provably wave-uniform
-    const int l32 = lane & 31;
-    const int hi = lane >> 5;
-
-    const int nkb = (N + BKV - 1) / BKV;
-    const int total = nkb * Hkv * B;
-    const int logical = xcd_remap((int)blockIdx.x, total);
-    const int jb = logical % nkb;  // ascending: under a causal mask block 0 is the longest
-    const int bhk = logical / nkb;
-    const int hk = bhk % Hkv;
-    const int b = bhk / Hkv;
-    const int G = Hq / Hkv;
-
-    const int kv0 = jb * BKV;
-    const int kw = kv0 + 32 * wave;
-    const int key = kw + l32;
-    const size_t kvoff = ((size_t)b * Hkv + hk) * (size_t)N * D;
-    const uint32_t head_bytes = (uint32_t)N * D * 2;
-
-    // K^T, V^T as B operands: lane holds K[key][16*ks + 8*hi .. +7].
-    u32x4 kf[NKS], vf[NKS];
-    {
-        const Buf Kb(K + kvoff, head_bytes), Vb(V + kvoff, head_bytes);
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            kf[ks] = Kb.load16((uint32_t)(key * D + 16 * ks + 8 * hi) * 2);
-            vf[ks] = Vb.load16((uint32_t)(key * D + 16 * ks + 8 * hi) * 2);
-        }
-    }
-
-    f32x16 dkt[NDB], dvt[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-        dkt[db] = zero16();
-        dvt[db] = zero16();
-    }
-
-    const int qb_first = CAUSAL ? kv0 / BQ : 0;
-    const int qb_count = (N + BQ - 1) / BQ - qb_first;
-    const int nsteps = G * qb_count;
-
-    // staging: thread -> tensor (Q or dO), chunk column sc, 8-position group pg
-    const bool st_do = wave >= 2;
-    const int st = tid & 127;
-    const int sc = st % KCH;
-    const int pg = st / KCH;
-    const uint16_t* src = st_do ? dO : Q;
-    u32x4 stg[8];
-    float sx = 0.f;
-
-    auto row_of = [&](int i) {  // query row (within the step) of position 8*pg + i
-        const int pos = 8 * pg + i;
-        return 16 * (pos >> 4) + v_key_of_pos((pos >> 3) & 1, pos & 7);
-    };
-    auto step_rows = [&](int s, int& h, int& q0) {
-        h = hk * G + s / qb_count;
-        q0 = (qb_first + s % qb_count) * BQ;
-    };
-    auto fetch = [&](int s) {
-        int h, q0;
-        step_rows(s, h, q0);
-        const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
-        const Buf Sb(src + qoff, head_bytes);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            stg[i] = Sb.load16((uint32_t)((q0 + row_of(i)) * D + 8 * sc) * 2);
-        const size_t roff = ((size_t)b * Hq + h) * (size_t)N;
-        if (tid < BQ)
-            sx = Buf(LSE + roff, (uint32_t)N * 4).load_f32((uint32_t)(q0 + tid) * 4) * kLog2e;
-        else if (tid >= 128 && tid < 128 + BQ)
-            sx = Buf(Delta + roff, (uint32_t)N * 4).load_f32((uint32_t)(q0 + tid - 128) * 4);
-    };
-    auto deposit = [&](int buf) {
-        unsigned char* base = smem + buf * STAGE;
-        unsigned char* rm = base + (st_do ? OFF_DOS : 0);
-        unsigned char* tr = base + (st_do ? OFF_DOT : OFF_QT);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            *reinterpret_cast<u32x4*>(rm + k_off<D>(row_of(i), sc)) = stg[i];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int sh = 16 * (e & 1);
-            u32x4 w;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                w[jj] = ((stg[2 * jj][e >> 1] >> sh) & 0xffffu) |
-                        (((stg[2 * jj + 1][e >> 1] >> sh) & 0xffffu) << 16);
-            *reinterpret_cast<u32x4*>(tr + v_off<BQ>(8 * sc + e, pg)) = w;
-        }
-        if (tid < BQ)
-            reinterpret_cast<float*>(base + OFF_LSE)[tid] = sx;
-        else if (tid >= 128 && tid < 128 + BQ)
-            reinterpret_cast<float*>(base + OFF_DL)[tid - 128] = sx;
-    };
-
-    if (nsteps > 0) {
-        fetch(0);
-        deposit(0);
-    }
-    __syncthreads();
-
-    // Prefetch and deposit run on every iteration (the last one re-fetches the
-    // last step into the buffer nobody reads again), so the compiler sees every
-    // prefetch consumed and places no wait for it ahead of the products.
-    for (int s = 0; s < nsteps; ++s) {
-        fetch(min(s + 1, nsteps - 1));
-        int h, q0;
-        step_rows(s, h, q0);
-        // rows of this step that see only some of the wave's keys, or lie past N
-        const bool need_mask = (CAUSAL && q0 < kw + 32) || (q0 + BQ > N) || (kw + 32 > N);
-        const unsigned char* base = smem + (s & 1) * STAGE;
-        const float* lse2s = reinterpret_cast<const float*>(base + OFF_LSE);
-        const float* dls = reinterpret_cast<const float*>(base + OFF_DL);
-        // one 32-row sub-block at a time keeps a single S / dP pair live
-#pragma unroll 1
-        for (int qs = 0; qs < NQB; ++qs) {
-            f32x16 sacc = zero16(), dpacc = zero16();
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const u32x4 aq = *reinterpret_cast<const u32x4*>(base + k_off<D>(32 * qs + l32, 2 * ks + hi));
-                const u32x4 ad = *reinterpret_cast<const u32x4*>(base + OFF_DOS + k_off<D>(32 * qs + l32, 2 * ks + hi));
-                sacc = Mma<T>::mma(aq, kf[ks], sacc);
-                dpacc = Mma<T>::mma(ad, vf[ks], dpacc);
-            }
-            float pv[16], dv[16];
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + 32 * qs + 8 * g + 4 * hi);
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + 32 * qs + 8 * g + 4 * hi);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 4 * g + i;
-                    pv[r] = fast_exp2(fmaf(sacc[r], cl2, -l4[i]));
-                    dv[r] = dpacc[r] - d4[i];
-                }
-            }
-            if (need_mask) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int q = q0 + 32 * qs + acc_row(r, hi);
-                    const bool vis = (!CAUSAL || key <= q) && q < N && key < N;
-                    pv[r] = vis ? pv[r] : 0.f;
-                }
-            }
-            u32x4 pb[2], dsb[2];
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int r = 8 * t + 2 * jj;
-                    pb[t][jj] = Mma<T>::pack2(pv[r], pv[r + 1]);
-                    dsb[t][jj] = Mma<T>::pack2(pv[r] * dv[r], pv[r + 1] * dv[r + 1]);
-                }
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const int off = v_off<BQ>(32 * db + l32, 2 * (2 * qs + t) + hi);
-                    const u32x4 ado = *reinterpret_cast<const u32x4*>(base + OFF_DOT + off);
-                    const u32x4 aqt = *reinterpret_cast<const u32x4*>(base + OFF_QT + off);
-                    dvt[db] = Mma<T>::mma(ado, pb[t], dvt[db]);
-                    dkt[db] = Mma<T>::mma(aqt, dsb[t], dkt[db]);
-                }
-        }
-        deposit((s + 1) & 1);
-        __syncthreads();
-    }
-
-    if (key < N) {
-        uint16_t* dkrow = dK + kvoff + (size_t)key * D;
-        uint16_t* dvrow = dV + kvoff + (size_t)key * D;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                u32x2 wk, wv;
-                wk[0] = Mma<T>::pack2(dkt[db][4 * g] * scale, dkt[db][4 * g + 1] * scale);
-                wk[1] = Mma<T>::pack2(dkt[db][4 * g + 2] * scale, dkt[db][4 * g + 3] * scale);
-                wv[0] = Mma<T>::pack2(dvt[db][4 * g], dvt[db][4 * g + 1]);
-                wv[1] = Mma<T>::pack2(dvt[db][4 * g + 2], dvt[db][4 * g + 3]);
-                *reinterpret_cast<u32x2*>(dkrow + 32 * db + 8 * g + 4 * hi) = wk;
-                *reinterpret_cast<u32x2*>(dvrow + 32 * db + 8 * g + 4 * hi) = wv;
-            }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// dQ for 16-bit inputs.  Four waves, 128 query rows per workgroup (32 per
-// wave, one per lane), BC keys per tile staged three ways: K and V row-major
-// (A operands of S^T = K Q^T, dP^T = V dO^T) and K transposed in position
-// order (A operand of dQ^T += K^T dS^T).
-template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(256)
-dq16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-            const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-            const float* __restrict__ LSE, const float* __restrict__ Delta,
-            uint16_t* __restrict__ dQ, int B, int Hq, int Hkv, int N, float cl2, float scale) {
-    constexpr int NW = 4;
-    constexpr int BR = 32 * NW;
-    constexpr int BC = D == 128 ? 64 : 128;
-    constexpr int KCH = D / 8;
-    constexpr int TB = BC * D * 2;
-    constexpr int STAGE = 3 * TB;
-    constexpr int NKB = BC / 32;
-    constexpr int NDB = D / 32;
-    constexpr int NKS = D / 16;
-    constexpr int ROWS = BC * KCH / 256;      // key rows staged per thread, at one chunk
-    static_assert(ROWS == 4, "staging split");
-
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // provably wave-uniform
-    const int l32 = lane & 31;
-    const int hi = lane >> 5;
-
-    const int nqb = (N + BR - 1) / BR;
-    const int total = nqb * Hq * B;
-    const int logical = xcd_remap((int)blockIdx.x, total);
-    const int qb_raw = logical % nqb;
-    const int bh = logical / nqb;
-    const int qb = CAUSAL ? (nqb - 1 - qb_raw) : qb_raw;
-    const int h = bh % Hq;
-    const int b = bh / Hq;
-    const int hk = h / (Hq / Hkv);
-
-    const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
-    const size_t koff = ((size_t)b * Hkv + hk) * (size_t)N * D;
-    const uint32_t head_bytes = (uint32_t)N * D * 2;
-    const Buf Kb(K + koff, head_bytes), Vb(V + koff, head_bytes);
-
-    const int q0 = qb * BR;
-    const int qw = q0 + 32 * wave;
-    const int q = qw + l32;
-
-    u32x4 qf[NKS], dof[NKS];
-    {
-        const Buf Qb(Q + qoff, head_bytes), Db(dO + qoff, head_bytes);
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            qf[ks] = Qb.load16((uint32_t)(q * D + 16 * ks + 8 * hi) * 2);
-            dof[ks] = Db.load16((uint32_t)(q * D + 16 * ks + 8 * hi) * 2);
-        }
-    }
-    const size_t roff = ((size_t)b * Hq + h) * (size_t)N;
-    const float lse2 = q < N ? LSE[roff + q] * kLog2e : 0.f;
-    const float dlt = q < N ? Delta[roff + q] : 0.f;
-
-    const int kv_len = CAUSAL ? min(N, q0 + BR) : N;
-    const int ntiles = (kv_len + BC - 1) / BC;
-
-    const int sc = tid % KCH;
-    const int pg = tid / KCH;  // positions ROWS*pg .. ROWS*pg + ROWS - 1
-    u32x4 sk[ROWS], sv[ROWS];
-
-    auto key_of = [&](int i) {
-        const int pos = ROWS * pg + i;
-        return 16 * (pos >> 4) + v_key_of_pos((pos >> 3) & 1, pos & 7);
-    };
-    auto fetch = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < ROWS; ++i) {
-            const uint32_t off = (uint32_t)((k0 + key_of(i)) * D + 8 * sc) * 2;
-            sk[i] = Kb.load16(off);
-            sv[i] = Vb.load16(off);
-        }
-    };
-    auto deposit = [&](int buf) {
-        unsigned char* base = smem + buf * STAGE;
-#pragma unroll
-        for (int i = 0; i < ROWS; ++i) {
-            *reinterpret_cast<u32x4*>(base + k_off<D>(key_of(i), sc)) = sk[i];
-            *reinterpret_cast<u32x4*>(base + TB + k_off<D>(key_of(i), sc)) = sv[i];
-        }
-        unsigned char* kt = base + 2 * TB;
-        const int chunk = (ROWS * pg) >> 3;
-        const int sub = ((ROWS * pg) & 7) * 2;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int sh = 16 * (e & 1);
-            u32x2 w;
-            w[0] = ((sk[0][e >> 1] >> sh) & 0xffffu) | (((sk[1][e >> 1] >> sh) & 0xffffu) << 16);
-            w[1] = ((sk[2][e >> 1] >> sh) & 0xffffu) | (((sk[3][e >> 1] >> sh) & 0xffffu) << 16);
-            *reinterpret_cast<u32x2*>(kt + v_off<BC>(8 * sc + e, chunk) + sub) = w;
-        }
-    };
-
-    f32x16 dq[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) dq[db] = zero16();
-
-    fetch(0);
-    deposit(0);
-    __syncthreads();
-
-    // Unconditional prefetch / deposit, as in the forward pass: the extra tile
-    // is inside this head's range (rows past N read as zeros).
-    for (int j = 0; j < ntiles; ++j) {
-        const int k0 = j * BC;
-        fetch(k0 + BC);
-        // No branch encloses the accumulating products: a wave whose rows see
-        // no key of this tile runs it with dS = 0.  One 32-key block at a time
-        // keeps a single S^T / dP^T pair live.
-        const unsigned char* base = smem + (j & 1) * STAGE;
-        const bool need_mask = (CAUSAL && k0 + BC - 1 > qw) || (k0 + BC > N);
-#pragma unroll 1
-        for (int kb = 0; kb < NKB; ++kb) {
-            f32x16 st = zero16(), dpt = zero16();
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const int off = k_off<D>(32 * kb + l32, 2 * ks + hi);
-                const u32x4 ak = *reinterpret_cast<const u32x4*>(base + off);
-                const u32x4 av = *reinterpret_cast<const u32x4*>(base + TB + off);
-                st = Mma<T>::mma(ak, qf[ks], st);
-                dpt = Mma<T>::mma(av, dof[ks], dpt);
-            }
-            float p[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) p[r] = fast_exp2(fmaf(st[r], cl2, -lse2));
-            if (need_mask) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int kk = k0 + 32 * kb + acc_row(r, hi);
-                    p[r] = ((!CAUSAL || kk <= q) && kk < N) ? p[r] : 0.f;
-                }
-            }
-            u32x4 dsb[2];
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int r = 8 * t + 2 * jj;
-                    dsb[t][jj] = Mma<T>::pack2(p[r] * (dpt[r] - dlt), p[r + 1] * (dpt[r + 1] - dlt));
-                }
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const u32x4 a = *reinterpret_cast<const u32x4*>(
-                        base + 2 * TB + v_off<BC>(32 * db + l32, 2 * (2 * kb + t) + hi));
-                    dq[db] = Mma<T>::mma(a, dsb[t], dq[db]);
-                }
-        }
-        deposit((j + 1) & 1);
-        __syncthreads();
-    }
-
-    if (q < N) {
-        uint16_t* row = dQ + qoff + (size_t)q * D;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                u32x2 w;
-                w[0] = Mma<T>::pack2(dq[db][4 * g] * scale, dq[db][4 * g + 1] * scale);
-                w[1] = Mma<T>::pack2(dq[db][4 * g + 2] * scale, dq[db][4 * g + 3] * scale);
-                *reinterpret_cast<u32x2*>(row + 32 * db + 8 * g + 4 * hi) = w;
-            }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Second-generation dK / dV kernel.  Same work split as dkdv16_kernel, but the
-// Q and dO tiles arrive in LDS through buffer-to-LDS copies (no staging
-// registers, rows past N read as zeros) and are stored row-major only, with a
+// Second-generation dK / dV kernel.  Four waves, 128 keys per workgroup (32
+// per wave, one per lane), query rows in steps.  The Q and dO tiles arrive in
+// LDS through buffer-to-LDS copies (no staging registers, rows past N read as
+// zeros) and are stored row-major only, with a
 // swizzle that suits both ways they are read: 128-bit reads of 16 consecutive
 // rows for the A operands of S = Q K^T and dP = dO V^T, and transposing reads
 // for the A operands of dV^T += dO^T P and dK^T += Q^T dS.
@@ -1800,37 +1401,20 @@ hipError_t dkdv16(const BwdArgs& a) {
                            a.dp, a.sp);
         return hipGetLastError();
     }
-    if (a.variant == 0) {
-        // persistent grid where the key blocks outnumber the compute units
-        const int grid = persistent_grid();
-        const long long total = (long long)nkb * a.Hkv * a.B;
-        if (grid >= 8 && total > grid) {
-            hipLaunchKernelGGL((dkdv16v3_kernel<T, D, CAUSAL, true>), dim3((unsigned)grid), dim3(256), 0,
-                               a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                               (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv,
-                               a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale);
-            return hipGetLastError();
-        }
-    }
-    if (a.variant == 0 || a.variant == 4) {
-        hipLaunchKernelGGL((dkdv16v3_kernel<T, D, CAUSAL>), dim3((unsigned)(nkb * a.Hkv * a.B)),
-                           dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                           (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
-                           (uint16_t*)a.dk, (uint16_t*)a.dv, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale);
+    // persistent grid where the key blocks outnumber the compute units
+    const int grid = persistent_grid();
+    const long long total = (long long)nkb * a.Hkv * a.B;
+    if (grid >= 8 && total > grid) {
+        hipLaunchKernelGGL((dkdv16v3_kernel<T, D, CAUSAL, true>), dim3((unsigned)grid), dim3(256), 0,
+                           a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                           (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv,
+                           a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale);
         return hipGetLastError();
     }
-    if (a.variant == 2) {
-        hipLaunchKernelGGL((dkdv16v2_kernel<T, D, CAUSAL>), dim3((unsigned)(nkb * a.Hkv * a.B)),
-                           dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                           (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
-                           (uint16_t*)a.dk, (uint16_t*)a.dv, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale,
-                           a.dp, a.sp);
-        return hipGetLastError();
-    }
-    hipLaunchKernelGGL((dkdv16_kernel<T, D, CAUSAL>), dim3((unsigned)(nkb * a.Hkv * a.B)), dim3(256), 0,
-                       a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv,
-                       a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale);
+    hipLaunchKernelGGL((dkdv16v3_kernel<T, D, CAUSAL>), dim3((unsigned)total), dim3(256), 0, a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.B,
+                       a.Hq, a.Hkv, a.N, a.cl2, a.scale);
     return hipGetLastError();
 }
 
@@ -1851,30 +1435,7 @@ hipError_t dq16(const BwdArgs& a) {
                            (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale, a.dp, a.sp);
         return hipGetLastError();
     }
-    if (a.variant == 3) {
-        // eight-wave tiling (one workgroup per compute unit), kept for sweeps
-        const int nqb8 = (a.N + 255) / 256;
-        hipLaunchKernelGGL((dq16v3_kernel<T, D, CAUSAL, 8>), dim3((unsigned)(nqb8 * a.Hq * a.B)),
-                           dim3(512), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                           (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
-                           (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale);
-        return hipGetLastError();
-    }
-    if (a.variant == 0 || a.variant == 4) {
-        hipLaunchKernelGGL((dq16v3_kernel<T, D, CAUSAL>), dim3((unsigned)(nqb * a.Hq * a.B)),
-                           dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                           (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
-                           (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale);
-        return hipGetLastError();
-    }
-    if (a.variant != 1) {
-        hipLaunchKernelGGL((dq16v2_kernel<T, D, CAUSAL>), dim3((unsigned)(nqb * a.Hq * a.B)),
-                           dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                           (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
-                           (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale, a.dp, a.sp);
-        return hipGetLastError();
-    }
-    hipLaunchKernelGGL((dq16_kernel<T, D, CAUSAL>), dim3((unsigned)(nqb * a.Hq * a.B)), dim3(256), 0,
+    hipLaunchKernelGGL((dq16v3_kernel<T, D, CAUSAL>), dim3((unsigned)(nqb * a.Hq * a.B)), dim3(256), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, a.B, a.Hq, a.Hkv,
                        a.N, a.cl2, a.scale);

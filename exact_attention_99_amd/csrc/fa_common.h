@@ -19,6 +19,7 @@
 
 #include "fa_launch.h"
 
+#include <atomic>
 #include <utility>
 #include <stdint.h>
 
@@ -147,16 +148,19 @@ __device__ __forceinline__ int persist_block(int p, int G, int total, int round)
 
 // Workgroups in a persistent grid of one workgroup per compute unit of the
 // current device, rounded down to a multiple of the 8 XCDs (0 if unknown).
+// The compute-unit count is cached per device in relaxed atomics: threads that
+// race on a first call each query the device and store the same value.
 inline int persistent_grid() {
+    static std::atomic<int> cus[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    static int cus[64];   // per device; a racing first call stores the same value
-    if (cus[dev] == 0) {
+    int c = cus[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
         int n = 0;
-        cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0
-                       ? n : -1;
+        c = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : -1;
+        cus[dev].store(c, std::memory_order_relaxed);
     }
-    return cus[dev] > 0 ? cus[dev] / 8 * 8 : 0;
+    return c > 0 ? c / 8 * 8 : 0;
 }
 
 // Raw buffer resource over one tensor region of `bytes` bytes.  Loads whose

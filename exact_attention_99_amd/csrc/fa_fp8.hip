@@ -192,7 +192,7 @@ __device__ __forceinline__ constexpr int key_perm(int m) {
 // exponent's multiplier.  The value block scales fold into the exponent's
 // offset as log2(s_v / s_vmax) <= 0 (and out of the row sum again), and the
 // head's largest value scale s_vmax multiplies the output at the end.
-template <int D, bool CAUSAL, int NW, int BC, typename TO, int WPE, bool PRE>
+template <int D, bool CAUSAL, int NW, int BC, typename TO, int WPE>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 fwd8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
             const uint8_t* __restrict__ V, const float* __restrict__ SQ,
@@ -361,8 +361,7 @@ fwd8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
                 }
         }
 
-        // V^T operands (PRE: read now so that their latency hides under the
-        // softmax; otherwise just before each product)
+        // V^T operands, read just before each product
         auto read_v = [&](int t, int cb) {
             i32x8 r;
 #pragma unroll
@@ -373,13 +372,6 @@ fwd8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
             }
             return r;
         };
-        i32x8 va[PRE ? NH : 1][PRE ? NDB : 1];
-        if (PRE) {
-#pragma unroll
-            for (int t = 0; t < NH; ++t)
-#pragma unroll
-                for (int cb = 0; cb < NDB; ++cb) va[PRE ? t : 0][PRE ? cb : 0] = read_v(t, cb);
-        }
 
         float mx = -INFINITY;
 #pragma unroll
@@ -427,7 +419,7 @@ fwd8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
         for (int t = 0; t < NH; ++t)
 #pragma unroll
             for (int cb = 0; cb < NDB; ++cb)
-                o[cb] = mma8(PRE ? va[PRE ? t : 0][PRE ? cb : 0] : read_v(t, cb), pb[t], o[cb]);
+                o[cb] = mma8(read_v(t, cb), pb[t], o[cb]);
     };
     // tile j in buffer BUFC, or (BUFC < 0) in buffer j & 1
     auto body = [&](int j, auto mask_tag, auto buf_tag) __attribute__((always_inline)) {
@@ -490,11 +482,11 @@ hipError_t quant8_d(const Fp8QuantArgs& a) {
     return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, int BC, typename TO, int NW, int WPE, bool PRE>
+template <int D, bool CAUSAL, int BC, typename TO, int NW, int WPE>
 hipError_t fwd8_launch(const Fp8FwdArgs& a) {
     const int nqb = (a.N + 32 * NW - 1) / (32 * NW);
     const int total = nqb * a.Hq * a.B;
-    hipLaunchKernelGGL((fwd8_kernel<D, CAUSAL, NW, BC, TO, WPE, PRE>), dim3((unsigned)total), dim3(NW * 64), 0,
+    hipLaunchKernelGGL((fwd8_kernel<D, CAUSAL, NW, BC, TO, WPE>), dim3((unsigned)total), dim3(NW * 64), 0,
                        a.stream, a.q, a.k, a.v, a.sq, a.sk, a.sv, (uint16_t*)a.o, a.lse, a.B, a.Hq,
                        a.Hkv, a.N, a.cl2);
     return hipGetLastError();
@@ -503,14 +495,11 @@ hipError_t fwd8_launch(const Fp8FwdArgs& a) {
 template <int D, typename TO>
 hipError_t fwd8_d(const Fp8FwdArgs& a) {
     // key tile: 64 keys at D = 128, 128 keys at D = 64 (8 KB per K or V tile).
-    // Default: 4-wave workgroups at 3 waves per SIMD, V^T read just before
-    // each P V product (the softmax of one wave hides under the products of
-    // the other two); variant 1: 8-wave workgroups at 2 waves per SIMD with
-    // the V^T operands read before the softmax.
+    // 4-wave workgroups at 3 waves per SIMD, V^T read just before each P V
+    // product (the softmax of one wave hides under the products of the other
+    // two).
     constexpr int BC = D == 64 ? 128 : 64;
-    if (a.variant == 1)
-        return a.causal ? fwd8_launch<D, true, BC, TO, 8, 2, true>(a) : fwd8_launch<D, false, BC, TO, 8, 2, true>(a);
-    return a.causal ? fwd8_launch<D, true, BC, TO, 4, 3, false>(a) : fwd8_launch<D, false, BC, TO, 4, 3, false>(a);
+    return a.causal ? fwd8_launch<D, true, BC, TO, 4, 3>(a) : fwd8_launch<D, false, BC, TO, 4, 3>(a);
 }
 
 }  // namespace

@@ -29,439 +29,11 @@ namespace fa355 {
 
 namespace {
 
-// 16-bit inputs (bf16 or fp16), head dim D, NW waves, BC keys per tile.  Half
-// of the waves stage K, the other half stage V transposed; every staging
-// thread moves NCH (4 or 8) 16-byte chunks per tile: NCH chunks of K rows, or
-// an NCH-key x 8-dim block of V that it transposes in registers.
-template <typename T, int D, bool CAUSAL, int NW, int BC>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-fwd16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-             const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-             int B, int Hq, int Hkv, int N, float cl2) {
-    constexpr int BR = 32 * NW;
-    constexpr int KCH = D / 8;                 // 16-byte chunks per K row
-    constexpr int TILE_BYTES = BC * D * 2;     // one of K or V^T
-    constexpr int STAGE = 2 * TILE_BYTES;
-    constexpr int NKB = BC / 32;               // 32-key blocks per tile
-    constexpr int NKG = BC / 16;               // 16-key groups per tile
-    constexpr int NDB = D / 32;                // 32-wide head-dim blocks
-    constexpr int NKS = D / 16;                // k-steps of QK^T
-    constexpr int LOADERS = NW * 32;           // threads per staging half
-    constexpr int NCH = BC * D / 8 / LOADERS;  // chunks per staging thread
-    static_assert(NCH == 4 || NCH == 8, "staging split");
-    static_assert(BC % 32 == 0 && BC >= 64, "tile width");
-
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // provably wave-uniform
-    const int l32 = lane & 31;
-    const int hi = lane >> 5;
-
-    const int nqb = (N + BR - 1) / BR;
-    const int total = nqb * Hq * B;
-    const int logical = xcd_remap((int)blockIdx.x, total);
-    const int qb_raw = logical % nqb;
-    const int bh = logical / nqb;
-    const int qb = CAUSAL ? (nqb - 1 - qb_raw) : qb_raw;  // longest rows first
-    const int h = bh % Hq;
-    const int b = bh / Hq;
-    const int hk = h / (Hq / Hkv);
-
-    const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
-    const size_t koff = ((size_t)b * Hkv + hk) * (size_t)N * D;
-    const uint32_t head_bytes = (uint32_t)N * D * 2;
-    const Buf Qb(Q + qoff, head_bytes), Kb(K + koff, head_bytes), Vb(V + koff, head_bytes);
-
-    const int q0 = qb * BR;
-    const int qw = q0 + 32 * wave;
-    const int q = qw + l32;
-
-    // Q^T as the B operand: lane holds Q[q][16*ks + 8*hi .. +7].
-    u32x4 qf[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-        qf[ks] = Qb.load16((uint32_t)(q * D + 16 * ks + 8 * hi) * 2);
-
-    const int kv_len = CAUSAL ? min(N, q0 + BR) : N;
-    const int ntiles = (kv_len + BC - 1) / BC;
-
-    // ---- staging: global -> registers -> LDS --------------------------------
-    const bool stage_v = wave < NW / 2;
-    const int st = stage_v ? tid : tid - LOADERS;
-    u32x4 stg[NCH];
-
-    auto fetch = [&](int k0) {
-        if (stage_v) {
-            // block (c, position group pg): positions NCH*pg .. NCH*pg+NCH-1
-            const int c = st % KCH;
-            const int pg = st / KCH;
-#pragma unroll
-            for (int i = 0; i < NCH; ++i) {
-                const int pos = NCH * pg + i;  // position inside the tile
-                const int key = k0 + 16 * (pos >> 4) + v_key_of_pos((pos >> 3) & 1, pos & 7);
-                stg[i] = Vb.load16((uint32_t)(key * D + 8 * c) * 2);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < NCH; ++i) {
-                const int ci = st + i * LOADERS;
-                const int key = k0 + ci / KCH;
-                stg[i] = Kb.load16((uint32_t)(key * D + 8 * (ci % KCH)) * 2);
-            }
-        }
-    };
-    auto deposit = [&](int buf) {
-        unsigned char* base = smem + buf * STAGE;
-        if (stage_v) {
-            unsigned char* vt = base + TILE_BYTES;
-            const int c = st % KCH;
-            const int pg = st / KCH;
-            const int chunk = (NCH * pg) >> 3;          // 16-byte chunk of the V^T row
-            const int sub = ((NCH * pg) & 7) * 2;       // byte offset inside it
-            // NCH keys x 8 dims -> 8 rows (dims) of NCH keys.
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int sh = 16 * (e & 1);
-                uint32_t w[NCH / 2];
-#pragma unroll
-                for (int jj = 0; jj < NCH / 2; ++jj) {
-                    const uint32_t x0 = (stg[2 * jj][e >> 1] >> sh) & 0xffffu;
-                    const uint32_t x1 = (stg[2 * jj + 1][e >> 1] >> sh) & 0xffffu;
-                    w[jj] = x0 | (x1 << 16);
-                }
-                unsigned char* dst = vt + v_off<BC>(8 * c + e, chunk) + sub;
-                if constexpr (NCH == 8) {
-                    u32x4 x; x[0] = w[0]; x[1] = w[1]; x[2] = w[2]; x[3] = w[3];
-                    *reinterpret_cast<u32x4*>(dst) = x;
-                } else {
-                    u32x2 x; x[0] = w[0]; x[1] = w[1];
-                    *reinterpret_cast<u32x2*>(dst) = x;
-                }
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < NCH; ++i) {
-                const int ci = st + i * LOADERS;
-                *reinterpret_cast<u32x4*>(base + k_off<D>(ci / KCH, ci % KCH)) = stg[i];
-            }
-        }
-    };
-
-    // ---- running state ---------------------------------------------------------
-    f32x16 o[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) o[db] = zero16();
-    float m_s = -INFINITY;  // running max of scale*log2(e)*s
-    float l_s = 0.f;        // this lane's share of the running sum
-
-    fetch(0);
-    deposit(0);
-    __syncthreads();
-
-    // The prefetch and its deposit run on every iteration, also the last: the
-    // extra tile lies inside this head's buffer range (past-the-end rows read
-    // as zeros) and lands in the buffer no later iteration reads.  Keeping them
-    // unconditional lets the compiler see that every prefetch is consumed, so
-    // it places no wait for them ahead of the score products.
-    for (int j = 0; j < ntiles; ++j) {
-        const int k0 = j * BC;
-        fetch(k0 + BC);
-
-        const bool active = !CAUSAL || (k0 <= qw + 31);
-        if (active) {
-            const unsigned char* ks_base = smem + (j & 1) * STAGE;
-            const unsigned char* vt_base = ks_base + TILE_BYTES;
-
-            f32x16 s[NKB];
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                s[kb] = zero16();
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    const u32x4 a = *reinterpret_cast<const u32x4*>(
-                        ks_base + k_off<D>(32 * kb + l32, 2 * ks + hi));
-                    s[kb] = Mma<T>::mma(a, qf[ks], s[kb]);
-                }
-            }
-
-            const bool need_mask = (CAUSAL && (k0 + BC - 1 > qw)) || (k0 + BC > N);
-            if (need_mask) {
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + 32 * kb + acc_row(r, hi);
-                        if ((CAUSAL && key > q) || key >= N) s[kb][r] = -INFINITY;
-                    }
-            }
-
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-            mx = fmaxf(mx, swap_halves(mx));
-            const float mt = mx * cl2;
-
-            if (__any(mt > m_s + kTau)) {
-                const float mn = fmaxf(m_s, mt);
-                const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m_s - mn);
-                l_s *= alpha;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-                m_s = mn;
-            }
-            const float mu = (m_s == -INFINITY) ? 0.f : m_s;
-
-            u32x4 pb[NKG];
-            float ls = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        const float p0 = fast_exp2(fmaf(s[kb][8 * t + 2 * jj], cl2, -mu));
-                        const float p1 = fast_exp2(fmaf(s[kb][8 * t + 2 * jj + 1], cl2, -mu));
-                        ls += p0 + p1;
-                        pb[2 * kb + t][jj] = Mma<T>::pack2(p0, p1);
-                    }
-            l_s += ls;
-
-#pragma unroll
-            for (int kg = 0; kg < NKG; ++kg)
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const u32x4 a = *reinterpret_cast<const u32x4*>(
-                        vt_base + v_off<BC>(32 * db + l32, 2 * kg + hi));
-                    o[db] = Mma<T>::mma(a, pb[kg], o[db]);
-                }
-        }
-
-        deposit((j + 1) & 1);
-        __syncthreads();
-    }
-
-    // ---- epilogue -----------------------------------------------------------------
-    const float l_tot = l_s + swap_halves(l_s);
-    if (q < N) {
-        const float inv = 1.f / l_tot;
-        uint16_t* Orow = O + qoff + (size_t)q * D;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                u32x2 w;
-                w[0] = Mma<T>::pack2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
-                w[1] = Mma<T>::pack2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-                *reinterpret_cast<u32x2*>(Orow + 32 * db + 8 * g + 4 * hi) = w;
-            }
-        if (hi == 0) LSE[(size_t)(b * Hq + h) * N + q] = (m_s + __log2f(l_tot)) * kLn2;
-    }
-}
-
-// Second-generation 16-bit forward kernel: K and V tiles are copied from
+// Fifth-generation 16-bit forward kernel.  K and V tiles are copied from
 // global memory straight into LDS by buffer-to-LDS loads (no staging
-// registers, no LDS stores; rows past N arrive as zeros), both row-major.
-// The V^T operand of the PV product is formed by two transposing LDS reads
-// per (16-key group, 32-dim block): source lane s addresses key 4*h + s/4 (+8
-// for the second read) of the group at dims 4*(s % 4) .. +3 of its 16-dim
-// half, so lane i receives dim i of four keys, which is the A-operand layout.
-template <typename T, int D, bool CAUSAL, int NW, int BC>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-fwd16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-               const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-               int B, int Hq, int Hkv, int N, float cl2) {
-    constexpr int BR = 32 * NW;
-    constexpr int KCH = D / 8;                 // 16-byte chunks per row
-    constexpr int TILE = BC * D * 2;           // bytes of one K or V tile
-    constexpr int STAGE = 2 * TILE;
-    constexpr int NKB = BC / 32;
-    constexpr int NKG = BC / 16;
-    constexpr int NDB = D / 32;
-    constexpr int NKS = D / 16;
-    constexpr int WI = TILE / 1024;            // 1 KB wave copies per tile
-    static_assert(WI % NW == 0, "tile copies split evenly over the waves");
-    constexpr int IPW = WI / NW;
-
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // provably wave-uniform
-    const int l32 = lane & 31;
-    const int hi = lane >> 5;
-
-    const int nqb = (N + BR - 1) / BR;
-    const int total = nqb * Hq * B;
-    const int logical = xcd_remap((int)blockIdx.x, total);
-    const int qb_raw = logical % nqb;
-    const int bh = logical / nqb;
-    const int qb = CAUSAL ? (nqb - 1 - qb_raw) : qb_raw;  // longest rows first
-    const int h = bh % Hq;
-    const int b = bh / Hq;
-    const int hk = h / (Hq / Hkv);
-
-    const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
-    const size_t koff = ((size_t)b * Hkv + hk) * (size_t)N * D;
-    const uint32_t head_bytes = (uint32_t)N * D * 2;
-    const Buf Qb(Q + qoff, head_bytes), Kb(K + koff, head_bytes), Vb(V + koff, head_bytes);
-
-    const int q0 = qb * BR;
-    const int qw = q0 + 32 * wave;
-    const int q = qw + l32;
-
-    u32x4 qf[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qf[ks] = Qb.load16((uint32_t)(q * D + 16 * ks + 8 * hi) * 2);
-
-    const int kv_len = CAUSAL ? min(N, q0 + BR) : N;
-    const int ntiles = (kv_len + BC - 1) / BC;
-
-    // Copy the K and V tiles starting at key k0 into LDS buffer `buf`: copy i
-    // of this wave fills bytes [1024 * bi, 1024 * bi + 1024) of each tile.
-    auto issue = [&](int k0, int buf) {
-        unsigned char* base = smem + buf * STAGE;
-#pragma unroll
-        for (int i = 0; i < IPW; ++i) {
-            const int bi = wave + NW * i;
-            const int p = bi * 64 + lane;  // 16-byte chunk slot in the tile
-            const int row = p / KCH, pc = p % KCH;
-            const uint32_t rowb = (uint32_t)(k0 + row) * D * 2;
-            buf_to_lds16(Kb, base + bi * 1024, rowb + (kq_off<D>(row, pc) - row * D * 2));
-            buf_to_lds16(Vb, base + TILE + bi * 1024, rowb + 16 * (pc ^ tr_swz<D>(row)));
-        }
-    };
-
-    // this lane's transposing-read coordinates inside a (16-key, 32-dim) block
-    const int g16 = lane >> 4;
-    const int j16 = lane & 15;
-    const int tr_row = 4 * hi + (j16 >> 2);
-    const int tr_col = 2 * (16 * (g16 & 1) + 4 * (j16 & 3));  // bytes
-
-    f32x16 o[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) o[db] = zero16();
-    float m_s = -INFINITY;
-    float l_s = 0.f;
-
-    issue(0, 0);
-    wait_vmem();
-    __syncthreads();
-
-    for (int j = 0; j < ntiles; ++j) {
-        const int k0 = j * BC;
-        // The copy of the next tile runs on every iteration, also the last
-        // (the extra tile lies inside this head's range and lands in the
-        // buffer no later iteration reads).
-        issue(k0 + BC, (j + 1) & 1);
-
-        const bool active = !CAUSAL || (k0 <= qw + 31);
-        if (active) {
-            const unsigned char* ks_base = smem + (j & 1) * STAGE;
-            const unsigned char* vt_base = ks_base + TILE;
-
-            // consecutive products go to different accumulators, so no product
-            // waits for the one issued just before it
-            f32x16 s[NKB];
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) s[kb] = zero16();
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) {
-                    const u32x4 a = *reinterpret_cast<const u32x4*>(
-                        ks_base + kq_off<D>(32 * kb + l32, 2 * ks + hi));
-                    s[kb] = Mma<T>::mma(a, qf[ks], s[kb]);
-                }
-
-            const bool need_mask = (CAUSAL && (k0 + BC - 1 > qw)) || (k0 + BC > N);
-            if (need_mask) {
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + 32 * kb + acc_row(r, hi);
-                        if ((CAUSAL && key > q) || key >= N) s[kb][r] = -INFINITY;
-                    }
-            }
-
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-            mx = fmaxf(mx, swap_halves(mx));
-            const float mt = mx * cl2;
-
-            if (__any(mt > m_s + kTau)) {
-                const float mn = fmaxf(m_s, mt);
-                const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m_s - mn);
-                l_s *= alpha;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-                m_s = mn;
-            }
-            const float mu = (m_s == -INFINITY) ? 0.f : m_s;
-
-            u32x4 pb[NKG];
-            float ls = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        const float p0 = fast_exp2(fmaf(s[kb][8 * t + 2 * jj], cl2, -mu));
-                        const float p1 = fast_exp2(fmaf(s[kb][8 * t + 2 * jj + 1], cl2, -mu));
-                        ls += p0 + p1;
-                        pb[2 * kb + t][jj] = Mma<T>::pack2(p0, p1);
-                    }
-            l_s += ls;
-
-#pragma unroll
-            for (int kg = 0; kg < NKG; ++kg)
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const int row = 16 * kg + tr_row;
-                    const int col = 64 * db + tr_col;
-                    const u32x2 lo = lds_read_tr16(vt_base + vt_off<D>(row, col));
-                    const u32x2 up = lds_read_tr16(vt_base + vt_off<D>(row + 8, col));
-                    u32x4 a;
-                    a[0] = lo[0]; a[1] = lo[1]; a[2] = up[0]; a[3] = up[1];
-                    o[db] = Mma<T>::mma(a, pb[kg], o[db]);
-                }
-        }
-
-        wait_vmem();
-        __syncthreads();
-    }
-
-    const float l_tot = l_s + swap_halves(l_s);
-    if (q < N) {
-        const float inv = 1.f / l_tot;
-        uint16_t* Orow = O + qoff + (size_t)q * D;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                u32x2 w;
-                w[0] = Mma<T>::pack2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
-                w[1] = Mma<T>::pack2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-                *reinterpret_cast<u32x2*>(Orow + 32 * db + 8 * g + 4 * hi) = w;
-            }
-        if (hi == 0) LSE[(size_t)(b * Hq + h) * N + q] = (m_s + __log2f(l_tot)) * kLn2;
-    }
-}
-
-// Fifth-generation 16-bit forward kernel: the v2 data path (buffer-to-LDS
-// copies, transposing V reads) with the key tiles split in two loops.  Tiles
+// registers; rows past N arrive as zeros), both row-major, and the V^T operand
+// of the P V product comes from transposing LDS reads.  The key tiles are
+// split in two loops.  Tiles
 // that lie wholly at or below every row of the block and inside the sequence
 // run a body with no mask code at all; the LDS buffer of each is a
 // compile-time constant (the loop handles tiles in pairs), so every LDS
@@ -784,18 +356,17 @@ fwd16v5_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 //    of a row, or scores that rose above m) the wave takes the slow path: the
 //    half's true row maximum, the rescale of the output and row sum, and the
 //    probabilities again.
-// 2. PIPE: the two halves of a tile are pipelined inside the wave: the
-//    scores of the second half are formed on the matrix cores while the vector
-//    unit exponentiates the first, and the P V products of the first half run
-//    while the second is exponentiated.  Without PIPE the halves run one after
-//    the other.
+// 2. The two halves of a tile are pipelined inside the wave: the scores of
+//    the second half are formed on the matrix cores while the vector unit
+//    exponentiates the first, and the P V products of the first half run
+//    while the second is exponentiated.
 // 3. As in the fifth generation, the tile's LDS reads go through a
 //    restrict-qualified buffer pointer, so they do not wait for the copies of
 //    the next tile.
 // 4. PERSIST: the grid holds one workgroup per compute unit, and each walks
 //    the row blocks persist_block() assigns it, which saves a workgroup launch
 //    per block.
-template <typename T, int D, bool CAUSAL, int NW, int BC, bool PIPE, bool PERSIST = false>
+template <typename T, int D, bool CAUSAL, int NW, int BC, bool PERSIST = false>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
@@ -963,26 +534,6 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 l_s += ls;
             };
 
-            if constexpr (!PIPE) {
-                static_for<2>([&](auto kc) {
-                    constexpr int kb = decltype(kc)::value;
-                    f32x16 sc = zero16();
-#pragma unroll
-                    for (int ks = 0; ks < NKS; ++ks) sc = Mma<T>::mma(kread(kb, ks), qf[ks], sc);
-                    mask_half(sc, kb);
-                    const float mu = (m_s == -INFINITY) ? 0.f : m_s;
-                    u32x4 pb[2];
-                    float ls = 0.f;
-#pragma unroll
-                    for (int t = 0; t < 8; ++t) exp_pair(sc, t, mu, ls, pb);
-                    settle(sc, ls, pb);
-#pragma unroll
-                    for (int t = 0; t < 2 * NDB; ++t)
-                        o[t % NDB] = Mma<T>::mma(vread(2 * kb + t / NDB, t % NDB), pb[t / NDB], o[t % NDB]);
-                });
-                return;
-            }
-
             const float mu = (m_s == -INFINITY) ? 0.f : m_s;
 
             // Every LDS operand is read at least one step before its product
@@ -1084,562 +635,6 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                     *reinterpret_cast<u32x2*>(Orow + 32 * db + 8 * g + 4 * hi) = w;
                 }
             if (hi == 0) LSE[(size_t)(b * Hq + h) * N + q] = (m_s + __log2f(l_tot)) * kLn2;
-        }
-    }
-}
-
-// Third-generation 16-bit forward kernel: the v2 data path (buffer-to-LDS
-// copies, transposing V reads) with a software pipeline across key tiles.
-// K runs one tile ahead of V: while a wave exponentiates the scores S_j of
-// tile j on the vector unit, it already issues the score products
-// S_{j+1} = K_{j+1} Q^T on the matrix cores (they do not depend on each
-// other), then the PV_j products.  LDS holds two K tiles (j+1 in use, j+2
-// arriving) and two V tiles (j in use, j+1 arriving).
-template <typename T, int D, bool CAUSAL, int NW, int BC>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-fwd16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-               const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-               int B, int Hq, int Hkv, int N, float cl2) {
-    constexpr int BR = 32 * NW;
-    constexpr int KCH = D / 8;
-    constexpr int TILE = BC * D * 2;
-    constexpr int NKB = BC / 32;
-    constexpr int NKG = BC / 16;
-    constexpr int NDB = D / 32;
-    constexpr int NKS = D / 16;
-    constexpr int WI = TILE / 1024;
-    static_assert(WI % NW == 0, "tile copies split evenly over the waves");
-    constexpr int IPW = WI / NW;
-    constexpr int KBUF = 0;          // two K tiles
-    constexpr int VBUF = 2 * TILE;   // two V tiles
-    constexpr int NSTEP = NKB * NKS; // score products per tile
-    constexpr int NPAIR = NKB * 8;   // packed probability pairs per tile
-    static_assert(NPAIR % NSTEP == 0, "pairs spread evenly over the products");
-    constexpr int PPS = NPAIR / NSTEP;
-    constexpr int AHEAD = 4;         // K operand reads issued ahead of use
-    constexpr int AHEAD_V = 3;       // V operands (two transposing reads each) ahead
-    constexpr int NPV = NKG * NDB;   // PV products per tile
-
-    __shared__ __attribute__((aligned(16))) unsigned char smem[4 * TILE];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l32 = lane & 31;
-    const int hi = lane >> 5;
-
-    const int nqb = (N + BR - 1) / BR;
-    const int total = nqb * Hq * B;
-    const int logical = xcd_remap((int)blockIdx.x, total);
-    const int qb_raw = logical % nqb;
-    const int bh = logical / nqb;
-    const int qb = CAUSAL ? (nqb - 1 - qb_raw) : qb_raw;
-    const int h = bh % Hq;
-    const int b = bh / Hq;
-    const int hk = h / (Hq / Hkv);
-
-    const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
-    const size_t koff = ((size_t)b * Hkv + hk) * (size_t)N * D;
-    const uint32_t head_bytes = (uint32_t)N * D * 2;
-    const Buf Qb(Q + qoff, head_bytes), Kb(K + koff, head_bytes), Vb(V + koff, head_bytes);
-
-    const int q0 = qb * BR;
-    const int qw = q0 + 32 * wave;
-    const int q = qw + l32;
-
-    u32x4 qf[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qf[ks] = Qb.load16((uint32_t)(q * D + 16 * ks + 8 * hi) * 2);
-
-    const int kv_len = CAUSAL ? min(N, q0 + BR) : N;
-    const int ntiles = (kv_len + BC - 1) / BC;
-    // tiles this wave needs (causal: those starting at or before its last row)
-    const int nact = CAUSAL ? min(ntiles, (qw + 31) / BC + 1) : ntiles;
-
-    // per-lane copy offsets (relative to the tile's first key)
-    uint32_t cpk[IPW], cpv[IPW];
-#pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-        const int p = (wave + NW * i) * 64 + lane;
-        const int row = p / KCH, pc = p % KCH;
-        cpk[i] = (uint32_t)kq_off<D>(row, pc);
-        cpv[i] = (uint32_t)(row * D * 2 + 16 * (pc ^ tr_swz<D>(row)));
-    }
-    auto issue_k = [&](int k0, int buf) {
-#pragma unroll
-        for (int i = 0; i < IPW; ++i)
-            buf_to_lds16(Kb, smem + KBUF + buf * TILE + (wave + NW * i) * 1024,
-                         (uint32_t)k0 * D * 2 + cpk[i]);
-    };
-    auto issue_v = [&](int k0, int buf) {
-#pragma unroll
-        for (int i = 0; i < IPW; ++i)
-            buf_to_lds16(Vb, smem + VBUF + buf * TILE + (wave + NW * i) * 1024,
-                         (uint32_t)k0 * D * 2 + cpv[i]);
-    };
-
-    // per-lane LDS read offsets
-    const int g16 = lane >> 4;
-    const int j16 = lane & 15;
-    const int tr_row = 4 * hi + (j16 >> 2);
-    int rv[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-        rv[db] = vt_off<D>(tr_row, 2 * (32 * db + 16 * (g16 & 1) + 4 * (j16 & 3)));
-
-    // lane parts of the K-row read offsets (block and buffer parts are added
-    // per tile, once, through lds_lane_off)
-    int rk[2][NKS];
-#pragma unroll
-    for (int par = 0; par < 2; ++par)
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) rk[par][ks] = kq_off<D>(32 * par + l32, 2 * ks + hi) - 32 * par * D * 2;
-    auto kread = [&](const uint32_t (&kl)[2][NKS], int step) {
-        const int kb = step / NKS;
-        return *reinterpret_cast<const u32x4*>(smem + kl[kb & 1][step % NKS] + 32 * kb * D * 2);
-    };
-    auto vread = [&](const uint32_t (&vl)[NDB], int pv) {
-        const int kg = pv / NDB, db = pv % NDB;
-        const u32x2 lo = lds_read_tr16(smem + vl[db] + 16 * kg * D * 2);
-        const u32x2 up = lds_read_tr16(smem + vl[db] + (16 * kg + 8) * D * 2);
-        u32x4 a;
-        a[0] = lo[0]; a[1] = lo[1]; a[2] = up[0]; a[3] = up[1];
-        return a;
-    };
-    // mask tile (k0) in place, then its row max in scale*log2(e) units
-    auto mask_max = [&](f32x16 (&sc)[NKB], int k0) {
-        const bool need_mask = (CAUSAL && (k0 + BC - 1 > qw)) || (k0 + BC > N);
-        if (need_mask) {
-            // a real branch: only the diagonal and ragged-end tiles pay for the mask
-            asm volatile("" ::: "memory");
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + 32 * kb + acc_row(r, hi);
-                    if ((CAUSAL && key > q) || key >= N) sc[kb][r] = -INFINITY;
-                }
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-        return halves_max(mx) * cl2;
-    };
-
-    f32x16 o[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) o[db] = zero16();
-    float m_s = -INFINITY;
-    float l_s = 0.f;
-
-    issue_k(0, 0);
-    issue_v(0, 0);
-    issue_k(BC, 1);
-    wait_vmem();
-    __syncthreads();
-
-    auto klanes = [&](uint32_t (&kl)[2][NKS], int buf) {
-#pragma unroll
-        for (int par = 0; par < 2; ++par)
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) kl[par][ks] = lds_lane_off((uint32_t)(KBUF + buf * TILE + rk[par][ks]));
-    };
-    f32x16 s[NKB];
-    {
-        uint32_t kl[2][NKS];
-        klanes(kl, 0);
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            s[kb] = zero16();
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) s[kb] = Mma<T>::mma(kread(kl, kb * NKS + ks), qf[ks], s[kb]);
-        }
-    }
-    float mt = mask_max(s, 0);
-
-    for (int j = 0; j < ntiles; ++j) {
-        const int k0 = j * BC;
-        // K_{j+2} replaces K_j (its scores were formed last iteration), V_{j+1}
-        // replaces V_{j-1}; every wave passed the barrier after their last use.
-        issue_k(k0 + 2 * BC, j & 1);
-        issue_v(k0 + BC, (j + 1) & 1);
-
-        if (j < nact) {
-            // s holds the masked scores of tile j and mt their row maximum
-            if (__any(mt > m_s + kTau)) {
-                const float mn = fmaxf(m_s, mt);
-                const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m_s - mn);
-                l_s *= alpha;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-                m_s = mn;
-            }
-            const float mu = (m_s == -INFINITY) ? 0.f : m_s;
-
-            // Region 1: score products of tile j+1 (matrix cores), one per
-            // step, interleaved with the probabilities of tile j (vector unit).
-            uint32_t kl[2][NKS];
-            klanes(kl, (j + 1) & 1);
-            f32x16 sn[NKB];
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) sn[kb] = zero16();
-            u32x4 ak[AHEAD];
-#pragma unroll
-            for (int t = 0; t < AHEAD; ++t) ak[t] = kread(kl, t);
-            u32x4 pb[NKG];
-            float ls = 0.f;
-#pragma unroll
-            for (int t = 0; t < NSTEP; ++t) {
-                const u32x4 a = ak[t % AHEAD];
-                if (t + AHEAD < NSTEP) ak[t % AHEAD] = kread(kl, t + AHEAD);
-                sn[t / NKS] = Mma<T>::mma(a, qf[t % NKS], sn[t / NKS]);
-#pragma unroll
-                for (int u = 0; u < PPS; ++u) {
-                    const int pr = t * PPS + u;              // pair index
-                    const int kb = pr >> 3, tt = (pr >> 2) & 1, jj = pr & 3;
-                    const int r = 8 * tt + 2 * jj;
-                    const float p0 = fast_exp2(fmaf(s[kb][r], cl2, -mu));
-                    const float p1 = fast_exp2(fmaf(s[kb][r + 1], cl2, -mu));
-                    ls += p0 + p1;
-                    pb[2 * kb + tt][jj] = Mma<T>::pack2(p0, p1);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            l_s += ls;
-
-            // Region 2: PV products of tile j, with the mask and row maximum of
-            // tile j+1 on the vector unit.
-            uint32_t vl[NDB];
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) vl[db] = lds_lane_off((uint32_t)(VBUF + (j & 1) * TILE + rv[db]));
-            u32x4 av[AHEAD_V];
-#pragma unroll
-            for (int t = 0; t < AHEAD_V; ++t) av[t] = vread(vl, t);
-#pragma unroll
-            for (int pv = 0; pv < NPV; ++pv) {
-                const u32x4 a = av[pv % AHEAD_V];
-                if (pv + AHEAD_V < NPV) av[pv % AHEAD_V] = vread(vl, pv + AHEAD_V);
-                o[pv % NDB] = Mma<T>::mma(a, pb[pv / NDB], o[pv % NDB]);
-            }
-            mt = mask_max(sn, k0 + BC);
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) s[kb] = sn[kb];
-        }
-
-        wait_vmem();
-        __syncthreads();
-    }
-
-    const float l_tot = l_s + swap_halves(l_s);
-    if (q < N) {
-        const float inv = 1.f / l_tot;
-        uint16_t* Orow = O + qoff + (size_t)q * D;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                u32x2 w;
-                w[0] = Mma<T>::pack2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
-                w[1] = Mma<T>::pack2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-                *reinterpret_cast<u32x2*>(Orow + 32 * db + 8 * g + 4 * hi) = w;
-            }
-        if (hi == 0) LSE[(size_t)(b * Hq + h) * N + q] = (m_s + __log2f(l_tot)) * kLn2;
-    }
-}
-
-// Fourth-generation 16-bit forward kernel.  Each of the four waves owns 64
-// query rows (two 32-row blocks), so every K or V^T operand read from LDS
-// feeds two matrix-core products: LDS read traffic per FLOP is half that of
-// the 32-row kernels, whose eight waves re-read every tile.  One wave per
-// SIMD (the O accumulators live in the accumulator registers); the overlap of
-// vector and matrix work comes from the software pipeline of the v3 kernel:
-// K runs one tile ahead of V, the score products of tile j+1 (both row
-// blocks, sharing each K read) are interleaved with the probabilities of tile
-// j, and the PV products of tile j carry the mask and row maximum of tile j+1.
-template <typename T, int D, bool CAUSAL, int BC>
-__global__ void __launch_bounds__(256)
-fwd16v4_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-               const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-               int B, int Hq, int Hkv, int N, float cl2) {
-    constexpr int NW = 4;
-    constexpr int QB = 2;                // 32-row blocks per wave
-    constexpr int BR = 32 * QB * NW;     // 256 rows per workgroup
-    constexpr int KCH = D / 8;
-    constexpr int TILE = BC * D * 2;
-    constexpr int NKB = BC / 32;
-    constexpr int NKG = BC / 16;
-    constexpr int NDB = D / 32;
-    constexpr int NKS = D / 16;
-    constexpr int WI = TILE / 1024;
-    static_assert(WI % NW == 0, "tile copies split evenly over the waves");
-    constexpr int IPW = WI / NW;
-    constexpr int KBUF = 0;
-    constexpr int VBUF = 2 * TILE;
-    constexpr int NSTEP = NKB * NKS;     // K operand reads per tile
-    constexpr int NPAIR = QB * NKB * 8;  // probability pairs per tile (both blocks)
-    static_assert(NPAIR % NSTEP == 0, "pairs spread evenly over the steps");
-    constexpr int PPS = NPAIR / NSTEP;
-    constexpr int AHEAD = 3;
-    constexpr int AHEAD_V = 2;
-    constexpr int NPV = NKG * NDB;       // V operands per tile
-
-    __shared__ __attribute__((aligned(16))) unsigned char smem[4 * TILE];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l32 = lane & 31;
-    const int hi = lane >> 5;
-
-    const int nqb = (N + BR - 1) / BR;
-    const int total = nqb * Hq * B;
-    const int logical = xcd_remap((int)blockIdx.x, total);
-    const int qb_raw = logical % nqb;
-    const int bh = logical / nqb;
-    const int qblk = CAUSAL ? (nqb - 1 - qb_raw) : qb_raw;
-    const int h = bh % Hq;
-    const int b = bh / Hq;
-    const int hk = h / (Hq / Hkv);
-
-    const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
-    const size_t koff = ((size_t)b * Hkv + hk) * (size_t)N * D;
-    const uint32_t head_bytes = (uint32_t)N * D * 2;
-    const Buf Qb(Q + qoff, head_bytes), Kb(K + koff, head_bytes), Vb(V + koff, head_bytes);
-
-    const int q0 = qblk * BR;
-    const int qw = q0 + 64 * wave;       // first row of this wave
-    int qrow[QB];
-#pragma unroll
-    for (int r = 0; r < QB; ++r) qrow[r] = qw + 32 * r + l32;
-
-    u32x4 qf[QB][NKS];
-#pragma unroll
-    for (int r = 0; r < QB; ++r)
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-            qf[r][ks] = Qb.load16((uint32_t)(qrow[r] * D + 16 * ks + 8 * hi) * 2);
-
-    const int kv_len = CAUSAL ? min(N, q0 + BR) : N;
-    const int ntiles = (kv_len + BC - 1) / BC;
-    const int nact = CAUSAL ? min(ntiles, (qw + 63) / BC + 1) : ntiles;
-
-    uint32_t cpk[IPW], cpv[IPW];
-#pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-        const int p = (wave + NW * i) * 64 + lane;
-        const int row = p / KCH, pc = p % KCH;
-        cpk[i] = (uint32_t)kq_off<D>(row, pc);
-        cpv[i] = (uint32_t)(row * D * 2 + 16 * (pc ^ tr_swz<D>(row)));
-    }
-    auto issue_k = [&](int k0, int buf) {
-#pragma unroll
-        for (int i = 0; i < IPW; ++i)
-            buf_to_lds16(Kb, smem + KBUF + buf * TILE + (wave + NW * i) * 1024,
-                         (uint32_t)k0 * D * 2 + cpk[i]);
-    };
-    auto issue_v = [&](int k0, int buf) {
-#pragma unroll
-        for (int i = 0; i < IPW; ++i)
-            buf_to_lds16(Vb, smem + VBUF + buf * TILE + (wave + NW * i) * 1024,
-                         (uint32_t)k0 * D * 2 + cpv[i]);
-    };
-
-    const int g16 = lane >> 4;
-    const int j16 = lane & 15;
-    const int tr_row = 4 * hi + (j16 >> 2);
-    int rv[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-        rv[db] = vt_off<D>(tr_row, 2 * (32 * db + 16 * (g16 & 1) + 4 * (j16 & 3)));
-    auto kread = [&](const unsigned char* kb_base, int step) {
-        return *reinterpret_cast<const u32x4*>(
-            kb_base + kq_off<D>(32 * (step / NKS) + l32, 2 * (step % NKS) + hi));
-    };
-    auto vread = [&](const unsigned char* v_base, int pv) {
-        const int kg = pv / NDB, db = pv % NDB;
-        const u32x2 lo = lds_read_tr16(v_base + rv[db] + 16 * kg * D * 2);
-        const u32x2 up = lds_read_tr16(v_base + rv[db] + (16 * kg + 8) * D * 2);
-        u32x4 a;
-        a[0] = lo[0]; a[1] = lo[1]; a[2] = up[0]; a[3] = up[1];
-        return a;
-    };
-    auto mask_max = [&](f32x16 (&sc)[NKB], int k0, int qr, int qfirst) {
-        const bool need_mask = (CAUSAL && (k0 + BC - 1 > qfirst)) || (k0 + BC > N);
-        if (need_mask) {
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + 32 * kb + acc_row(r, hi);
-                    if ((CAUSAL && key > qr) || key >= N) sc[kb][r] = -INFINITY;
-                }
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-        mx = fmaxf(mx, swap_halves(mx));
-        return mx * cl2;
-    };
-
-    f32x16 o[QB][NDB];
-#pragma unroll
-    for (int r = 0; r < QB; ++r)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) o[r][db] = zero16();
-    float m_s[QB], l_s[QB], mt[QB];
-#pragma unroll
-    for (int r = 0; r < QB; ++r) {
-        m_s[r] = -INFINITY;
-        l_s[r] = 0.f;
-    }
-
-    issue_k(0, 0);
-    issue_v(0, 0);
-    issue_k(BC, 1);
-    wait_vmem();
-    __syncthreads();
-
-    f32x16 s[QB][NKB];
-#pragma unroll
-    for (int r = 0; r < QB; ++r)
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) s[r][kb] = zero16();
-#pragma unroll
-    for (int t = 0; t < NSTEP; ++t) {
-        const u32x4 a = kread(smem + KBUF, t);
-#pragma unroll
-        for (int r = 0; r < QB; ++r) s[r][t / NKS] = Mma<T>::mma(a, qf[r][t % NKS], s[r][t / NKS]);
-    }
-#pragma unroll
-    for (int r = 0; r < QB; ++r) {
-        mt[r] = mask_max(s[r], 0, qrow[r], qw + 32 * r);
-        m_s[r] = mt[r];  // O and l are still zero: no rescale for the first tile
-    }
-
-    // The fast loop never touches O on the vector unit (O only accumulates
-    // matrix-core products), which keeps it in the accumulator registers.
-    // When a tile's maximum exceeds the running one by more than kTau, the
-    // loop exits to the rescale below and resumes at the same tile.
-    int j = 0;
-    for (;;) {
-        for (; j < ntiles; ++j) {
-            const int k0 = j * BC;
-            if (j < nact) {
-                bool grow = false;
-#pragma unroll
-                for (int r = 0; r < QB; ++r) grow |= __any(mt[r] > m_s[r] + kTau);
-                if (grow) break;
-            }
-            issue_k(k0 + 2 * BC, j & 1);
-            issue_v(k0 + BC, (j + 1) & 1);
-
-            if (j < nact) {
-                float mu[QB];
-#pragma unroll
-                for (int r = 0; r < QB; ++r) mu[r] = (m_s[r] == -INFINITY) ? 0.f : m_s[r];
-
-                // Region 1: score products of tile j+1 (each K read feeds both
-                // row blocks) interleaved with the probabilities of tile j.
-                const unsigned char* kn = smem + KBUF + ((j + 1) & 1) * TILE;
-                f32x16 sn[QB][NKB];
-#pragma unroll
-                for (int r = 0; r < QB; ++r)
-#pragma unroll
-                    for (int kb = 0; kb < NKB; ++kb) sn[r][kb] = zero16();
-                u32x4 ak[AHEAD];
-#pragma unroll
-                for (int t = 0; t < AHEAD; ++t) ak[t] = kread(kn, t);
-                u32x4 pb[QB][NKG];
-                float ls[QB];
-#pragma unroll
-                for (int r = 0; r < QB; ++r) ls[r] = 0.f;
-#pragma unroll
-                for (int t = 0; t < NSTEP; ++t) {
-                    const u32x4 a = ak[t % AHEAD];
-                    if (t + AHEAD < NSTEP) ak[t % AHEAD] = kread(kn, t + AHEAD);
-#pragma unroll
-                    for (int r = 0; r < QB; ++r)
-                        sn[r][t / NKS] = Mma<T>::mma(a, qf[r][t % NKS], sn[r][t / NKS]);
-#pragma unroll
-                    for (int u = 0; u < PPS; ++u) {
-                        const int pr = t * PPS + u;
-                        const int r = pr / (NKB * 8);
-                        const int pq = pr % (NKB * 8);
-                        const int kb = pq >> 3, tt = (pq >> 2) & 1, jj = pq & 3;
-                        const int e = 8 * tt + 2 * jj;
-                        const float p0 = fast_exp2(fmaf(s[r][kb][e], cl2, -mu[r]));
-                        const float p1 = fast_exp2(fmaf(s[r][kb][e + 1], cl2, -mu[r]));
-                        ls[r] += p0 + p1;
-                        pb[r][2 * kb + tt][jj] = Mma<T>::pack2(p0, p1);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-#pragma unroll
-                for (int r = 0; r < QB; ++r) l_s[r] += ls[r];
-
-                // Region 2: PV products of tile j (each V^T operand feeds both
-                // row blocks), then the mask and row maximum of tile j+1.
-                const unsigned char* v_base = smem + VBUF + (j & 1) * TILE;
-                u32x4 av[AHEAD_V];
-#pragma unroll
-                for (int t = 0; t < AHEAD_V; ++t) av[t] = vread(v_base, t);
-#pragma unroll
-                for (int pv = 0; pv < NPV; ++pv) {
-                    const u32x4 a = av[pv % AHEAD_V];
-                    if (pv + AHEAD_V < NPV) av[pv % AHEAD_V] = vread(v_base, pv + AHEAD_V);
-#pragma unroll
-                    for (int r = 0; r < QB; ++r)
-                        o[r][pv % NDB] = Mma<T>::mma(a, pb[r][pv / NDB], o[r][pv % NDB]);
-                }
-#pragma unroll
-                for (int r = 0; r < QB; ++r) {
-                    mt[r] = mask_max(sn[r], k0 + BC, qrow[r], qw + 32 * r);
-#pragma unroll
-                    for (int kb = 0; kb < NKB; ++kb) s[r][kb] = sn[r][kb];
-                }
-            }
-
-            wait_vmem();
-            __syncthreads();
-        }
-        if (j >= ntiles) break;
-        // rescale for the maximum of tile j, then resume at tile j
-#pragma unroll
-        for (int r = 0; r < QB; ++r) {
-            const float mn = fmaxf(m_s[r], mt[r]);
-            const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m_s[r] - mn);
-            l_s[r] *= alpha;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) o[r][db][e] *= alpha;
-            m_s[r] = mn;
-        }
-    }
-
-#pragma unroll
-    for (int r = 0; r < QB; ++r) {
-        const int q = qrow[r];
-        const float l_tot = l_s[r] + swap_halves(l_s[r]);
-        if (q < N) {
-            const float inv = 1.f / l_tot;
-            uint16_t* Orow = O + qoff + (size_t)q * D;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    u32x2 w;
-                    w[0] = Mma<T>::pack2(o[r][db][4 * g] * inv, o[r][db][4 * g + 1] * inv);
-                    w[1] = Mma<T>::pack2(o[r][db][4 * g + 2] * inv, o[r][db][4 * g + 3] * inv);
-                    *reinterpret_cast<u32x2*>(Orow + 32 * db + 8 * g + 4 * hi) = w;
-                }
-            if (hi == 0) LSE[(size_t)(b * Hq + h) * N + q] = (m_s[r] + __log2f(l_tot)) * kLn2;
         }
     }
 }
@@ -1757,28 +752,6 @@ fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const flo
     }
 }
 
-template <typename T, int D, bool CAUSAL, int NW, int BC>
-hipError_t launch16(const FwdArgs& a) {
-    constexpr int BR = 32 * NW;
-    const int nqb = (a.N + BR - 1) / BR;
-    const long long total = (long long)nqb * a.Hq * a.B;
-    hipLaunchKernelGGL((fwd16_kernel<T, D, CAUSAL, NW, BC>), dim3((unsigned)total), dim3(NW * 64), 0,
-                       a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.N, a.cl2);
-    return hipGetLastError();
-}
-
-template <typename T, int D, bool CAUSAL, int NW, int BC>
-hipError_t launch16v2(const FwdArgs& a) {
-    constexpr int BR = 32 * NW;
-    const int nqb = (a.N + BR - 1) / BR;
-    const long long total = (long long)nqb * a.Hq * a.B;
-    hipLaunchKernelGGL((fwd16v2_kernel<T, D, CAUSAL, NW, BC>), dim3((unsigned)total), dim3(NW * 64),
-                       0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                       (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.N, a.cl2);
-    return hipGetLastError();
-}
-
 template <typename T, int D, bool CAUSAL, int NW, int BC, bool DROP = false, bool SPARSE = false>
 hipError_t launch16v5(const FwdArgs& a) {
     constexpr int BR = 32 * NW;
@@ -1791,7 +764,7 @@ hipError_t launch16v5(const FwdArgs& a) {
     return hipGetLastError();
 }
 
-template <typename T, int D, bool CAUSAL, int NW, int BC, bool PIPE, bool PERSIST = false>
+template <typename T, int D, bool CAUSAL, int NW, int BC, bool PERSIST = false>
 hipError_t launch16v6(const FwdArgs& a) {
     constexpr int BR = 32 * NW;
     const int nqb = (a.N + BR - 1) / BR;
@@ -1802,41 +775,19 @@ hipError_t launch16v6(const FwdArgs& a) {
         static const int per_cu = [] {
             int n = 0;
             return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                       &n, reinterpret_cast<const void*>(fwd16v6_kernel<T, D, CAUSAL, NW, BC, PIPE, true>), NW * 64,
+                       &n, reinterpret_cast<const void*>(fwd16v6_kernel<T, D, CAUSAL, NW, BC, true>), NW * 64,
                        0) == hipSuccess ? n : 0;
         }();
         grid = persistent_grid() * per_cu;
     }
     if (grid >= 8 && total > grid)
-        hipLaunchKernelGGL((fwd16v6_kernel<T, D, CAUSAL, NW, BC, PIPE, true>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((fwd16v6_kernel<T, D, CAUSAL, NW, BC, true>), dim3((unsigned)grid),
                            dim3(NW * 64), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                            (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.N, a.cl2);
     else
-        hipLaunchKernelGGL((fwd16v6_kernel<T, D, CAUSAL, NW, BC, PIPE>), dim3((unsigned)total), dim3(NW * 64),
+        hipLaunchKernelGGL((fwd16v6_kernel<T, D, CAUSAL, NW, BC>), dim3((unsigned)total), dim3(NW * 64),
                            0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                            (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.N, a.cl2);
-    return hipGetLastError();
-}
-
-template <typename T, int D, bool CAUSAL, int NW, int BC>
-hipError_t launch16v3(const FwdArgs& a) {
-    constexpr int BR = 32 * NW;
-    const int nqb = (a.N + BR - 1) / BR;
-    const long long total = (long long)nqb * a.Hq * a.B;
-    hipLaunchKernelGGL((fwd16v3_kernel<T, D, CAUSAL, NW, BC>), dim3((unsigned)total), dim3(NW * 64),
-                       0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                       (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.N, a.cl2);
-    return hipGetLastError();
-}
-
-template <typename T, int D, bool CAUSAL, int BC>
-hipError_t launch16v4(const FwdArgs& a) {
-    constexpr int BR = 256;
-    const int nqb = (a.N + BR - 1) / BR;
-    const long long total = (long long)nqb * a.Hq * a.B;
-    hipLaunchKernelGGL((fwd16v4_kernel<T, D, CAUSAL, BC>), dim3((unsigned)total), dim3(256), 0,
-                       a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.N, a.cl2);
     return hipGetLastError();
 }
 
@@ -1850,19 +801,20 @@ hipError_t launch32(const FwdArgs& a) {
     return hipGetLastError();
 }
 
-// Kernel / tile variants.  The default at d = 128 is the sixth generation
-// with eight 32-row waves (one workgroup per compute unit, two waves per
-// SIMD; the pipelined halves give each wave its own overlap of matrix and
-// vector work, and eight waves halve the copies per wave and the L2 traffic
-// per query row); at d = 64 it is the sixth generation with four waves and
-// 64-key tiles (three waves per SIMD fit in the registers).  Dropout and block
-// masks run on the fifth generation with four waves (variant 14 of both
-// tables: two workgroups per compute unit, so the waves that share a SIMD
-// belong to different workgroups).  The others are kept for tile sweeps.
+// Kernel choice.  d = 128: the sixth generation with eight 32-row waves (one
+// workgroup per compute unit, two waves per SIMD; the pipelined halves give
+// each wave its own overlap of matrix and vector work, and eight waves halve
+// the copies per wave and the L2 traffic per query row), on the persistent
+// grid.  d = 64: the sixth generation with four waves and 64-key tiles (three
+// waves per SIMD fit in the registers), on the persistent grid under the
+// causal mask only (without it, one row block per workgroup measures faster
+// at this head dimension).  Dropout runs the fifth generation with eight
+// waves at d = 128 and four waves with 128-key tiles at d = 64; block masks
+// and variable lengths run it with four waves (two workgroups per compute
+// unit, so the waves that share a SIMD belong to different workgroups).
 template <typename T, int D, bool CAUSAL>
 hipError_t dispatch16c(const FwdArgs& a) {
     if (a.drop) {
-        // dropout and block masks run on the default tiling only
         if constexpr (D == 128) return launch16v5<T, D, CAUSAL, 8, 64, true>(a);
         else return launch16v5<T, D, CAUSAL, 4, 128, true>(a);
     }
@@ -1870,53 +822,9 @@ hipError_t dispatch16c(const FwdArgs& a) {
         if constexpr (D == 128) return launch16v5<T, D, CAUSAL, 4, 64, false, true>(a);
         else return launch16v5<T, D, CAUSAL, 4, 128, false, true>(a);
     }
-    if constexpr (D == 128) {
-        switch (a.fwd_variant) {
-            case 1: return launch16<T, D, CAUSAL, 4, 64>(a);
-            case 2: return launch16<T, D, CAUSAL, 8, 128>(a);
-            case 3: return launch16v2<T, D, CAUSAL, 8, 64>(a);
-            case 4: return launch16v2<T, D, CAUSAL, 4, 64>(a);
-            case 5: return launch16v3<T, D, CAUSAL, 8, 64>(a);
-            case 6: return launch16v3<T, D, CAUSAL, 4, 64>(a);
-            case 7: return launch16v4<T, D, CAUSAL, 32>(a);
-            case 8: return launch16v4<T, D, CAUSAL, 64>(a);
-            case 9: return launch16<T, D, CAUSAL, 8, 64>(a);
-            case 10: return launch16v5<T, D, CAUSAL, 8, 64>(a);
-            case 11: return launch16v5<T, D, CAUSAL, 4, 64>(a);
-            case 12: return launch16v2<T, D, CAUSAL, 8, 64>(a);
-            case 13: return launch16v6<T, D, CAUSAL, 4, 64, true>(a);
-            case 14: return launch16v5<T, D, CAUSAL, 4, 64>(a);
-            case 15: return launch16v6<T, D, CAUSAL, 4, 64, false>(a);
-            case 16: return launch16v6<T, D, CAUSAL, 8, 128, true>(a);
-            case 17: return launch16v6<T, D, CAUSAL, 8, 64, true>(a);
-            default: return launch16v6<T, D, CAUSAL, 8, 64, true, true>(a);
-        }
-    } else {
-        switch (a.fwd_variant) {
-            case 1: return launch16<T, D, CAUSAL, 4, 64>(a);
-            case 2: return launch16<T, D, CAUSAL, 4, 128>(a);
-            case 3: return launch16v2<T, D, CAUSAL, 8, 128>(a);
-            case 4: return launch16v2<T, D, CAUSAL, 4, 128>(a);
-            case 5: return launch16v3<T, D, CAUSAL, 8, 64>(a);
-            case 6: return launch16v3<T, D, CAUSAL, 4, 64>(a);
-            case 7: return launch16v4<T, D, CAUSAL, 32>(a);
-            case 8: return launch16v4<T, D, CAUSAL, 64>(a);
-            case 9: return launch16<T, D, CAUSAL, 8, 128>(a);
-            case 10: return launch16v5<T, D, CAUSAL, 8, 128>(a);
-            case 11: return launch16v5<T, D, CAUSAL, 4, 128>(a);
-            case 12: return launch16v2<T, D, CAUSAL, 8, 128>(a);
-            case 13: return launch16v6<T, D, CAUSAL, 4, 128, true>(a);
-            case 14: return launch16v5<T, D, CAUSAL, 4, 128>(a);
-            case 15: return launch16v6<T, D, CAUSAL, 8, 64, true>(a);
-            case 16: return launch16v6<T, D, CAUSAL, 8, 128, true>(a);
-            case 17: return launch16v6<T, D, CAUSAL, 4, 64, true>(a);
-            default:
-                // persistent grid under the causal mask only (without it, one row
-                // block per workgroup measures faster at this head dimension)
-                if constexpr (CAUSAL) return launch16v6<T, D, CAUSAL, 4, 64, true, true>(a);
-                else return launch16v6<T, D, CAUSAL, 4, 64, true>(a);
-        }
-    }
+    if constexpr (D == 128) return launch16v6<T, D, CAUSAL, 8, 64, true>(a);
+    else if constexpr (CAUSAL) return launch16v6<T, D, CAUSAL, 4, 64, true>(a);
+    else return launch16v6<T, D, CAUSAL, 4, 64, false>(a);
 }
 
 template <typename T, int D>

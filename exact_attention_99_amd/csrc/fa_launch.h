@@ -39,7 +39,6 @@ struct FwdArgs {
     int causal;
     float cl2;       // scale * log2(e)
     int dtype;       // fa_dtype value
-    int fwd_variant; // tile variant of the 16-bit kernel (0 = default)
     int drop;        // 1: apply dropout with dp
     DropParams dp;
     int sparse;      // 1: apply the block mask sp
@@ -63,7 +62,6 @@ struct BwdArgs {
     float scale;
     float cl2;
     int dtype;
-    int variant;     // kernel generation of the 16-bit passes (0 = default)
     int drop;        // 1: apply dropout with dp
     DropParams dp;
     int sparse;      // 1: apply the block mask sp
@@ -112,7 +110,6 @@ struct Fp8FwdArgs {
     int causal;
     float cl2;
     int out_dtype;
-    int variant;         // tile variant (0 = default)
     hipStream_t stream;
 };
 

@@ -28,7 +28,9 @@
  * Ownership: every pointer is a device pointer owned by the caller; the
  * library allocates no device memory and keeps no pointer after a call
  * returns.  Inputs are only read.  Outputs must not overlap inputs or each
- * other.  Every buffer must be 16-byte aligned.
+ * other.  Every buffer must be 16-byte aligned.  The library's only state is
+ * a per-device cache of the compute-unit count, initialised once in a
+ * thread-safe way.
  *
  * Timing and errors: calls enqueue work on `stream` and return without
  * synchronising.  Argument errors are reported synchronously and nothing is

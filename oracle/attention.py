@@ -9,10 +9,9 @@ arithmetic.
 
 What it computes is the plain definition, not the tiled algorithm.  The pages
 state that FlashAttention returns the same result as standard attention, up to
-floating-point rounding ("FlashAttention" glossary page: "mathematically
-identical results"; "FlashAttention and the Kernel Era", The Breakthrough:
-"the same output, to floating-point precision"), so the reference answer is
-standard attention evaluated in float64, materialising S and P:
+floating-point rounding (the "FlashAttention" glossary page, first paragraph;
+"FlashAttention and the Kernel Era", The Breakthrough), so the reference
+answer is standard attention evaluated in float64, materialising S and P:
 
     S = scale * Q K^T                 ("FlashAttention and the Kernel Era",
     P = softmax(S)  (row-wise)          The Mathematics, the SDPA equation;

@@ -30,7 +30,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_blocksparse", "fa_bwd_dkdv", "fa_bwd_dq",
-                                    "fa_bwd_dropout", "fa_bwd_prepare", "fa_bwd_varlen",
+                                    "fa_bwd_dropout", "fa_bwd_prepare",
+                                    "fa_bwd_varlen",
                                     "fa_bwd_workspace_size", "fa_fp8_quantize", "fa_fwd",
                                     "fa_fwd_blocksparse", "fa_fwd_dropout", "fa_fwd_fp8",
                                     "fa_fwd_splitkv", "fa_fwd_splitkv_default_splits",
@@ -288,3 +289,34 @@ def test_varlen_entry_points_reject(lib):
     assert lib.fa_bwd_varlen(*([A] * 10), need, None, 2, 4, 2, 300, 128, 1, 0.1, BF16, None) == INVALID
     assert lib.fa_bwd_varlen(*([A] * 10), need - 1, A, 2, 4, 2, 300, 128, 1, 0.1, BF16, None) == INVALID
     assert lib.fa_bwd_varlen(*([A] * 10), need, A, 2, 4, 2, 300, 128, 1, 0.1, FP32, None) == UNSUPPORTED
+
+
+def test_binding_checks_buffers_before_the_call(lib):
+    """The binding checks the shape and dtype of every tensor it hands over
+    (the layouts of include/fa355.h) and that they live on a GPU, so a
+    mis-sized output raises instead of reaching a kernel."""
+    import torch
+    B, Hq, Hkv, N, d = 1, 4, 2, 64, 64
+    q = torch.zeros(B, Hq, N, d, dtype=torch.bfloat16)
+    k = torch.zeros(B, Hkv, N, d, dtype=torch.bfloat16)
+    v = torch.zeros_like(k)
+    lse = torch.zeros(B, Hq, N)
+    with pytest.raises(ValueError, match="o must be"):
+        _abi.fa_fwd(q, k, v, True, 0.1, o=torch.zeros(B, Hq, N - 1, d, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="lse must be"):
+        _abi.fa_fwd(q, k, v, True, 0.1, lse=torch.zeros(B, Hq, N, dtype=torch.float64))
+    with pytest.raises(ValueError, match="GPU"):
+        _abi.fa_fwd(q, k, v, True, 0.1)
+    with pytest.raises(ValueError, match="dout must be"):
+        _abi.fa_bwd(q, k, v, q, lse, q.to(torch.float16), True, 0.1)
+    with pytest.raises(ValueError, match="dk must be"):
+        _abi.fa_bwd(q, k, v, q, lse, q, True, 0.1, dk=torch.zeros_like(q))
+    with pytest.raises(ValueError, match="lse must be"):
+        _abi.fa_bwd_dq(q, k, v, lse[:, :2], q, lse, True, 0.1)
+    with pytest.raises(ValueError, match="delta must be"):
+        _abi.fa_bwd_dkdv(q, k, v, lse, q, lse[..., :8], True, 0.1)
+    with pytest.raises(ValueError, match="dout must be"):
+        _abi.fa_bwd_prepare(q, k)
+    with pytest.raises(TypeError, match="share a dtype"):
+        _abi.fa_bwd(q, k.float(), v, q, lse, q, True, 0.1)
+

@@ -179,9 +179,10 @@ def test_scale_values(scale):
     torch.cuda.synchronize()
     O, L = oracle.attention_forward(workloads.to_f64(q), workloads.to_f64(k), workloads.to_f64(v),
                                     scale, True)
-    omax, _ = errs(o, O)
-    lmax, _ = errs(lse, L)
-    assert omax <= 2e-2 and lmax <= 1e-3 * max(1.0, scale * 20), (omax, lmax)
+    # the 16-bit tolerances at every scale: the lse is an fp32 sum of exponentials
+    # of fp32 scores (relative error ~1e-6 of its magnitude, which grows with
+    # the scale to about 10^2 here), far below the 1e-3 bound
+    check_fwd(o, lse, O, L, "bf16", f"scale={scale}")
 
 
 @pytest.mark.parametrize("pattern", ["rising", "falling", "huge_first"])

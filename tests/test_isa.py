@@ -6,9 +6,8 @@ from the copies' LDS writes, it puts a wait on the vector-memory counter right
 before the read, so the read waits for the copy of the *next* tile and the copy
 no longer overlaps the current one (dK/dV ran 6% slower that way).  The kernels
 read each tile through restrict-qualified buffer pointers so that the compiler
-can tell; this test keeps it that way for every instantiation of the kernels
-that the entry points run (the older generations kept for tile sweeps are not
-checked).
+can tell; this test keeps it that way for every kernel instantiation in the
+library (all of them are reachable through the entry points).
 """
 from __future__ import annotations
 

@@ -1,0 +1,98 @@
+"""Many short heads: the row and key blocks outnumber the compute units, so the
+forward and the dK/dV pass run on their persistent grids (each workgroup walks
+several blocks, and under grouped K/V heads the dK/dV pass walks the query
+heads of a group per step), with a ragged sequence end in every head.
+
+B = 16, H_q = 32, H_kv = 8 (G = 4), N = 700, d in {64, 128}, bf16 and fp16,
+both masks.  Sampled heads (first, last and one whole K/V group) are compared
+with the fp64 oracle; every head is checked through properties that hold at
+any size: the Q = 0 closed form of the forward, and the backward identities
+sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i over each K/V group.
+"""
+from __future__ import annotations
+
+import math
+
+import pytest
+import torch
+
+import oracle
+import workloads
+from exact_attention_99_amd import fa_bwd, fa_fwd
+
+from .parity import TOL, check_fwd, check_grads
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+f64 = workloads.to_f64
+
+B, HQ, HKV, N = 16, 32, 8, 700
+G = HQ // HKV
+HEADS = ((0, 0), (7, 4), (7, 5), (7, 6), (7, 7), (B - 1, HQ - 1))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_many_short_heads_forward_and_backward(dtype, d, causal):
+    print(f"case dtype={dtype} d={d} causal={causal}", flush=True)
+    scale = 1.0 / math.sqrt(d)
+    q, k, v, do = workloads.make_inputs(B, HQ, HKV, N, d, dtype, 4100 + d + (7 if causal else 0),
+                                        with_dout=True)
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    o, lse = fa_fwd(qd, kd, vd, causal, scale)
+    dq, dk, dv = fa_bwd(qd, kd, vd, o, lse, dod, causal, scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t).all()
+
+    for (b, h) in HEADS:
+        hk = h // G
+        O, L = oracle.attention_forward(f64(q[b:b + 1, h:h + 1]), f64(k[b:b + 1, hk:hk + 1]),
+                                        f64(v[b:b + 1, hk:hk + 1]), scale, causal)
+        check_fwd(o[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1], O, L, dtype, f"b={b} h={h}")
+
+    # backward: one whole K/V group (its dK, dV sum the group's G query heads)
+    for (b, hk) in ((0, 0), (7, 1), (B - 1, HKV - 1)):
+        hs = slice(hk * G, (hk + 1) * G)
+        dQ, dK, dV, _, _ = oracle.attention_backward(
+            f64(q[b:b + 1, hs]), f64(k[b:b + 1, hk:hk + 1]), f64(v[b:b + 1, hk:hk + 1]),
+            f64(do[b:b + 1, hs]), scale, causal)
+        check_grads(dq[b:b + 1, hs], dk[b:b + 1, hk:hk + 1], dv[b:b + 1, hk:hk + 1], dQ, dK, dV,
+                    dtype, f"b={b} kv head {hk}")
+
+    # every K/V group: rowsum(dS) = 0 gives sum_j dK_j = 0 and
+    # sum_j dV_j = sum over the group's query heads and rows of dO
+    dk64, dv64 = dk.to(torch.float64), dv.to(torch.float64)
+    sk = dk64.sum(dim=2)
+    assert (sk.abs() <= 1e-3 * dk64.abs().sum(dim=2) + 1e-3).all(), sk.abs().max().item()
+    target = dod.to(torch.float64).view(B, HKV, G, N, d).sum(dim=(2, 3))
+    sv = dv64.sum(dim=2)
+    err = (sv - target).abs()
+    assert (err <= 1e-3 * dv64.abs().sum(dim=2) + 1e-3).all(), err.max().item()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_many_short_heads_closed_form(dtype, d, causal):
+    """Q = 0 on every row of every head: causal row i is the mean of V[0..i]
+    with lse ln(i + 1); without the mask every row is the mean of V, lse ln N."""
+    _, k, v, _ = workloads.make_inputs(B, HQ, HKV, N, d, dtype, 4200 + d)
+    q = torch.zeros((B, HQ, N, d), dtype=k.dtype, device=DEV)
+    o, lse = fa_fwd(q, k.to(DEV), v.to(DEV), causal, 1.0 / math.sqrt(d))
+    torch.cuda.synchronize()
+    vv = v.to(DEV).to(torch.float64)
+    if causal:
+        ref = torch.cumsum(vv, dim=2) / torch.arange(1, N + 1, device=DEV, dtype=torch.float64)[:, None]
+        lref = torch.log(torch.arange(1, N + 1, device=DEV, dtype=torch.float64))
+    else:
+        ref = vv.mean(dim=2, keepdim=True).expand(-1, -1, N, -1)
+        lref = torch.full((N,), math.log(N), device=DEV, dtype=torch.float64)
+    ref = ref.repeat_interleave(G, dim=1)
+    err = (o.to(torch.float64) - ref).abs()
+    tol = TOL[dtype]
+    assert err.max().item() <= tol["o_max"], err.max().item()
+    assert err.mean().item() <= tol["o_mean"], err.mean().item()
+    assert (lse.to(torch.float64) - lref).abs().max().item() <= tol["lse_max"]

@@ -56,12 +56,14 @@ class Workload:
 
 # The five workloads.  Sizes come from the pages' examples:
 #  * single_head_fp32: a one-head case small enough for a brute-force check.
-#  * gpt2_small: "sequence length 2048 with batch size 16 and 12 heads"
-#    (21medien "Performance Benchmarks"), head_dim 64 as in its code example.
+#  * gpt2_small: the B = 16, H = 12, N = 2048 example of the Performance
+#    Benchmarks section ("Flash Attention", 21medien), head_dim 64 as in that
+#    page's code example.
 #  * llama_mha_8k: 32 heads x 128 = hidden 4096 of the Llama-2-7b example and
 #    the [4, 8192, .] input of the same page's training example.
-#  * genome_gqa_64k: ">64k tokens on a single GPU" for whole-genome windows
-#    (inferensys "FlashAttention Kernel"), with grouped K/V heads (GQA).
+#  * genome_gqa_64k: a single-GPU context window of more than 64k tokens,
+#    the whole-genome case of the "FlashAttention Kernel" glossary page, with
+#    grouped K/V heads (GQA).
 #  * train_bwd_16k: the 16K-token training case ("Performance Benchmarks";
 #    initnode section 1 uses N = 16,384).
 WORKLOADS: Dict[str, Workload] = {
