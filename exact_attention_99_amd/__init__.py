@@ -9,6 +9,7 @@ Names mirror the C entry points of ``include/fa355.h``:
 
     fa_fwd(q, k, v, causal, scale, o=None, lse=None, stream=None) -> (o, lse)
     fa_bwd(q, k, v, o, lse, dout, causal, scale, ...) -> (dq, dk, dv)
+    fa_bwd_noalloc(q, k, v, o, lse, dout, causal, scale, ...) -> (dq, dk, dv)
     fa_bwd_prepare(o, dout) -> delta
     fa_bwd_dkdv(q, k, v, lse, dout, delta, causal, scale) -> (dk, dv)
     fa_bwd_dq(q, k, v, lse, dout, delta, causal, scale) -> dq
@@ -27,8 +28,8 @@ Names mirror the C entry points of ``include/fa355.h``:
     fa_status_string(code) -> str
     fa_version() -> int
 """
-from ._abi import (FA_DTYPE, FP8_BLOCK_ROWS, FaError, fa_bwd,
-                   fa_bwd_dkdv, fa_bwd_dq,
+from ._abi import (FA_DTYPE, FP8_BLOCK_ROWS, NOALLOC_SCRATCH_BYTES, FaError, fa_bwd,
+                   fa_bwd_dkdv, fa_bwd_dq, fa_bwd_noalloc,
                    fa_bwd_blocksparse, fa_bwd_dropout, fa_bwd_prepare, fa_bwd_workspace_size,
                    fa_bwd_varlen, fa_fp8_quantize, fa_fwd, fa_fwd_blocksparse, fa_fwd_dropout,
                    fa_fwd_fp8, fa_fwd_varlen,
@@ -36,7 +37,7 @@ from ._abi import (FA_DTYPE, FP8_BLOCK_ROWS, FaError, fa_bwd,
                    fa_fwd_splitkv_workspace_size, fa_status_string, fa_version, lib_path,
                    load_library)
 
-__all__ = ["fa_fwd", "fa_bwd", "fa_bwd_prepare", "fa_bwd_dkdv", "fa_bwd_dq",
+__all__ = ["fa_fwd", "fa_bwd", "fa_bwd_noalloc", "NOALLOC_SCRATCH_BYTES", "fa_bwd_prepare", "fa_bwd_dkdv", "fa_bwd_dq",
            "fa_bwd_workspace_size", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
            "fa_fwd_splitkv_default_splits", "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_blocksparse", "fa_bwd_blocksparse", "fa_fwd_varlen", "fa_bwd_varlen", "fa_fp8_quantize", "fa_fwd_fp8", "FP8_BLOCK_ROWS",
            "fa_status_string", "fa_version", "FaError", "FA_DTYPE",

@@ -12,7 +12,11 @@ _LIB_NAME = "libfa355.so"
 # fa_dtype values (include/fa355.h)
 FA_DTYPE = {"fp32": 0, "fp16": 1, "bf16": 2}
 
-STATUS = {0: "FA_OK", 1: "FA_ERR_INVALID_ARG", 2: "FA_ERR_UNSUPPORTED", 3: "FA_ERR_HIP"}
+STATUS = {0: "FA_OK", 1: "FA_ERR_INVALID_ARG", 2: "FA_ERR_UNSUPPORTED", 3: "FA_ERR_HIP",
+          4: "FA_ERR_TOO_LARGE"}
+
+# fixed scratch of fa_bwd_noalloc (FA_NOALLOC_SCRATCH_BYTES in include/fa355.h)
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 _lock = threading.Lock()
 _lib: Optional[ctypes.CDLL] = None
@@ -46,6 +50,8 @@ def load_library() -> ctypes.CDLL:
         lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                i, i, i, i, i, i, f, i, vp]
         lib.fa_bwd.restype = i
+        lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+        lib.fa_bwd_noalloc.restype = i
         lib.fa_bwd_prepare.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
         lib.fa_bwd_prepare.restype = i
         lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
@@ -256,6 +262,33 @@ def fa_bwd(q, k, v, o, lse, dout, causal: bool, scale: float, dq=None, dk=None, 
                     _stream(q, stream))
     if st != 0:
         raise FaError(st, "fa_bwd")
+    return dq, dk, dv
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, dout, causal: bool, scale: float, dq=None, dk=None, dv=None,
+                   stream=None):
+    """fa_bwd without a workspace: the library's fixed per-device scratch holds
+    the row terms (at most NOALLOC_SCRATCH_BYTES / 4 rows of B * H_q * N), so
+    the entry point itself allocates nothing.  Returns (dq, dk, dv)."""
+    import torch
+    lib = load_library()
+    B, Hq, Hkv, N, d = _shape(q, k, v)
+    dt = _dtype_name(q)
+    _check_qkv_dtype(q, k, v)
+    if dq is None:
+        dq = torch.empty_like(q)
+    if dk is None:
+        dk = torch.empty_like(k)
+    if dv is None:
+        dv = torch.empty_like(v)
+    _check_bwd_args(q, k, o, lse, dout, dq, dk, dv, B, Hq, N)
+    _check_same(q, k, v, o, lse, dout, dq, dk, dv)
+    st = lib.fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                            dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                            B, Hq, Hkv, N, d, int(bool(causal)), float(scale), FA_DTYPE[dt],
+                            _stream(q, stream))
+    if st != 0:
+        raise FaError(st, "fa_bwd_noalloc")
     return dq, dk, dv
 
 

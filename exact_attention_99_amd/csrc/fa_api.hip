@@ -4,7 +4,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <atomic>
 #include <initializer_list>
+#include <mutex>
 
 #include "fa355.h"
 #include "fa_launch.h"
@@ -305,6 +307,57 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
     if (e == hipSuccess) e = fa355::launch_bwd_dq(a);
     return hip_status(e);
 }
+}  // extern "C"
+
+namespace {
+
+// Scratch of fa_bwd_noalloc: the D row terms that fa_bwd keeps in its
+// workspace.  One copy per device, held until the process ends.  In host code
+// the name stands for a host-side shadow, not a device address: kernels and
+// copies take the address scratch_ptr() returns.
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+// Device address of the scratch array on the current device, looked up once
+// per device with that device current (null if the lookup fails).
+void* scratch_ptr() {
+    static std::atomic<void*> ptrs[64];
+    static std::mutex mu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    void* p = ptrs[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(mu);
+    p = ptrs[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        ptrs[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                         int H_q, int H_kv, int N, int d, int causal, float scale, fa_dtype dtype,
+                         hipStream_t stream) {
+    if (!ptrs_ok({q, k, v, o, lse, dout, dq, dk, dv})) return FA_ERR_INVALID_ARG;
+    const fa_status st = check_common(B, H_q, H_kv, N, d, causal, scale, dtype);
+    if (st != FA_OK) return st;
+    if (fa_bwd_workspace_size(B, H_q, H_kv, N, d, dtype) > FA_NOALLOC_SCRATCH_BYTES)
+        return FA_ERR_TOO_LARGE;
+    void* ws = scratch_ptr();
+    if (!ws) return FA_ERR_HIP;
+    const auto a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(ws), B, H_q,
+                            H_kv, N, d, causal, scale, dtype, stream);
+    hipError_t e = fa355::launch_bwd_prepare(a);
+    if (e == hipSuccess) e = fa355::launch_bwd_dkdv(a);
+    if (e == hipSuccess) e = fa355::launch_bwd_dq(a);
+    return hip_status(e);
+}
+
 
 fa_status fa_fp8_quantize(const void* x, const float* signs, unsigned char* codes, float* scales,
                           int B, int H, int N, int d, fa_dtype dtype, hipStream_t stream) {
@@ -446,6 +499,9 @@ const char* fa_status_string(fa_status s) {
                    "or workspace too small";
         case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dim or dtype not built";
         case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime refused a kernel launch";
+        case FA_ERR_TOO_LARGE:
+            return "FA_ERR_TOO_LARGE: the problem needs more than the fixed scratch of "
+                   "fa_bwd_noalloc (FA_NOALLOC_SCRATCH_BYTES)";
     }
     return "unknown fa_status";
 }

@@ -29,7 +29,8 @@
  * library allocates no device memory and keeps no pointer after a call
  * returns.  Inputs are only read.  Outputs must not overlap inputs or each
  * other.  Every buffer must be 16-byte aligned.  The library's only state is
- * a per-device cache of the compute-unit count, initialised once in a
+ * a per-device cache of the compute-unit count and, for fa_bwd_noalloc, one
+ * fixed scratch array per device (see there), each initialised once in a
  * thread-safe way.
  *
  * Timing and errors: calls enqueue work on `stream` and return without
@@ -52,7 +53,8 @@ typedef enum {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, bad flag, small workspace */
     FA_ERR_UNSUPPORTED = 2, /* head dim or dtype the library has no kernel for */
-    FA_ERR_HIP = 3          /* the HIP runtime refused a launch */
+    FA_ERR_HIP = 3,         /* the HIP runtime refused a launch */
+    FA_ERR_TOO_LARGE = 4    /* exceeds the fixed scratch of fa_bwd_noalloc */
 } fa_status;
 
 typedef enum {
@@ -113,6 +115,31 @@ fa_status fa_bwd(const void* q, const void* k, const void* v,
                  void* workspace, size_t workspace_bytes,
                  int B, int H_q, int H_kv, int N, int d,
                  int causal, float scale, fa_dtype dtype, hipStream_t stream);
+
+/*
+ * fa_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Arguments and results are those of fa_bwd, and it
+ * runs the same kernels; the row terms fa_bwd keeps in `workspace` live in a
+ * fixed device array of FA_NOALLOC_SCRATCH_BYTES bytes that the library holds
+ * on every device it runs on until the process ends.
+ *
+ * Limit: fa_bwd_workspace_size(B, H_q, H_kv, N, d, dtype) must not exceed
+ * FA_NOALLOC_SCRATCH_BYTES (B * H_q * N <= 4,194,304 rows); larger problems
+ * return FA_ERR_TOO_LARGE and enqueue nothing.  The call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine).  Every call on one
+ * device shares that device's array and leaves its contents behind; each
+ * call writes every entry it reads before reading it, so nothing needs
+ * clearing.  Calls that overlap on one device (different streams, or
+ * threads, without ordering between them) race on the array: order them.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v,
+                         const void* o, const float* lse, const void* dout,
+                         void* dq, void* dk, void* dv,
+                         int B, int H_q, int H_kv, int N, int d,
+                         int causal, float scale, fa_dtype dtype, hipStream_t stream);
 
 /*
  * The three phases fa_bwd runs, for callers that schedule them themselves

@@ -30,7 +30,7 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_blocksparse", "fa_bwd_dkdv", "fa_bwd_dq",
-                                    "fa_bwd_dropout", "fa_bwd_prepare",
+                                    "fa_bwd_dropout", "fa_bwd_noalloc", "fa_bwd_prepare",
                                     "fa_bwd_varlen",
                                     "fa_bwd_workspace_size", "fa_fp8_quantize", "fa_fwd",
                                     "fa_fwd_blocksparse", "fa_fwd_dropout", "fa_fwd_fp8",
@@ -49,7 +49,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     assert _abi.fa_version() == 100
-    for code in range(4):
+    for code in range(5):
         s = _abi.fa_status_string(code)
         assert s.startswith(_abi.STATUS[code])
     assert _abi.fa_status_string(99) == "unknown fa_status"
@@ -320,3 +320,27 @@ def test_binding_checks_buffers_before_the_call(lib):
     with pytest.raises(TypeError, match="share a dtype"):
         _abi.fa_bwd(q, k.float(), v, q, lse, q, True, 0.1)
 
+
+def test_noalloc_rejects(lib):
+    """fa_bwd_noalloc takes fa_bwd's checks, and problems whose row terms do
+    not fit the fixed scratch (more than FA_NOALLOC_SCRATCH_BYTES / 4 rows of
+    B * H_q * N) get FA_ERR_TOO_LARGE before anything is enqueued."""
+    TOO_LARGE = 4
+
+    def call(ptrs=None, B=1, Hq=2, Hkv=1, N=16, d=64, causal=0, scale=0.125, dtype=BF16):
+        p = ptrs or [A] * 9
+        return lib.fa_bwd_noalloc(*p, B, Hq, Hkv, N, d, causal, scale, dtype, None)
+
+    for i in range(9):
+        p = [A] * 9
+        p[i] = None
+        assert call(ptrs=p) == INVALID
+        p[i] = MIS
+        assert call(ptrs=p) == INVALID
+    assert call(d=96) == UNSUPPORTED
+    assert call(causal=3) == INVALID
+    assert call(Hq=3, Hkv=2) == INVALID
+    rows_max = _abi.NOALLOC_SCRATCH_BYTES // 4
+    assert call(B=1, Hq=32, Hkv=8, N=rows_max // 32 + 1) == TOO_LARGE
+    assert call(B=4, Hq=32, Hkv=32, N=65536) == TOO_LARGE
+    assert _abi.fa_status_string(TOO_LARGE).startswith("FA_ERR_TOO_LARGE")
