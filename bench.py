@@ -16,6 +16,11 @@ run on, around every launch inside the timed region.  After it, every kernel
 is also timed cold (each launch preceded by an untimed 512 MB fill that evicts
 L2 and the MALL), reported as median and minimum per kernel.
 
+The CPU baseline (`cpu_baseline`: the fp64 oracle, one process per host core)
+runs first, before the GPU is touched.  `configs` holds every workload in each
+of its masks and passes (forward; forward and backward where the workload has
+one): times, TFLOP/s and % of the matrix-core peak.
+
 Further objects in the same line: `splitkv` (the split-KV forward on
 decoding shapes, K/V bytes per second against the HBM peak), `dropout` (the
 forward and backward with fused dropout, p = 0.1, on the same workload),
@@ -74,35 +79,134 @@ def stored_traffic(kernel: str):
         return None
 
 
-def cpu_baseline(w, q, k, v, do, budget_s: float = 12.0, max_heads: int = 32):
-    """The fp64 oracle (as it stands) on whole heads of the same workload,
-    head after head until ~budget_s of CPU time; rate scaled to TFLOP/s."""
+def cpu_model() -> str:
+    """CPU model name of the host (from /proc/cpuinfo, else lscpu)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    return "unknown"
+
+
+def _oracle_task(task):
+    """One unit of the CPU baseline, in a worker process: the fp64 oracle on
+    one head (or one slice of query rows of one head) of a workload's shape,
+    inputs drawn as seeded N(0, 1) float64 values.  Returns (tag, seconds)."""
     import numpy as np
     import oracle
+    tag, N, d, causal, scale, what, seed, rows = task
+    rng = np.random.default_rng(seed)
+    Q, K, V, dO = (rng.standard_normal((1, 1, N, d)) for _ in range(4))
+    t0 = time.perf_counter()
+    if what == "fwd":
+        oracle.attention_forward(Q, K, V, scale, causal,
+                                 rows=None if rows is None else np.arange(rows[0], rows[1]))
+    else:   # forward and backward (the backward recomputes O and lse first)
+        oracle.attention_backward(Q, K, V, dO, scale, causal)
+    return tag, time.perf_counter() - t0
+
+
+def _worker_init():
     try:
         import threadpoolctl
-        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+        threadpoolctl.threadpool_limits(1)
     except Exception:
-        threads = os.cpu_count() or 1
-    heads = []
-    t_total = 0.0
-    for h in range(min(max_heads, w.H_q)):
-        hk = h // (w.H_q // w.H_kv)
-        sl = lambda x, hh: x[0:1, hh:hh + 1].to("cpu").to(dtype=__import__("torch").float64).numpy()
-        Q, K, V, dO = sl(q, h), sl(k, hk), sl(v, hk), sl(do, h)
-        t0 = time.perf_counter()
-        oracle.attention_backward(Q, K, V, dO, w.scale, True)  # computes O, lse, dQ, dK, dV
-        t_total += time.perf_counter() - t0
-        heads.append(h)
-        if t_total >= budget_s:
-            break
-    per_head = w.flops_fwd(True) / (w.B * w.H_q) * 3.5
-    value = per_head * len(heads) / t_total / 1e12
-    return {"value": value, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": (f"fp64 NumPy oracle, forward+backward of {len(heads)} whole head(s) "
-                       f"(b=0, h=0..{len(heads) - 1}) of the same workload, causal, "
-                       f"{t_total:.1f} s; rate = conventional FLOPs of those heads / time"),
-            "seconds": t_total}
+        pass
+
+
+def cpu_baseline(headline: str, max_workers: int = 16):
+    """The fp64 oracle as it stands, timed on the host cores with one process
+    per core (BLAS at one thread each), before the GPU is touched.
+
+    GPT-2-small (both masks) and the single-head fp32 case are timed in full.
+    The larger workloads are timed on a fixed sample and scaled to the whole
+    workload (labelled "extrapolated"): whole heads (forward + backward) of the
+    8k and 16k workloads, scaled by the head count; slices of 128 query rows of
+    the 64k workload (the oracle's cost per row does not depend on the row,
+    since it forms every score of the row before masking), scaled by the row
+    count.  Each rate uses the conventional FLOPs of the full workload."""
+    import multiprocessing as mp
+    import workloads
+    workers = max(1, min(max_workers, len(os.sched_getaffinity(0))))
+    tasks, plan = [], {}
+    for name, w in workloads.WORKLOADS.items():
+        for causal in w.causal_modes:
+            tag = f"{name}|{'causal' if causal else 'full'}"
+            what = "fwd+bwd" if "bwd" in w.passes else "fwd"
+            if name in ("single_head_fp32", "gpt2_small"):
+                heads = w.B * w.H_q
+                tasks += [(tag, w.N, w.d, causal, w.scale, what, 10 * w.seed + i, None) for i in range(heads)]
+                plan[tag] = (w, causal, what, 1.0, f"all {heads} heads", heads, w.N)
+            elif name == "genome_gqa_64k":
+                rows = 128
+                starts = [int(w.N * (i + 0.5) / workers) // rows * rows for i in range(workers)]
+                tasks += [(tag, w.N, w.d, causal, w.scale, what, 10 * w.seed + i, (r0, r0 + rows))
+                          for i, r0 in enumerate(starts)]
+                total_rows = w.B * w.H_q * w.N
+                plan[tag] = (w, causal, what, total_rows / (rows * workers),
+                             f"{workers} slices of {rows} rows spread over one head, "
+                             f"scaled to {total_rows} rows (extrapolated)", workers, rows)
+            else:
+                n = workers if name == "llama_mha_8k" else max(1, workers // 2)
+                tasks += [(tag, w.N, w.d, causal, w.scale, what, 10 * w.seed + i, None) for i in range(n)]
+                heads = w.B * w.H_q
+                plan[tag] = (w, causal, what, heads / n,
+                             f"{n} whole heads, scaled to {heads} heads (extrapolated)", n, w.N)
+    # longest tasks first (list scheduling over the pool)
+    # cost of one task ~ rows x keys (x 3 with the backward)
+    cost = {tag: rows * w.N * (3.0 if what != "fwd" else 1.0)
+            for tag, (w, causal, what, _, _, _, rows) in plan.items()}
+    tasks.sort(key=lambda t: -cost[t[0]])
+    saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    for k in saved:
+        os.environ[k] = "1"
+    t0 = time.perf_counter()
+    try:
+        with mp.get_context("spawn").Pool(workers, initializer=_worker_init) as pool:
+            results = pool.map(_oracle_task, tasks, chunksize=1)
+    finally:
+        for k, val in saved.items():
+            if val is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = val
+    wall = time.perf_counter() - t0
+    secs = {}
+    for tag, t in results:
+        secs[tag] = secs.get(tag, 0.0) + t
+    configs = []
+    head_rate = None
+    for tag, (w, causal, what, factor, how, ntask, _) in plan.items():
+        flops = w.flops_fwd(causal) + (w.flops_bwd(causal) if what != "fwd" else 0.0)
+        # process-seconds of the sample, scaled to the whole workload and shared
+        # by the pool's processes (a workload of fewer units than processes
+        # cannot use them all)
+        t_full = secs[tag] * factor / min(workers, ntask * factor)
+        rate = flops / t_full / 1e12
+        configs.append({"workload": w.name, "causal": causal, "pass": what, "sample": how,
+                        "cpu_seconds_sample": secs[tag], "seconds_full_on_pool": t_full,
+                        "tflops": rate})
+        if w.name == headline and causal:
+            head_rate = rate
+    return {"value": head_rate, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": (f"fp64 NumPy oracle, one process per core ({workers} processes, BLAS at 1 "
+                       f"thread each), seeded N(0,1) inputs of each workload's per-head shape; "
+                       f"value = {headline} causal forward+backward: conventional FLOPs of the "
+                       f"whole workload / its time scaled from {workers} whole heads; "
+                       f"pool wall time {wall:.1f} s for all configs"),
+            "wall_seconds": wall, "configs": configs}
 
 
 def measure_splitkv(dw, dev, stream, iters: int = 20, one_chunk: bool = True):
@@ -337,6 +441,79 @@ def measure_varlen(w, q, k, v, do, stream, iters: int = 10):
             "bwd_tflops": 2.5 * F / (med["bwd"] * 1e-3) / 1e12}
 
 
+def time_calls(fn, stream, iters: int, warmup: int = 2):
+    """Event-timed durations (ms, sorted) of `iters` launches of fn on stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    ts = []
+    for _ in range(iters):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return sorted(ts)
+
+
+PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 matrix-core peak
+
+
+def measure_configs(dev, stream):
+    """Every workload in each of its masks and passes, in the default launch
+    configuration, on device-drawn inputs of its shape: median and minimum of
+    event-timed calls, TFLOP/s with the conventional count, and % of the
+    matrix-core peak of the workload's type (bf16 2.5 PF; fp32 157.3 TF).
+    The backward is fa_bwd's three phases, also timed one by one."""
+    import torch
+    import workloads
+    from exact_attention_99_amd import fa_bwd_dkdv, fa_bwd_dq, fa_bwd_prepare, fa_fwd
+    out = []
+    for name, w in workloads.WORKLOADS.items():
+        q, k, v, do = workloads.workload_inputs(w, with_dout="bwd" in w.passes, device=dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H_q, w.N), dtype=torch.float32, device=dev)
+        peak = PEAK_FP32_TFLOPS if w.dtype == "fp32" else PEAK_BF16_TFLOPS
+        F0 = w.flops_fwd(False)
+        iters = max(5, min(50, int(2e13 / F0)))
+        for causal in w.causal_modes:
+            base = {"workload": name, "B": w.B, "H_q": w.H_q, "H_kv": w.H_kv, "N": w.N, "d": w.d,
+                    "dtype": w.dtype, "causal": causal}
+            ts = time_calls(lambda: fa_fwd(q, k, v, causal, w.scale, o=o, lse=lse, stream=stream),
+                            stream, iters)
+            F = w.flops_fwd(causal)
+            tf = F / (ts[len(ts) // 2] * 1e-3) / 1e12
+            out.append(dict(base, **{"pass": "fwd", "iters": iters, "ms_median": ts[len(ts) // 2],
+                                     "ms_min": ts[0], "tflops": tf, "peak_tflops": peak,
+                                     "pct_of_peak": 100.0 * tf / peak}))
+            if "bwd" not in w.passes:
+                continue
+            delta = torch.empty_like(lse)
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+            fa_fwd(q, k, v, causal, w.scale, o=o, lse=lse, stream=stream)
+            phases = {
+                "bwd_prepare": lambda: fa_bwd_prepare(o, do, delta, stream=stream),
+                "bwd_dkdv": lambda: fa_bwd_dkdv(q, k, v, lse, do, delta, causal, w.scale, dk=dk, dv=dv,
+                                                stream=stream),
+                "bwd_dq": lambda: fa_bwd_dq(q, k, v, lse, do, delta, causal, w.scale, dq=dq, stream=stream),
+            }
+            kms = {n: time_calls(fn, stream, iters)[iters // 2] for n, fn in phases.items()}
+
+            def whole():
+                for fn in phases.values():
+                    fn()
+            ts = time_calls(whole, stream, iters)
+            Fb = w.flops_bwd(causal)
+            tf = Fb / (ts[len(ts) // 2] * 1e-3) / 1e12
+            out.append(dict(base, **{"pass": "bwd", "iters": iters, "ms_median": ts[len(ts) // 2],
+                                     "ms_min": ts[0], "tflops": tf, "peak_tflops": peak,
+                                     "pct_of_peak": 100.0 * tf / peak, "phases_ms": kms}))
+        del q, k, v, do, o, lse
+        torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -344,6 +521,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama_mha_8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", dest="configs", action="store_false",
+                    help="skip the per-workload measurements")
+    ap.add_argument("--configs-only", action="store_true",
+                    help="only measure every workload in each of its masks and passes")
     ap.add_argument("--no-splitkv", dest="splitkv", action="store_false",
                     help="skip the split-KV decoding measurements")
     ap.add_argument("--splitkv-only", default=None, metavar="DECODE_WORKLOAD",
@@ -376,6 +557,13 @@ def main() -> int:
               "the attention path here has no multi-GPU mode; run with --gpus 1.", file=sys.stderr)
         return 2
 
+    # The CPU baseline runs first, in worker processes started before this
+    # process touches the GPU.
+    cpu = None
+    if not (args.no_cpu_baseline or args.copy_calibration or args.splitkv_only or args.fp8_only
+            or args.blocksparse_only or args.dropout_only or args.configs_only):
+        cpu = cpu_baseline(args.workload)
+
     import torch
     import workloads
     from exact_attention_99_amd import fa_bwd_dkdv, fa_bwd_dq, fa_bwd_prepare, fa_fwd
@@ -398,6 +586,10 @@ def main() -> int:
         rec = measure_splitkv(workloads.DECODE_WORKLOADS[args.splitkv_only], "cuda:0",
                               torch.cuda.current_stream(), one_chunk=False)
         print(json.dumps({"splitkv": rec}), flush=True)
+        return 0
+    if args.configs_only:
+        torch.cuda.set_device(0)
+        print(json.dumps({"configs": measure_configs("cuda:0", torch.cuda.current_stream())}), flush=True)
         return 0
     w = workloads.WORKLOADS[args.workload]
     causal = True in w.causal_modes
@@ -548,8 +740,11 @@ def main() -> int:
     if args.fp8:
         out["fp8"] = measure_fp8(w, q, k, v, stream)
         out["fp8"]["speedup_vs_16bit_fwd"] = fwd_ms / out["fp8"]["fwd_fp8"]["ms"]
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, q, k, v, do)
+    if args.configs:
+        del q, k, v, do, o, lse, delta, dq, dk, dv
+        torch.cuda.empty_cache()
+        out["configs"] = measure_configs(dev, stream)
+    out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
     return 0
 

@@ -207,9 +207,10 @@ int fa_fwd_splitkv_default_splits(int B, int H_q, int H_kv, int N_q, int N_kv, i
     if (!split_sizes_ok(B, H_q, H_kv, N_q, N_kv) || (d != 64 && d != 128)) return 0;
     const long long G = H_q / H_kv;
     const long long groups = (long long)B * H_kv * ((G * N_q + 31) / 32);
-    // about eight one-wave workgroups per compute unit, chunks of at least
-    // four key tiles
-    const long long want = (2048 + groups - 1) / groups;
+    // about two one-wave workgroups per compute unit of a 256-unit device
+    // (the rate of the decoding shapes peaks there: more, smaller chunks only
+    // add partials for the merge to read), chunks of at least four key tiles
+    const long long want = (512 + groups - 1) / groups;
     const long long tile = fa355::split_tile_keys(d);
     const long long most = (N_kv + 4 * tile - 1) / (4 * tile);
     long long n = want < most ? want : most;

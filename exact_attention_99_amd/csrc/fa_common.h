@@ -316,12 +316,24 @@ __device__ __forceinline__ int pos_of_elem(int x) {
 // (seed, offset) and counter (j / 32, i, b H_q + h, 0): one call gives the
 // 32 bytes of one row and one aligned 32-key block, little-endian, byte
 // j % 32 for key j (dword (j % 32) / 4 of the result).
-__device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64_t k1) {
-    // multipliers and Weyl key increments of Philox4x64 (Salmon et al.)
-    constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
-    constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
-#pragma unroll
-    for (int r = 0; r < 10; ++r) {
+// Philox4x64 state, advanced one round at a time, so that a kernel can spread
+// the ten rounds over instructions that would otherwise wait.
+struct Philox4x64 {
+    uint64_t c[4];
+    uint64_t k0, k1;
+    // counter (kblk, row, bh, 0), key (seed, offset)
+    __device__ __forceinline__ void start(uint32_t kblk, uint32_t row, uint32_t bh, const DropParams& dp) {
+        c[0] = kblk;
+        c[1] = row;
+        c[2] = bh;
+        c[3] = 0;
+        k0 = dp.seed;
+        k1 = dp.offset;
+    }
+    __device__ __forceinline__ void round() {
+        // multipliers and Weyl key increments of Philox4x64 (Salmon et al.)
+        constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+        constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
         const uint64_t lo0 = M0 * c[0], hi0 = __umul64hi(M0, c[0]);
         const uint64_t lo1 = M1 * c[2], hi1 = __umul64hi(M1, c[2]);
         const uint64_t n0 = hi1 ^ c[1] ^ k0;
@@ -333,18 +345,24 @@ __device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64
         k0 += W0;
         k1 += W1;
     }
-}
+    // the 32 output bytes as 8 little-endian dwords
+    __device__ __forceinline__ void words(uint32_t w[8]) const {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            w[2 * i] = (uint32_t)c[i];
+            w[2 * i + 1] = (uint32_t)(c[i] >> 32);
+        }
+    }
+};
 
 // The 32 random bytes of (row, key block kblk) of head index bh, as 8 dwords.
 __device__ __forceinline__ void drop_bytes(uint32_t w[8], uint32_t kblk, uint32_t row, uint32_t bh,
                                            const DropParams& dp) {
-    uint64_t c[4] = {kblk, row, bh, 0};
-    philox4x64_10(c, dp.seed, dp.offset);
+    Philox4x64 g;
+    g.start(kblk, row, bh, dp);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        w[2 * i] = (uint32_t)c[i];
-        w[2 * i + 1] = (uint32_t)(c[i] >> 32);
-    }
+    for (int r = 0; r < 10; ++r) g.round();
+    g.words(w);
 }
 
 // In the score layouts where a lane owns one query row and, in each 32-key

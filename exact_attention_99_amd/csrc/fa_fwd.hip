@@ -29,324 +29,22 @@ namespace fa355 {
 
 namespace {
 
-// Fifth-generation 16-bit forward kernel.  K and V tiles are copied from
-// global memory straight into LDS by buffer-to-LDS loads (no staging
-// registers; rows past N arrive as zeros), both row-major, and the V^T operand
-// of the P V product comes from transposing LDS reads.  The key tiles are
-// split in two loops.  Tiles
-// that lie wholly at or below every row of the block and inside the sequence
-// run a body with no mask code at all; the LDS buffer of each is a
-// compile-time constant (the loop handles tiles in pairs), so every LDS
-// address is a per-lane register plus an immediate offset.  The remaining
-// tiles (the causal diagonal of each wave, the ragged end of the sequence)
-// run the masked body.
+// Sixth-generation 16-bit forward kernel: NW waves of 32 query rows, tiles of
+// 64 keys.
 //
-// DROP: attention dropout (fa_common.h) on the probabilities before the P V
-// product; the row sums and lse stay those of the undropped probabilities.
-// Lane half hi draws the bytes of key block 2 kp + hi of its row, and one
-// exchange between the halves gives each lane its bytes of both blocks.
+// Data path.  K and V tiles go from global memory straight into LDS by
+// buffer-to-LDS copies (no staging registers; rows past the end of the
+// sequence arrive as zeros), both row-major, double-buffered: the copy of tile
+// j + 1 is issued at the start of tile j.  The V^T operand of the P V product
+// comes from transposing LDS reads.  Tiles that lie wholly at or below every
+// row of the block and inside the sequence run a body with no mask code, two
+// at a time so that both LDS buffers are compile-time constants; the diagonal
+// and ragged-end tiles run the masked body, and a wave skips tiles above its
+// rows.  A tile's LDS reads go through a restrict-qualified pointer to its
+// buffer, so the compiler does not make them wait for the copies of the next
+// tile into the other buffer.
 //
-// SPARSE: block-sparse attention (SparseParams): the workgroup walks only the
-// key tiles that the block mask allows for one of its rows (the copy of the
-// next such tile overlaps the current one), and a wave computes a tile only
-// if its own 32 rows may see it.  Rows that see no key get O = 0 and
-// lse = -inf.
-//
-// A tile's LDS reads go through a restrict-qualified pointer to its buffer.
-// The transposing reads then carry alias information, and the compiler no
-// longer makes them wait for the copies of the next tile into the other
-// buffer, which it must otherwise assume they may overlap (with a plain
-// pointer every tile waited for its successor's copies before its first V^T
-// read).
-template <typename T, int D, bool CAUSAL, int NW, int BC, bool DROP = false, bool SPARSE = false>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
-fwd16v5_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-               const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-               int B, int Hq, int Hkv, int N, float cl2, DropParams dp, SparseParams sp) {
-    constexpr int BR = 32 * NW;
-    constexpr int KCH = D / 8;
-    constexpr int TILE = BC * D * 2;
-    constexpr int STAGE = 2 * TILE;
-    constexpr int NKB = BC / 32;
-    constexpr int NKG = BC / 16;
-    constexpr int NDB = D / 32;
-    constexpr int NKS = D / 16;
-    constexpr int WI = TILE / 1024;
-    static_assert(WI % NW == 0, "tile copies split evenly over the waves");
-    constexpr int IPW = WI / NW;
-    static_assert(2 * STAGE <= 65536, "both buffers addressable by immediate offsets");
-    static_assert(BR % BC == 0, "row blocks start on a key-tile boundary");
-
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l32 = lane & 31;
-    const int hi = lane >> 5;
-
-    const int nqb = (N + BR - 1) / BR;
-    const int total = nqb * Hq * B;
-    const int logical = xcd_remap((int)blockIdx.x, total);
-    const int qb_raw = logical % nqb;
-    const int bh = logical / nqb;
-    const int qb = CAUSAL ? (nqb - 1 - qb_raw) : qb_raw;  // longest rows first
-    // the masked path takes the batch index fastest, so that the XCDs (each
-    // runs a contiguous range of heads) share sequences of different lengths
-    const int h = SPARSE ? bh / B : bh % Hq;
-    const int b = SPARSE ? bh % B : bh / Hq;
-    const int hk = h / (Hq / Hkv);
-
-    const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
-    const size_t koff = ((size_t)b * Hkv + hk) * (size_t)N * D;
-    // valid positions of this sequence (the masked path's lengths; else N)
-    const int Nk = (SPARSE && sp.seqlens) ? min(max(sp.seqlens[b], 0), N) : N;
-    // positions past Nk read as zeros (padded queries then score 0 against
-    // every key and never move the rescale decision of their wave)
-    const uint32_t kv_bytes = (uint32_t)Nk * D * 2;
-    const Buf Qb(Q + qoff, kv_bytes), Kb(K + koff, kv_bytes), Vb(V + koff, kv_bytes);
-
-    const int q0 = qb * BR;
-    const int qw = q0 + 32 * wave;
-    const int q = qw + l32;
-
-    u32x4 qf[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qf[ks] = Qb.load16((uint32_t)(q * D + 16 * ks + 8 * hi) * 2);
-
-    const int kv_len = q0 >= Nk ? 0 : (CAUSAL ? min(Nk, q0 + BR) : Nk);
-    const int ntiles = (kv_len + BC - 1) / BC;
-    // tiles below the whole row block (causal) and inside the sequence
-    const int nfull = min(CAUSAL ? q0 / BC : ntiles, Nk / BC);
-
-    uint32_t cpk[IPW], cpv[IPW];
-#pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-        const int p = (wave + NW * i) * 64 + lane;
-        const int row = p / KCH, pc = p % KCH;
-        cpk[i] = (uint32_t)kq_off<D>(row, pc);
-        cpv[i] = (uint32_t)(row * D * 2 + 16 * (pc ^ tr_swz<D>(row)));
-    }
-    auto issue = [&](int k0, int buf) {
-        unsigned char* base = smem + buf * STAGE;
-#pragma unroll
-        for (int i = 0; i < IPW; ++i) {
-            const int bi = wave + NW * i;
-            const uint32_t rowb = (uint32_t)k0 * D * 2;
-            buf_to_lds16(Kb, base + bi * 1024, rowb + cpk[i]);
-            buf_to_lds16(Vb, base + TILE + bi * 1024, rowb + cpv[i]);
-        }
-    };
-
-    const int g16 = lane >> 4;
-    const int j16 = lane & 15;
-    const int tr_row = 4 * hi + (j16 >> 2);
-    const int tr_col = 2 * (16 * (g16 & 1) + 4 * (j16 & 3));
-
-    // lane parts of the LDS addresses (block, group and buffer offsets are
-    // immediates): K rows 32 kb + l32, chunk 2 ks + hi; V^T rows 16 kg +
-    // tr_row (+ 8), bytes 64 db + tr_col
-    uint32_t ko[2][NKS], vo[NDB];
-#pragma unroll
-    for (int par = 0; par < 2; ++par)
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) ko[par][ks] = lds_lane_off((uint32_t)kq_off<D>(32 * par + l32, 2 * ks + hi) - 32 * par * D * 2);
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) vo[db] = lds_lane_off((uint32_t)vt_off<D>(tr_row, 64 * db + tr_col));
-
-    f32x16 o[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) o[db] = zero16();
-    float m_s = -INFINITY;
-    float l_s = 0.f;
-
-    // tile j from the buffer at cur
-    auto body_at = [&](const unsigned char* __restrict__ cur, int j, auto mask_tag)
-                       __attribute__((always_inline)) {
-        constexpr bool MASK = decltype(mask_tag)::value;
-        const int k0 = j * BC;
-        const unsigned char* kbase = cur;
-        const unsigned char* vbase = cur + TILE;
-
-        f32x16 s[NKB];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) s[kb] = zero16();
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                const u32x4 a = *reinterpret_cast<const u32x4*>(kbase + ko[kb & 1][ks] + 32 * kb * D * 2);
-                s[kb] = Mma<T>::mma(a, qf[ks], s[kb]);
-            }
-        if (MASK) {
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + 32 * kb + acc_row(r, hi);
-                    // (masked path: padded query rows see nothing, so they
-                    // never move the wave's rescale decision)
-                    if ((CAUSAL && key > q) || key >= Nk || (SPARSE && q >= Nk)) s[kb][r] = -INFINITY;
-                }
-        }
-
-        // V^T operands of this tile: read now, so their latency hides under
-        // the softmax
-        u32x4 va[NKG][NDB];
-#pragma unroll
-        for (int kg = 0; kg < NKG; ++kg)
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const u32x2 lo = lds_read_tr16(vbase + vo[db] + 16 * kg * D * 2);
-                const u32x2 up = lds_read_tr16(vbase + vo[db] + (16 * kg + 8) * D * 2);
-                va[kg][db] = u32x4{lo[0], lo[1], up[0], up[1]};
-            }
-
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        const float mt = halves_max(mx) * cl2;
-
-        if (__any(mt > m_s + kTau)) {
-            const float mn = fmaxf(m_s, mt);
-            const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m_s - mn);
-            l_s *= alpha;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-            m_s = mn;
-        }
-        const float mu = (m_s == -INFINITY) ? 0.f : m_s;
-
-        u32x4 pb[NKG];
-        float ls = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const float p0 = fast_exp2(fmaf(s[kb][8 * t + 2 * jj], cl2, -mu));
-                    const float p1 = fast_exp2(fmaf(s[kb][8 * t + 2 * jj + 1], cl2, -mu));
-                    ls += p0 + p1;
-                    pb[2 * kb + t][jj] = Mma<T>::pack2(p0, p1);
-                }
-        l_s += ls;
-        if constexpr (DROP) {
-            // pair (8 t + 2 jj, +1) of block kb: bytes 2 (jj & 1), +1 of dword 2 t + jj / 2
-#pragma unroll
-            for (int kp = 0; kp < NKB / 2; ++kp) {
-                uint32_t w[8], dm[2][4];
-                drop_bytes(w, (uint32_t)(k0 / 32 + 2 * kp + hi), (uint32_t)q, (uint32_t)(b * Hq + h), dp);
-                drop_pair_exchange(w, dm[0], dm[1]);
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                    for (int t = 0; t < 2; ++t)
-#pragma unroll
-                        for (int jj = 0; jj < 4; ++jj)
-                            pb[2 * (2 * kp + kk) + t][jj] &=
-                                drop_mask16x2(dm[kk][2 * t + (jj >> 1)], 2 * (jj & 1), dp.t8);
-            }
-        }
-
-#pragma unroll
-        for (int kg = 0; kg < NKG; ++kg)
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) o[db] = Mma<T>::mma(va[kg][db], pb[kg], o[db]);
-    };
-    // tile j in buffer BUFC, or (BUFC < 0) in buffer par & 1
-    auto body = [&](int j, auto mask_tag, auto buf_tag, int par) __attribute__((always_inline)) {
-        constexpr int BUFC = decltype(buf_tag)::value;
-        body_at(smem + (BUFC >= 0 ? BUFC * STAGE : (par & 1) * STAGE), j, mask_tag);
-    };
-
-    bool compact = false;   // walk only the tiles a block mask allows
-    if constexpr (SPARSE) compact = sp.mask != nullptr;
-    if (compact) {
-        const int nb = sp.nb;
-        const unsigned char* mk = sp.mask ? sp.mask + (size_t)(sp.heads == 1 ? 0 : h) * nb * nb : nullptr;
-        const int mr0 = min(q0 / 128, nb - 1);
-        const int mr1 = min((q0 + BR - 1) / 128, nb - 1);
-        const unsigned char* mw = mk ? mk + min(qw / 128, nb - 1) * nb : nullptr;
-        auto wg_need = [&](int jt) {
-            if (!mk) return true;
-            const int c = jt * BC / 128;
-            bool any = false;
-            for (int r = mr0; r <= mr1; ++r) any |= mk[r * nb + c] != 0;
-            return any;
-        };
-        int jt = 0;
-        while (jt < ntiles && !wg_need(jt)) ++jt;
-        if (jt < ntiles) issue(jt * BC, 0);
-        wait_vmem();
-        __syncthreads();
-        int par = 0;
-        while (jt < ntiles) {
-            int jn = jt + 1;
-            while (jn < ntiles && !wg_need(jn)) ++jn;
-            // past the last needed tile the copy reads this head's range or
-            // zeros and lands in the buffer no later tile reads
-            issue(jn * BC, par ^ 1);
-            // one (masked) body keeps the register allocation of the dense loops
-            if ((!mw || mw[jt * BC / 128] != 0) && (!CAUSAL || jt * BC <= qw + 31))
-                body(jt, std::true_type{}, std::integral_constant<int, -1>{}, par);
-            wait_vmem();
-            __syncthreads();
-            jt = jn;
-            par ^= 1;
-        }
-    } else {
-        issue(0, 0);
-        wait_vmem();
-        __syncthreads();
-
-        // The copy of the next tile is issued at the start of every tile, also
-        // the last (the extra tile lies in this head's range or past its end,
-        // reads as zeros, and lands in the buffer no later tile reads).
-        int j = 0;
-        for (; j + 1 < nfull; j += 2) {
-            issue((j + 1) * BC, 1);
-            body(j, std::false_type{}, std::integral_constant<int, 0>{}, 0);
-            wait_vmem();
-            __syncthreads();
-            issue((j + 2) * BC, 0);
-            body(j + 1, std::false_type{}, std::integral_constant<int, 1>{}, 1);
-            wait_vmem();
-            __syncthreads();
-        }
-        for (; j < ntiles; ++j) {
-            issue((j + 1) * BC, (j + 1) & 1);
-            if (!CAUSAL || j * BC <= qw + 31) body(j, std::true_type{}, std::integral_constant<int, -1>{}, j);
-            wait_vmem();
-            __syncthreads();
-        }
-    }
-
-    const float l_tot = l_s + swap_halves(l_s);
-    if (q < N) {
-        const bool empty = SPARSE && (!(l_tot > 0.f) || q >= Nk);
-        const float inv = empty ? 0.f : (DROP ? dp.scale : 1.f) / l_tot;
-        uint16_t* Orow = O + qoff + (size_t)q * D;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                u32x2 w;
-                w[0] = Mma<T>::pack2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
-                w[1] = Mma<T>::pack2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-                *reinterpret_cast<u32x2*>(Orow + 32 * db + 8 * g + 4 * hi) = w;
-            }
-        if (hi == 0) LSE[(size_t)(b * Hq + h) * N + q] = empty ? -INFINITY : (m_s + __log2f(l_tot)) * kLn2;
-    }
-}
-
-// Sixth-generation 16-bit forward kernel (d = 128 tiles of 64 keys): the data
-// path of the fifth generation with two changes to the softmax.
-//
+// Softmax.
 // 1. The running maximum is not recomputed per tile.  The probabilities of a
 //    32-key half tile are formed against the current maximum m and summed; if
 //    every lane's sum stays at or below 2^kTau (and m is finite), no
@@ -360,17 +58,28 @@ fwd16v5_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 //    the second half are formed on the matrix cores while the vector unit
 //    exponentiates the first, and the P V products of the first half run
 //    while the second is exponentiated.
-// 3. As in the fifth generation, the tile's LDS reads go through a
-//    restrict-qualified buffer pointer, so they do not wait for the copies of
-//    the next tile.
-// 4. PERSIST: the grid holds one workgroup per compute unit, and each walks
-//    the row blocks persist_block() assigns it, which saves a workgroup launch
-//    per block.
-template <typename T, int D, bool CAUSAL, int NW, int BC, bool PERSIST = false>
+//
+// PERSIST: the grid holds as many workgroups as fit on the device at once,
+// and each walks the row blocks persist_block() assigns it, which saves a
+// workgroup launch per block.
+//
+// DROP: attention dropout (fa_common.h) on the probabilities before the P V
+// product; the row sums and lse stay those of the undropped probabilities.
+// Lane half hi draws the bytes of key block k0 / 32 + hi of its row, and one
+// exchange between the halves gives each lane its bytes of both blocks.
+//
+// SPARSE: block-sparse attention and variable-length batches (SparseParams).
+// With a block mask the workgroup walks only the key tiles that the mask
+// allows for one of its rows (the copy of the next such tile overlaps the
+// current one), and a wave computes a tile only if its own 32 rows may see it;
+// with sequence lengths the length replaces N in every range check.  Rows that
+// see no key get O = 0 and lse = -inf.
+template <typename T, int D, bool CAUSAL, int NW, int BC, bool PERSIST = false, bool DROP = false,
+          bool SPARSE = false>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-               int B, int Hq, int Hkv, int N, float cl2) {
+               int B, int Hq, int Hkv, int N, float cl2, DropParams dp, SparseParams sp) {
     static_assert(BC == 64 || BC == 128, "tiles of one or two 64-key sub-tiles");
     static_assert(D == 64 || D == 128, "head dimensions with a K tile swizzle");
     constexpr int PPB = 8 / (D / 16);    // probability pairs per second-half score product
@@ -413,13 +122,19 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         const int qb_raw = logical % nqb;
         const int bh = logical / nqb;
         const int qb = CAUSAL ? (nqb - 1 - qb_raw) : qb_raw;  // longest rows first
-        const int h = bh % Hq;
-        const int b = bh / Hq;
+        // the masked path takes the batch index fastest, so that the XCDs (each
+        // runs a contiguous range of heads) share sequences of different lengths
+        const int h = SPARSE ? bh / B : bh % Hq;
+        const int b = SPARSE ? bh % B : bh / Hq;
         const int hk = h / (Hq / Hkv);
 
         const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
         const size_t koff = ((size_t)b * Hkv + hk) * (size_t)N * D;
-        const uint32_t head_bytes = (uint32_t)N * D * 2;
+        // valid positions of this sequence (variable lengths; else N).  Positions
+        // past Nk read as zeros: padded queries then score 0 against every key,
+        // and padded keys are masked.
+        const int Nk = (SPARSE && sp.seqlens) ? min(max(sp.seqlens[b], 0), N) : N;
+        const uint32_t head_bytes = (uint32_t)Nk * D * 2;
         const Buf Qb(Q + qoff, head_bytes), Kb(K + koff, head_bytes), Vb(V + koff, head_bytes);
 
         const int q0 = qb * BR;
@@ -430,9 +145,9 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) qf[ks] = Qb.load16((uint32_t)(q * D + 16 * ks + 8 * hi) * 2);
 
-        const int kv_len = CAUSAL ? min(N, q0 + BR) : N;
+        const int kv_len = q0 >= Nk ? 0 : (CAUSAL ? min(Nk, q0 + BR) : Nk);
         const int ntiles = (kv_len + BC - 1) / BC;
-        const int nfull = min(CAUSAL ? q0 / BC : ntiles, N / BC);
+        const int nfull = min(CAUSAL ? q0 / BC : ntiles, Nk / BC);
 
         uint32_t cpk[IPW], cpv[IPW];
 #pragma unroll
@@ -498,7 +213,9 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             // register's constant part 8 (r / 4) + r % 4 is at most lim
             auto mask_half = [&](f32x16& s, int kb) {
                 if (MASK) {
-                    const int lim = (CAUSAL ? min(q, N - 1) : N - 1) - (k0 + 32 * kb) - 4 * hi;
+                    // (padded queries of a variable-length batch see no key)
+                    const int lim = (SPARSE && q >= Nk) ? -1024
+                                                         : (CAUSAL ? min(q, Nk - 1) : Nk - 1) - (k0 + 32 * kb) - 4 * hi;
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
                         if (8 * (r >> 2) + (r & 3) > lim) s[r] = -INFINITY;
@@ -544,12 +261,20 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) ka[ks] = kread(0, ks);
 
+            // dropout: lane half hi draws the keep bytes of key block k0 / 32 + hi
+            // of its row; the ten generator rounds run under the score products,
+            // and one exchange between the halves gives every lane its bytes of
+            // both blocks
+            Philox4x64 pg;
+            if constexpr (DROP) pg.start((uint32_t)(k0 / 32 + hi), (uint32_t)q, (uint32_t)(b * Hq + h), dp);
+
             // scores of the first half | K reads of the second
             f32x16 s0 = zero16(), s1 = zero16();
             static_for<NKS>([&](auto tc) {
                 constexpr int t = decltype(tc)::value;
                 s0 = Mma<T>::mma(ka[t], qf[t], s0);
                 kb2[t] = kread(1, t);
+                if constexpr (DROP) pg.round();
                 __builtin_amdgcn_sched_barrier(0);
             });
             mask_half(s0, 0);
@@ -558,29 +283,95 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             // of the first half
             u32x4 pb0[2], pb1[2];
             float ls0 = 0.f, ls1 = 0.f;
-            static_for<NKS>([&](auto tc) {
-                constexpr int t = decltype(tc)::value;
-                s1 = Mma<T>::mma(kb2[t], qf[t], s1);
+            // With one probability pair per product (d = 128) the pairs run in a
+            // three-stage pipeline over the steps: step t forms the exponent
+            // arguments of pair t + 1, the exponentials of pair t and the sum and
+            // packing of pair t - 1, so no step waits on its own chain.
+            float ea[8][2], ee[8][2];
+            auto arg = [&](const f32x16& sv, int t, float m) {
+                ea[t][0] = fmaf(sv[2 * t], cl2, -m);
+                ea[t][1] = fmaf(sv[2 * t + 1], cl2, -m);
+            };
+            auto ex = [&](int t) {
+                ee[t][0] = fast_exp2(ea[t][0]);
+                ee[t][1] = fast_exp2(ea[t][1]);
+            };
+            auto fin = [&](int t, float& ls, u32x4 (&pb)[2]) {
+                ls += ee[t][0] + ee[t][1];
+                pb[t >> 2][t & 3] = Mma<T>::pack2(ee[t][0], ee[t][1]);
+            };
+            if constexpr (PPB == 1) {
+                arg(s0, 0, mu);
+                static_for<NKS>([&](auto tc) {
+                    constexpr int t = decltype(tc)::value;
+                    s1 = Mma<T>::mma(kb2[t], qf[t], s1);
+                    if constexpr (t + 1 < 8) arg(s0, t + 1, mu);
+                    ex(t);
+                    if constexpr (t > 0) fin(t - 1, ls0, pb0);
+                    if (t < 2 * NDB) va[t] = vread(t / NDB, t % NDB);
+                    if constexpr (DROP && NKS + t < 10) pg.round();
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+                fin(7, ls0, pb0);
+            } else {
+                static_for<NKS>([&](auto tc) {
+                    constexpr int t = decltype(tc)::value;
+                    s1 = Mma<T>::mma(kb2[t], qf[t], s1);
 #pragma unroll
-                for (int u = 0; u < PPB; ++u) exp_pair(s0, PPB * t + u, mu, ls0, pb0);
-                if (t < 2 * NDB) va[t] = vread(t / NDB, t % NDB);
-                __builtin_amdgcn_sched_barrier(0);
-            });
+                    for (int u = 0; u < PPB; ++u) exp_pair(s0, PPB * t + u, mu, ls0, pb0);
+                    if (t < 2 * NDB) va[t] = vread(t / NDB, t % NDB);
+                    if constexpr (DROP && NKS + t < 10) pg.round();
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+            }
             mask_half(s1, 1);
             settle(s0, ls0, pb0);
+            // keep masks of both 32-key blocks: dword 2 t + jj / 2 holds the bytes
+            // of pair (8 t + 2 jj, +1) of a block; the row sums above stay those
+            // of the undropped probabilities
+            uint32_t dm[2][4];
+            auto drop_mask = [&](u32x4 (&pb)[2], const uint32_t (&m)[4]) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) pb[t][jj] &= drop_mask16x2(m[2 * t + (jj >> 1)], 2 * (jj & 1), dp.t8);
+            };
+            if constexpr (DROP) {
+#pragma unroll
+                for (int r = 2 * NKS; r < 10; ++r) pg.round();
+                uint32_t w[8];
+                pg.words(w);
+                drop_pair_exchange(w, dm[0], dm[1]);
+                drop_mask(pb0, dm[0]);
+            }
 
             // P V of the first half | probabilities of the second | V^T reads of
             // the second half
             const float mu1 = (m_s == -INFINITY) ? 0.f : m_s;
-            static_for<2 * NDB>([&](auto tc) {
-                constexpr int t = decltype(tc)::value;
-                o[t % NDB] = Mma<T>::mma(va[t], pb0[t / NDB], o[t % NDB]);
+            if constexpr (PPC == 1) {
+                arg(s1, 0, mu1);
+                static_for<2 * NDB>([&](auto tc) {
+                    constexpr int t = decltype(tc)::value;
+                    o[t % NDB] = Mma<T>::mma(va[t], pb0[t / NDB], o[t % NDB]);
+                    if constexpr (t + 1 < 8) arg(s1, t + 1, mu1);
+                    ex(t);
+                    if constexpr (t > 0) fin(t - 1, ls1, pb1);
+                    vb[t] = vread(2 + t / NDB, t % NDB);
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+                fin(7, ls1, pb1);
+            } else {
+                static_for<2 * NDB>([&](auto tc) {
+                    constexpr int t = decltype(tc)::value;
+                    o[t % NDB] = Mma<T>::mma(va[t], pb0[t / NDB], o[t % NDB]);
 #pragma unroll
-                for (int u = 0; u < PPC; ++u) exp_pair(s1, PPC * t + u, mu1, ls1, pb1);
-                vb[t] = vread(2 + t / NDB, t % NDB);
-                __builtin_amdgcn_sched_barrier(0);
-            });
+                    for (int u = 0; u < PPC; ++u) exp_pair(s1, PPC * t + u, mu1, ls1, pb1);
+                    vb[t] = vread(2 + t / NDB, t % NDB);
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+            }
             settle(s1, ls1, pb1);
+            if constexpr (DROP) drop_mask(pb1, dm[1]);
 
             // P V of the second half
 #pragma unroll
@@ -596,6 +387,42 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             });
         };
 
+        bool compact = false;   // walk only the tiles a block mask allows
+        if constexpr (SPARSE) compact = sp.mask != nullptr;
+        if (compact) {
+            const int nb = sp.nb;
+            const unsigned char* mk = sp.mask + (size_t)(sp.heads == 1 ? 0 : h) * nb * nb;
+            const int mr0 = min(q0 / 128, nb - 1);
+            const int mr1 = min((q0 + BR - 1) / 128, nb - 1);
+            // this wave's 32 rows lie in one mask row, and a 64-key tile in one
+            // mask column: a wave computes a tile whole or not at all
+            const unsigned char* mw = mk + min(qw / 128, nb - 1) * nb;
+            auto wg_need = [&](int jt) {
+                const int c = jt * BC / 128;
+                bool any = false;
+                for (int r = mr0; r <= mr1; ++r) any |= mk[r * nb + c] != 0;
+                return any;
+            };
+            int jt = 0;
+            while (jt < ntiles && !wg_need(jt)) ++jt;
+            if (jt < ntiles) issue_to(smem, jt * BC);
+            wait_vmem();
+            __syncthreads();
+            int par = 0;
+            while (jt < ntiles) {
+                int jn = jt + 1;
+                while (jn < ntiles && !wg_need(jn)) ++jn;
+                // past the last allowed tile the copy reads this head's range or
+                // zeros and lands in the buffer no later tile reads
+                issue_to(smem + (par ^ 1) * STAGE, jn * BC);
+                if (mw[jt * BC / 128] != 0 && (!CAUSAL || jt * BC <= qw + 31))
+                    tile(jt, std::true_type{}, smem + par * STAGE);
+                wait_vmem();
+                __syncthreads();
+                jt = jn;
+                par ^= 1;
+            }
+        } else {
         issue_to(smem, 0);
         wait_vmem();
         __syncthreads();
@@ -620,10 +447,14 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             wait_vmem();
             __syncthreads();
         }
+        }
 
         const float l_tot = l_s + swap_halves(l_s);
         if (q < N) {
-            const float inv = 1.f / l_tot;
+            // rows that see no key (block masks, padding) get O = 0 and lse = -inf;
+            // kept probabilities are scaled by 256 / t8 here
+            const bool empty = SPARSE && (!(l_tot > 0.f) || q >= Nk);
+            const float inv = empty ? 0.f : (DROP ? dp.scale : 1.f) / l_tot;
             uint16_t* Orow = O + qoff + (size_t)q * D;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
@@ -634,7 +465,7 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                     w[1] = Mma<T>::pack2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
                     *reinterpret_cast<u32x2*>(Orow + 32 * db + 8 * g + 4 * hi) = w;
                 }
-            if (hi == 0) LSE[(size_t)(b * Hq + h) * N + q] = (m_s + __log2f(l_tot)) * kLn2;
+            if (hi == 0) LSE[(size_t)(b * Hq + h) * N + q] = empty ? -INFINITY : (m_s + __log2f(l_tot)) * kLn2;
         }
     }
 }
@@ -752,19 +583,8 @@ fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const flo
     }
 }
 
-template <typename T, int D, bool CAUSAL, int NW, int BC, bool DROP = false, bool SPARSE = false>
-hipError_t launch16v5(const FwdArgs& a) {
-    constexpr int BR = 32 * NW;
-    const int nqb = (a.N + BR - 1) / BR;
-    const long long total = (long long)nqb * a.Hq * a.B;
-    hipLaunchKernelGGL((fwd16v5_kernel<T, D, CAUSAL, NW, BC, DROP, SPARSE>), dim3((unsigned)total),
-                       dim3(NW * 64), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                       (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.N, a.cl2,
-                       a.dp, a.sp);
-    return hipGetLastError();
-}
-
-template <typename T, int D, bool CAUSAL, int NW, int BC, bool PERSIST = false>
+template <typename T, int D, bool CAUSAL, int NW, int BC, bool PERSIST = false, bool DROP = false,
+          bool SPARSE = false>
 hipError_t launch16v6(const FwdArgs& a) {
     constexpr int BR = 32 * NW;
     const int nqb = (a.N + BR - 1) / BR;
@@ -775,19 +595,19 @@ hipError_t launch16v6(const FwdArgs& a) {
         static const int per_cu = [] {
             int n = 0;
             return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                       &n, reinterpret_cast<const void*>(fwd16v6_kernel<T, D, CAUSAL, NW, BC, true>), NW * 64,
-                       0) == hipSuccess ? n : 0;
+                       &n, reinterpret_cast<const void*>(fwd16v6_kernel<T, D, CAUSAL, NW, BC, true, DROP, SPARSE>),
+                       NW * 64, 0) == hipSuccess ? n : 0;
         }();
         grid = persistent_grid() * per_cu;
     }
     if (grid >= 8 && total > grid)
-        hipLaunchKernelGGL((fwd16v6_kernel<T, D, CAUSAL, NW, BC, true>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((fwd16v6_kernel<T, D, CAUSAL, NW, BC, true, DROP, SPARSE>), dim3((unsigned)grid),
                            dim3(NW * 64), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                           (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.N, a.cl2);
+                           (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.dp, a.sp);
     else
-        hipLaunchKernelGGL((fwd16v6_kernel<T, D, CAUSAL, NW, BC>), dim3((unsigned)total), dim3(NW * 64),
-                           0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                           (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.N, a.cl2);
+        hipLaunchKernelGGL((fwd16v6_kernel<T, D, CAUSAL, NW, BC, false, DROP, SPARSE>), dim3((unsigned)total),
+                           dim3(NW * 64), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                           (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.dp, a.sp);
     return hipGetLastError();
 }
 
@@ -801,30 +621,28 @@ hipError_t launch32(const FwdArgs& a) {
     return hipGetLastError();
 }
 
-// Kernel choice.  d = 128: the sixth generation with eight 32-row waves (one
-// workgroup per compute unit, two waves per SIMD; the pipelined halves give
-// each wave its own overlap of matrix and vector work, and eight waves halve
-// the copies per wave and the L2 traffic per query row), on the persistent
-// grid.  d = 64: the sixth generation with four waves and 64-key tiles (three
-// waves per SIMD fit in the registers), on the persistent grid under the
-// causal mask only (without it, one row block per workgroup measures faster
-// at this head dimension).  Dropout runs the fifth generation with eight
-// waves at d = 128 and four waves with 128-key tiles at d = 64; block masks
-// and variable lengths run it with four waves (two workgroups per compute
-// unit, so the waves that share a SIMD belong to different workgroups).
+// Kernel choice: the sixth generation throughout.  d = 128: eight 32-row waves
+// (one workgroup per compute unit, two waves per SIMD; the pipelined halves
+// give each wave its own overlap of matrix and vector work, and eight waves
+// halve the copies per wave and the L2 traffic per query row), on the
+// persistent grid.  d = 64: four waves and 64-key tiles (three waves per SIMD
+// fit in the registers), on the persistent grid under the causal mask only
+// (without it, one row block per workgroup measures faster at this head
+// dimension).  Dropout, block masks and variable lengths are compile-time
+// variants of the same kernels.
 template <typename T, int D, bool CAUSAL>
 hipError_t dispatch16c(const FwdArgs& a) {
-    if (a.drop) {
-        if constexpr (D == 128) return launch16v5<T, D, CAUSAL, 8, 64, true>(a);
-        else return launch16v5<T, D, CAUSAL, 4, 128, true>(a);
-    }
-    if (a.sparse) {
-        if constexpr (D == 128) return launch16v5<T, D, CAUSAL, 4, 64, false, true>(a);
-        else return launch16v5<T, D, CAUSAL, 4, 128, false, true>(a);
-    }
-    if constexpr (D == 128) return launch16v6<T, D, CAUSAL, 8, 64, true>(a);
-    else if constexpr (CAUSAL) return launch16v6<T, D, CAUSAL, 4, 64, true>(a);
-    else return launch16v6<T, D, CAUSAL, 4, 64, false>(a);
+    constexpr int NW = D == 128 ? 8 : 4;
+    constexpr bool PERS = D == 128 || CAUSAL;
+    // (with dropout the persistent round loop pushes the d = 128 build past the
+    // register file, so each row block gets a workgroup of its own)
+    if (a.drop) return launch16v6<T, D, CAUSAL, NW, 64, D == 64 && CAUSAL, true>(a);
+    // block masks: 128-row blocks (four waves), one mask row per workgroup, so
+    // that no wave waits through the tiles that only another mask row allows;
+    // sequence lengths alone keep the dense tiling
+    if (a.sparse && a.sp.mask) return launch16v6<T, D, CAUSAL, 4, 64, true, false, true>(a);
+    if (a.sparse) return launch16v6<T, D, CAUSAL, NW, 64, PERS, false, true>(a);
+    return launch16v6<T, D, CAUSAL, NW, 64, PERS>(a);
 }
 
 template <typename T, int D>

@@ -24,7 +24,7 @@ from exact_attention_99_amd import build as fabuild
 FUNC = re.compile(r"^(_Z\S+):\s*(?:;.*)?$", re.M)
 
 # kernel families the entry points launch
-CHECKED = ("fwd16v5_kernel", "fwd16v6_kernel", "fwd8_kernel", "fwd_split16_kernel",
+CHECKED = ("fwd16v6_kernel", "fwd8_kernel", "fwd_split16_kernel",
            "dq16v2_kernel", "dq16v3_kernel", "dkdv16v2_kernel", "dkdv16v3_kernel")
 
 
