@@ -424,13 +424,20 @@ __host__ __device__ constexpr int dkdv_seg_block(int seg) {
 // as zeros (Q, dO, the logsumexp and D row terms alike), which makes their
 // P * (dP - D) and P^T dO contributions exactly zero, and keys past N are never
 // written back, so only the causal condition needs a mask.
-template <typename T, int D, bool CAUSAL, bool PERSIST = false>
+//
+// MASKED = 1: variable lengths.  Everything past the sequence's length reads as
+// zeros like the rows past N above, and the dK and dV of keys past it are
+// written as zeros.  MASKED = 2: block masks (and lengths).  The workgroup's 128
+// keys are one mask column: the walk visits only the steps whose query rows
+// meet a set mask block, all through the masked path, with one allow bit per
+// 32-row block.
+template <typename T, int D, bool CAUSAL, bool PERSIST = false, int MASKED = 0>
 __global__ void __launch_bounds__(256)
 dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                 const float* __restrict__ LSE, const float* __restrict__ Delta,
                 uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int B, int Hq, int Hkv, int N,
-                float cl2, float scale) {
+                float cl2, float scale, SparseParams sp) {
     constexpr int NW = 4;
     constexpr int BKV = 128;
     constexpr int BQ = 16384 / D;
@@ -447,6 +454,8 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     static_assert(WI % NW == 0, "tile copies split evenly over the waves");
     constexpr int IPW = WI / NW;
     static_assert(BQ <= 256, "row terms staged one per thread");
+    constexpr bool SPARSE = MASKED != 0;
+    constexpr bool BLOCKMASK = MASKED == 2;
     constexpr int NSLOT = 2 * NKS;          // MFMAs per segment (== 4 * NDB)
     static_assert(NSLOT == 4 * NDB, "S/dP and dV/dK segments hold the same MFMA count");
     constexpr int EPS = 16 / NSLOT;         // softmax elements per slot
@@ -477,15 +486,19 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         }
         const int jb = logical % nkb;
         const int bhk = logical / nkb;
-        const int hk = bhk % Hkv;
-        const int b = bhk / Hkv;
+        // the masked path takes the batch index fastest (XCD balance across
+        // sequences of different lengths)
+        const int hk = SPARSE ? bhk / B : bhk % Hkv;
+        const int b = SPARSE ? bhk % B : bhk / Hkv;
         const int G = Hq / Hkv;
 
         const int kv0 = jb * BKV;
         const int kw = kv0 + 32 * wave;
         const int key = kw + l32;
         const size_t kvoff = ((size_t)b * Hkv + hk) * (size_t)N * D;
-        const uint32_t head_bytes = (uint32_t)N * D * 2;
+        // valid positions of this sequence (the masked path's lengths; else N)
+        const int Nk = (SPARSE && sp.seqlens) ? min(max(sp.seqlens[b], 0), N) : N;
+        const uint32_t head_bytes = (uint32_t)Nk * D * 2;
 
         u32x4 kf[NKS], vf[NKS];
         {
@@ -512,7 +525,7 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         }
 
         const int qb_first = CAUSAL ? kv0 / BQ : 0;
-        const int qb_count = (N + BQ - 1) / BQ - qb_first;
+        const int qb_count = kv0 >= Nk ? 0 : (Nk + BQ - 1) / BQ - qb_first;
         const int nsteps = G * qb_count;
 
         uint32_t cp[IPW];
@@ -527,7 +540,7 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         // Tile order: under a causal mask the G diagonal tiles (the first query
         // tile of each head, the only ones that need the mask) come first, then
         // the remaining tiles head by head.
-        const int ndiag = CAUSAL ? G : 0;
+        const int ndiag = (CAUSAL && qb_count > 0) ? G : 0;
         const int nrest = qb_count - (CAUSAL ? 1 : 0);
         auto step_rows = [&](int s, int& h, int& q0) {
             if (CAUSAL && s < ndiag) {
@@ -558,8 +571,8 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             if (tid < BQ) {
                 // scaled to base 2 when it is published (a use here would make the
                 // wave wait for the tile copies issued just before)
-                sl = Buf(LSE + roff, (uint32_t)N * 4).load_f32((uint32_t)(q0 + tid) * 4);
-                sd = Buf(Delta + roff, (uint32_t)N * 4).load_f32((uint32_t)(q0 + tid) * 4);
+                sl = Buf(LSE + roff, (uint32_t)Nk * 4).load_f32((uint32_t)(q0 + tid) * 4);
+                sd = Buf(Delta + roff, (uint32_t)Nk * 4).load_f32((uint32_t)(q0 + tid) * 4);
             }
         };
         auto put_rows = [&](int buf) {
@@ -579,15 +592,16 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         // products of block (seg + 1) / 2; the others the dV/dK products of block
         // seg / 2 - 1, and the last one those of block NQB - 1.
         // mlim: element (block blk, row offset o) of this lane is visible when
-        // 32 blk + o >= mlim (causal: the query row is at or after the key)
+        // 32 blk + o >= mlim (causal: the query row is at or after the key) and
+        // (block masks) bit blk of allow is set
         // rt_base: the tile's buffer.  Every LDS read of the step goes through
         // this restrict-qualified pointer, so the transposing reads carry alias
         // information and the compiler does not make them wait for the copies of
         // the next step into the other buffer.
         // (The buffer is a run-time argument of the step, not a template one: a
         // step specialised on a constant buffer would lose that information.)
-        auto run_step = [&](auto mask_tag, const unsigned char* __restrict__ rt_base, int mlim)
-                            __attribute__((always_inline)) {
+        auto run_step = [&](auto mask_tag, const unsigned char* __restrict__ rt_base, int mlim,
+                            uint32_t allow) __attribute__((always_inline)) {
             constexpr bool MASK = decltype(mask_tag)::value;
             // The lane-dependent parts of every LDS address, with the buffer's base
             // folded in, are formed once per tile; each read then adds only an
@@ -639,7 +653,10 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             auto soft = [&](int blk, int r) {
                 const int g = r >> 2, i = r & 3;
                 float p = fast_exp2(fmaf(sacc[r], cl2, -lc[g][i]));
-                if (MASK) p = (32 * blk + 8 * g + i >= mlim) ? p : 0.f;
+                if (MASK)
+                    p = ((!CAUSAL || 32 * blk + 8 * g + i >= mlim) && (!BLOCKMASK || ((allow >> blk) & 1u)))
+                            ? p
+                            : 0.f;
                 pv[r] = p;
                 dsv[r] = p * (dpacc[r] - dc[g][i]);
                 if (r & 1) {
@@ -693,7 +710,7 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             });
         };
 
-        if (nsteps > 0) {
+        if (!BLOCKMASK && nsteps > 0) {
             issue(0, buf_of(0));
             put_rows(buf_of(0));
             wait_vmem();
@@ -709,21 +726,100 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             step_rows(s, h, q0);
             (void)h;
             // rows q0 + 4 hi + (32 blk + 8 g + i) are visible when at or after the key
-            run_step(mask_tag, smem + (BUFC >= 0 ? BUFC : buf_of(s)) * STAGE, key - q0 - 4 * hi);
+            run_step(mask_tag, smem + (BUFC >= 0 ? BUFC : buf_of(s)) * STAGE, key - q0 - 4 * hi, ~0u);
             put_rows(nb);
             wait_vmem();
             __syncthreads();
         };
-        for (int s = 0; s < ndiag; ++s)
-            tile(s, std::true_type{}, std::integral_constant<int, -1>{});
-        for (int s = ndiag; s < nsteps; s += 2) {
-            tile(s, std::false_type{}, std::integral_constant<int, 0>{});
-            if (s + 1 < nsteps) tile(s + 1, std::false_type{}, std::integral_constant<int, 1>{});
+        if constexpr (!BLOCKMASK) {
+            for (int s = 0; s < ndiag; ++s)
+                tile(s, std::true_type{}, std::integral_constant<int, -1>{});
+            for (int s = ndiag; s < nsteps; s += 2) {
+                tile(s, std::false_type{}, std::integral_constant<int, 0>{});
+                if (s + 1 < nsteps) tile(s + 1, std::false_type{}, std::integral_constant<int, 1>{});
+            }
+        } else {
+            // allow bit blk: the mask block of query rows q0 + 32 blk .. and
+            // this workgroup's keys is set
+            const int mc = min(kv0 / 128, sp.nb - 1);
+            auto allow_of = [&](int st) {
+                int h, q0;
+                step_rows(st, h, q0);
+                const unsigned char* col = sp.mask + (size_t)(sp.heads == 1 ? 0 : h) * sp.nb * sp.nb + mc;
+                uint32_t m = 0;
+#pragma unroll
+                for (int r = 0; r < BQ / 128; ++r)
+                    if (col[(size_t)min(q0 / 128 + r, sp.nb - 1) * sp.nb]) m |= ((1u << 4) - 1) << (4 * r);
+                return m;
+            };
+            // The next step with a set bit, and its bits.  Each lane of the wave
+            // tests one candidate (scan_load fetches its bits), so a scan costs
+            // one load latency per 64 steps; scan_pick takes the first hit, or
+            // loads the next 64 candidates.  The walk loads the candidates
+            // after the next step before running the current one, so their
+            // latency hides behind its matrix work.
+            int cbase = 0;
+            uint32_t cand = 0;
+            auto scan_load = [&](int after) {
+                cbase = after + 1;
+                cand = cbase + lane < nsteps ? allow_of(cbase + lane) : 0u;
+            };
+            auto scan_pick = [&](uint32_t& m) {
+                for (;;) {
+                    const uint64_t bal = __ballot(cand != 0);
+                    if (bal) {
+                        const int f = __builtin_ctzll(bal);
+                        m = (uint32_t)__builtin_amdgcn_readlane((int)cand, f);
+                        return cbase + f;
+                    }
+                    if (cbase + 64 >= nsteps) break;
+                    scan_load(cbase + 63);
+                }
+                m = 0;
+                return nsteps;
+            };
+            // the allowed steps in the order above, buffers alternating from 0
+            uint32_t m = 0, mn = 0;
+            scan_load(-1);
+            int s = scan_pick(m);
+            if (s < nsteps) {
+                issue(s, 0);
+                put_rows(0);
+                wait_vmem();
+            }
+            __syncthreads();
+            int sn = nsteps;
+            if (s < nsteps) {
+                scan_load(s);
+                sn = scan_pick(mn);
+            }
+            for (int par = 0; s < nsteps; par ^= 1) {
+                // past the last allowed step, re-copy a valid step into the
+                // buffer nobody reads again
+                issue(min(sn, nsteps - 1), par ^ 1);
+                if (sn < nsteps) scan_load(sn);
+                int h, q0;
+                step_rows(s, h, q0);
+                (void)h;
+                run_step(std::true_type{}, smem + par * STAGE, key - q0 - 4 * hi, m);
+                put_rows(par ^ 1);
+                uint32_t mnn = 0;
+                const int snn = sn < nsteps ? scan_pick(mnn) : nsteps;
+                wait_vmem();
+                __syncthreads();
+                s = sn;
+                m = mn;
+                sn = snn;
+                mn = mnn;
+            }
         }
 
         if (key < N) {
             uint16_t* dkrow = dK + kvoff + (size_t)key * D;
             uint16_t* dvrow = dV + kvoff + (size_t)key * D;
+            // keys past the sequence's length (their columns of dS and P need
+            // not be finite) get zero gradients
+            const bool pad = SPARSE && key >= Nk;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -733,6 +829,7 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                     wk[1] = Mma<T>::pack2(dkt[db][4 * g + 2] * scale, dkt[db][4 * g + 3] * scale);
                     wv[0] = Mma<T>::pack2(dvt[db][4 * g], dvt[db][4 * g + 1]);
                     wv[1] = Mma<T>::pack2(dvt[db][4 * g + 2], dvt[db][4 * g + 3]);
+                    if (pad) wk = wv = u32x2{0u, 0u};
                     *reinterpret_cast<u32x2*>(dkrow + 32 * db + 8 * g + 4 * hi) = wk;
                     *reinterpret_cast<u32x2*>(dvrow + 32 * db + 8 * g + 4 * hi) = wv;
                 }
@@ -742,24 +839,32 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 }
 
 // ---------------------------------------------------------------------------
-// Second-generation dQ kernel: K and V tiles arrive by buffer-to-LDS copies,
-// row-major only; K^T operands of dQ^T += K^T dS^T come from transposing reads
-// of the same K tile (dual swizzle), so no transposed copy is built.
+// Third-generation dQ kernel, query-outer: a workgroup holds 32 NW query rows
+// (Q and dO in registers, one row per lane) and walks the key tiles, which
+// arrive by buffer-to-LDS copies, row-major only; the K^T operands of
+// dQ^T += K^T dS^T come from transposing reads of the same K tile (dual
+// swizzle), so no transposed copy is built.  The key tiles are split in two
+// loops.  Tiles wholly below every row of the block (and inside the sequence)
+// run a body with no mask code, two at a time so that both LDS buffers have
+// compile-time offsets; the diagonal and ragged-end tiles run the masked body.
 //
 // DROP: attention dropout (fa_common.h): dS = P * (Z dP 256 / t8 - D), with
 // the keep bytes of a tile's key blocks drawn as in the forward kernel (lane
 // half hi draws block 2 kp + hi of its row, one exchange per block pair).
 //
-// SPARSE: block-sparse attention (SparseParams): the workgroup's 128 rows are
-// one mask row; it walks only the key tiles the mask allows for them.
-template <typename T, int D, bool CAUSAL, bool DROP = false, bool SPARSE = false>
-__global__ void __launch_bounds__(256)
-dq16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+// SPARSE: variable lengths and block masks.  Keys past the sequence's length
+// read as zeros and are masked like a ragged end; a row past it, or a row with
+// no visible key (logsumexp -inf), takes an infinite logsumexp, so its P and
+// dS are exactly zero on every tile.  With a block mask the workgroup's 128
+// rows are one mask row and the walk visits only the key tiles it allows.
+template <typename T, int D, bool CAUSAL, int NW = 4, bool DROP = false, bool SPARSE = false>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+dq16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
               const float* __restrict__ LSE, const float* __restrict__ Delta,
               uint16_t* __restrict__ dQ, int B, int Hq, int Hkv, int N, float cl2, float scale,
               DropParams dp, SparseParams sp) {
-    constexpr int NW = 4;
+    static_assert(!SPARSE || NW == 4, "a block-mask row spans the workgroup's 128 rows");
     constexpr int BR = 32 * NW;
     constexpr int BC = D == 128 ? 64 : 128;
     constexpr int KCH = D / 8;
@@ -813,221 +918,12 @@ dq16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         }
     }
     const size_t roff = ((size_t)b * Hq + h) * (size_t)N;
-    const float lse2 = Buf(LSE + roff, (uint32_t)N * 4).load_f32((uint32_t)q * 4) * kLog2e;
+    float lse2 = Buf(LSE + roff, (uint32_t)N * 4).load_f32((uint32_t)q * 4) * kLog2e;
     const float dlt = Buf(Delta + roff, (uint32_t)N * 4).load_f32((uint32_t)q * 4);
+    // padded and empty rows: P = exp2(S - inf) = 0 everywhere
+    if (SPARSE && (q >= Nk || !(lse2 > -INFINITY))) lse2 = INFINITY;
 
-    const int kv_len = q0 >= Nk ? 0 : (CAUSAL ? min(Nk, q0 + BR) : Nk);
-    const int ntiles = (kv_len + BC - 1) / BC;
-
-    uint32_t cp[IPW];
-#pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-        const int p = (wave + NW * i) * 64 + lane;
-        const int row = p / KCH, pc = p % KCH;
-        cp[i] = (uint32_t)(row * D * 2 + 16 * (pc ^ dual_swz<D>(row)));
-    }
-    auto issue = [&](int k0, int buf) {
-        unsigned char* base = smem + buf * STAGE;
-#pragma unroll
-        for (int i = 0; i < IPW; ++i) {
-            const uint32_t off = (uint32_t)k0 * D * 2 + cp[i];
-            buf_to_lds16(Kb, base + (wave + NW * i) * 1024, off);
-            buf_to_lds16(Vb, base + TB + (wave + NW * i) * 1024, off);
-        }
-    };
-
-    const int g16 = lane >> 4;
-    const int j16 = lane & 15;
-    const int tr_row = 4 * hi + (j16 >> 2);
-    const int tr_col = 2 * (16 * (g16 & 1) + 4 * (j16 & 3));
-
-    f32x16 dq[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) dq[db] = zero16();
-
-    // tile j from the buffer at base; the LDS reads go through this
-    // restrict-qualified pointer, so the compiler does not make the
-    // transposing reads wait for the copies of the next tile into the other
-    // buffer
-    auto tile_at = [&](int j, const unsigned char* __restrict__ base) __attribute__((always_inline)) {
-        const int k0 = j * BC;
-        const bool need_mask = (CAUSAL && k0 + BC - 1 > qw) || (k0 + BC > Nk) || (qw + 32 > Nk);
-        uint32_t dm[DROP ? NKB : 1][4];
-        if constexpr (DROP) {
-#pragma unroll
-            for (int kp = 0; kp < NKB / 2; ++kp) {
-                uint32_t w[8];
-                drop_bytes(w, (uint32_t)(k0 / 32 + 2 * kp + hi), (uint32_t)q, (uint32_t)(b * Hq + h), dp);
-                drop_pair_exchange(w, dm[2 * kp], dm[2 * kp + 1]);
-            }
-        }
-        auto kb_body = [&](int kb, const uint32_t* m) __attribute__((always_inline)) {
-            f32x16 st = zero16(), dpt = zero16();
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const int off = dual_off<D>(32 * kb + l32, 16 * (2 * ks + hi));
-                const u32x4 ak = *reinterpret_cast<const u32x4*>(base + off);
-                const u32x4 av = *reinterpret_cast<const u32x4*>(base + TB + off);
-                st = Mma<T>::mma(ak, qf[ks], st);
-                dpt = Mma<T>::mma(av, dof[ks], dpt);
-            }
-            float p[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) p[r] = fast_exp2(fmaf(st[r], cl2, -lse2));
-            if (need_mask) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int kk = k0 + 32 * kb + acc_row(r, hi);
-                    p[r] = ((!CAUSAL || kk <= q) && kk < Nk && q < Nk) ? p[r] : 0.f;
-                }
-            }
-            if constexpr (DROP) {
-                // register r: byte r % 4 of dword r / 4
-#pragma unroll
-                for (int r = 0; r < 16; ++r) dpt[r] = drop_keep(m[r >> 2], r & 3, dp.t8) ? dpt[r] * dp.scale : 0.f;
-            }
-            u32x4 dsb[2];
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int r = 8 * t + 2 * jj;
-                    dsb[t][jj] = Mma<T>::pack2(p[r] * (dpt[r] - dlt), p[r + 1] * (dpt[r + 1] - dlt));
-                }
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const int row = 32 * kb + 16 * t + tr_row;
-                    const int col = 64 * db + tr_col;
-                    const u32x2 lo = lds_read_tr16(base + dual_off<D>(row, col));
-                    const u32x2 up = lds_read_tr16(base + dual_off<D>(row + 8, col));
-                    u32x4 a;
-                    a[0] = lo[0]; a[1] = lo[1]; a[2] = up[0]; a[3] = up[1];
-                    dq[db] = Mma<T>::mma(a, dsb[t], dq[db]);
-                }
-        };
-        if constexpr (DROP) {
-            static_for<NKB>([&](auto kbc) { kb_body(kbc.value, dm[kbc.value]); });
-        } else {
-#pragma unroll 1
-            for (int kb = 0; kb < NKB; ++kb) kb_body(kb, nullptr);
-        }
-    };
-    // tile j from buffer par & 1
-    auto tile = [&](int j, int par) __attribute__((always_inline)) { tile_at(j, smem + (par & 1) * STAGE); };
-
-    if constexpr (SPARSE) {
-        const int nb = sp.nb;
-        const unsigned char* mrow = sp.mask ? sp.mask + ((size_t)(sp.heads == 1 ? 0 : h) * nb + min(q0 / 128, nb - 1)) * nb : nullptr;
-        auto need = [&](int jt) { return !mrow || mrow[jt * BC / 128] != 0; };
-        int jt = 0;
-        while (jt < ntiles && !need(jt)) ++jt;
-        if (jt < ntiles) issue(jt * BC, 0);
-        wait_vmem();
-        __syncthreads();
-        int par = 0;
-        while (jt < ntiles) {
-            int jn = jt + 1;
-            while (jn < ntiles && !need(jn)) ++jn;
-            issue(jn * BC, par ^ 1);
-            tile(jt, par);
-            wait_vmem();
-            __syncthreads();
-            jt = jn;
-            par ^= 1;
-        }
-    } else {
-        issue(0, 0);
-        wait_vmem();
-        __syncthreads();
-        for (int j = 0; j < ntiles; ++j) {
-            issue((j + 1) * BC, (j + 1) & 1);
-            tile(j, j);
-            wait_vmem();
-            __syncthreads();
-        }
-    }
-
-    if (q < N) {
-        const float sc = q < Nk ? scale : 0.f;   // padded rows get no gradient
-        uint16_t* row = dQ + qoff + (size_t)q * D;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                u32x2 w;
-                w[0] = Mma<T>::pack2(dq[db][4 * g] * sc, dq[db][4 * g + 1] * sc);
-                w[1] = Mma<T>::pack2(dq[db][4 * g + 2] * sc, dq[db][4 * g + 3] * sc);
-                *reinterpret_cast<u32x2*>(row + 32 * db + 8 * g + 4 * hi) = w;
-            }
-    }
-}
-
-// Third-generation dQ kernel: the data path of the second generation with the
-// key tiles split in two loops.  Tiles wholly below every row of the block
-// (and inside the sequence) run a body with no mask code, two at a time so
-// that both LDS buffers have compile-time offsets; the diagonal and ragged-end
-// tiles run the masked body.
-template <typename T, int D, bool CAUSAL, int NW = 4>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
-dq16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-              const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-              const float* __restrict__ LSE, const float* __restrict__ Delta,
-              uint16_t* __restrict__ dQ, int B, int Hq, int Hkv, int N, float cl2, float scale) {
-    constexpr int BR = 32 * NW;
-    constexpr int BC = D == 128 ? 64 : 128;
-    constexpr int KCH = D / 8;
-    constexpr int TB = BC * D * 2;
-    constexpr int STAGE = 2 * TB;
-    constexpr int NKB = BC / 32;
-    constexpr int NDB = D / 32;
-    constexpr int NKS = D / 16;
-    constexpr int WI = TB / 1024;
-    static_assert(WI % NW == 0, "tile copies split evenly over the waves");
-    constexpr int IPW = WI / NW;
-
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l32 = lane & 31;
-    const int hi = lane >> 5;
-
-    const int nqb = (N + BR - 1) / BR;
-    const int total = nqb * Hq * B;
-    const int logical = xcd_remap((int)blockIdx.x, total);
-    const int qb_raw = logical % nqb;
-    const int bh = logical / nqb;
-    const int qb = CAUSAL ? (nqb - 1 - qb_raw) : qb_raw;
-    const int h = bh % Hq;
-    const int b = bh / Hq;
-    const int hk = h / (Hq / Hkv);
-
-    const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
-    const size_t koff = ((size_t)b * Hkv + hk) * (size_t)N * D;
-    const uint32_t head_bytes = (uint32_t)N * D * 2;
-    const Buf Kb(K + koff, head_bytes), Vb(V + koff, head_bytes);
-
-    const int q0 = qb * BR;
-    const int qw = q0 + 32 * wave;
-    const int q = qw + l32;
-
-    u32x4 qf[NKS], dof[NKS];
-    {
-        const Buf Qb(Q + qoff, head_bytes), Db(dO + qoff, head_bytes);
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            qf[ks] = Qb.load16((uint32_t)(q * D + 16 * ks + 8 * hi) * 2);
-            dof[ks] = Db.load16((uint32_t)(q * D + 16 * ks + 8 * hi) * 2);
-        }
-    }
-    const size_t roff = ((size_t)b * Hq + h) * (size_t)N;
-    const float lse2 = Buf(LSE + roff, (uint32_t)N * 4).load_f32((uint32_t)q * 4) * kLog2e;
-    const float dlt = Buf(Delta + roff, (uint32_t)N * 4).load_f32((uint32_t)q * 4);
-
-    const int kv_len = CAUSAL ? min(N, q0 + BR) : N;
+    const int kv_len = (SPARSE && q0 >= Nk) ? 0 : (CAUSAL ? min(Nk, q0 + BR) : Nk);
     const int ntiles = (kv_len + BC - 1) / BC;
 
     uint32_t cp[IPW];
@@ -1064,6 +960,15 @@ dq16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         constexpr bool MASK = decltype(mask_tag)::value;
         if constexpr (decltype(issue_tag)::value) issue_to(nxt, kn);
         const int k0 = j * BC;
+        uint32_t dm[DROP ? NKB : 1][4];
+        if constexpr (DROP) {
+#pragma unroll
+            for (int kp = 0; kp < NKB / 2; ++kp) {
+                uint32_t w[8];
+                drop_bytes(w, (uint32_t)(k0 / 32 + 2 * kp + hi), (uint32_t)q, (uint32_t)(b * Hq + h), dp);
+                drop_pair_exchange(w, dm[2 * kp], dm[2 * kp + 1]);
+            }
+        }
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             f32x16 st = zero16(), dpt = zero16();
@@ -1080,11 +985,17 @@ dq16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             for (int r = 0; r < 16; ++r) p[r] = fast_exp2(fmaf(st[r], cl2, -lse2));
             if (MASK) {
                 // key k0 + 32 kb + acc_row(r, hi) is visible iff it is at most
-                // min(q, N - 1) (N - 1 without the causal mask): one compare of
+                // min(q, Nk - 1) (Nk - 1 without the causal mask): one compare of
                 // the register's constant part against a per-lane limit
-                const int lim = (CAUSAL ? min(q, N - 1) : N - 1) - (k0 + 32 * kb) - 4 * hi;
+                const int lim = (CAUSAL ? min(q, Nk - 1) : Nk - 1) - (k0 + 32 * kb) - 4 * hi;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) p[r] = (8 * (r >> 2) + (r & 3) <= lim) ? p[r] : 0.f;
+            }
+            if constexpr (DROP) {
+                // register r: byte r % 4 of dword r / 4
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    dpt[r] = drop_keep(dm[kb][r >> 2], r & 3, dp.t8) ? dpt[r] * dp.scale : 0.f;
             }
             u32x4 dsb[2];
 #pragma unroll
@@ -1110,27 +1021,71 @@ dq16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     };
 
     // tiles below every row of the block and inside the sequence
-    const int nfull = min(CAUSAL ? q0 / BC : ntiles, N / BC);
-    issue_to(smem, 0);
-    wait_vmem();
-    __syncthreads();
+    const int nfull = min(min(CAUSAL ? q0 / BC : ntiles, Nk / BC), ntiles);
     // The copy of the next tile is issued at the start of every tile, also the
     // last (it lies in this head's range or past its end and reads as zeros).
-    int j = 0;
-    for (; j + 1 < nfull; j += 2) {
-        body(j, std::false_type{}, std::true_type{}, smem, smem + STAGE, (j + 1) * BC);
+    if constexpr (!SPARSE) {
+        issue_to(smem, 0);
         wait_vmem();
         __syncthreads();
-        body(j + 1, std::false_type{}, std::true_type{}, smem + STAGE, smem, (j + 2) * BC);
+        int j = 0;
+        for (; j + 1 < nfull; j += 2) {
+            body(j, std::false_type{}, std::true_type{}, smem, smem + STAGE, (j + 1) * BC);
+            wait_vmem();
+            __syncthreads();
+            body(j + 1, std::false_type{}, std::true_type{}, smem + STAGE, smem, (j + 2) * BC);
+            wait_vmem();
+            __syncthreads();
+        }
+        for (; j < ntiles; ++j) {
+            issue_to(smem + ((j + 1) & 1) * STAGE, (j + 1) * BC);
+            if (!CAUSAL || j * BC <= qw + 31)
+                body(j, std::true_type{}, std::false_type{}, smem + (j & 1) * STAGE, nullptr, 0);
+            wait_vmem();
+            __syncthreads();
+        }
+    } else {
+        // the same walk over the key tiles the block mask allows for this row
+        // block (all of them without one)
+        const unsigned char* mrow =
+            sp.mask ? sp.mask + ((size_t)(sp.heads == 1 ? 0 : h) * sp.nb + min(q0 / 128, sp.nb - 1)) * sp.nb
+                    : nullptr;
+        // the next allowed tile after jt: each lane of the wave tests one
+        // candidate, so a scan costs one load latency per 64 tiles
+        auto next = [&](int jt) {
+            if (!mrow) return jt + 1;
+            for (int base = jt + 1; base < ntiles; base += 64) {
+                const int c = base + lane;
+                const uint64_t bal = __ballot(c < ntiles && mrow[c * BC / 128] != 0);
+                if (bal) return base + __builtin_ctzll(bal);
+            }
+            return ntiles;
+        };
+        int j = next(-1);
+        issue_to(smem, j * BC);
         wait_vmem();
         __syncthreads();
-    }
-    for (; j < ntiles; ++j) {
-        issue_to(smem + ((j + 1) & 1) * STAGE, (j + 1) * BC);
-        if (!CAUSAL || j * BC <= qw + 31)
-            body(j, std::true_type{}, std::false_type{}, smem + (j & 1) * STAGE, nullptr, 0);
-        wait_vmem();
-        __syncthreads();
+        for (;;) {
+            const int j1 = next(j);
+            if (j1 >= nfull) break;
+            const int j2 = next(j1);
+            body(j, std::false_type{}, std::true_type{}, smem, smem + STAGE, j1 * BC);
+            wait_vmem();
+            __syncthreads();
+            body(j1, std::false_type{}, std::true_type{}, smem + STAGE, smem, j2 * BC);
+            wait_vmem();
+            __syncthreads();
+            j = j2;
+        }
+        for (int par = 0; j < ntiles; par ^= 1) {
+            const int jn = next(j);
+            issue_to(smem + (par ^ 1) * STAGE, jn * BC);
+            if (!CAUSAL || j * BC <= qw + 31)
+                body(j, std::true_type{}, std::false_type{}, smem + par * STAGE, nullptr, 0);
+            wait_vmem();
+            __syncthreads();
+            j = jn;
+        }
     }
 
     if (q < N) {
@@ -1384,62 +1339,45 @@ hipError_t prepare32(const BwdArgs& a) {
 template <typename T, int D, bool CAUSAL>
 hipError_t dkdv16(const BwdArgs& a) {
     const int nkb = (a.N + 127) / 128;
-    if (a.sparse) {
-        // dropout and block masks run on the second-generation kernels
-        hipLaunchKernelGGL((dkdv16v2_kernel<T, D, CAUSAL, false, true>), dim3((unsigned)(nkb * a.Hkv * a.B)),
-                           dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                           (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
-                           (uint16_t*)a.dk, (uint16_t*)a.dv, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale,
-                           a.dp, a.sp);
-        return hipGetLastError();
-    }
-    if (a.drop) {
-        hipLaunchKernelGGL((dkdv16v2_kernel<T, D, CAUSAL, true>), dim3((unsigned)(nkb * a.Hkv * a.B)),
-                           dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                           (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
-                           (uint16_t*)a.dk, (uint16_t*)a.dv, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale,
-                           a.dp, a.sp);
-        return hipGetLastError();
-    }
-    // persistent grid where the key blocks outnumber the compute units
-    const int grid = persistent_grid();
     const long long total = (long long)nkb * a.Hkv * a.B;
-    if (grid >= 8 && total > grid) {
-        hipLaunchKernelGGL((dkdv16v3_kernel<T, D, CAUSAL, true>), dim3((unsigned)grid), dim3(256), 0,
+    if (a.drop) {
+        hipLaunchKernelGGL((dkdv16v2_kernel<T, D, CAUSAL, true>), dim3((unsigned)total), dim3(256), 0,
                            a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                            (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv,
-                           a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale);
+                           a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale, a.dp, a.sp);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((dkdv16v3_kernel<T, D, CAUSAL>), dim3((unsigned)total), dim3(256), 0, a.stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.B,
-                       a.Hq, a.Hkv, a.N, a.cl2, a.scale);
-    return hipGetLastError();
+    // persistent grid where the key blocks outnumber the compute units; the
+    // masked path keeps one workgroup per key block, since its steps per key
+    // block vary with the lengths and the mask, and a static schedule would
+    // leave the compute units unevenly loaded
+    const int grid = persistent_grid();
+    const bool pers = !a.sparse && grid >= 8 && total > grid;
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)(pers ? grid : total)), dim3(256), 0, a.stream,
+                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                           (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.B,
+                           a.Hq, a.Hkv, a.N, a.cl2, a.scale, a.sp);
+        return hipGetLastError();
+    };
+    if (a.sparse)
+        return a.sp.mask ? go(dkdv16v3_kernel<T, D, CAUSAL, false, 2>) : go(dkdv16v3_kernel<T, D, CAUSAL, false, 1>);
+    return pers ? go(dkdv16v3_kernel<T, D, CAUSAL, true>) : go(dkdv16v3_kernel<T, D, CAUSAL>);
 }
 
 template <typename T, int D, bool CAUSAL>
 hipError_t dq16(const BwdArgs& a) {
     const int nqb = (a.N + 127) / 128;
-    if (a.sparse) {
-        hipLaunchKernelGGL((dq16v2_kernel<T, D, CAUSAL, false, true>), dim3((unsigned)(nqb * a.Hq * a.B)),
-                           dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                           (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
-                           (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale, a.dp, a.sp);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)(nqb * a.Hq * a.B)), dim3(256), 0, a.stream,
+                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                           (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, a.B, a.Hq, a.Hkv,
+                           a.N, a.cl2, a.scale, a.dp, a.sp);
         return hipGetLastError();
-    }
-    if (a.drop) {
-        hipLaunchKernelGGL((dq16v2_kernel<T, D, CAUSAL, true>), dim3((unsigned)(nqb * a.Hq * a.B)),
-                           dim3(256), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                           (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
-                           (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale, a.dp, a.sp);
-        return hipGetLastError();
-    }
-    hipLaunchKernelGGL((dq16v3_kernel<T, D, CAUSAL>), dim3((unsigned)(nqb * a.Hq * a.B)), dim3(256), 0,
-                       a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, a.B, a.Hq, a.Hkv,
-                       a.N, a.cl2, a.scale);
-    return hipGetLastError();
+    };
+    if (a.sparse) return go(dq16v3_kernel<T, D, CAUSAL, 4, false, true>);
+    if (a.drop) return go(dq16v3_kernel<T, D, CAUSAL, 4, true>);
+    return go(dq16v3_kernel<T, D, CAUSAL>);
 }
 
 template <int D, bool CAUSAL>

@@ -147,7 +147,7 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
         const int kv_len = q0 >= Nk ? 0 : (CAUSAL ? min(Nk, q0 + BR) : Nk);
         const int ntiles = (kv_len + BC - 1) / BC;
-        const int nfull = min(CAUSAL ? q0 / BC : ntiles, Nk / BC);
+        const int nfull = min(min(CAUSAL ? q0 / BC : ntiles, Nk / BC), ntiles);
 
         uint32_t cpk[IPW], cpv[IPW];
 #pragma unroll
@@ -397,21 +397,27 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             // this wave's 32 rows lie in one mask row, and a 64-key tile in one
             // mask column: a wave computes a tile whole or not at all
             const unsigned char* mw = mk + min(qw / 128, nb - 1) * nb;
-            auto wg_need = [&](int jt) {
-                const int c = jt * BC / 128;
-                bool any = false;
-                for (int r = mr0; r <= mr1; ++r) any |= mk[r * nb + c] != 0;
-                return any;
+            // the next tile after jt that some row of the workgroup may see:
+            // each lane of the wave tests one candidate, so a scan costs one
+            // load latency per 64 tiles
+            auto next = [&](int jt) {
+                for (int base = jt + 1; base < ntiles; base += 64) {
+                    const int c = base + lane;
+                    bool any = false;
+                    if (c < ntiles)
+                        for (int r = mr0; r <= mr1; ++r) any |= mk[r * nb + c * BC / 128] != 0;
+                    const uint64_t bal = __ballot(any);
+                    if (bal) return base + __builtin_ctzll(bal);
+                }
+                return ntiles;
             };
-            int jt = 0;
-            while (jt < ntiles && !wg_need(jt)) ++jt;
+            int jt = next(-1);
             if (jt < ntiles) issue_to(smem, jt * BC);
             wait_vmem();
             __syncthreads();
             int par = 0;
             while (jt < ntiles) {
-                int jn = jt + 1;
-                while (jn < ntiles && !wg_need(jn)) ++jn;
+                const int jn = next(jt);
                 // past the last allowed tile the copy reads this head's range or
                 // zeros and lands in the buffer no later tile reads
                 issue_to(smem + (par ^ 1) * STAGE, jn * BC);
@@ -639,9 +645,12 @@ hipError_t dispatch16c(const FwdArgs& a) {
     if (a.drop) return launch16v6<T, D, CAUSAL, NW, 64, D == 64 && CAUSAL, true>(a);
     // block masks: 128-row blocks (four waves), one mask row per workgroup, so
     // that no wave waits through the tiles that only another mask row allows;
-    // sequence lengths alone keep the dense tiling
-    if (a.sparse && a.sp.mask) return launch16v6<T, D, CAUSAL, 4, 64, true, false, true>(a);
-    if (a.sparse) return launch16v6<T, D, CAUSAL, NW, 64, PERS, false, true>(a);
+    // sequence lengths alone keep the dense tiling.  Both take one workgroup
+    // per row block: their work per row block varies with the mask and the
+    // lengths, which the hardware's dispatch balances and a static schedule
+    // does not.
+    if (a.sparse && a.sp.mask) return launch16v6<T, D, CAUSAL, 4, 64, false, false, true>(a);
+    if (a.sparse) return launch16v6<T, D, CAUSAL, NW, 64, false, false, true>(a);
     return launch16v6<T, D, CAUSAL, NW, 64, PERS>(a);
 }
 

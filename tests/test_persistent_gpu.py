@@ -96,3 +96,51 @@ def test_many_short_heads_closed_form(dtype, d, causal):
     assert err.max().item() <= tol["o_max"], err.max().item()
     assert err.mean().item() <= tol["o_mean"], err.mean().item()
     assert (lse.to(torch.float64) - lref).abs().max().item() <= tol["lse_max"]
+
+
+@pytest.mark.parametrize("kind", ["varlen", "blockmask"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_many_short_heads_masked(kind, d, causal):
+    """The masked path on the persistent grids: per-sequence lengths (one empty
+    sequence, one full, the rest ragged) or a per-head block mask over the same
+    many short heads; three whole K/V groups against the oracle."""
+    from exact_attention_99_amd import fa_bwd_blocksparse, fa_bwd_varlen, fa_fwd_blocksparse, fa_fwd_varlen
+    from oracle import blocksparse as obs
+    from oracle import varlen as ovl
+
+    from .test_varlen_gpu import _check
+
+    print(f"case kind={kind} d={d} causal={causal}", flush=True)
+    dtype = "bf16"
+    scale = 1.0 / math.sqrt(d)
+    seed = 4300 + d + (7 if causal else 0) + (1 if kind == "blockmask" else 0)
+    q, k, v, do = workloads.make_inputs(B, HQ, HKV, N, d, dtype, seed, with_dout=True)
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    if kind == "varlen":
+        g = torch.Generator().manual_seed(seed + 1)
+        lens = torch.randint(1, N + 1, (B,), generator=g)
+        lens[0], lens[7] = 0, N
+        sl = lens.to(torch.int32).to(DEV)
+        o, lse = fa_fwd_varlen(qd, kd, vd, sl, causal, scale)
+        dq, dk, dv = fa_bwd_varlen(qd, kd, vd, o, lse, dod, sl, causal, scale)
+    else:
+        M = workloads.make_block_mask(HQ, N, 0.4, seed + 1, True)
+        Md = M.to(DEV)
+        o, lse = fa_fwd_blocksparse(qd, kd, vd, Md, causal, scale)
+        dq, dk, dv = fa_bwd_blocksparse(qd, kd, vd, o, lse, dod, Md, causal, scale)
+    torch.cuda.synchronize()
+    for (b, hk) in ((0, 0), (7, 1), (B - 1, HKV - 1)):
+        hs = slice(hk * G, (hk + 1) * G)
+        args = (f64(q[b:b + 1, hs]), f64(k[b:b + 1, hk:hk + 1]), f64(v[b:b + 1, hk:hk + 1]),
+                f64(do[b:b + 1, hs]), scale, causal)
+        got = (o[b:b + 1, hs], lse[b:b + 1, hs], dq[b:b + 1, hs], dk[b:b + 1, hk:hk + 1],
+               dv[b:b + 1, hk:hk + 1])
+        what = f"b={b} kv head {hk}"
+        if kind == "varlen":
+            n = int(lens[b])
+            _check(*got, ovl.attention_backward_varlen(*args, [n]), [n], dtype, what)
+        else:
+            ref = obs.attention_backward_blocksparse(*args, M[hs].numpy())
+            check_fwd(*got[:2], *ref[:2], dtype, what)
+            check_grads(*got[2:], *ref[2:], dtype, what)
