@@ -79,322 +79,6 @@ delta32_kernel(const float* __restrict__ O, const float* __restrict__ dO, float*
 }
 
 // ---------------------------------------------------------------------------
-// Second-generation dK / dV kernel.  Four waves, 128 keys per workgroup (32
-// per wave, one per lane), query rows in steps.  The Q and dO tiles arrive in
-// LDS through buffer-to-LDS copies (no staging registers, rows past N read as
-// zeros) and are stored row-major only, with a
-// swizzle that suits both ways they are read: 128-bit reads of 16 consecutive
-// rows for the A operands of S = Q K^T and dP = dO V^T, and transposing reads
-// for the A operands of dV^T += dO^T P and dK^T += Q^T dS.
-//
-// DROP: attention dropout (fa_common.h): dV^T += dO^T (Z P 256 / t8) and
-// dS = P * (Z dP 256 / t8 - D).  A wave's 32 keys are one key block, so each
-// query row of a step needs one generator call: lane l draws row q0 + l (and
-// q0 + 64 + l), writes the 32 bytes to its wave's LDS area, and transposing
-// byte reads give every lane the bytes of its key for its 16 rows.
-//
-// SPARSE: block-sparse attention (SparseParams): the workgroup's 128 keys are
-// one mask column; it walks only the (query head, query block) steps whose
-// mask block is set.
-template <typename T, int D, bool CAUSAL, bool DROP = false, bool SPARSE = false>
-__global__ void __launch_bounds__(256)
-dkdv16v2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                const float* __restrict__ LSE, const float* __restrict__ Delta,
-                uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int B, int Hq, int Hkv, int N,
-                float cl2, float scale, DropParams dp, SparseParams sp) {
-    constexpr int NW = 4;
-    constexpr int BKV = 128;
-    constexpr int BQ = 8192 / D;
-    constexpr int NQB = BQ / 32;
-    constexpr int KCH = D / 8;
-    constexpr int TB = BQ * D * 2;            // one tile, bytes
-    constexpr int OFF_DOS = TB;
-    constexpr int OFF_LSE = 2 * TB;
-    constexpr int OFF_DL = OFF_LSE + BQ * 4;
-    constexpr int STAGE = OFF_DL + BQ * 4;
-    constexpr int NDB = D / 32;
-    constexpr int NKS = D / 16;
-    constexpr int WI = TB / 1024;             // 1 KB wave copies per tile
-    static_assert(WI % NW == 0, "tile copies split evenly over the waves");
-    constexpr int IPW = WI / NW;
-    static_assert(BQ <= 128, "row terms staged by the first 2*BQ threads");
-
-    constexpr int DROP_BYTES = DROP ? NW * BQ * 32 : 0;   // per wave: BQ rows x 32 keys
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE + DROP_BYTES];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l32 = lane & 31;
-    const int hi = lane >> 5;
-
-    const int nkb = (N + BKV - 1) / BKV;
-    const int total = nkb * Hkv * B;
-    const int logical = xcd_remap((int)blockIdx.x, total);
-    const int jb = logical % nkb;  // ascending: under a causal mask block 0 is the longest
-    const int bhk = logical / nkb;
-    // the masked path takes the batch index fastest (XCD balance across
-    // sequences of different lengths)
-    const int hk = SPARSE ? bhk / B : bhk % Hkv;
-    const int b = SPARSE ? bhk % B : bhk / Hkv;
-    const int G = Hq / Hkv;
-
-    const int kv0 = jb * BKV;
-    const int kw = kv0 + 32 * wave;
-    const int key = kw + l32;
-    const size_t kvoff = ((size_t)b * Hkv + hk) * (size_t)N * D;
-    // valid positions of this sequence (the masked path's lengths; else N)
-    const int Nk = (SPARSE && sp.seqlens) ? min(max(sp.seqlens[b], 0), N) : N;
-    const uint32_t head_bytes = (uint32_t)Nk * D * 2;
-
-    u32x4 kf[NKS], vf[NKS];
-    {
-        const Buf Kb(K + kvoff, head_bytes), Vb(V + kvoff, head_bytes);
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            kf[ks] = Kb.load16((uint32_t)(key * D + 16 * ks + 8 * hi) * 2);
-            vf[ks] = Vb.load16((uint32_t)(key * D + 16 * ks + 8 * hi) * 2);
-        }
-    }
-
-    f32x16 dkt[NDB], dvt[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-        dkt[db] = zero16();
-        dvt[db] = zero16();
-    }
-
-    const int qb_first = CAUSAL ? kv0 / BQ : 0;
-    const int qb_count = max((Nk + BQ - 1) / BQ - qb_first, 0);
-    const int nsteps = G * qb_count;
-
-    // copy slots: this wave's copy i fills bytes [1024*bi, 1024*bi + 1024) of
-    // the Q and dO tiles; cp[i] is the lane's source offset relative to the
-    // step's first row
-    uint32_t cp[IPW];
-#pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-        const int p = (wave + NW * i) * 64 + lane;
-        const int row = p / KCH, pc = p % KCH;
-        cp[i] = (uint32_t)(row * D * 2 + 16 * (pc ^ dual_swz<D>(row)));
-    }
-    float sx = 0.f;
-
-    auto step_rows = [&](int s, int& h, int& q0) {
-        h = hk * G + s / qb_count;
-        q0 = (qb_first + s % qb_count) * BQ;
-    };
-    auto issue = [&](int s, int buf) {
-        int h, q0;
-        step_rows(s, h, q0);
-        const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
-        const Buf Qb(Q + qoff, head_bytes), Db(dO + qoff, head_bytes);
-        unsigned char* base = smem + buf * STAGE;
-#pragma unroll
-        for (int i = 0; i < IPW; ++i) {
-            const uint32_t off = (uint32_t)q0 * D * 2 + cp[i];
-            buf_to_lds16(Qb, base + (wave + NW * i) * 1024, off);
-            buf_to_lds16(Db, base + OFF_DOS + (wave + NW * i) * 1024, off);
-        }
-        const size_t roff = ((size_t)b * Hq + h) * (size_t)N;
-        if (tid < BQ)
-            sx = Buf(LSE + roff, (uint32_t)N * 4).load_f32((uint32_t)(q0 + tid) * 4) * kLog2e;
-        else if (tid >= 128 && tid < 128 + BQ)
-            sx = Buf(Delta + roff, (uint32_t)N * 4).load_f32((uint32_t)(q0 + tid - 128) * 4);
-    };
-    auto put_rows = [&](int buf) {
-        unsigned char* base = smem + buf * STAGE;
-        if (tid < BQ)
-            reinterpret_cast<float*>(base + OFF_LSE)[tid] = sx;
-        else if (tid >= 128 && tid < 128 + BQ)
-            reinterpret_cast<float*>(base + OFF_DL)[tid - 128] = sx;
-    };
-
-    // transposing-read coordinates of this lane inside a (16-row, 32-dim) block
-    const int g16 = lane >> 4;
-    const int j16 = lane & 15;
-    const int tr_row = 4 * hi + (j16 >> 2);
-    const int tr_col = 2 * (16 * (g16 & 1) + 4 * (j16 & 3));
-
-    // step s from the buffer at base (dbase: this wave's dropout-mask area).
-    // The LDS reads go through these restrict-qualified pointers, so the
-    // compiler does not make the transposing reads wait for the copies of the
-    // next step into the other buffer.
-    auto run_step_at = [&](int s, const unsigned char* __restrict__ base, unsigned char* __restrict__ dbase)
-                           __attribute__((always_inline)) {
-        int h, q0;
-        step_rows(s, h, q0);
-        const bool need_mask = (CAUSAL && q0 < kw + 32) || (q0 + BQ > Nk) || (kw + 32 > Nk);
-        const float* lse2s = reinterpret_cast<const float*>(base + OFF_LSE);
-        const float* dls = reinterpret_cast<const float*>(base + OFF_DL);
-        if constexpr (DROP) {
-#pragma unroll
-            for (int rr = 0; rr < BQ / 64; ++rr) {
-                uint32_t w[8];
-                drop_bytes(w, (uint32_t)(kw / 32), (uint32_t)(q0 + 64 * rr + lane), (uint32_t)(b * Hq + h), dp);
-                u32x4 lo, up;
-                lo[0] = w[0]; lo[1] = w[1]; lo[2] = w[2]; lo[3] = w[3];
-                up[0] = w[4]; up[1] = w[5]; up[2] = w[6]; up[3] = w[7];
-                *reinterpret_cast<u32x4*>(dbase + (64 * rr + lane) * 32) = lo;
-                *reinterpret_cast<u32x4*>(dbase + (64 * rr + lane) * 32 + 16) = up;
-            }
-        }
-#pragma unroll 1
-        for (int qs = 0; qs < NQB; ++qs) {
-            f32x16 sacc = zero16(), dpacc = zero16();
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const int off = dual_off<D>(32 * qs + l32, 16 * (2 * ks + hi));
-                const u32x4 aq = *reinterpret_cast<const u32x4*>(base + off);
-                const u32x4 ad = *reinterpret_cast<const u32x4*>(base + OFF_DOS + off);
-                sacc = Mma<T>::mma(aq, kf[ks], sacc);
-                dpacc = Mma<T>::mma(ad, vf[ks], dpacc);
-            }
-            float pv[16], dv[16], d4s[16];
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + 32 * qs + 8 * g + 4 * hi);
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + 32 * qs + 8 * g + 4 * hi);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 4 * g + i;
-                    pv[r] = fast_exp2(fmaf(sacc[r], cl2, -l4[i]));
-                    dv[r] = dpacc[r] - d4[i];
-                    d4s[r] = d4[i];
-                }
-            }
-            if (need_mask) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int q = q0 + 32 * qs + acc_row(r, hi);
-                    const bool vis = (!CAUSAL || key <= q) && q < Nk && key < Nk;
-                    pv[r] = vis ? pv[r] : 0.f;
-                }
-            }
-            float pd[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) pd[r] = pv[r];
-            if constexpr (DROP) {
-                // rows 8 g .. 8 g + 7 of block qs at this lane's key; register
-                // 4 g + i (row 8 g + 4 hi + i) is byte i of dword hi
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int s16 = lane & 15;
-                    const int off = (32 * qs + 8 * g + (s16 >> 1)) * 32 + 16 * ((lane >> 4) & 1) + 8 * (s16 & 1);
-                    const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                        (__attribute__((address_space(3))) i32x2*)(dbase + off));
-                    const uint32_t m = (uint32_t)(hi ? x[1] : x[0]);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int r = 4 * g + i;
-                        const bool keep = drop_keep(m, i, dp.t8);
-                        pd[r] = keep ? pv[r] * dp.scale : 0.f;
-                        dv[r] = (keep ? dpacc[r] * dp.scale : 0.f) - d4s[r];
-                    }
-                }
-            }
-            u32x4 pb[2], dsb[2];
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int r = 8 * t + 2 * jj;
-                    pb[t][jj] = Mma<T>::pack2(pd[r], pd[r + 1]);
-                    dsb[t][jj] = Mma<T>::pack2(pv[r] * dv[r], pv[r + 1] * dv[r + 1]);
-                }
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const int row = 32 * qs + 16 * t + tr_row;
-                    const int col = 64 * db + tr_col;
-                    const int o_lo = dual_off<D>(row, col), o_up = dual_off<D>(row + 8, col);
-                    const u32x2 d_lo = lds_read_tr16(base + OFF_DOS + o_lo);
-                    const u32x2 d_up = lds_read_tr16(base + OFF_DOS + o_up);
-                    const u32x2 q_lo = lds_read_tr16(base + o_lo);
-                    const u32x2 q_up = lds_read_tr16(base + o_up);
-                    u32x4 ado, aqt;
-                    ado[0] = d_lo[0]; ado[1] = d_lo[1]; ado[2] = d_up[0]; ado[3] = d_up[1];
-                    aqt[0] = q_lo[0]; aqt[1] = q_lo[1]; aqt[2] = q_up[0]; aqt[3] = q_up[1];
-                    dvt[db] = Mma<T>::mma(ado, pb[t], dvt[db]);
-                    dkt[db] = Mma<T>::mma(aqt, dsb[t], dkt[db]);
-                }
-        }
-    };
-    // step s from buffer par & 1
-    auto run_step = [&](int s, int par) __attribute__((always_inline)) {
-        run_step_at(s, smem + (par & 1) * STAGE, smem + 2 * STAGE + wave * (BQ * 32));
-    };
-
-    if constexpr (SPARSE) {
-        const int nb = sp.nb;
-        const int mc = min(kv0 / 128, nb - 1);
-        auto need = [&](int st) {
-            if (!sp.mask) return true;   // lengths only: every step of the sequence
-            int h, q0;
-            step_rows(st, h, q0);
-            return sp.mask[((size_t)(sp.heads == 1 ? 0 : h) * nb + min(q0 / 128, nb - 1)) * nb + mc] != 0;
-        };
-        int st = 0;
-        while (st < nsteps && !need(st)) ++st;
-        if (st < nsteps) {
-            issue(st, 0);
-            put_rows(0);
-            wait_vmem();
-        }
-        __syncthreads();
-        int par = 0;
-        while (st < nsteps) {
-            int sn = st + 1;
-            while (sn < nsteps && !need(sn)) ++sn;
-            // past the last needed step, re-copy a valid step into the buffer
-            // nobody reads again
-            issue(min(sn, nsteps - 1), par ^ 1);
-            run_step(st, par);
-            put_rows(par ^ 1);
-            wait_vmem();
-            __syncthreads();
-            st = sn;
-            par ^= 1;
-        }
-    } else {
-        if (nsteps > 0) {
-            issue(0, 0);
-            put_rows(0);
-            wait_vmem();
-        }
-        __syncthreads();
-
-        for (int s = 0; s < nsteps; ++s) {
-            // The copy of the next step runs on every iteration (the last one
-            // re-copies the last step into the buffer nobody reads again).
-            issue(min(s + 1, nsteps - 1), (s + 1) & 1);
-            run_step(s, s);
-            put_rows((s + 1) & 1);
-            wait_vmem();
-            __syncthreads();
-        }
-    }
-
-    if (key < N) {
-        uint16_t* dkrow = dK + kvoff + (size_t)key * D;
-        uint16_t* dvrow = dV + kvoff + (size_t)key * D;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                u32x2 wk, wv;
-                wk[0] = Mma<T>::pack2(dkt[db][4 * g] * scale, dkt[db][4 * g + 1] * scale);
-                wk[1] = Mma<T>::pack2(dkt[db][4 * g + 2] * scale, dkt[db][4 * g + 3] * scale);
-                wv[0] = Mma<T>::pack2(dvt[db][4 * g], dvt[db][4 * g + 1]);
-                wv[1] = Mma<T>::pack2(dvt[db][4 * g + 2], dvt[db][4 * g + 3]);
-                *reinterpret_cast<u32x2*>(dkrow + 32 * db + 8 * g + 4 * hi) = wk;
-                *reinterpret_cast<u32x2*>(dvrow + 32 * db + 8 * g + 4 * hi) = wv;
-            }
-    }
-}
-
 // Segment seg of a dK/dV query tile of NQB blocks: 0 and the odd segments
 // before the last hold the S/dP products of block (seg + 1) / 2; the others the
 // dV/dK products of block seg / 2 - 1, and the last one those of block NQB - 1.
@@ -408,7 +92,13 @@ __host__ __device__ constexpr int dkdv_seg_block(int seg) {
 }
 
 // ---------------------------------------------------------------------------
-// Software-pipelined dK / dV kernel.  One wave per SIMD (the dK/dV
+// Software-pipelined dK / dV kernel.  Four waves, 128 keys per workgroup (32
+// per wave, one per lane), query rows in steps.  The Q and dO tiles arrive in
+// LDS through buffer-to-LDS copies (no staging registers) and are stored
+// row-major only, with a swizzle that suits both ways they are read: 128-bit
+// reads of 16 consecutive rows for the A operands of S = Q K^T and
+// dP = dO V^T, and transposing reads for the A operands of dV^T += dO^T P and
+// dK^T += Q^T dS.  One wave per SIMD (the dK/dV
 // accumulators and the K/V operands fill most of the register file), so the
 // overlap of matrix work, softmax arithmetic and LDS traffic has to come from
 // the instruction order of a single wave.  A query tile of NQB 32-row blocks
@@ -431,16 +121,28 @@ __host__ __device__ constexpr int dkdv_seg_block(int seg) {
 // keys are one mask column: the walk visits only the steps whose query rows
 // meet a set mask block, all through the masked path, with one allow bit per
 // 32-row block.
-template <typename T, int D, bool CAUSAL, bool PERSIST = false, int MASKED = 0>
+//
+// DROP: attention dropout (fa_common.h): dV^T += dO^T (Z P 256 / t8) and
+// dS = P * (Z dP 256 / t8 - D).  A wave's 32 keys are one key block, so each
+// query row of a step needs one generator call: lane l draws rows q0 + l and
+// q0 + 64 + l.  The ten rounds of the next step's calls run in the slots of
+// the step's last segment, the one without softmax work (spreading them over
+// the S/dP segments as well made the compiler fail); at the end of the step
+// the bytes go to the wave's LDS area, and transposing byte reads, issued in
+// each block's S/dP segment, give every lane the bytes of its key for its 16
+// rows.  At d = 64 the query tile has 128 rows under dropout, so that the byte
+// areas fit in LDS beside the double-buffered tiles.
+template <typename T, int D, bool CAUSAL, bool PERSIST = false, int MASKED = 0, bool DROP = false>
 __global__ void __launch_bounds__(256)
 dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                 const float* __restrict__ LSE, const float* __restrict__ Delta,
                 uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int B, int Hq, int Hkv, int N,
-                float cl2, float scale, SparseParams sp) {
+                float cl2, float scale, DropParams dp, SparseParams sp) {
+    static_assert(!(DROP && MASKED), "dropout runs on the dense walk");
     constexpr int NW = 4;
     constexpr int BKV = 128;
-    constexpr int BQ = 16384 / D;
+    constexpr int BQ = (DROP && D == 64) ? 128 : 16384 / D;
     constexpr int NQB = BQ / 32;
     constexpr int KCH = D / 8;
     constexpr int TB = BQ * D * 2;
@@ -462,8 +164,12 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     constexpr int NSEG = 2 * NQB;
     constexpr int TSLOT = NSEG * NSLOT;
     constexpr int AHEAD = 4;                // operand read distance, in slots
+    // dropout: generator calls per lane and step, and their rounds
+    constexpr int NCALL = BQ / 64;
+    constexpr int NROUND = 10 * NCALL;
+    constexpr int DROP_AREA = BQ * 32;      // per wave: BQ rows x 32 keys
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE + (DROP ? NW * DROP_AREA : 0)];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -588,6 +294,31 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         const int tr_row = 4 * hi + (j16 >> 2);
         const int tr_col = 2 * (16 * (g16 & 1) + 4 * (j16 & 3));
 
+        // dropout: the generator calls of one step (rows q0 + 64 c + lane of
+        // head h, this wave's key block) and the wave's byte area
+        Philox4x64 pg[DROP ? NCALL : 1];
+        unsigned char* __restrict__ dbase = smem + 2 * STAGE + (DROP ? wave * DROP_AREA : 0);
+        auto drop_start = [&](int st) {
+            if constexpr (DROP) {
+                int h, q0;
+                step_rows(st, h, q0);
+#pragma unroll
+                for (int c = 0; c < NCALL; ++c)
+                    pg[c].start((uint32_t)(kw / 32), (uint32_t)(q0 + 64 * c + lane), (uint32_t)(b * Hq + h), dp);
+            }
+        };
+        auto drop_store = [&]() {
+            if constexpr (DROP) {
+#pragma unroll
+                for (int c = 0; c < NCALL; ++c) {
+                    uint32_t w[8];
+                    pg[c].words(w);
+                    *reinterpret_cast<u32x4*>(dbase + (64 * c + lane) * 32) = u32x4{w[0], w[1], w[2], w[3]};
+                    *reinterpret_cast<u32x4*>(dbase + (64 * c + lane) * 32 + 16) = u32x4{w[4], w[5], w[6], w[7]};
+                }
+            }
+        };
+
         // Segment seg of a tile: 0 and odd segments before the last hold the S/dP
         // products of block (seg + 1) / 2; the others the dV/dK products of block
         // seg / 2 - 1, and the last one those of block NQB - 1.
@@ -600,8 +331,9 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         // the next step into the other buffer.
         // (The buffer is a run-time argument of the step, not a template one: a
         // step specialised on a constant buffer would lose that information.)
+        // sn: the step whose dropout bytes this step draws (DROP)
         auto run_step = [&](auto mask_tag, const unsigned char* __restrict__ rt_base, int mlim,
-                            uint32_t allow) __attribute__((always_inline)) {
+                            uint32_t allow, int sn) __attribute__((always_inline)) {
             constexpr bool MASK = decltype(mask_tag)::value;
             // The lane-dependent parts of every LDS address, with the buffer's base
             // folded in, are formed once per tile; each read then adds only an
@@ -623,6 +355,8 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             f32x16 sacc = zero16(), dpacc = zero16();
             u32x4 pb[2][2], dsb[2][2];
             f32x4 lc[4], dc[4];
+            uint32_t md[4];   // DROP: keep bytes of the current block, dword g
+            drop_start(sn);
 
             auto load_op = [&](auto nc) {
                 constexpr int n = decltype(nc)::value;
@@ -648,6 +382,15 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 else
                     lc[g] = *reinterpret_cast<const f32x4*>(rt_base + (ro - bb) + imm);
             };
+            // keep bytes of rows 8 g .. 8 g + 7 of block blk at this lane's key:
+            // register 4 g + i (row 8 g + 4 hi + i) is byte i of dword hi
+            auto load_drop = [&](int blk, int g) {
+                const int s16 = lane & 15;
+                const int off = (32 * blk + 8 * g + (s16 >> 1)) * 32 + 16 * ((lane >> 4) & 1) + 8 * (s16 & 1);
+                const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) i32x2*)(dbase + off));
+                md[g] = (uint32_t)(hi ? x[1] : x[0]);
+            };
             // softmax and dS of element r of block blk (row 32 blk + acc_row(r, hi))
             float pv[16], dsv[16];
             auto soft = [&](int blk, int r) {
@@ -657,8 +400,14 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                     p = ((!CAUSAL || 32 * blk + 8 * g + i >= mlim) && (!BLOCKMASK || ((allow >> blk) & 1u)))
                             ? p
                             : 0.f;
-                pv[r] = p;
-                dsv[r] = p * (dpacc[r] - dc[g][i]);
+                if constexpr (DROP) {
+                    const bool keep = drop_keep(md[g], i, dp.t8);
+                    pv[r] = keep ? p * dp.scale : 0.f;
+                    dsv[r] = p * ((keep ? dpacc[r] * dp.scale : 0.f) - dc[g][i]);
+                } else {
+                    pv[r] = p;
+                    dsv[r] = p * (dpacc[r] - dc[g][i]);
+                }
                 if (r & 1) {
                     const int par = blk & 1;
                     pb[par][r >> 3][(r & 7) >> 1] = Mma<T>::pack2(pv[r - 1], pv[r]);
@@ -668,6 +417,9 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
 #pragma unroll
             for (int k = 0; k < 8; ++k) load_rows(0, k);
+            if constexpr (DROP)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) load_drop(0, g);
             static_for<AHEAD>([&](auto nc) { load_op(nc); });
             static_for<TSLOT>([&](auto nc) {
                 constexpr int n = decltype(nc)::value;
@@ -706,13 +458,32 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                     // row terms of the block whose S/dP this segment computes
                     load_rows(blk, j - (NSLOT - 8));
                 }
+                // keep bytes of the block whose S/dP this segment computes
+                if constexpr (DROP && is_s && seg > 0 && j < 4) load_drop(blk, j);
+                if constexpr (DROP && seg == NSEG - 1) {
+                    // the rounds of the next step's generator calls, spread over
+                    // the last segment (it carries no softmax work)
+#pragma unroll
+                    for (int ri = j * NROUND / NSLOT; ri < (j + 1) * NROUND / NSLOT; ++ri) pg[ri % NCALL].round();
+                }
                 __builtin_amdgcn_sched_barrier(0);
             });
+            // this step's byte reads are all issued, and the wave's LDS
+            // operations run in order: the next step's bytes can replace them
+            drop_store();
         };
 
         if (!BLOCKMASK && nsteps > 0) {
             issue(0, buf_of(0));
             put_rows(buf_of(0));
+            if constexpr (DROP) {
+                drop_start(0);
+#pragma unroll
+                for (int r = 0; r < 10; ++r)
+#pragma unroll
+                    for (int c = 0; c < NCALL; ++c) pg[c].round();
+                drop_store();
+            }
             wait_vmem();
         }
         __syncthreads();
@@ -726,7 +497,8 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             step_rows(s, h, q0);
             (void)h;
             // rows q0 + 4 hi + (32 blk + 8 g + i) are visible when at or after the key
-            run_step(mask_tag, smem + (BUFC >= 0 ? BUFC : buf_of(s)) * STAGE, key - q0 - 4 * hi, ~0u);
+            run_step(mask_tag, smem + (BUFC >= 0 ? BUFC : buf_of(s)) * STAGE, key - q0 - 4 * hi, ~0u,
+                     min(s + 1, nsteps - 1));
             put_rows(nb);
             wait_vmem();
             __syncthreads();
@@ -801,7 +573,7 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 int h, q0;
                 step_rows(s, h, q0);
                 (void)h;
-                run_step(std::true_type{}, smem + par * STAGE, key - q0 - 4 * hi, m);
+                run_step(std::true_type{}, smem + par * STAGE, key - q0 - 4 * hi, m, 0);
                 put_rows(par ^ 1);
                 uint32_t mnn = 0;
                 const int snn = sn < nsteps ? scan_pick(mnn) : nsteps;
@@ -1340,13 +1112,6 @@ template <typename T, int D, bool CAUSAL>
 hipError_t dkdv16(const BwdArgs& a) {
     const int nkb = (a.N + 127) / 128;
     const long long total = (long long)nkb * a.Hkv * a.B;
-    if (a.drop) {
-        hipLaunchKernelGGL((dkdv16v2_kernel<T, D, CAUSAL, true>), dim3((unsigned)total), dim3(256), 0,
-                           a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                           (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv,
-                           a.B, a.Hq, a.Hkv, a.N, a.cl2, a.scale, a.dp, a.sp);
-        return hipGetLastError();
-    }
     // persistent grid where the key blocks outnumber the compute units; the
     // masked path keeps one workgroup per key block, since its steps per key
     // block vary with the lengths and the mask, and a static schedule would
@@ -1357,11 +1122,13 @@ hipError_t dkdv16(const BwdArgs& a) {
         hipLaunchKernelGGL(kern, dim3((unsigned)(pers ? grid : total)), dim3(256), 0, a.stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                            (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.B,
-                           a.Hq, a.Hkv, a.N, a.cl2, a.scale, a.sp);
+                           a.Hq, a.Hkv, a.N, a.cl2, a.scale, a.dp, a.sp);
         return hipGetLastError();
     };
     if (a.sparse)
         return a.sp.mask ? go(dkdv16v3_kernel<T, D, CAUSAL, false, 2>) : go(dkdv16v3_kernel<T, D, CAUSAL, false, 1>);
+    if (a.drop)
+        return pers ? go(dkdv16v3_kernel<T, D, CAUSAL, true, 0, true>) : go(dkdv16v3_kernel<T, D, CAUSAL, false, 0, true>);
     return pers ? go(dkdv16v3_kernel<T, D, CAUSAL, true>) : go(dkdv16v3_kernel<T, D, CAUSAL>);
 }
 

@@ -25,7 +25,7 @@ FUNC = re.compile(r"^(_Z\S+):\s*(?:;.*)?$", re.M)
 
 # kernel families the entry points launch
 CHECKED = ("fwd16v6_kernel", "fwd8_kernel", "fwd_split16_kernel",
-           "dq16v3_kernel", "dkdv16v2_kernel", "dkdv16v3_kernel")
+           "dq16v3_kernel", "dkdv16v3_kernel")
 
 
 def _asm(src: str, out: str) -> str:
