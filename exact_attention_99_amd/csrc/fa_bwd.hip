@@ -297,7 +297,7 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         // dropout: the generator calls of one step (rows q0 + 64 c + lane of
         // head h, this wave's key block) and the wave's byte area
         Philox4x64 pg[DROP ? NCALL : 1];
-        unsigned char* __restrict__ dbase = smem + 2 * STAGE + (DROP ? wave * DROP_AREA : 0);
+        unsigned char* const dbase = smem + 2 * STAGE + (DROP ? wave * DROP_AREA : 0);
         auto drop_start = [&](int st) {
             if constexpr (DROP) {
                 int h, q0;
@@ -307,14 +307,14 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                     pg[c].start((uint32_t)(kw / 32), (uint32_t)(q0 + 64 * c + lane), (uint32_t)(b * Hq + h), dp);
             }
         };
-        auto drop_store = [&]() {
+        auto drop_store = [&](unsigned char* dr) {
             if constexpr (DROP) {
 #pragma unroll
                 for (int c = 0; c < NCALL; ++c) {
                     uint32_t w[8];
                     pg[c].words(w);
-                    *reinterpret_cast<u32x4*>(dbase + (64 * c + lane) * 32) = u32x4{w[0], w[1], w[2], w[3]};
-                    *reinterpret_cast<u32x4*>(dbase + (64 * c + lane) * 32 + 16) = u32x4{w[4], w[5], w[6], w[7]};
+                    *reinterpret_cast<u32x4*>(dr + (64 * c + lane) * 32) = u32x4{w[0], w[1], w[2], w[3]};
+                    *reinterpret_cast<u32x4*>(dr + (64 * c + lane) * 32 + 16) = u32x4{w[4], w[5], w[6], w[7]};
                 }
             }
         };
@@ -331,9 +331,10 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         // the next step into the other buffer.
         // (The buffer is a run-time argument of the step, not a template one: a
         // step specialised on a constant buffer would lose that information.)
-        // sn: the step whose dropout bytes this step draws (DROP)
+        // sn: the step whose dropout bytes this step draws, dr: the wave's byte
+        // area (DROP; restrict-qualified like the buffer, for the same reason)
         auto run_step = [&](auto mask_tag, const unsigned char* __restrict__ rt_base, int mlim,
-                            uint32_t allow, int sn) __attribute__((always_inline)) {
+                            uint32_t allow, int sn, unsigned char* __restrict__ dr) __attribute__((always_inline)) {
             constexpr bool MASK = decltype(mask_tag)::value;
             // The lane-dependent parts of every LDS address, with the buffer's base
             // folded in, are formed once per tile; each read then adds only an
@@ -388,7 +389,7 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const int s16 = lane & 15;
                 const int off = (32 * blk + 8 * g + (s16 >> 1)) * 32 + 16 * ((lane >> 4) & 1) + 8 * (s16 & 1);
                 const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (__attribute__((address_space(3))) i32x2*)(dbase + off));
+                    (__attribute__((address_space(3))) i32x2*)(dr + off));
                 md[g] = (uint32_t)(hi ? x[1] : x[0]);
             };
             // softmax and dS of element r of block blk (row 32 blk + acc_row(r, hi))
@@ -470,7 +471,7 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             });
             // this step's byte reads are all issued, and the wave's LDS
             // operations run in order: the next step's bytes can replace them
-            drop_store();
+            drop_store(dr);
         };
 
         if (!BLOCKMASK && nsteps > 0) {
@@ -482,7 +483,7 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 for (int r = 0; r < 10; ++r)
 #pragma unroll
                     for (int c = 0; c < NCALL; ++c) pg[c].round();
-                drop_store();
+                drop_store(dbase);
             }
             wait_vmem();
         }
@@ -498,7 +499,7 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             (void)h;
             // rows q0 + 4 hi + (32 blk + 8 g + i) are visible when at or after the key
             run_step(mask_tag, smem + (BUFC >= 0 ? BUFC : buf_of(s)) * STAGE, key - q0 - 4 * hi, ~0u,
-                     min(s + 1, nsteps - 1));
+                     min(s + 1, nsteps - 1), dbase);
             put_rows(nb);
             wait_vmem();
             __syncthreads();
@@ -573,7 +574,7 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 int h, q0;
                 step_rows(s, h, q0);
                 (void)h;
-                run_step(std::true_type{}, smem + par * STAGE, key - q0 - 4 * hi, m, 0);
+                run_step(std::true_type{}, smem + par * STAGE, key - q0 - 4 * hi, m, 0, dbase);
                 put_rows(par ^ 1);
                 uint32_t mnn = 0;
                 const int snn = sn < nsteps ? scan_pick(mnn) : nsteps;
