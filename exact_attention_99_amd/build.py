@@ -1,9 +1,13 @@
 """Compile libfa355.so (HIP kernels + C-ABI) for gfx950, in-tree.
 
     python -m exact_attention_99_amd.build
+    python -m exact_attention_99_amd.build --out /tmp/alt.so -DFA355_FWD_NW128=4
 
 Always recompiles.  Each ``csrc/*.hip`` file is compiled to an object in
 parallel, then the objects are linked into ``exact_attention_99_amd/libfa355.so``.
+With ``--out`` and -D overrides of the tile parameters (fa_common.h) it builds
+an alternative library elsewhere, for measurements only (select it with the
+FA355_LIB environment variable); the package's own library keeps the defaults.
 """
 from __future__ import annotations
 
@@ -46,22 +50,28 @@ def _compile(src: str, obj: str, extra) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra=()) -> str:
+def build(verbose: bool = False, extra=(), out: str = LIB) -> str:
     srcs = sources()
     with tempfile.TemporaryDirectory(prefix="fa355_build_") as tmp:
         objs = [os.path.join(tmp, os.path.basename(s) + ".o") for s in srcs]
         with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
             list(ex.map(lambda so: _compile(so[0], so[1], list(extra)), zip(srcs, objs)))
-        tmp_lib = LIB + ".tmp"
+        tmp_lib = out + ".tmp"
         cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp_lib]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-        os.replace(tmp_lib, LIB)
+        os.replace(tmp_lib, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":
-    build(verbose=True, extra=sys.argv[1:])
+    args = sys.argv[1:]
+    out = LIB
+    if "--out" in args:
+        i = args.index("--out")
+        out = os.path.abspath(args[i + 1])
+        del args[i:i + 2]
+    build(verbose=True, extra=args, out=out)

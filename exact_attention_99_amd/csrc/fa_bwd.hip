@@ -142,7 +142,7 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     static_assert(!(DROP && MASKED), "dropout runs on the dense walk");
     constexpr int NW = 4;
     constexpr int BKV = 128;
-    constexpr int BQ = (DROP && D == 64) ? 128 : 16384 / D;
+    constexpr int BQ = (DROP && D == 64) ? 128 : (D == 128 ? FA355_DKDV_BQ128 : 256);
     constexpr int NQB = BQ / 32;
     constexpr int KCH = D / 8;
     constexpr int TB = BQ * D * 2;
@@ -156,6 +156,7 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     static_assert(WI % NW == 0, "tile copies split evenly over the waves");
     constexpr int IPW = WI / NW;
     static_assert(BQ <= 256, "row terms staged one per thread");
+    static_assert(BQ >= BKV, "only a key block's first query tile meets its diagonal");
     constexpr bool SPARSE = MASKED != 0;
     constexpr bool BLOCKMASK = MASKED == 2;
     constexpr int NSLOT = 2 * NKS;          // MFMAs per segment (== 4 * NDB)
@@ -163,7 +164,7 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     constexpr int EPS = 16 / NSLOT;         // softmax elements per slot
     constexpr int NSEG = 2 * NQB;
     constexpr int TSLOT = NSEG * NSLOT;
-    constexpr int AHEAD = 4;                // operand read distance, in slots
+    constexpr int AHEAD = FA355_DKDV_AHEAD;  // operand read distance, in slots
     // dropout: generator calls per lane and step, and their rounds
     constexpr int NCALL = BQ / 64;
     constexpr int NROUND = 10 * NCALL;
@@ -639,7 +640,7 @@ dq16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               DropParams dp, SparseParams sp) {
     static_assert(!SPARSE || NW == 4, "a block-mask row spans the workgroup's 128 rows");
     constexpr int BR = 32 * NW;
-    constexpr int BC = D == 128 ? 64 : 128;
+    constexpr int BC = D == 128 ? FA355_DQ_BC128 : 128;
     constexpr int KCH = D / 8;
     constexpr int TB = BC * D * 2;
     constexpr int STAGE = 2 * TB;
@@ -1135,9 +1136,11 @@ hipError_t dkdv16(const BwdArgs& a) {
 
 template <typename T, int D, bool CAUSAL>
 hipError_t dq16(const BwdArgs& a) {
-    const int nqb = (a.N + 127) / 128;
     auto go = [&](auto kern) {
-        hipLaunchKernelGGL(kern, dim3((unsigned)(nqb * a.Hq * a.B)), dim3(256), 0, a.stream,
+        // kern's rows per workgroup: 32 per wave (dense path: FA355_DQ_NW waves)
+        const int nw = (a.sparse || a.drop) ? 4 : FA355_DQ_NW;
+        const int nqb = (a.N + 32 * nw - 1) / (32 * nw);
+        hipLaunchKernelGGL(kern, dim3((unsigned)(nqb * a.Hq * a.B)), dim3(64 * nw), 0, a.stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                            (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, a.B, a.Hq, a.Hkv,
                            a.N, a.cl2, a.scale, a.dp, a.sp);
@@ -1145,7 +1148,7 @@ hipError_t dq16(const BwdArgs& a) {
     };
     if (a.sparse) return go(dq16v3_kernel<T, D, CAUSAL, 4, false, true>);
     if (a.drop) return go(dq16v3_kernel<T, D, CAUSAL, 4, true>);
-    return go(dq16v3_kernel<T, D, CAUSAL>);
+    return go(dq16v3_kernel<T, D, CAUSAL, FA355_DQ_NW>);
 }
 
 template <int D, bool CAUSAL>

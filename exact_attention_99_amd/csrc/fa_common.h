@@ -23,6 +23,31 @@
 #include <utility>
 #include <stdint.h>
 
+// Tile parameters of the default kernels.  A build may override them (-D) to
+// produce an alternative library for measurements; the library the package
+// ships and tests is built with these values.
+#ifndef FA355_FWD_NW128
+#define FA355_FWD_NW128 8      // forward waves per workgroup at d = 128
+#endif
+#ifndef FA355_FWD_BC128
+#define FA355_FWD_BC128 64     // forward keys per tile at d = 128
+#endif
+#ifndef FA355_FWD_PERSIST
+#define FA355_FWD_PERSIST 1    // forward persistent grid
+#endif
+#ifndef FA355_DKDV_BQ128
+#define FA355_DKDV_BQ128 128   // dK/dV query rows per step at d = 128
+#endif
+#ifndef FA355_DKDV_AHEAD
+#define FA355_DKDV_AHEAD 4     // dK/dV operand read distance, in products
+#endif
+#ifndef FA355_DQ_NW
+#define FA355_DQ_NW 4          // dQ waves per workgroup
+#endif
+#ifndef FA355_DQ_BC128
+#define FA355_DQ_BC128 64      // dQ keys per tile at d = 128
+#endif
+
 namespace fa355 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

@@ -638,8 +638,8 @@ hipError_t launch32(const FwdArgs& a) {
 // variants of the same kernels.
 template <typename T, int D, bool CAUSAL>
 hipError_t dispatch16c(const FwdArgs& a) {
-    constexpr int NW = D == 128 ? 8 : 4;
-    constexpr bool PERS = D == 128 || CAUSAL;
+    constexpr int NW = D == 128 ? FA355_FWD_NW128 : 4;
+    constexpr bool PERS = FA355_FWD_PERSIST && (D == 128 || CAUSAL);
     // (with dropout the persistent round loop pushes the d = 128 build past the
     // register file, so each row block gets a workgroup of its own)
     if (a.drop) return launch16v6<T, D, CAUSAL, NW, 64, D == 64 && CAUSAL, true>(a);
@@ -651,7 +651,7 @@ hipError_t dispatch16c(const FwdArgs& a) {
     // does not.
     if (a.sparse && a.sp.mask) return launch16v6<T, D, CAUSAL, 4, 64, false, false, true>(a);
     if (a.sparse) return launch16v6<T, D, CAUSAL, NW, 64, false, false, true>(a);
-    return launch16v6<T, D, CAUSAL, NW, 64, PERS>(a);
+    return launch16v6<T, D, CAUSAL, NW, (D == 128 ? FA355_FWD_BC128 : 64), PERS>(a);
 }
 
 template <typename T, int D>
