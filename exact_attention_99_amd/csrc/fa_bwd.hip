@@ -746,6 +746,10 @@ dq16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             f32x16 st = zero16(), dpt = zero16();
+            // raised priority while the wave issues its S and dP products: when
+            // both waves of a SIMD are ready, the one feeding the matrix cores
+            // issues first
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 const int off = dual_off<D>(32 * kb + l32, 16 * (2 * ks + hi));
@@ -754,6 +758,7 @@ dq16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 st = Mma<T>::mma(ak, qf[ks], st);
                 dpt = Mma<T>::mma(av, dof[ks], dpt);
             }
+            __builtin_amdgcn_s_setprio(0);
             float p[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) p[r] = fast_exp2(fmaf(st[r], cl2, -lse2));

@@ -138,7 +138,10 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         const Buf Qb(Q + qoff, head_bytes), Kb(K + koff, head_bytes), Vb(V + koff, head_bytes);
 
         const int q0 = qb * BR;
-        const int qw = q0 + 32 * wave;
+        // waves w and w + NW/2 share a SIMD: give them complementary row slices
+        // (w and NW - 1 - (w - NW/2)) so the diagonal tiles split evenly
+        const int slice = wave < NW / 2 ? wave : (NW - 1) - (wave - NW / 2);
+        const int qw = q0 + 32 * slice;
         const int q = qw + l32;
 
         u32x4 qf[NKS];
@@ -268,6 +271,11 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             Philox4x64 pg;
             if constexpr (DROP) pg.start((uint32_t)(k0 / 32 + hi), (uint32_t)q, (uint32_t)(b * Hq + h), dp);
 
+            // The wave's priority is raised while it issues the score products of
+            // the first half and the second (whose slots carry the first half's
+            // exponentials): when both waves of a SIMD are ready, the one feeding
+            // the matrix cores issues first.
+            __builtin_amdgcn_s_setprio(1);
             // scores of the first half | K reads of the second
             f32x16 s0 = zero16(), s1 = zero16();
             static_for<NKS>([&](auto tc) {
@@ -324,6 +332,7 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                     __builtin_amdgcn_sched_barrier(0);
                 });
             }
+            __builtin_amdgcn_s_setprio(0);
             mask_half(s1, 1);
             settle(s0, ls0, pb0);
             // keep masks of both 32-key blocks: dword 2 t + jj / 2 holds the bytes
