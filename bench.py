@@ -19,7 +19,12 @@ L2 and the MALL), reported as median and minimum per kernel.
 The CPU baseline (`cpu_baseline`: the fp64 oracle, one process per host core)
 runs first, before the GPU is touched.  `configs` holds every workload in each
 of its masks and passes (forward; forward and backward where the workload has
-one): times, TFLOP/s and % of the matrix-core peak.
+one): times, TFLOP/s and % of the matrix-core peak.  Outside the timed steps
+every call is timed as the per-call share of a batch of back-to-back launches
+between two events (the host runs ahead of the GPU, as in the timed steps and
+in a loop of calls, so no host launch latency is counted); the split-KV
+records also give the isolated-call time (`ms_single_call`, launch latency
+included).
 
 Further objects in the same line: `splitkv` (the split-KV forward on
 decoding shapes, K/V bytes per second against the HBM peak), `dropout` (the
@@ -211,8 +216,10 @@ def cpu_baseline(headline: str, max_workers: int = 16):
 
 def measure_splitkv(dw, dev, stream, iters: int = 20, one_chunk: bool = True):
     """Split-KV forward on a decoding shape: median time of the whole call
-    (chunk kernel + merge) over `iters` launches, K/V bytes per second against
-    the HBM peak, and the same call with a single chunk for comparison."""
+    (chunk kernel + merge) per call of back-to-back calls (time_calls), K/V
+    bytes per second against the HBM peak, the same call with a single chunk
+    for comparison, and the median of isolated calls (host launch latency
+    included)."""
     import torch
     import workloads
     from exact_attention_99_amd import fa_fwd_splitkv, fa_fwd_splitkv_default_splits, fa_fwd_splitkv_workspace_size
@@ -225,26 +232,19 @@ def measure_splitkv(dw, dev, stream, iters: int = 20, one_chunk: bool = True):
     def timed(splits):
         ws = torch.empty(fa_fwd_splitkv_workspace_size(dw.B, dw.H_q, dw.N_q, dw.d, splits),
                          dtype=torch.uint8, device=dev)
-        for _ in range(3):
+        def call():
             fa_fwd_splitkv(q, k, v, dw.causal, scale, splits, o=o, lse=lse, workspace=ws, stream=stream)
-        ts = []
-        for _ in range(iters):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            fa_fwd_splitkv(q, k, v, dw.causal, scale, splits, o=o, lse=lse, workspace=ws, stream=stream)
-            e1.record(stream)
-            e1.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        ts.sort()
-        return ts[len(ts) // 2], ts[0]
+        ts = time_calls(call, stream, iters, warmup=3)
+        single = time_single(call, stream, iters)
+        return ts[len(ts) // 2], ts[0], single[len(single) // 2]
 
     splits = fa_fwd_splitkv_default_splits(dw.B, dw.H_q, dw.H_kv, dw.N_q, dw.N_kv, dw.d)
-    med, mn = timed(splits)
+    med, mn, single = timed(splits)
     one = timed(1)[0] if one_chunk else None
     gbs = dw.kv_bytes() / (med * 1e-3) / 1e9
     return {"workload": dw.name, "B": dw.B, "H_q": dw.H_q, "H_kv": dw.H_kv, "N_q": dw.N_q,
             "N_kv": dw.N_kv, "d": dw.d, "causal": dw.causal, "splits": splits,
-            "ms_median": med, "ms_min": mn, "kv_bytes": dw.kv_bytes(),
+            "ms_median": med, "ms_min": mn, "ms_single_call": single, "kv_bytes": dw.kv_bytes(),
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": gbs / PEAK_HBM_GBS},
             "ms_one_chunk": one}
@@ -252,8 +252,8 @@ def measure_splitkv(dw, dev, stream, iters: int = 20, one_chunk: bool = True):
 
 def measure_fp8(w, q, k, v, stream, iters: int = 20):
     """FP8 forward on the workload's own Q, K, V: block quantization of Q and K
-    (with the rotation) and of V, then the e4m3 forward.  Median of `iters`
-    event-timed launches of each kernel, warm."""
+    (with the rotation) and of V, then the e4m3 forward.  Median per-call time
+    of each kernel (time_calls), warm."""
     import torch
     import workloads
     from exact_attention_99_amd import fa_fp8_quantize, fa_fwd_fp8
@@ -272,17 +272,7 @@ def measure_fp8(w, q, k, v, stream, iters: int = 20):
     }
     med = {}
     for name, fn in launches.items():
-        for _ in range(3):
-            fn()
-        ts = []
-        for _ in range(iters):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-            e1.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        ts.sort()
+        ts = time_calls(fn, stream, iters, warmup=3)
         med[name] = ts[len(ts) // 2]
     F = w.flops_fwd(causal)
     tf = F / (med["fwd_fp8"] * 1e-3) / 1e12
@@ -309,7 +299,7 @@ def measure_fp8(w, q, k, v, stream, iters: int = 20):
 
 def measure_dropout(w, q, k, v, do, stream, p: float = 0.1, iters: int = 10):
     """Forward and backward with fused dropout (probability p) on the
-    workload's tensors: median event-timed durations of each call, and the
+    workload's tensors: median per-call durations (time_calls), and the
     rate with the same conventional FLOP count as the step without dropout."""
     import torch
     from exact_attention_99_amd import fa_bwd_dropout, fa_bwd_workspace_size, fa_fwd_dropout
@@ -326,17 +316,7 @@ def measure_dropout(w, q, k, v, do, stream, p: float = 0.1, iters: int = 10):
     }
     med = {}
     for name, fn in calls.items():
-        for _ in range(2):
-            fn()
-        ts = []
-        for _ in range(iters):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-            e1.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        ts.sort()
+        ts = time_calls(fn, stream, iters)
         med[name] = ts[len(ts) // 2]
     F = w.flops_fwd(causal)
     Fb = w.flops_bwd(causal)
@@ -350,7 +330,7 @@ def measure_dropout(w, q, k, v, do, stream, p: float = 0.1, iters: int = 10):
 def measure_blocksparse(w, q, k, v, do, stream, width: int = 4, globals_: int = 1, iters: int = 10):
     """Forward and backward under a block mask (a local band of `width`
     128-key blocks plus the first `globals_` key blocks, with the workload's
-    causal mask): median event-timed durations, and rates over the FLOPs of
+    causal mask): median per-call durations (time_calls), and rates over the FLOPs of
     the visible elements only (4 d per visible score forward, 2.5x that
     backward)."""
     import torch
@@ -370,17 +350,7 @@ def measure_blocksparse(w, q, k, v, do, stream, width: int = 4, globals_: int = 
     }
     med = {}
     for name, fn in calls.items():
-        for _ in range(2):
-            fn()
-        ts = []
-        for _ in range(iters):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-            e1.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        ts.sort()
+        ts = time_calls(fn, stream, iters)
         med[name] = ts[len(ts) // 2]
     # visible (row, key) pairs of one head
     idx = torch.arange(w.N, device="cpu") // 128
@@ -402,7 +372,7 @@ def measure_blocksparse(w, q, k, v, do, stream, width: int = 4, globals_: int = 
 
 def measure_varlen(w, q, k, v, do, stream, iters: int = 10):
     """Forward and backward of the workload's batch with per-sequence lengths
-    N, 3N/4, N/2, N/4 (cycled over the batch): median event-timed durations,
+    N, 3N/4, N/2, N/4 (cycled over the batch): median per-call durations (time_calls),
     and rates over the FLOPs of the valid elements only."""
     import torch
     from exact_attention_99_amd import fa_bwd_varlen, fa_bwd_workspace_size, fa_fwd_varlen
@@ -421,17 +391,7 @@ def measure_varlen(w, q, k, v, do, stream, iters: int = 10):
     }
     med = {}
     for name, fn in calls.items():
-        for _ in range(2):
-            fn()
-        ts = []
-        for _ in range(iters):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-            e1.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        ts.sort()
+        ts = time_calls(fn, stream, iters)
         med[name] = ts[len(ts) // 2]
     pairs = sum((n * (n + 1) / 2 if causal else n * n) for n in lens)
     F = 4.0 * w.d * pairs * w.H_q
@@ -442,7 +402,36 @@ def measure_varlen(w, q, k, v, do, stream, iters: int = 10):
 
 
 def time_calls(fn, stream, iters: int, warmup: int = 2):
-    """Event-timed durations (ms, sorted) of `iters` launches of fn on stream."""
+    """Per-call GPU durations (ms, sorted) of fn on stream.  Each of the
+    `iters` samples times a batch of back-to-back launches between two events
+    and divides by the batch size, so the host runs ahead of the GPU as in a
+    loop of calls (and as in the timed steps) and the figure holds no host
+    launch latency.  The batch is sized from one isolated call to last about
+    2 ms (1 call for calls of 2 ms and more, at most 50)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    fn()
+    e1.record(stream)
+    e1.synchronize()
+    batch = max(1, min(50, int(2.0 / max(e0.elapsed_time(e1), 1e-3))))
+    ts = []
+    for _ in range(iters):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(batch):
+            fn()
+        e1.record(stream)
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1) / batch)
+    return sorted(ts)
+
+
+def time_single(fn, stream, iters: int, warmup: int = 2):
+    """Durations (ms, sorted) of isolated calls: one launch between two events
+    on an idle GPU, host launch latency included."""
     import torch
     for _ in range(warmup):
         fn()
@@ -462,8 +451,8 @@ PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 matrix-core peak
 
 def measure_configs(dev, stream):
     """Every workload in each of its masks and passes, in the default launch
-    configuration, on device-drawn inputs of its shape: median and minimum of
-    event-timed calls, TFLOP/s with the conventional count, and % of the
+    configuration, on device-drawn inputs of its shape: median and minimum
+    per-call time (time_calls), TFLOP/s with the conventional count, and % of the
     matrix-core peak of the workload's type (bf16 2.5 PF; fp32 157.3 TF).
     The backward is fa_bwd's three phases, also timed one by one."""
     import torch
