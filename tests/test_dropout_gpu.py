@@ -145,3 +145,23 @@ def test_long_sequence_sampled():
     O, L, dQ, dK, dV = odrop.attention_backward_dropout(f(q), f(k), f(v), f(do), scale, True, p, 77, 1)
     check_fwd(o, lse, O, L, "bf16", "8k")
     check_grads(dq, dk, dv, dQ, dK, dV, "bf16", "8k")
+
+
+@pytest.mark.parametrize("d,causal", [(128, True), (128, False), (64, True)])
+def test_many_heads_persistent_grid(d, causal):
+    """Enough key blocks (3 per head, 6 x 16 K/V heads) that the dK/dV pass runs
+    on its persistent grid, each workgroup drawing the keep bytes of several
+    key blocks and steps in turn (and, at d = 64 under the causal mask, the
+    forward too); every element against the oracle."""
+    B, Hq, Hkv, N, p = 6, 32, 16, 300, 0.2
+    print(f"case d={d} causal={causal}", flush=True)
+    q, k, v, do = workloads.make_inputs(B, Hq, Hkv, N, d, "bf16", 950 + d + int(causal), with_dout=True)
+    scale = 1 / math.sqrt(d)
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    o, lse = fa_fwd_dropout(qd, kd, vd, causal, scale, p, 2024, 3)
+    dq, dk, dv = fa_bwd_dropout(qd, kd, vd, o, lse, dod, causal, scale, p, 2024, 3)
+    torch.cuda.synchronize()
+    f = workloads.to_f64
+    O, L, dQ, dK, dV = odrop.attention_backward_dropout(f(q), f(k), f(v), f(do), scale, causal, p, 2024, 3)
+    check_fwd(o, lse, O, L, "bf16", f"d={d} causal={causal}")
+    check_grads(dq, dk, dv, dQ, dK, dV, "bf16", f"d={d} causal={causal}")
