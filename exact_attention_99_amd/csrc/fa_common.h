@@ -35,6 +35,9 @@
 #ifndef FA355_FWD_PERSIST
 #define FA355_FWD_PERSIST 1    // forward persistent grid
 #endif
+#ifndef FA355_FWD_STACK
+#define FA355_FWD_STACK 1      // forward: stack the query heads of a K/V group
+#endif
 #ifndef FA355_DKDV_BQ128
 #define FA355_DKDV_BQ128 128   // dK/dV query rows per step at d = 128
 #endif

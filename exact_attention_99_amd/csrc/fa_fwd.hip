@@ -75,7 +75,7 @@ namespace {
 // with sequence lengths the length replaces N in every range check.  Rows that
 // see no key get O = 0 and lse = -inf.
 template <typename T, int D, bool CAUSAL, int NW, int BC, bool PERSIST = false, bool DROP = false,
-          bool SPARSE = false>
+          bool SPARSE = false, int GS = 1>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
@@ -85,7 +85,7 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     constexpr int PPB = 8 / (D / 16);    // probability pairs per second-half score product
     constexpr int PPC = 8 / (2 * (D / 32));  // probability pairs per first-half P V product
     constexpr int NSUB = BC / 64;
-    constexpr int BR = 32 * NW;
+    constexpr int BR = 32 * NW / GS;     // rows of each of the block's GS query heads
     constexpr int KCH = D / 8;
     constexpr int TILE = BC * D * 2;
     constexpr int STAGE = 2 * TILE;
@@ -95,6 +95,7 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     static_assert(WI % NW == 0, "tile copies split evenly over the waves");
     constexpr int IPW = WI / NW;
     static_assert(BR % BC == 0, "row blocks start on a key-tile boundary");
+    static_assert(GS == 1 || (!DROP && !SPARSE && NW % GS == 0), "stacked query heads: dense path only");
     constexpr float kSumCap = 256.0f;   // 2^kTau
     static_assert(kTau == 8.0f, "sum cap matches the lazy-rescale threshold");
 
@@ -107,7 +108,7 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int hi = lane >> 5;
 
     const int nqb = (N + BR - 1) / BR;
-    const int total = nqb * Hq * B;
+    const int total = nqb * (Hq / GS) * B;
     // One block per workgroup, or (PERSIST) a grid of one workgroup per compute
     // unit that walks its blocks in rounds.
     for (int round = 0;; ++round) {
@@ -123,9 +124,11 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         const int bh = logical / nqb;
         const int qb = CAUSAL ? (nqb - 1 - qb_raw) : qb_raw;  // longest rows first
         // the masked path takes the batch index fastest, so that the XCDs (each
-        // runs a contiguous range of heads) share sequences of different lengths
-        const int h = SPARSE ? bh / B : bh % Hq;
-        const int b = SPARSE ? bh % B : bh / Hq;
+        // runs a contiguous range of heads) share sequences of different lengths.
+        // GS > 1: the block is the same rows of GS query heads of one K/V group
+        // (wave w serves head w % GS), which share every K/V tile.
+        const int h = SPARSE ? bh / B : (GS > 1 ? (bh % (Hq / GS)) * GS + wave % GS : bh % Hq);
+        const int b = SPARSE ? bh % B : bh / (Hq / GS);
         const int hk = h / (Hq / Hkv);
 
         const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * D;
@@ -139,8 +142,9 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
         const int q0 = qb * BR;
         // waves w and w + NW/2 share a SIMD: give them complementary row slices
-        // (w and NW - 1 - (w - NW/2)) so the diagonal tiles split evenly
-        const int slice = wave < NW / 2 ? wave : (NW - 1) - (wave - NW / 2);
+        // (w and NW - 1 - (w - NW/2)) so the diagonal tiles split evenly (with
+        // stacked heads, wave w takes slice w / GS of its head)
+        const int slice = GS > 1 ? wave / GS : (wave < NW / 2 ? wave : (NW - 1) - (wave - NW / 2));
         const int qw = q0 + 32 * slice;
         const int q = qw + l32;
 
@@ -599,30 +603,34 @@ fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const flo
 }
 
 template <typename T, int D, bool CAUSAL, int NW, int BC, bool PERSIST = false, bool DROP = false,
-          bool SPARSE = false>
+          bool SPARSE = false, int GS = 1>
 hipError_t launch16v6(const FwdArgs& a) {
-    constexpr int BR = 32 * NW;
+    constexpr int BR = 32 * NW / GS;
     const int nqb = (a.N + BR - 1) / BR;
-    const long long total = (long long)nqb * a.Hq * a.B;
+    const long long total = (long long)nqb * (a.Hq / GS) * a.B;
     int grid = 0;
     if constexpr (PERSIST) {
         // workgroups resident per compute unit for this instantiation
         static const int per_cu = [] {
             int n = 0;
             return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                       &n, reinterpret_cast<const void*>(fwd16v6_kernel<T, D, CAUSAL, NW, BC, true, DROP, SPARSE>),
+                       &n, reinterpret_cast<const void*>(fwd16v6_kernel<T, D, CAUSAL, NW, BC, true, DROP, SPARSE, GS>),
                        NW * 64, 0) == hipSuccess ? n : 0;
         }();
         grid = persistent_grid() * per_cu;
     }
-    if (grid >= 8 && total > grid)
-        hipLaunchKernelGGL((fwd16v6_kernel<T, D, CAUSAL, NW, BC, true, DROP, SPARSE>), dim3((unsigned)grid),
-                           dim3(NW * 64), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                           (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.dp, a.sp);
-    else
-        hipLaunchKernelGGL((fwd16v6_kernel<T, D, CAUSAL, NW, BC, false, DROP, SPARSE>), dim3((unsigned)total),
-                           dim3(NW * 64), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                           (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.dp, a.sp);
+    if constexpr (PERSIST) {
+        if (grid >= 8 && total > grid) {
+            hipLaunchKernelGGL((fwd16v6_kernel<T, D, CAUSAL, NW, BC, true, DROP, SPARSE, GS>), dim3((unsigned)grid),
+                               dim3(NW * 64), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                               (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.dp,
+                               a.sp);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((fwd16v6_kernel<T, D, CAUSAL, NW, BC, false, DROP, SPARSE, GS>), dim3((unsigned)total),
+                       dim3(NW * 64), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                       (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.dp, a.sp);
     return hipGetLastError();
 }
 
@@ -660,6 +668,15 @@ hipError_t dispatch16c(const FwdArgs& a) {
     // does not.
     if (a.sparse && a.sp.mask) return launch16v6<T, D, CAUSAL, 4, 64, false, false, true>(a);
     if (a.sparse) return launch16v6<T, D, CAUSAL, NW, 64, false, false, true>(a);
+#if FA355_FWD_STACK
+    // grouped K/V heads at d = 128: one workgroup takes the same rows of 2 or 4
+    // query heads of a group, which then share every K/V tile it stages
+    if constexpr (D == 128 && NW % 4 == 0) {
+        const int G = a.Hq / a.Hkv;
+        if (G % 4 == 0) return launch16v6<T, D, CAUSAL, NW, (D == 128 ? FA355_FWD_BC128 : 64), PERS, false, false, 4>(a);
+        if (G % 2 == 0) return launch16v6<T, D, CAUSAL, NW, (D == 128 ? FA355_FWD_BC128 : 64), PERS, false, false, 2>(a);
+    }
+#endif
     return launch16v6<T, D, CAUSAL, NW, (D == 128 ? FA355_FWD_BC128 : 64), PERS>(a);
 }
 
