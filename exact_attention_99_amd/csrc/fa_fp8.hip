@@ -65,89 +65,123 @@ __device__ __forceinline__ int pack4_e4m3(float a, float b, float c, float d) {
 
 // ---------------------------------------------------------------- quantizer
 
-// One workgroup of 256 threads per block of 64 rows of one head; thread t
-// holds D / 4 consecutive elements of row t / 4.  The rotation's butterflies
-// run with strides 1, 2, 4, ... (inside a thread up to D / 8, then across the
-// four threads of a row), then one multiplication by rs = fp32(1 / sqrt(D)).
+// XOR swizzles of the quantizer's LDS tiles (16-byte chunks): chunk k of row
+// r sits in slot k ^ sw(r) of that row, so that the 8 or 16 lanes of one
+// 128-bit LDS access (one row each, or one row's chunks) fall on distinct
+// banks.
+template <int D>
+__device__ __forceinline__ int qin_sw(int r) {   // input rows: 2 D bytes
+    return D == 128 ? (r & 15) : ((r & 7) ^ ((r >> 3) & 1));
+}
+template <int D>
+__device__ __forceinline__ int qout_sw(int r) {  // code rows: D bytes
+    return D == 128 ? ((r & 7) ^ ((r >> 3) & 1)) : ((r >> 1) & 3);
+}
+
+// One wave per block of 64 rows of one head; lane l holds row 64 blk + l
+// whole, so every butterfly of the rotation is a pair of registers of one lane
+// (no lane exchanges).  The block (contiguous in memory) comes in through
+// coalesced buffer-to-LDS copies and the codes leave through coalesced stores;
+// the LDS tile turns rows into lanes.  Butterflies with strides 1, 2, 4, ...,
+// D / 2, then one multiplication by rs = fp32(1 / sqrt(D)).  The signs are
+// wave-uniform (scalar loads); as they are +-1, the stride-1 butterfly takes
+// them in exactly: (s_a a + s_b b, s_a a - s_b b) = (fma(b, s_b, t),
+// fma(b, -s_b, t)) with t = s_a a, the same roundings as multiplying first.
 template <typename T, int D, bool ROT>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(64)
 quant8_kernel(const uint16_t* __restrict__ X, const float* __restrict__ signs, float rs,
               uint8_t* __restrict__ C, float* __restrict__ S, int N, int nblk) {
-    constexpr int E = D / 4;
-    const int tid = threadIdx.x;
-    const int part = tid & 3;
+    constexpr int RC = D / 8;     // 16-byte chunks per input row
+    constexpr int RPI = 64 / RC;  // input rows per 1 KB copy
+    constexpr int OC = D / 16;    // 16-byte chunks per code row
+    constexpr int OPI = 64 / OC;  // code rows per 1 KB store
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kQBlk * D * 2];
+    const int lane = threadIdx.x;
     const int blk = (int)blockIdx.x % nblk;
     const size_t head = blockIdx.x / nblk;
-    const int r = blk * kQBlk + (tid >> 2);
     const Buf xb(X + head * (size_t)N * D, (uint32_t)N * D * 2);
 
-    float y[E];
+    // copy c: lane j brings chunk (j % RC) ^ qin_sw(row) of row RPI c + j / RC
+    // to tile byte 1024 c + 16 j, which is where that chunk's slot is; rows
+    // past N arrive as zeros (buffer range)
 #pragma unroll
-    for (int c = 0; c < E / 8; ++c) {
-        const u32x4 w = xb.load16((uint32_t)(r * D + part * E + 8 * c) * 2);
+    for (int c = 0; c < kQBlk / RPI; ++c) {
+        const int row = RPI * c + lane / RC;
+        const int chunk = (lane % RC) ^ qin_sw<D>(row);
+        buf_to_lds16(xb, tile + 1024 * c, (uint32_t)(((blk * kQBlk + row) * D + 8 * chunk) * 2));
+    }
+    wait_vmem();
+    __syncthreads();
+
+    float y[D];
+#pragma unroll
+    for (int k = 0; k < RC; ++k) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(tile + lane * 2 * D + 16 * (k ^ qin_sw<D>(lane)));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            y[8 * c + 2 * i] = Mma<T>::to_f32((uint16_t)(w[i] & 0xFFFFu));
-            y[8 * c + 2 * i + 1] = Mma<T>::to_f32((uint16_t)(w[i] >> 16));
+            y[8 * k + 2 * i] = Mma<T>::to_f32((uint16_t)(w[i] & 0xFFFFu));
+            y[8 * k + 2 * i + 1] = Mma<T>::to_f32((uint16_t)(w[i] >> 16));
         }
     }
     if (ROT) {
 #pragma unroll
-        for (int c = 0; c < E / 4; ++c) {
-            const f32x4 s = *reinterpret_cast<const f32x4*>(signs + part * E + 4 * c);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) y[4 * c + i] *= s[i];
+        for (int i = 0; i < D; i += 2) {
+            const float t = y[i] * signs[i];
+            const float b = y[i + 1], sb = signs[i + 1];
+            y[i] = fmaf(b, sb, t);
+            y[i + 1] = fmaf(b, -sb, t);
         }
 #pragma unroll
-        for (int h = 1; h < E; h *= 2)
+        for (int h = 2; h < D; h *= 2)
 #pragma unroll
-            for (int i = 0; i < E; ++i)
+            for (int i = 0; i < D; ++i)
                 if ((i & h) == 0) {
                     const float a = y[i], b = y[i + h];
                     y[i] = a + b;
                     y[i + h] = a - b;
                 }
-        // partner lanes t ^ 1, then t ^ 2, through quad permutes (DPP
-        // quad_perm [1,0,3,2] and [2,3,0,1])
 #pragma unroll
-        for (int i = 0; i < E; ++i) {
-            const float o = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y[i]), 0xB1, 0xF, 0xF, true));
-            y[i] = (part & 1) ? (o - y[i]) : (y[i] + o);
-        }
-#pragma unroll
-        for (int i = 0; i < E; ++i) {
-            const float o = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y[i]), 0x4E, 0xF, 0xF, true));
-            y[i] = (part & 2) ? (o - y[i]) : (y[i] + o);
-        }
-#pragma unroll
-        for (int i = 0; i < E; ++i) y[i] *= rs;
+        for (int i = 0; i < D; ++i) y[i] *= rs;
     }
 
-    float amax = 0.f;
+    float mx[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < E; ++i) amax = fmaxf(amax, fabsf(y[i]));
+    for (int i = 0; i < D; ++i) mx[i & 3] = fmaxf(mx[i & 3], fabsf(y[i]));
+    float amax = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
 #pragma unroll
     for (int m = 32; m >= 1; m /= 2) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
-    __shared__ float red[4];
-    if ((tid & 63) == 0) red[tid >> 6] = amax;
-    __syncthreads();
-    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-
     const float inv = amax > 0.f ? kE4m3Max / amax : 1.f;
-    if (r < N) {
-        u32x4 out[E / 16];
+
+    // codes of row `lane` into its tile row (slots qout_sw), then out in
+    // coalesced 1 KB stores (store c covers rows OPI c .. OPI c + OPI - 1),
+    // non-temporal: nothing reads them back before they leave the caches.
+    // No clamp to +-448 is needed: |y inv| <= amax fl(448 / amax) rounds to at
+    // most 448 (1 + 2^-23)^2, and the conversion rounds to nearest before its
+    // range check (values below 464 encode as 448).
+    __syncthreads();
 #pragma unroll
-        for (int c = 0; c < E / 4; ++c) {
+    for (int c = 0; c < OC; ++c) {
+        u32x4 out;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
             float v[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = fminf(fmaxf(y[4 * c + i] * inv, -kE4m3Max), kE4m3Max);
-            out[c / 4][c % 4] = (uint32_t)pack4_e4m3(v[0], v[1], v[2], v[3]);
+            for (int i = 0; i < 4; ++i) v[i] = y[16 * c + 4 * j + i] * inv;
+            out[j] = (uint32_t)pack4_e4m3(v[0], v[1], v[2], v[3]);
         }
-        uint8_t* dst = C + head * (size_t)N * D + (size_t)r * D + part * E;
-#pragma unroll
-        for (int c = 0; c < E / 16; ++c) *reinterpret_cast<u32x4*>(dst + 16 * c) = out[c];
+        *reinterpret_cast<u32x4*>(tile + lane * D + 16 * (c ^ qout_sw<D>(lane))) = out;
     }
-    if (tid == 0) S[head * nblk + blk] = amax > 0.f ? amax / kE4m3Max : 1.f;
+    __syncthreads();
+    uint8_t* dst = C + head * (size_t)N * D + (size_t)blk * kQBlk * D;
+    const bool full = (blk + 1) * kQBlk <= N;
+#pragma unroll
+    for (int c = 0; c < kQBlk / OPI; ++c) {
+        const int row = OPI * c + lane / OC;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(tile + row * D + 16 * ((lane % OC) ^ qout_sw<D>(row)));
+        if (full || blk * kQBlk + row < N)
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + 1024 * c + 16 * lane));
+    }
+    if (lane == 0) S[head * nblk + blk] = amax > 0.f ? amax / kE4m3Max : 1.f;
 }
 
 // ------------------------------------------------------------ the forward
@@ -474,10 +508,10 @@ hipError_t quant8_d(const Fp8QuantArgs& a) {
     const int nblk = (a.N + kQBlk - 1) / kQBlk;
     const dim3 grid((unsigned)(nblk * a.B * a.H));
     if (a.signs)
-        hipLaunchKernelGGL((quant8_kernel<T, D, true>), grid, dim3(256), 0, a.stream,
+        hipLaunchKernelGGL((quant8_kernel<T, D, true>), grid, dim3(64), 0, a.stream,
                            (const uint16_t*)a.x, a.signs, a.rs, a.codes, a.scales, a.N, nblk);
     else
-        hipLaunchKernelGGL((quant8_kernel<T, D, false>), grid, dim3(256), 0, a.stream,
+        hipLaunchKernelGGL((quant8_kernel<T, D, false>), grid, dim3(64), 0, a.stream,
                            (const uint16_t*)a.x, a.signs, a.rs, a.codes, a.scales, a.N, nblk);
     return hipGetLastError();
 }
