@@ -47,6 +47,9 @@
 #ifndef FA355_DQ_NW
 #define FA355_DQ_NW 4          // dQ waves per workgroup
 #endif
+#ifndef FA355_SPLIT_NS
+#define FA355_SPLIT_NS 2       // LDS stages of the split-KV chunk kernel
+#endif
 #ifndef FA355_DQ_BC128
 #define FA355_DQ_BC128 64      // dQ keys per tile at d = 128
 #endif
@@ -220,6 +223,13 @@ __device__ __forceinline__ void buf_to_lds16(const Buf& b, void* lds, uint32_t o
 // Wait until this wave's outstanding vector-memory operations (including
 // buffer-to-LDS copies) have completed.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding (they complete in issue order, so the older ones are done).
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+    static_assert(N >= 0 && N <= 63, "vmcnt holds 6 bits");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
 // lane i receives element (i % 4) of the 8-byte chunk addressed by lane

@@ -18,9 +18,12 @@ namespace fa355 {
 namespace {
 
 // One wave per workgroup: partial attention of 32 stacked rows over the keys
-// [c0, c1) of one chunk.  K and V tiles of BC keys stream through a
-// double-buffered LDS area by buffer-to-LDS copies (keys past N_kv read as
-// zeros and are masked, as are keys of the next chunk).
+// [c0, c1) of one chunk.  K and V tiles of BC keys stream through a ring of NS
+// LDS stages by buffer-to-LDS copies (keys past N_kv read as zeros and are
+// masked, as are keys of the next chunk): tile j waits for its own copies,
+// then issues those of tile j + NS - 1 and is computed while they fly.  Two
+// stages measure best; three or four (more bytes in flight, fewer workgroups
+// per compute unit) are slower.
 template <typename T, int D, bool CAUSAL>
 __global__ void __launch_bounds__(64)
 fwd_split16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -36,8 +39,11 @@ fwd_split16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     constexpr int NDB = D / 32;
     constexpr int NKS = D / 16;
     constexpr int WI = TILE / 1024;           // 1 KB wave copies per tile
+    constexpr int NS = FA355_SPLIT_NS;        // LDS stages
+    constexpr int CPT = 2 * WI;               // copies per tile (K and V)
+    static_assert(NS >= 2 && (NS - 1) * CPT <= 63, "copies in flight fit the vector-memory counter");
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[NS * STAGE];
 
     const int lane = threadIdx.x;
     const int l32 = lane & 31;
@@ -91,11 +97,9 @@ fwd_split16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     float m_s = -INFINITY;
     float l_s = 0.f;
 
-    if (ntiles > 0) {
-        issue(c0, 0);
-        wait_vmem();
-    }
-    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j)
+        if (j < ntiles) issue(c0 + j * BC, j);
     // One tile from the buffer at cur.  Its LDS reads go through this
     // restrict-qualified pointer, so the compiler does not make the transposing
     // reads wait for the copy of the next tile into the other buffer.
@@ -173,12 +177,18 @@ fwd_split16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                 o[db] = Mma<T>::mma(a, pb[kg], o[db]);
             }
     };
+    // tile j waits only for its own copies: the copies of the tiles after it
+    // (at most NS - 2 of them issued yet, in issue order) may stay in flight
     for (int j = 0; j < ntiles; ++j) {
         const int k0 = c0 + j * BC;
-        if (j + 1 < ntiles) issue(k0 + BC, (j + 1) & 1);
-        tile(smem + (j & 1) * STAGE, k0);
-        wait_vmem();
+        const int later = min(NS - 2, ntiles - 1 - j);
+        static_for<NS - 1>([&](auto lc) {
+            constexpr int L = decltype(lc)::value;
+            if (later == L) wait_vmem_n<L * CPT>();
+        });
         __syncthreads();
+        if (j + NS - 1 < ntiles) issue(k0 + (NS - 1) * BC, (j + NS - 1) % NS);
+        tile(smem + (j % NS) * STAGE, k0);
     }
 
     // partial result of this chunk: O normalised over the chunk's keys and
