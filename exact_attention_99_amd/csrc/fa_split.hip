@@ -215,60 +215,103 @@ fwd_split16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 
 // Merge of the partials of one row per 256-thread workgroup:
 // lse = log sum_s exp(lse_s), O = sum_s exp(lse_s - lse) O_s, rounded to the
-// output dtype.  The chunk weights are formed in parallel (one chunk per
-// thread, at most kMaxSplits chunks) and kept in LDS; then 256 / D groups of
-// D threads each accumulate one output dimension over every (256 / D)-th
-// chunk, and the groups' sums are added in LDS.
+// output dtype.  The work is a few dependent memory round trips, so every
+// load is issued before anything waits on one: thread t takes output
+// dimensions 4 (t % TPD) .. + 3 of the chunks g, g + NG, g + 2 NG, ...
+// (g = t / TPD) as 16-byte loads, up to MB chunks at a time, while wave 0
+// reads the chunks' logsumexps (chunk s in lane s % 64) and forms the weights
+// exp(lse_s - max) into LDS.  Each thread sums its chunks, then the NG group
+// sums are added in LDS in group order.
 constexpr int kMaxSplits = 1024;
 
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
 merge_split_kernel(const float* __restrict__ Opart, const float* __restrict__ Lpart,
                    uint16_t* __restrict__ O, float* __restrict__ LSE, int nrows, int nsplit) {
-    constexpr int NG = 256 / D;
+    constexpr int TPD = D / 4;         // threads per partial row
+    constexpr int NG = 256 / TPD;      // chunk groups
+    constexpr int MB = 8;              // chunks per thread per batch
+    constexpr int LPL = kMaxSplits / 64;
     __shared__ float w[kMaxSplits];
-    __shared__ float red[8];
-    __shared__ float part[NG][D];
+    __shared__ float red[2];
+    __shared__ f32x4 part[NG][TPD];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wv = tid >> 6;
     const int R = blockIdx.x;
+    const int g = tid / TPD, c4 = tid % TPD;
+    const float* ob = Opart + (size_t)R * D + 4 * c4;
+    const size_t cstride = (size_t)nrows * D;   // floats between chunks
 
-    // the largest partial logsumexp
-    float m = -INFINITY;
-    for (int s = tid; s < nsplit; s += 256) m = fmaxf(m, Lpart[(size_t)s * nrows + R]);
+    auto load_batch = [&](int s0, f32x4 (&buf)[MB]) {
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    if (lane == 0) red[wv] = m;
-    __syncthreads();
-    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    // chunk weights relative to it, and their sum
-    float ws = 0.f;
-    for (int s = tid; s < nsplit; s += 256) {
-        const float ls = Lpart[(size_t)s * nrows + R];
-        const float x = (ls == -INFINITY || m == -INFINITY) ? 0.f : __expf(ls - m);
-        w[s] = x;
-        ws += x;
+        for (int i = 0; i < MB; ++i) {
+            const int s = s0 + g + NG * i;
+            buf[i] = s < nsplit ? *reinterpret_cast<const f32x4*>(ob + (size_t)s * cstride) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    f32x4 pb[MB];
+    load_batch(0, pb);
+
+    if (tid < 64) {
+        float lv[LPL];
+#pragma unroll
+        for (int k = 0; k < LPL; ++k) {
+            const int s = lane + 64 * k;
+            lv[k] = (64 * k < nsplit && s < nsplit) ? Lpart[(size_t)s * nrows + R] : -INFINITY;
+        }
+        float m = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < LPL; ++k) m = fmaxf(m, lv[k]);
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+        float ws = 0.f;
+#pragma unroll
+        for (int k = 0; k < LPL; ++k) {
+            const int s = lane + 64 * k;
+            if (64 * k < nsplit && s < nsplit) {
+                const float x = (lv[k] == -INFINITY || m == -INFINITY) ? 0.f : __expf(lv[k] - m);
+                w[s] = x;
+                ws += x;
+            }
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) ws += __shfl_xor(ws, o, 64);
+        if (lane == 0) {
+            red[0] = m;
+            red[1] = ws;
+        }
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) ws += __shfl_xor(ws, o, 64);
-    if (lane == 0) red[4 + wv] = ws;
     __syncthreads();
-    const float wsum = red[4] + red[5] + red[6] + red[7];
 
-    const int dim = tid % D, grp = tid / D;
-    float acc = 0.f;
-#pragma unroll 8
-    for (int s = grp; s < nsplit; s += NG) acc = fmaf(w[s], Opart[((size_t)s * nrows + R) * D + dim], acc);
-    part[grp][dim] = acc;
-    __syncthreads();
-    if (grp == 0) {
-        float t = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0;; s0 += NG * MB) {
 #pragma unroll
-        for (int g = 0; g < NG; ++g) t += part[g][dim];
+        for (int i = 0; i < MB; ++i) {
+            const int s = s0 + g + NG * i;
+            if (s < nsplit) {
+                const float ws = w[s];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = fmaf(ws, pb[i][e], acc[e]);
+            }
+        }
+        if (s0 + NG * MB >= nsplit) break;
+        load_batch(s0 + NG * MB, pb);
+    }
+    part[g][c4] = acc;
+    __syncthreads();
+    if (g == 0) {
+        f32x4 t = part[0][c4];
+#pragma unroll
+        for (int gg = 1; gg < NG; ++gg)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) t[e] += part[gg][c4][e];
+        const float wsum = red[1];
         const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-        O[(size_t)R * D + dim] = (uint16_t)(Mma<T>::pack2(t * inv, 0.f) & 0xFFFFu);
-        if (dim == 0) LSE[R] = wsum > 0.f ? m + __logf(wsum) : -INFINITY;
+        u32x2 out;
+        out[0] = Mma<T>::pack2(t[0] * inv, t[1] * inv);
+        out[1] = Mma<T>::pack2(t[2] * inv, t[3] * inv);
+        *reinterpret_cast<u32x2*>(O + (size_t)R * D + 4 * c4) = out;
+        if (c4 == 0) LSE[R] = wsum > 0.f ? red[0] + __logf(wsum) : -INFINITY;
     }
 }
 
