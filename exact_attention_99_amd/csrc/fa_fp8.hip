@@ -150,7 +150,10 @@ quant8_kernel(const uint16_t* __restrict__ X, const float* __restrict__ signs, f
     float amax = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
 #pragma unroll
     for (int m = 32; m >= 1; m /= 2) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
-    const float inv = amax > 0.f ? kE4m3Max / amax : 1.f;
+    // a block whose amax is 0, or so small that 448 / amax overflows, is
+    // stored as zeros with scale 1
+    const float inv = kE4m3Max / amax;
+    const bool flush = __builtin_amdgcn_readfirstlane(!(inv <= __FLT_MAX__) ? 1 : 0) != 0;
 
     // codes of row `lane` into its tile row (slots qout_sw), then out in
     // coalesced 1 KB stores (store c covers rows OPI c .. OPI c + OPI - 1),
@@ -158,6 +161,8 @@ quant8_kernel(const uint16_t* __restrict__ X, const float* __restrict__ signs, f
     // No clamp to +-448 is needed: |y inv| <= amax fl(448 / amax) rounds to at
     // most 448 (1 + 2^-23)^2, and the conversion rounds to nearest before its
     // range check (values below 464 encode as 448).
+    // (A flushed block's codes are formed like any other and then replaced by
+    // zeros in the stores below, where none of y is live any more.)
     __syncthreads();
 #pragma unroll
     for (int c = 0; c < OC; ++c) {
@@ -174,14 +179,22 @@ quant8_kernel(const uint16_t* __restrict__ X, const float* __restrict__ signs, f
     __syncthreads();
     uint8_t* dst = C + head * (size_t)N * D + (size_t)blk * kQBlk * D;
     const bool full = (blk + 1) * kQBlk <= N;
+    auto store_rows = [&](auto zero_tag) {
 #pragma unroll
-    for (int c = 0; c < kQBlk / OPI; ++c) {
-        const int row = OPI * c + lane / OC;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(tile + row * D + 16 * ((lane % OC) ^ qout_sw<D>(row)));
-        if (full || blk * kQBlk + row < N)
-            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + 1024 * c + 16 * lane));
-    }
-    if (lane == 0) S[head * nblk + blk] = amax > 0.f ? amax / kE4m3Max : 1.f;
+        for (int c = 0; c < kQBlk / OPI; ++c) {
+            const int row = OPI * c + lane / OC;
+            const u32x4 v = decltype(zero_tag)::value
+                                ? u32x4{0u, 0u, 0u, 0u}
+                                : *reinterpret_cast<const u32x4*>(tile + row * D + 16 * ((lane % OC) ^ qout_sw<D>(row)));
+            if (full || blk * kQBlk + row < N)
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + 1024 * c + 16 * lane));
+        }
+    };
+    if (flush)
+        store_rows(std::true_type{});
+    else
+        store_rows(std::false_type{});
+    if (lane == 0) S[head * nblk + blk] = flush ? 1.f : amax / kE4m3Max;
 }
 
 // ------------------------------------------------------------ the forward

@@ -339,11 +339,13 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v,
  *            matrix, evaluated in float32 as the fast Walsh-Hadamard transform
  *            (butterflies (a, b) -> (a + b, a - b) with strides 1, 2, 4, ...,
  *            then one multiplication by float32(1 / sqrt(d)));
- *   amax   = max |y| over the block;  scale = amax / 448 (1 if amax == 0);
+ *   amax   = max |y| over the block;  scale = amax / 448;
  *   codes  = e4m3(clamp(y * (448 / amax), -448, 448)), round to nearest even,
- *            sign bit kept for negative values that round to zero.
+ *            sign bit kept for negative values that round to zero;
+ *            a block with amax == 0, or with 448 / amax beyond the float32
+ *            range (amax below about 1.3e-36), gets scale 1 and zero codes.
  *   x      in : [B, H, N, d] bf16 or fp16 (`dtype`; fp32 returns
- *               FA_ERR_UNSUPPORTED), 16-byte aligned.
+ *               FA_ERR_UNSUPPORTED), finite values, 16-byte aligned.
  *   signs  in : NULL, or d float32 values (+1 / -1), 16-byte aligned.  Pass
  *               the same signs for Q and K (the rotation is orthogonal, so
  *               scores are unchanged) and NULL for V.

@@ -18,7 +18,11 @@ FA3 paragraph) is not exact attention of the inputs: Q, K and V are rounded to
      * per block: amax = max |y|, inv = 448 / amax, scale = amax / 448, and
        the code of y * inv rounded to nearest (ties to even) in the OCP
        e4m3 format (4 exponent bits, bias 7, 3 mantissa bits, largest finite
-       value 448, no infinities).
+       value 448, no infinities).  A block with amax = 0, or with amax so
+       small (below 448 / FLT_MAX, about 1.3e-36) that 448 / amax overflows
+       float32, gets scale 1 and zero codes: its values are below anything
+       e4m3 times a float32 scale can resolve, and flushing them keeps every
+       code finite.
    Every step is written in float32 in a fixed order (the butterflies of the
    fast Walsh-Hadamard transform with strides 1, 2, 4, ..., then the scale),
    so that the rounded codes are a deterministic function of the input and
@@ -111,13 +115,16 @@ def quantize_blocks(x: np.ndarray, block_rows: int,
     for i in range(nb):
         blk = y[:, :, i * block_rows:(i + 1) * block_rows]
         amax = np.abs(blk).max(axis=(2, 3)).astype(np.float32)
-        zero = amax == 0
-        inv = np.where(zero, np.float32(1), np.float32(E4M3_MAX) / np.where(zero, np.float32(1), amax))
-        inv = inv.astype(np.float32)
+        with np.errstate(divide="ignore", over="ignore"):
+            raw = (np.float32(E4M3_MAX) / np.where(amax == 0, np.float32(1), amax)).astype(np.float32)
+        zero = (amax == 0) | ~np.isfinite(raw)
+        inv = np.where(zero, np.float32(1), raw).astype(np.float32)
         scales[:, :, i] = np.where(zero, np.float32(1), amax / np.float32(E4M3_MAX)).astype(np.float32)
         v = (blk * inv[:, :, None, None]).astype(np.float32)
         v = np.clip(v, -E4M3_MAX, E4M3_MAX)
-        codes[:, :, i * block_rows:(i + 1) * block_rows] = e4m3_encode(v)
+        c = e4m3_encode(v)
+        c[zero] = 0
+        codes[:, :, i * block_rows:(i + 1) * block_rows] = c
     return codes, scales
 
 

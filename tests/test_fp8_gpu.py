@@ -95,6 +95,69 @@ def test_quantizer_special_values():
     assert np.array_equal(codes.cpu().numpy(), ref_c)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_quantizer_limits_of_the_block_scale(dtype):
+    """Blocks at both ends of the scale's range, bit for bit against the oracle.
+
+    block 0: amax = 0.60546875, a value whose product amax * fl(448 / amax)
+             rounds above 448 in float32; that element (and its negation)
+             must still encode as +-448.
+    block 1 (bf16 only): amax = 2^-122, below 448 / FLT_MAX, where 448 / amax
+             overflows: the block is stored as zeros (also its negative
+             values) with scale 1.
+    block 2: amax = 2^-119 (bf16) just above that limit: ordinary scale.
+    block 3: random values, for contrast.
+    """
+    B, H, N, d = 1, 2, 4 * BLK, 128
+    amax0 = np.float32(0.60546875)
+    assert np.float32(amax0 * (np.float32(448) / amax0)) > np.float32(448)
+    gen = torch.Generator().manual_seed(77)
+    x = torch.randn((B, H, N, d), generator=gen) * 0.1
+    x[:, :, 0:BLK] = x[:, :, 0:BLK].clamp(-0.5, 0.5)
+    x[:, 0, 3, 7] = float(amax0)
+    x[:, 1, 10, 0] = -float(amax0)
+    x[:, 1, 11, 1] = float(amax0)
+    if dtype == "bf16":
+        x[:, :, BLK:2 * BLK] = torch.sign(torch.randn((B, H, BLK, d), generator=gen)) * 2.0 ** -124
+        x[:, :, BLK + 5, 3] = -(2.0 ** -122)
+        x[:, :, 2 * BLK:3 * BLK] = torch.sign(torch.randn((B, H, BLK, d), generator=gen)) * 2.0 ** -121
+        x[:, :, 2 * BLK + 9, 2] = 2.0 ** -119
+    x = x.to(workloads.DTYPES[dtype])
+    codes, scales = fa_fp8_quantize(x.to(DEV))
+    torch.cuda.synchronize()
+    ref_c, ref_s = _oracle_quant(x)
+    got_c, got_s = codes.cpu().numpy(), scales.cpu().numpy()
+    assert np.array_equal(got_s, ref_s)
+    assert np.array_equal(got_c, ref_c), np.argwhere(got_c != ref_c)[:4].tolist()
+    assert got_c[0, 0, 3, 7] == 0x7E and got_c[0, 1, 10, 0] == 0xFE and got_c[0, 1, 11, 1] == 0x7E
+    if dtype == "bf16":
+        assert (got_s[:, :, 1] == 1.0).all() and not got_c[:, :, BLK:2 * BLK].any()
+        assert (got_s[:, :, 2] == np.float32(2.0 ** -119) / np.float32(448)).all()
+        assert got_c[0, 0, 2 * BLK + 9, 2] == 0x7E
+
+
+def test_quantizer_full_size_sampled_heads():
+    """The bench workload's shape (B=4, H=32, N=8192, d=128, rotated), every
+    head in one call; three heads bit for bit against the oracle, and every
+    block's scale against the amax the codes imply."""
+    B, H, N, d = 4, 32, 8192, 128
+    x = workloads.make_inputs(B, H, H, N, d, "bf16", 4242)[0]
+    signs = workloads.make_signs(d, 4243)
+    codes, scales = fa_fp8_quantize(x.to(DEV), signs.to(DEV))
+    torch.cuda.synchronize()
+    codes, scales = codes.cpu(), scales.cpu()
+    for b, h in ((0, 0), (1, 17), (3, 31)):
+        print(f"quant full size head b={b} h={h}", flush=True)
+        rc, rs = _oracle_quant(x[b:b + 1, h:h + 1], signs.numpy())
+        assert np.array_equal(scales[b:b + 1, h:h + 1].numpy(), rs)
+        assert np.array_equal(codes[b:b + 1, h:h + 1].numpy(), rc)
+    # every block holds a code of magnitude 448 (its largest element), and
+    # no NaN code anywhere
+    c = codes.view(B, H, N // BLK, BLK * d).numpy()
+    assert ((c & 0x7F) == 0x7E).any(axis=-1).all()
+    assert not ((c & 0x7F) == 0x7F).any()
+
+
 # ----------------------------------------------------------------- forward
 
 def _bound(Qd, Kd, Vd, scale, causal, O, with_mean=False):

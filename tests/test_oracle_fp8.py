@@ -82,6 +82,15 @@ def check_block_quantization_closed_forms(fp8):
     # an all-zero block gets scale 1 and zero codes
     z, zs = fp8.quantize_blocks(np.zeros((1, 1, 8, 64), np.float32), 8)
     assert zs[0, 0, 0] == 1.0 and not z.any()
+    # so does a block whose 448 / amax overflows float32 (amax = 2^-122 <
+    # 448 / FLT_MAX ~ 2^-119.2), while one just above that limit (2^-119)
+    # keeps its scale and puts its largest element on 448
+    t = np.zeros((1, 1, 16, 64), np.float32)
+    t[0, 0, 3, 5] = -(2.0 ** -122)
+    t[0, 0, 8, 9] = 2.0 ** -119
+    tc, ts = fp8.quantize_blocks(t, 8)
+    assert ts[0, 0, 0] == 1.0 and not tc[0, 0, :8].any()
+    assert ts[0, 0, 1] == np.float32(2.0 ** -119) / np.float32(448) and tc[0, 0, 8, 9] == 0x7E
 
 
 def check_exactly_representable_inputs_give_exact_attention(fp8):
