@@ -61,7 +61,10 @@ namespace {
 //
 // PERSIST: the grid holds as many workgroups as fit on the device at once,
 // and each walks the row blocks persist_block() assigns it, which saves a
-// workgroup launch per block.
+// workgroup launch per block.  On this path (dense) Q also goes through LDS:
+// each wave owns 32 rows of an LDS Q tile, copies the next block's Q rows
+// there after writing its output, and stages its output rows there so that
+// they leave in 1 KB stores of consecutive rows.
 //
 // DROP: attention dropout (fa_common.h) on the probabilities before the P V
 // product; the row sums and lse stay those of the undropped probabilities.
@@ -95,11 +98,20 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     static_assert(WI % NW == 0, "tile copies split evenly over the waves");
     constexpr int IPW = WI / NW;
     static_assert(BR % BC == 0, "row blocks start on a key-tile boundary");
+    // QL (the persistent dense path): Q goes through LDS as well.  The next
+    // block's Q tile and first K/V tile are copied while this block's output
+    // is formed, and every wave reads its Q fragments from LDS (stored with the
+    // K tiles' swizzle, so the reads are conflict-free) instead of issuing
+    // 16-byte loads 256 bytes apart from global memory at the start of every
+    // block, which cost several tile-times per block.
+    constexpr bool QL = PERSIST && !DROP && !SPARSE && (2 * STAGE + 32 * NW * D * 2 <= 160 * 1024);
+    constexpr int QTILE = QL ? 32 * NW * D * 2 : 0;
     static_assert(GS == 1 || (!DROP && !SPARSE && NW % GS == 0), "stacked query heads: dense path only");
     constexpr float kSumCap = 256.0f;   // 2^kTau
     static_assert(kTau == 8.0f, "sum cap matches the lazy-rescale threshold");
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE + QTILE];
+    unsigned char* const qlds = smem + 2 * STAGE;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -109,6 +121,53 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
     const int nqb = (N + BR - 1) / BR;
     const int total = nqb * (Hq / GS) * B;
+
+    // this lane's parts of the K/V tile copies (source offsets for its LDS
+    // slots: chunk pc of row `row` holds the row's chunk pc ^ swizzle)
+    uint32_t cpk[IPW], cpv[IPW];
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+        const int p = (wave + NW * i) * 64 + lane;
+        const int row = p / KCH, pc = p % KCH;
+        cpk[i] = (uint32_t)kq_off<D>(row, pc);
+        cpv[i] = (uint32_t)(row * D * 2 + 16 * (pc ^ tr_swz<D>(row)));
+    }
+    // QL: block lg's coordinates; the copies of this wave's 32 Q rows into its
+    // own 8 KB (d = 128) of the Q tile (rows ra0 .. ra0 + 31 of the tile, which
+    // are rows q0 + 32 slice .. of head h0 + wave % GS), and this wave's share
+    // of the copies of the block's first K/V tile into buffer 0.  Rows past N
+    // read zeros (past the end of a head's range).
+    // (The lane index is passed through an empty asm at each call, so that the
+    // lane-dependent offsets are formed where the copies are issued instead of
+    // being hoisted out of the block loop and held through every tile.)
+    constexpr int QRPC = 1024 / (D * 2);   // Q rows per 1 KB copy
+    const int slice_w = GS > 1 ? wave / GS : (wave < NW / 2 ? wave : (NW - 1) - (wave - NW / 2));
+    const int ra0 = (GS > 1 ? (wave % GS) * BR : 0) + 32 * slice_w;
+    unsigned char* const qown = qlds + ra0 * D * 2;
+    auto issue_start = [&](int lg) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int qbr = lg % nqb, bhh = lg / nqb;
+        const int q00 = (CAUSAL ? (nqb - 1 - qbr) : qbr) * BR;
+        const int h0 = GS > 1 ? (bhh % (Hq / GS)) * GS : bhh % Hq;
+        const int bb = bhh / (Hq / GS);
+        const int hw = h0 + (GS > 1 ? wave % GS : 0);
+        const Buf Qg(Q + ((size_t)bb * Hq + hw) * (size_t)N * D, (uint32_t)N * D * 2);
+#pragma unroll
+        for (int k = 0; k < 32 / QRPC; ++k) {
+            const int r = QRPC * k + ln / KCH, pc = ln % KCH;   // local row, LDS chunk
+            const uint32_t src = (uint32_t)(q00 + 32 * slice_w + r) * (D * 2);
+            buf_to_lds16(Qg, qown + 1024 * k, src + (uint32_t)(kq_off<D>(ra0 + r, pc) - (ra0 + r) * D * 2));
+        }
+        const size_t kv0 = ((size_t)bb * Hkv + h0 / (Hq / Hkv)) * (size_t)N * D;
+        const Buf Kg(K + kv0, (uint32_t)N * D * 2), Vg(V + kv0, (uint32_t)N * D * 2);
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            const int bi = wave + NW * i;
+            buf_to_lds16(Kg, smem + bi * 1024, cpk[i]);
+            buf_to_lds16(Vg, smem + TILE + bi * 1024, cpv[i]);
+        }
+    };
     // One block per workgroup, or (PERSIST) a grid of one workgroup per compute
     // unit that walks its blocks in rounds.
     for (int round = 0;; ++round) {
@@ -149,21 +208,24 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         const int q = qw + l32;
 
         u32x4 qf[NKS];
+        if constexpr (QL) {
+            // the first block's copies are issued here, the others' during the
+            // previous block's epilogue
+            if (round == 0) issue_start(logical);
+            wait_vmem();
+            __syncthreads();
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) qf[ks] = Qb.load16((uint32_t)(q * D + 16 * ks + 8 * hi) * 2);
+            for (int ks = 0; ks < NKS; ++ks)
+                qf[ks] = *reinterpret_cast<const u32x4*>(qlds + kq_off<D>(ra0 + l32, 2 * ks + hi));
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) qf[ks] = Qb.load16((uint32_t)(q * D + 16 * ks + 8 * hi) * 2);
+        }
 
         const int kv_len = q0 >= Nk ? 0 : (CAUSAL ? min(Nk, q0 + BR) : Nk);
         const int ntiles = (kv_len + BC - 1) / BC;
         const int nfull = min(min(CAUSAL ? q0 / BC : ntiles, Nk / BC), ntiles);
 
-        uint32_t cpk[IPW], cpv[IPW];
-#pragma unroll
-        for (int i = 0; i < IPW; ++i) {
-            const int p = (wave + NW * i) * 64 + lane;
-            const int row = p / KCH, pc = p % KCH;
-            cpk[i] = (uint32_t)kq_off<D>(row, pc);
-            cpv[i] = (uint32_t)(row * D * 2 + 16 * (pc ^ tr_swz<D>(row)));
-        }
         auto issue_to = [&](unsigned char* base, int k0) {
 #pragma unroll
             for (int i = 0; i < IPW; ++i) {
@@ -442,9 +504,11 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 par ^= 1;
             }
         } else {
-        issue_to(smem, 0);
-        wait_vmem();
-        __syncthreads();
+        if constexpr (!QL) {   // (QL: tile 0 is in buffer 0 already)
+            issue_to(smem, 0);
+            wait_vmem();
+            __syncthreads();
+        }
 
         // The copy of the next tile is issued at the start of every tile, also the
         // last (the extra tile lies in this head's range or past its end, reads as
@@ -469,7 +533,39 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         }
 
         const float l_tot = l_s + swap_halves(l_s);
-        if (q < N) {
+        if constexpr (QL) {
+            // The wave's rows go through its own part of the Q tile (its Q rows
+            // are in registers since the block began): each lane writes its
+            // 8-byte pieces in the Q tile's swizzled layout, then reads back
+            // 16-byte chunks in row order, so that each store writes 1 KB of
+            // consecutive rows instead of 8 bytes in each of 32 rows.  The loops
+            // ended in a barrier, so buffer 0 is free for the next block's
+            // first K/V tile; the wave's own Q rows follow its stores.
+            // (lane laundered as in issue_start: the staging addresses are formed
+            // here, not held through the block loop)
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            const float inv = 1.f / l_tot;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    u32x2 w;
+                    w[0] = Mma<T>::pack2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
+                    w[1] = Mma<T>::pack2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+                    *reinterpret_cast<u32x2*>(qlds + kq_off<D>(ra0 + (ln & 31), 4 * db + g) + 8 * (ln >> 5)) = w;
+                }
+            uint16_t* Ow = O + qoff + (size_t)qw * D;
+#pragma unroll
+            for (int k = 0; k < 32 / QRPC; ++k) {
+                const int r = QRPC * k + ln / KCH;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(qlds + kq_off<D>(ra0 + r, ln % KCH));
+                if (qw + r < N) *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(Ow) + 1024 * k + 16 * ln) = v;
+            }
+            if (q < N && hi == 0) LSE[(size_t)(b * Hq + h) * N + q] = (m_s + __log2f(l_tot)) * kLn2;
+            const int nxt = persist_block((int)blockIdx.x, (int)gridDim.x, total, round + 1);
+            if (nxt >= 0) issue_start(nxt);
+        } else if (q < N) {
             // rows that see no key (block masks, padding) get O = 0 and lse = -inf;
             // kept probabilities are scaled by 256 / t8 here
             const bool empty = SPARSE && (!(l_tot > 0.f) || q >= Nk);
