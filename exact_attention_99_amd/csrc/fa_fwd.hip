@@ -98,19 +98,26 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     static_assert(WI % NW == 0, "tile copies split evenly over the waves");
     constexpr int IPW = WI / NW;
     static_assert(BR % BC == 0, "row blocks start on a key-tile boundary");
-    // QL (the persistent dense path): Q goes through LDS as well.  The next
-    // block's Q tile and first K/V tile are copied while this block's output
-    // is formed, and every wave reads its Q fragments from LDS (stored with the
-    // K tiles' swizzle, so the reads are conflict-free) instead of issuing
+    // QL (the persistent dense path): Q goes through LDS as well, and the next
+    // block's data is in flight before the current block ends.  Every wave
+    // reads its Q fragments from its own 32 rows of an LDS Q tile (stored with
+    // the K tiles' swizzle, so the reads are conflict-free) instead of issuing
     // 16-byte loads 256 bytes apart from global memory at the start of every
-    // block, which cost several tile-times per block.
-    constexpr bool QL = PERSIST && !DROP && !SPARSE && (2 * STAGE + 32 * NW * D * 2 <= 160 * 1024);
+    // block, which cost several tile-times per block; right after those reads
+    // it copies the next block's Q rows there.  The copy slot of the block's
+    // last tile carries the next block's first K/V tile, so tile j of a block
+    // lies in buffer (j + p0) & 1 with p0 alternating between blocks.  The
+    // output rows are staged in LDS (the last tile's buffer and a spare
+    // region) and leave in 1 KB stores of consecutive rows.
+    constexpr bool QL = PERSIST && !DROP && !SPARSE && (2 * STAGE + 48 * NW * D * 2 <= 160 * 1024);
     constexpr int QTILE = QL ? 32 * NW * D * 2 : 0;
+    constexpr int OSPARE = QTILE / 2;   // output staging of waves NW/2 .. NW - 1
+    constexpr int OWAVE = 32 * D * 2;   // a wave's output rows
     static_assert(GS == 1 || (!DROP && !SPARSE && NW % GS == 0), "stacked query heads: dense path only");
     constexpr float kSumCap = 256.0f;   // 2^kTau
     static_assert(kTau == 8.0f, "sum cap matches the lazy-rescale threshold");
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE + QTILE];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE + QTILE + OSPARE];
     unsigned char* const qlds = smem + 2 * STAGE;
 
     const int tid = threadIdx.x;
@@ -135,8 +142,8 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     // QL: block lg's coordinates; the copies of this wave's 32 Q rows into its
     // own 8 KB (d = 128) of the Q tile (rows ra0 .. ra0 + 31 of the tile, which
     // are rows q0 + 32 slice .. of head h0 + wave % GS), and this wave's share
-    // of the copies of the block's first K/V tile into buffer 0.  Rows past N
-    // read zeros (past the end of a head's range).
+    // of the copies of the block's first K/V tile into the buffer at `base`.
+    // Rows past N read zeros (past the end of a head's range).
     // (The lane index is passed through an empty asm at each call, so that the
     // lane-dependent offsets are formed where the copies are issued instead of
     // being hoisted out of the block loop and held through every tile.)
@@ -144,13 +151,17 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int slice_w = GS > 1 ? wave / GS : (wave < NW / 2 ? wave : (NW - 1) - (wave - NW / 2));
     const int ra0 = (GS > 1 ? (wave % GS) * BR : 0) + 32 * slice_w;
     unsigned char* const qown = qlds + ra0 * D * 2;
-    auto issue_start = [&](int lg) {
+    auto block_of = [&](int lg, int& q00, int& h0, int& bb) {
+        const int qbr = lg % nqb, bhh = lg / nqb;
+        q00 = (CAUSAL ? (nqb - 1 - qbr) : qbr) * BR;
+        h0 = GS > 1 ? (bhh % (Hq / GS)) * GS : bhh % Hq;
+        bb = bhh / (Hq / GS);
+    };
+    auto issue_q = [&](int lg) {
         int ln = lane;
         asm volatile("" : "+v"(ln));
-        const int qbr = lg % nqb, bhh = lg / nqb;
-        const int q00 = (CAUSAL ? (nqb - 1 - qbr) : qbr) * BR;
-        const int h0 = GS > 1 ? (bhh % (Hq / GS)) * GS : bhh % Hq;
-        const int bb = bhh / (Hq / GS);
+        int q00, h0, bb;
+        block_of(lg, q00, h0, bb);
         const int hw = h0 + (GS > 1 ? wave % GS : 0);
         const Buf Qg(Q + ((size_t)bb * Hq + hw) * (size_t)N * D, (uint32_t)N * D * 2);
 #pragma unroll
@@ -159,22 +170,28 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             const uint32_t src = (uint32_t)(q00 + 32 * slice_w + r) * (D * 2);
             buf_to_lds16(Qg, qown + 1024 * k, src + (uint32_t)(kq_off<D>(ra0 + r, pc) - (ra0 + r) * D * 2));
         }
+    };
+    auto issue_kv0 = [&](int lg, unsigned char* base) {
+        int q00, h0, bb;
+        block_of(lg, q00, h0, bb);
         const size_t kv0 = ((size_t)bb * Hkv + h0 / (Hq / Hkv)) * (size_t)N * D;
         const Buf Kg(K + kv0, (uint32_t)N * D * 2), Vg(V + kv0, (uint32_t)N * D * 2);
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
             const int bi = wave + NW * i;
-            buf_to_lds16(Kg, smem + bi * 1024, cpk[i]);
-            buf_to_lds16(Vg, smem + TILE + bi * 1024, cpv[i]);
+            buf_to_lds16(Kg, base + bi * 1024, cpk[i]);
+            buf_to_lds16(Vg, base + TILE + bi * 1024, cpv[i]);
         }
     };
+    int p0 = 0;   // QL: buffer of the current block's tile 0
     // One block per workgroup, or (PERSIST) a grid of one workgroup per compute
     // unit that walks its blocks in rounds.
     for (int round = 0;; ++round) {
-        int logical;
+        int logical, nxt = -1;
         if constexpr (PERSIST) {
             logical = persist_block((int)blockIdx.x, (int)gridDim.x, total, round);
             if (logical < 0) break;
+            nxt = persist_block((int)blockIdx.x, (int)gridDim.x, total, round + 1);
         } else {
             if (round > 0) break;
             logical = xcd_remap((int)blockIdx.x, total);
@@ -210,13 +227,21 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         u32x4 qf[NKS];
         if constexpr (QL) {
             // the first block's copies are issued here, the others' during the
-            // previous block's epilogue
-            if (round == 0) issue_start(logical);
+            // previous block
+            if (round == 0) {
+                issue_q(logical);
+                issue_kv0(logical, smem);
+            }
             wait_vmem();
             __syncthreads();
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks)
                 qf[ks] = *reinterpret_cast<const u32x4*>(qlds + kq_off<D>(ra0 + l32, 2 * ks + hi));
+            if (nxt >= 0) {
+                // the next block's Q rows replace these once they are read
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                issue_q(nxt);
+            }
         } else {
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) qf[ks] = Qb.load16((uint32_t)(q * D + 16 * ks + 8 * hi) * 2);
@@ -234,6 +259,15 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 buf_to_lds16(Kb, base + bi * 1024, rowb + cpk[i]);
                 buf_to_lds16(Vb, base + TILE + bi * 1024, rowb + cpv[i]);
             }
+        };
+        // copies of tile jj into the buffer at base; past the last tile, the
+        // next block's first tile (QL) or a tile past the end, which reads this
+        // head's range or zeros and lands in the buffer no later tile reads
+        auto issue_tile = [&](unsigned char* base, int jj) {
+            if (!QL || jj < ntiles)
+                issue_to(base, jj * BC);
+            else if (nxt >= 0)
+                issue_kv0(nxt, base);
         };
 
         const int g16 = lane >> 4;
@@ -504,29 +538,39 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 par ^= 1;
             }
         } else {
-        if constexpr (!QL) {   // (QL: tile 0 is in buffer 0 already)
+        if constexpr (!QL) {   // (QL: tile 0 is in buffer p0 already)
             issue_to(smem, 0);
             wait_vmem();
             __syncthreads();
         }
 
         // The copy of the next tile is issued at the start of every tile, also the
-        // last (the extra tile lies in this head's range or past its end, reads as
-        // zeros, and lands in the buffer no later tile reads).
+        // last (issue_tile).  The pairs of unmasked tiles start in buffer 0; with
+        // QL and p0 = 1, tile 0 (in buffer 1) runs alone first.
         int j = 0;
+        if constexpr (QL) {
+            if (p0 && nfull >= 1) {
+                issue_tile(smem, 1);
+                tile(0, std::false_type{}, smem + STAGE);
+                wait_vmem();
+                __syncthreads();
+                j = 1;
+            }
+        }
         for (; j + 1 < nfull; j += 2) {
-            issue_to(smem + STAGE, (j + 1) * BC);
+            issue_tile(smem + STAGE, j + 1);
             tile(j, std::false_type{}, smem);
             wait_vmem();
             __syncthreads();
-            issue_to(smem, (j + 2) * BC);
+            issue_tile(smem, j + 2);
             tile(j + 1, std::false_type{}, smem + STAGE);
             wait_vmem();
             __syncthreads();
         }
         for (; j < ntiles; ++j) {
-            issue_to(smem + ((j + 1) & 1) * STAGE, (j + 1) * BC);
-            if (!CAUSAL || j * BC <= qw + 31) tile(j, std::true_type{}, smem + (j & 1) * STAGE);
+            const int pj = (j + (QL ? p0 : 0)) & 1;
+            issue_tile(smem + (pj ^ 1) * STAGE, j + 1);
+            if (!CAUSAL || j * BC <= qw + 31) tile(j, std::true_type{}, smem + pj * STAGE);
             wait_vmem();
             __syncthreads();
         }
@@ -534,17 +578,20 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
         const float l_tot = l_s + swap_halves(l_s);
         if constexpr (QL) {
-            // The wave's rows go through its own part of the Q tile (its Q rows
-            // are in registers since the block began): each lane writes its
-            // 8-byte pieces in the Q tile's swizzled layout, then reads back
-            // 16-byte chunks in row order, so that each store writes 1 KB of
-            // consecutive rows instead of 8 bytes in each of 32 rows.  The loops
-            // ended in a barrier, so buffer 0 is free for the next block's
-            // first K/V tile; the wave's own Q rows follow its stores.
-            // (lane laundered as in issue_start: the staging addresses are formed
+            // The wave's rows go through LDS: each lane writes its 8-byte pieces
+            // in the swizzled layout of the Q tile, then reads back 16-byte
+            // chunks in row order, so that each store writes 1 KB of consecutive
+            // rows instead of 8 bytes in each of 32 rows.
+            // (lane laundered as in issue_q: the staging addresses are formed
             // here, not held through the block loop)
             int ln = lane;
             asm volatile("" : "+v"(ln));
+            // staging: the buffer of the block's last tile (free after the loops'
+            // final barrier; the other holds the next block's first tile) for
+            // waves 0 .. NW/2 - 1, the spare region for the others
+            unsigned char* const ost = wave < NW / 2
+                                           ? smem + ((ntiles - 1 + p0) & 1) * STAGE + wave * OWAVE
+                                           : smem + 2 * STAGE + QTILE + (wave - NW / 2) * OWAVE;
             const float inv = 1.f / l_tot;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
@@ -553,18 +600,17 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                     u32x2 w;
                     w[0] = Mma<T>::pack2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
                     w[1] = Mma<T>::pack2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-                    *reinterpret_cast<u32x2*>(qlds + kq_off<D>(ra0 + (ln & 31), 4 * db + g) + 8 * (ln >> 5)) = w;
+                    *reinterpret_cast<u32x2*>(ost + kq_off<D>(ln & 31, 4 * db + g) + 8 * (ln >> 5)) = w;
                 }
             uint16_t* Ow = O + qoff + (size_t)qw * D;
 #pragma unroll
             for (int k = 0; k < 32 / QRPC; ++k) {
                 const int r = QRPC * k + ln / KCH;
-                const u32x4 v = *reinterpret_cast<const u32x4*>(qlds + kq_off<D>(ra0 + r, ln % KCH));
+                const u32x4 v = *reinterpret_cast<const u32x4*>(ost + kq_off<D>(r, ln % KCH));
                 if (qw + r < N) *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(Ow) + 1024 * k + 16 * ln) = v;
             }
             if (q < N && hi == 0) LSE[(size_t)(b * Hq + h) * N + q] = (m_s + __log2f(l_tot)) * kLn2;
-            const int nxt = persist_block((int)blockIdx.x, (int)gridDim.x, total, round + 1);
-            if (nxt >= 0) issue_start(nxt);
+            p0 = (ntiles + p0) & 1;   // where the next block's tile 0 went
         } else if (q < N) {
             // rows that see no key (block masks, padding) get O = 0 and lse = -inf;
             // kept probabilities are scaled by 256 / t8 here
