@@ -32,6 +32,9 @@
 #ifndef FA355_FWD_BC128
 #define FA355_FWD_BC128 64     // forward keys per tile at d = 128
 #endif
+#ifndef FA355_FWD_QLDS
+#define FA355_FWD_QLDS 1       // forward persistent grid: Q and output staged in LDS
+#endif
 #ifndef FA355_FWD_PERSIST
 #define FA355_FWD_PERSIST 1    // forward persistent grid
 #endif

@@ -109,7 +109,10 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     // lies in buffer (j + p0) & 1 with p0 alternating between blocks.  The
     // output rows are staged in LDS (the last tile's buffer and a spare
     // region) and leave in 1 KB stores of consecutive rows.
-    constexpr bool QL = PERSIST && !DROP && !SPARSE && (2 * STAGE + 48 * NW * D * 2 <= 160 * 1024);
+    // (only where the LDS still fits the 8 / NW workgroups per compute unit that
+    // give 2 waves per SIMD)
+    constexpr bool QL = FA355_FWD_QLDS && PERSIST && !DROP && !SPARSE &&
+                        (2 * STAGE + 48 * NW * D * 2) * (8 / NW) <= 160 * 1024;
     constexpr int QTILE = QL ? 32 * NW * D * 2 : 0;
     constexpr int OSPARE = QTILE / 2;   // output staging of waves NW/2 .. NW - 1
     constexpr int OWAVE = 32 * D * 2;   // a wave's output rows
@@ -813,10 +816,15 @@ hipError_t dispatch16c(const FwdArgs& a) {
 #if FA355_FWD_STACK
     // grouped K/V heads at d = 128: one workgroup takes the same rows of 2 or 4
     // query heads of a group, which then share every K/V tile it stages
-    if constexpr (D == 128 && NW % 4 == 0) {
+    // (a stacking factor is used only where each head's row block, 32 NW / GS
+    // rows, stays a multiple of the key tile)
+    if constexpr (D == 128) {
+        constexpr int BCD = FA355_FWD_BC128;
         const int G = a.Hq / a.Hkv;
-        if (G % 4 == 0) return launch16v6<T, D, CAUSAL, NW, (D == 128 ? FA355_FWD_BC128 : 64), PERS, false, false, 4>(a);
-        if (G % 2 == 0) return launch16v6<T, D, CAUSAL, NW, (D == 128 ? FA355_FWD_BC128 : 64), PERS, false, false, 2>(a);
+        if constexpr ((32 * NW / 4) % BCD == 0)
+            if (G % 4 == 0) return launch16v6<T, D, CAUSAL, NW, BCD, PERS, false, false, 4>(a);
+        if constexpr ((32 * NW / 2) % BCD == 0)
+            if (G % 2 == 0) return launch16v6<T, D, CAUSAL, NW, BCD, PERS, false, false, 2>(a);
     }
 #endif
     return launch16v6<T, D, CAUSAL, NW, (D == 128 ? FA355_FWD_BC128 : 64), PERS>(a);
