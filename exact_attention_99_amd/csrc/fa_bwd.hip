@@ -207,13 +207,34 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         const int Nk = (SPARSE && sp.seqlens) ? min(max(sp.seqlens[b], 0), N) : N;
         const uint32_t head_bytes = (uint32_t)Nk * D * 2;
 
-        u32x4 kf[NKS], vf[NKS];
+        // This wave's 32 K and V rows arrive by coalesced buffer-to-LDS copies
+        // (1 KB of consecutive rows each, stored with the K tiles' swizzle)
+        // into its own 16 KB of the buffer the first step does not use, and are
+        // read from there into registers between two barriers (the second keeps
+        // the next step's copies from overwriting another wave's rows early).
+        // (Loaded directly, a lane's 16-byte pieces lie 256 bytes apart: every
+        // load touches 32 cache lines.)  Keys past the sequence read zeros.
+        constexpr int KRPC = 1024 / (D * 2);   // rows per 1 KB copy
+        const int kvbuf = BLOCKMASK ? 1 : ((CAUSAL && kv0 < Nk ? Hq / Hkv : 0) & 1) ^ 1;
+        unsigned char* const kvst = smem + kvbuf * STAGE + wave * (2 * 32 * D * 2);
         {
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
             const Buf Kb(K + kvoff, head_bytes), Vb(V + kvoff, head_bytes);
 #pragma unroll
+            for (int k = 0; k < 32 / KRPC; ++k) {
+                const int r = KRPC * k + ln / KCH, pc = ln % KCH;
+                const uint32_t src = (uint32_t)kw * D * 2 + (uint32_t)kq_off<D>(r, pc);
+                buf_to_lds16(Kb, kvst + 1024 * k, src);
+                buf_to_lds16(Vb, kvst + 32 * D * 2 + 1024 * k, src);
+            }
+        }
+        u32x4 kf[NKS], vf[NKS];
+        auto read_kv = [&]() {
+#pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
-                kf[ks] = Kb.load16((uint32_t)(key * D + 16 * ks + 8 * hi) * 2);
-                vf[ks] = Vb.load16((uint32_t)(key * D + 16 * ks + 8 * hi) * 2);
+                kf[ks] = *reinterpret_cast<const u32x4*>(kvst + kq_off<D>(l32, 2 * ks + hi));
+                vf[ks] = *reinterpret_cast<const u32x4*>(kvst + 32 * D * 2 + kq_off<D>(l32, 2 * ks + hi));
             }
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
@@ -222,7 +243,7 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 asm volatile("" : "+a"(kf[ks]));
                 asm volatile("" : "+a"(vf[ks]));
             }
-        }
+        };
 
         f32x16 dkt[NDB], dvt[NDB];
 #pragma unroll
@@ -486,9 +507,11 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                     for (int c = 0; c < NCALL; ++c) pg[c].round();
                 drop_store(dbase);
             }
-            wait_vmem();
         }
+        wait_vmem();
         __syncthreads();
+        read_kv();
+        __syncthreads();   // every wave holds its K/V before the next step's copies
 
         // one tile: prefetch the next one into the other buffer, compute, publish
         auto tile = [&](int s, auto mask_tag, auto buf_tag) __attribute__((always_inline)) {
@@ -588,12 +611,19 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             }
         }
 
-        if (key < N) {
-            uint16_t* dkrow = dK + kvoff + (size_t)key * D;
-            uint16_t* dvrow = dV + kvoff + (size_t)key * D;
-            // keys past the sequence's length (their columns of dS and P need
-            // not be finite) get zero gradients
-            const bool pad = SPARSE && key >= Nk;
+        {
+            // dK and dV rows go through this wave's own 16 KB of buffer 0 (free
+            // after the walk's last barrier): each lane writes its 8-byte pieces
+            // in the swizzled layout, then reads back 16-byte chunks in row
+            // order, so that each store writes 1 KB of consecutive rows.  Keys
+            // past the sequence's length (their columns of dS and P need not be
+            // finite) get zero gradients.  A barrier ends the block, so that no
+            // wave copies the next block's first step over rows another wave is
+            // still reading back.
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            unsigned char* const ost = smem + wave * (2 * 32 * D * 2);
+            const bool pad = SPARSE && kw + (ln & 31) >= Nk;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -604,9 +634,24 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                     wv[0] = Mma<T>::pack2(dvt[db][4 * g], dvt[db][4 * g + 1]);
                     wv[1] = Mma<T>::pack2(dvt[db][4 * g + 2], dvt[db][4 * g + 3]);
                     if (pad) wk = wv = u32x2{0u, 0u};
-                    *reinterpret_cast<u32x2*>(dkrow + 32 * db + 8 * g + 4 * hi) = wk;
-                    *reinterpret_cast<u32x2*>(dvrow + 32 * db + 8 * g + 4 * hi) = wv;
+                    const int o = kq_off<D>(ln & 31, 4 * db + g) + 8 * (ln >> 5);
+                    *reinterpret_cast<u32x2*>(ost + o) = wk;
+                    *reinterpret_cast<u32x2*>(ost + 32 * D * 2 + o) = wv;
                 }
+            unsigned char* const dkw = reinterpret_cast<unsigned char*>(dK + kvoff + (size_t)kw * D);
+            unsigned char* const dvw = reinterpret_cast<unsigned char*>(dV + kvoff + (size_t)kw * D);
+#pragma unroll
+            for (int k = 0; k < 32 / KRPC; ++k) {
+                const int r = KRPC * k + ln / KCH;
+                const int o = kq_off<D>(r, ln % KCH);
+                const u32x4 vk = *reinterpret_cast<const u32x4*>(ost + o);
+                const u32x4 vv = *reinterpret_cast<const u32x4*>(ost + 32 * D * 2 + o);
+                if (kw + r < N) {
+                    *reinterpret_cast<u32x4*>(dkw + 1024 * k + 16 * ln) = vk;
+                    *reinterpret_cast<u32x4*>(dvw + 1024 * k + 16 * ln) = vv;
+                }
+            }
+            __syncthreads();
         }
 
     }
