@@ -912,8 +912,18 @@ dq16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         }
     }
 
-    if (q < N) {
-        uint16_t* row = dQ + qoff + (size_t)q * D;
+    {
+        // dQ rows go through LDS (free after the walk's last barrier): each lane
+        // writes its 8-byte pieces in the swizzled layout, then reads back
+        // 16-byte chunks in row order, so that each store writes 1 KB of
+        // consecutive rows instead of 8 bytes in each of 32 rows.  (The lane
+        // index goes through an empty asm, so that the staging addresses are
+        // formed here rather than held through the walk.)
+        static_assert(NW * 32 * D * 2 <= 2 * STAGE, "dQ staging fits the K/V buffers");
+        constexpr int RPC = 1024 / (D * 2);   // rows per 1 KB store
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        unsigned char* const ost = smem + wave * (32 * D * 2);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -921,8 +931,15 @@ dq16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 u32x2 w;
                 w[0] = Mma<T>::pack2(dq[db][4 * g] * scale, dq[db][4 * g + 1] * scale);
                 w[1] = Mma<T>::pack2(dq[db][4 * g + 2] * scale, dq[db][4 * g + 3] * scale);
-                *reinterpret_cast<u32x2*>(row + 32 * db + 8 * g + 4 * hi) = w;
+                *reinterpret_cast<u32x2*>(ost + kq_off<D>(ln & 31, 4 * db + g) + 8 * (ln >> 5)) = w;
             }
+        unsigned char* const dqw = reinterpret_cast<unsigned char*>(dQ + qoff + (size_t)qw * D);
+#pragma unroll
+        for (int k = 0; k < 32 / RPC; ++k) {
+            const int r = RPC * k + ln / KCH;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(ost + kq_off<D>(r, ln % KCH));
+            if (qw + r < N) *reinterpret_cast<u32x4*>(dqw + 1024 * k + 16 * ln) = v;
+        }
     }
 }
 
