@@ -109,9 +109,10 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     // lies in buffer (j + p0) & 1 with p0 alternating between blocks.  The
     // output rows are staged in LDS (the last tile's buffer and a spare
     // region) and leave in 1 KB stores of consecutive rows.
-    // (only where the LDS still fits the 8 / NW workgroups per compute unit that
-    // give 2 waves per SIMD)
-    constexpr bool QL = FA355_FWD_QLDS && PERSIST && !DROP && !SPARSE &&
+    // (d = 128 only, and only where the LDS still fits the 8 / NW workgroups per
+    // compute unit that give 2 waves per SIMD; the d = 64 build runs 3 waves
+    // per SIMD, which the larger LDS area and the extra registers would cost)
+    constexpr bool QL = FA355_FWD_QLDS && PERSIST && !DROP && !SPARSE && D == 128 &&
                         (2 * STAGE + 48 * NW * D * 2) * (8 / NW) <= 160 * 1024;
     constexpr int QTILE = QL ? 32 * NW * D * 2 : 0;
     constexpr int OSPARE = QTILE / 2;   // output staging of waves NW/2 .. NW - 1
