@@ -114,8 +114,13 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     // per SIMD, which the larger LDS area and the extra registers would cost)
     constexpr bool QL = FA355_FWD_QLDS && PERSIST && !DROP && !SPARSE && D == 128 &&
                         (2 * STAGE + 48 * NW * D * 2) * (8 / NW) <= 160 * 1024;
-    constexpr int QTILE = QL ? 32 * NW * D * 2 : 0;
-    constexpr int OSPARE = QTILE / 2;   // output staging of waves NW/2 .. NW - 1
+    // QN (one row block per workgroup, 8 waves, d = 128: the dropout and
+    // variable-length builds): the same Q tile, without the next block's
+    // copies; each wave stages its output rows in its own Q rows.
+    constexpr bool QN = FA355_FWD_QLDS && !PERSIST && D == 128 && NW == 8 && GS == 1 &&
+                        2 * STAGE + 32 * NW * D * 2 <= 160 * 1024;
+    constexpr int QTILE = (QL || QN) ? 32 * NW * D * 2 : 0;
+    constexpr int OSPARE = QL ? QTILE / 2 : 0;   // output staging of waves NW/2 .. NW - 1
     constexpr int OWAVE = 32 * D * 2;   // a wave's output rows
     static_assert(GS == 1 || (!DROP && !SPARSE && NW % GS == 0), "stacked query heads: dense path only");
     constexpr float kSumCap = 256.0f;   // 2^kTau
@@ -246,6 +251,17 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 issue_q(nxt);
             }
+        } else if constexpr (QN) {
+            // this wave's Q rows (past the sequence's length: zeros), read into
+            // qf after the first tile's barrier
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+#pragma unroll
+            for (int k = 0; k < 32 / QRPC; ++k) {
+                const int r = QRPC * k + ln / KCH, pc = ln % KCH;
+                buf_to_lds16(Qb, qown + 1024 * k,
+                             (uint32_t)(qw + r) * (D * 2) + (uint32_t)(kq_off<D>(ra0 + r, pc) - (ra0 + r) * D * 2));
+            }
         } else {
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) qf[ks] = Qb.load16((uint32_t)(q * D + 16 * ks + 8 * hi) * 2);
@@ -272,6 +288,14 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 issue_to(base, jj * BC);
             else if (nxt >= 0)
                 issue_kv0(nxt, base);
+        };
+        // QN: this wave's Q fragments from its rows of the Q tile
+        auto read_qn = [&]() {
+            if constexpr (QN) {
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    qf[ks] = *reinterpret_cast<const u32x4*>(qlds + kq_off<D>(ra0 + l32, 2 * ks + hi));
+            }
         };
 
         const int g16 = lane >> 4;
@@ -528,6 +552,7 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             if (jt < ntiles) issue_to(smem, jt * BC);
             wait_vmem();
             __syncthreads();
+            read_qn();
             int par = 0;
             while (jt < ntiles) {
                 const int jn = next(jt);
@@ -546,6 +571,7 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             issue_to(smem, 0);
             wait_vmem();
             __syncthreads();
+            read_qn();
         }
 
         // The copy of the next tile is issued at the start of every tile, also the
@@ -615,6 +641,31 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             }
             if (q < N && hi == 0) LSE[(size_t)(b * Hq + h) * N + q] = (m_s + __log2f(l_tot)) * kLn2;
             p0 = (ntiles + p0) & 1;   // where the next block's tile 0 went
+        } else if constexpr (QN) {
+            // as above, staged in the wave's own Q rows; rows that see no key
+            // (padding) get O = 0 and lse = -inf, kept probabilities are scaled
+            // by 256 / t8
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            const bool empty = SPARSE && (!(l_tot > 0.f) || q >= Nk);
+            const float inv = empty ? 0.f : (DROP ? dp.scale : 1.f) / l_tot;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    u32x2 w;
+                    w[0] = Mma<T>::pack2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
+                    w[1] = Mma<T>::pack2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+                    *reinterpret_cast<u32x2*>(qlds + kq_off<D>(ra0 + (ln & 31), 4 * db + g) + 8 * (ln >> 5)) = w;
+                }
+            unsigned char* const Ow = reinterpret_cast<unsigned char*>(O + qoff + (size_t)qw * D);
+#pragma unroll
+            for (int k = 0; k < 32 / QRPC; ++k) {
+                const int r = QRPC * k + ln / KCH;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(qlds + kq_off<D>(ra0 + r, ln % KCH));
+                if (qw + r < N) *reinterpret_cast<u32x4*>(Ow + 1024 * k + 16 * ln) = v;
+            }
+            if (q < N && hi == 0) LSE[(size_t)(b * Hq + h) * N + q] = empty ? -INFINITY : (m_s + __log2f(l_tot)) * kLn2;
         } else if (q < N) {
             // rows that see no key (block masks, padding) get O = 0 and lse = -inf;
             // kept probabilities are scaled by 256 / t8 here
