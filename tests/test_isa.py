@@ -1,5 +1,8 @@
 """Checks of the compiler's gfx950 output for the kernels (CPU: hipcc cross-compiles).
 
+Two properties: LDS reads do not wait for the next tile's copies (below), and
+every kernel keeps the occupancy its tiling is built for (at the end).
+
 Every tiled kernel issues buffer-to-LDS copies of its next tile while it reads the
 current tile from the other LDS buffer.  When the compiler cannot tell those reads
 from the copies' LDS writes, it puts a wait on the vector-memory counter right
@@ -70,12 +73,21 @@ def test_detector_flags_a_wait_before_an_lds_read():
     assert lds_reads_after_vmem_waits(body.replace("vmcnt(0)", "lgkmcnt(0)")) == []
 
 
-@pytest.mark.skipif(not shutil.which(fabuild.HIPCC) and not os.path.exists(fabuild.HIPCC),
-                    reason="hipcc is not installed")
-def test_no_lds_read_waits_for_the_next_tiles_copies(tmp_path):
+needs_hipcc = pytest.mark.skipif(not shutil.which(fabuild.HIPCC) and not os.path.exists(fabuild.HIPCC),
+                                 reason="hipcc is not installed")
+
+
+@pytest.fixture(scope="module")
+def asms(tmp_path_factory):
+    """gfx950 assembly of every library source, compiled once for this module."""
+    d = tmp_path_factory.mktemp("isa")
     srcs = fabuild.sources()
     with cf.ThreadPoolExecutor(max_workers=min(4, len(srcs))) as ex:
-        asms = list(ex.map(lambda s: _asm(s, str(tmp_path / (os.path.basename(s) + ".s"))), srcs))
+        return list(ex.map(lambda s: _asm(s, str(d / (os.path.basename(s) + ".s"))), srcs))
+
+
+@needs_hipcc
+def test_no_lds_read_waits_for_the_next_tiles_copies(asms):
     checked, bad = 0, []
     for asm in asms:
         for name, body in _functions(asm):
@@ -87,3 +99,75 @@ def test_no_lds_read_waits_for_the_next_tiles_copies(tmp_path):
                 bad.append((name, hits[:2]))
     assert checked >= 80, f"only {checked} checked kernels with buffer-to-LDS copies found"
     assert not bad, bad
+
+
+# ----------------------------------------------------------------- occupancy
+
+KDESC = re.compile(r"^\s*\.amdhsa_kernel (\S+)$(.*?)^\s*\.end_amdhsa_kernel", re.M | re.S)
+LDS_BYTES = 160 * 1024      # per compute unit
+REGS = 512                  # vector + accumulation registers per SIMD lane
+
+
+def kernel_resources(asm: str):
+    """(mangled name, registers, LDS bytes, scratch bytes) of every kernel."""
+    for m in KDESC.finditer(asm):
+        body = m.group(2)
+        get = lambda k: int(re.search(r"\.amdhsa_" + k + r" (\d+)", body).group(1))
+        yield m.group(1), get("next_free_vgpr"), get("group_segment_fixed_size"), \
+            get("private_segment_fixed_size")
+
+
+def waves_per_simd(regs: int) -> int:
+    return REGS // (-(-regs // 8) * 8)
+
+
+FWD = re.compile(r"fwd16v6_kernelINS_4(?:BF16|FP16)ELi(\d+)ELb(\d)ELi(\d+)ELi(\d+)ELb(\d)ELb(\d)ELb(\d)ELi(\d+)E")
+DQ = re.compile(r"dq16v3_kernelINS_4(?:BF16|FP16)ELi(\d+)ELb(\d)ELi(\d+)ELb(\d)ELb(\d)E")
+
+
+def test_occupancy_rule():
+    assert waves_per_simd(168) == 3 and waves_per_simd(169) == 2 and waves_per_simd(256) == 2
+
+
+@needs_hipcc
+def test_kernels_keep_the_occupancy_they_are_tiled_for(asms):
+    """Each kernel's tiling assumes a number of waves per SIMD and of
+    workgroups per compute unit; more registers or LDS than that allows would
+    silently cost a wave (at d = 64 the forward once lost its third wave per
+    SIMD this way).  Scratch (spilled registers) is checked too: the causal
+    dense paths have none; the known exceptions are the dQ pass without the
+    causal mask (masked-tile loop only) and with dropout at d = 128."""
+    res = [r for asm in asms for r in kernel_resources(asm)]
+    seen = set()
+    for name, regs, lds, scratch in res:
+        m = FWD.search(name)
+        if m:
+            d, _causal, nw, _bc, _pers, drop, _sparse, _gs = (int(x) for x in m.groups())
+            seen.add("fwd")
+            assert scratch == 0, (name, scratch)
+            if d == 128:   # 2 waves per SIMD, NW / 4 waves per SIMD per workgroup
+                assert waves_per_simd(regs) >= 2, (name, regs)
+                assert (8 // nw) * lds <= LDS_BYTES, (name, lds)
+            elif not drop:  # d = 64: 3 waves per SIMD (3 four-wave workgroups)
+                assert waves_per_simd(regs) >= 3, (name, regs)
+                assert 3 * lds <= LDS_BYTES, (name, lds)
+            continue
+        m = DQ.search(name)
+        if m:
+            d, causal, nw, drop, _sparse = (int(x) for x in m.groups())
+            seen.add("dq")
+            assert waves_per_simd(regs) >= 2, (name, regs)
+            assert (8 // nw) * lds <= LDS_BYTES, (name, lds)
+            if causal and not drop:
+                assert scratch == 0, (name, scratch)
+            continue
+        if "fwd8_kernel" in name:   # three four-wave workgroups per compute unit
+            seen.add("fwd8")
+            assert waves_per_simd(regs) >= 3 and 3 * lds <= LDS_BYTES and scratch == 0, (name, regs, lds, scratch)
+        elif "dkdv16v3_kernel" in name:   # one workgroup per compute unit
+            seen.add("dkdv")
+            assert lds <= LDS_BYTES and scratch == 0, (name, lds, scratch)
+        elif any(k in name for k in ("quant8_kernel", "fwd_split16_kernel", "merge_split_kernel")):
+            seen.add(name.split("_kernel")[0][-10:])
+            assert scratch == 0 and lds <= LDS_BYTES, (name, lds, scratch)
+    assert {"fwd", "dq", "fwd8", "dkdv"} <= seen, seen
