@@ -147,11 +147,13 @@ def test_many_short_heads_masked(kind, d, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("hkv", [16, 32])
+@pytest.mark.parametrize("hkv", [4, 16, 32])
 def test_many_short_heads_other_groups(hkv, causal):
-    """Groups of 2 query heads (the forward stacks them in one workgroup) and no
-    grouping, on the persistent grid at d = 128: sampled heads against the
-    oracle, every head through the Q = 0 closed form."""
+    """Groups of 8 query heads (two stacks of 4 heads per K/V head: heads 17
+    and 31 below lie in the first and second stack of theirs), groups of 2
+    (one stack of 2) and no grouping, on the persistent grid at d = 128:
+    sampled heads against the oracle, every head through the Q = 0 closed
+    form."""
     d = 128
     G2 = HQ // hkv
     print(f"case hkv={hkv} causal={causal}", flush=True)
