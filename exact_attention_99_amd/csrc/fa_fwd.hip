@@ -119,6 +119,12 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     // copies; each wave stages its output rows in its own Q rows.
     constexpr bool QN = FA355_FWD_QLDS && !PERSIST && D == 128 && NW == 8 && GS == 1 &&
                         2 * STAGE + 32 * NW * D * 2 <= 160 * 1024;
+    // QB (the block-mask build: 4 waves, two workgroups per compute unit): the
+    // same, with the Q rows in K/V buffer 1 before the first tile (a second
+    // barrier keeps the first copy into that buffer from overwriting them),
+    // so the LDS per workgroup stays as it is.
+    constexpr bool QB = FA355_FWD_QLDS && !PERSIST && SPARSE && D == 128 && NW == 4 && GS == 1 &&
+                        32 * NW * D * 2 <= STAGE;
     constexpr int QTILE = (QL || QN) ? 32 * NW * D * 2 : 0;
     constexpr int OSPARE = QL ? QTILE / 2 : 0;   // output staging of waves NW/2 .. NW - 1
     constexpr int OWAVE = 32 * D * 2;   // a wave's output rows
@@ -127,7 +133,7 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     static_assert(kTau == 8.0f, "sum cap matches the lazy-rescale threshold");
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE + QTILE + OSPARE];
-    unsigned char* const qlds = smem + 2 * STAGE;
+    unsigned char* const qlds = smem + (QB ? STAGE : 2 * STAGE);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -251,7 +257,7 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 issue_q(nxt);
             }
-        } else if constexpr (QN) {
+        } else if constexpr (QN || QB) {
             // this wave's Q rows (past the sequence's length: zeros), read into
             // qf after the first tile's barrier
             int ln = lane;
@@ -289,13 +295,15 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             else if (nxt >= 0)
                 issue_kv0(nxt, base);
         };
-        // QN: this wave's Q fragments from its rows of the Q tile
+        // QN, QB: this wave's Q fragments from its rows of the Q tile (QB: then
+        // a barrier, as the next copy goes to the buffer that holds them)
         auto read_qn = [&]() {
-            if constexpr (QN) {
+            if constexpr (QN || QB) {
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks)
                     qf[ks] = *reinterpret_cast<const u32x4*>(qlds + kq_off<D>(ra0 + l32, 2 * ks + hi));
             }
+            if constexpr (QB) __syncthreads();
         };
 
         const int g16 = lane >> 4;
@@ -641,7 +649,7 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             }
             if (q < N && hi == 0) LSE[(size_t)(b * Hq + h) * N + q] = (m_s + __log2f(l_tot)) * kLn2;
             p0 = (ntiles + p0) & 1;   // where the next block's tile 0 went
-        } else if constexpr (QN) {
+        } else if constexpr (QN || QB) {
             // as above, staged in the wave's own Q rows; rows that see no key
             // (padding) get O = 0 and lse = -inf, kept probabilities are scaled
             // by 256 / t8
