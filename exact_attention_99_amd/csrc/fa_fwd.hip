@@ -119,12 +119,13 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     // copies; each wave stages its output rows in its own Q rows.
     constexpr bool QN = FA355_FWD_QLDS && !PERSIST && D == 128 && NW == 8 && GS == 1 &&
                         2 * STAGE + 32 * NW * D * 2 <= 160 * 1024;
-    // QB (the block-mask build: 4 waves, two workgroups per compute unit): the
-    // same, with the Q rows in K/V buffer 1 before the first tile (a second
-    // barrier keeps the first copy into that buffer from overwriting them),
-    // so the LDS per workgroup stays as it is.
-    constexpr bool QB = FA355_FWD_QLDS && !PERSIST && SPARSE && D == 128 && NW == 4 && GS == 1 &&
-                        32 * NW * D * 2 <= STAGE;
+    // QB (the other builds whose Q rows fit one K/V buffer: 4 waves, at d = 64
+    // or with a block mask): the same, with the Q rows in K/V buffer 1 before
+    // the first tile (a second barrier keeps the first copy into that buffer
+    // from overwriting them), so the LDS per workgroup stays as it is.  On the
+    // persistent grid a wave that starts the next block early only copies into
+    // its own rows of buffer 1 and into buffer 0, which every wave is done with.
+    constexpr bool QB = FA355_FWD_QLDS && !QL && !QN && GS == 1 && 32 * NW * D * 2 <= STAGE;
     constexpr int QTILE = (QL || QN) ? 32 * NW * D * 2 : 0;
     constexpr int OSPARE = QL ? QTILE / 2 : 0;   // output staging of waves NW/2 .. NW - 1
     constexpr int OWAVE = 32 * D * 2;   // a wave's output rows
