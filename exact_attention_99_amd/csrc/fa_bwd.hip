@@ -30,6 +30,8 @@
 
 namespace fa355 {
 
+FA355_CLOCK_PROBE_ARRAY(fa355_clock_bwd)
+
 namespace {
 
 // ---------------------------------------------------------------------------
@@ -139,6 +141,7 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const float* __restrict__ LSE, const float* __restrict__ Delta,
                 uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int B, int Hq, int Hkv, int N,
                 float cl2, float scale, DropParams dp, SparseParams sp) {
+    FA355_CLOCK_BEGIN
     static_assert(!(DROP && MASKED), "dropout runs on the dense walk");
     constexpr int NW = 4;
     constexpr int BKV = 128;
@@ -655,6 +658,7 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         }
 
     }
+    FA355_CLOCK_END(fa355_clock_bwd)
 }
 
 // ---------------------------------------------------------------------------
@@ -683,6 +687,7 @@ dq16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const float* __restrict__ LSE, const float* __restrict__ Delta,
               uint16_t* __restrict__ dQ, int B, int Hq, int Hkv, int N, float cl2, float scale,
               DropParams dp, SparseParams sp) {
+    FA355_CLOCK_BEGIN
     static_assert(!SPARSE || NW == 4, "a block-mask row spans the workgroup's 128 rows");
     constexpr int BR = 32 * NW;
     constexpr int BC = D == 128 ? FA355_DQ_BC128 : 128;
@@ -941,6 +946,7 @@ dq16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             if (qw + r < N) *reinterpret_cast<u32x4*>(dqw + 1024 * k + 16 * ln) = v;
         }
     }
+    FA355_CLOCK_END(fa355_clock_bwd)
 }
 
 // ---------------------------------------------------------------------------

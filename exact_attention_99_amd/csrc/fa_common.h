@@ -57,6 +57,46 @@
 #define FA355_DQ_BC128 64      // dQ keys per tile at d = 128
 #endif
 
+// Clock probe, for measurement builds only (-DFA355_CLOCK_PROBE=1).  Each wave of
+// the forward, dK/dV and dQ kernels records the shader-clock counter and the
+// fixed 100 MHz real-time counter when it starts and when it ends, one record
+// per wave slot (blockIdx.x * waves + wave, the first FA355_CLOCK_PROBE_SLOTS
+// slots), read back by <array>_read(host).  Their ratio is the clock the chip
+// ran the kernel at; the spread of the end times is the grid's tail.  The
+// default library compiles all of it away.
+#ifndef FA355_CLOCK_PROBE
+#define FA355_CLOCK_PROBE 0
+#endif
+#if FA355_CLOCK_PROBE
+#define FA355_CLOCK_PROBE_SLOTS 8192
+#define FA355_CLOCK_PROBE_ARRAY(NAME)                                                      \
+    __device__ unsigned long long NAME[FA355_CLOCK_PROBE_SLOTS][4];                         \
+    extern "C" int NAME##_read(void* host) {                                               \
+        return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(NAME), sizeof(NAME), 0,            \
+                                        hipMemcpyDeviceToHost);                            \
+    }
+#define FA355_CLOCK_BEGIN                                                                  \
+    const unsigned long long clock_c0_ = __builtin_amdgcn_s_memtime();                     \
+    const unsigned long long clock_r0_ = __builtin_amdgcn_s_memrealtime();
+#define FA355_CLOCK_END(NAME)                                                              \
+    {                                                                                     \
+        const unsigned long long c1 = __builtin_amdgcn_s_memtime();                        \
+        const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();                    \
+        const unsigned slot = blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;           \
+        if ((threadIdx.x & 63) == 0 && slot < FA355_CLOCK_PROBE_SLOTS) {                   \
+            unsigned long long* rec = NAME[slot];                                          \
+            rec[0] = clock_c0_;                                                            \
+            rec[1] = c1;                                                                   \
+            rec[2] = clock_r0_;                                                            \
+            rec[3] = r1;                                                                   \
+        }                                                                                 \
+    }
+#else
+#define FA355_CLOCK_PROBE_ARRAY(NAME)
+#define FA355_CLOCK_BEGIN
+#define FA355_CLOCK_END(NAME)
+#endif
+
 namespace fa355 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

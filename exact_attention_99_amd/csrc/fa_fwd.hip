@@ -27,6 +27,8 @@
 
 namespace fa355 {
 
+FA355_CLOCK_PROBE_ARRAY(fa355_clock_fwd)
+
 namespace {
 
 // Sixth-generation 16-bit forward kernel: NW waves of 32 query rows, tiles of
@@ -83,6 +85,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)
 fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
                int B, int Hq, int Hkv, int N, float cl2, DropParams dp, SparseParams sp) {
+    FA355_CLOCK_BEGIN
     static_assert(BC == 64 || BC == 128, "tiles of one or two 64-key sub-tiles");
     static_assert(D == 64 || D == 128, "head dimensions with a K tile swizzle");
     constexpr int PPB = 8 / (D / 16);    // probability pairs per second-half score product
@@ -693,6 +696,7 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             if (hi == 0) LSE[(size_t)(b * Hq + h) * N + q] = empty ? -INFINITY : (m_s + __log2f(l_tot)) * kLn2;
         }
     }
+    FA355_CLOCK_END(fa355_clock_fwd)
 }
 
 // fp32 inputs: the same walk with the fp32 matrix-core op (32x32x2), P kept in

@@ -47,6 +47,15 @@ def test_every_declared_symbol_is_exported(lib):
         getattr(raw, name)
 
 
+def test_shipped_library_has_no_clock_probe(lib):
+    """The per-wave clock records exist only in measurement builds
+    (FA355_CLOCK_PROBE=1); the package's own library compiles them away."""
+    if os.environ.get("FA355_LIB"):
+        pytest.skip("an alternative library is selected")
+    for name in ("fa355_clock_fwd_read", "fa355_clock_bwd_read"):
+        assert not hasattr(lib, name), name
+
+
 def test_version_and_status_strings(lib):
     assert _abi.fa_version() == 100
     for code in range(5):
