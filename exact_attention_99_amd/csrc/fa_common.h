@@ -220,6 +220,38 @@ __device__ __forceinline__ int persist_block(int p, int G, int total, int round)
     return k < cnt ? start + k : -1;
 }
 
+// The shared tail of that schedule: once every workgroup has walked its first
+// rs rounds (stat = rs * G/8 blocks of each XCD's range), the blocks left in
+// all ranges form one pool, numbered XCD by XCD in turn (c % 8 is the XCD, c / 8
+// the j-th block of its rest) and, past 8 times the shortest rest, the ranges'
+// one extra block each.  Where an XCD's rest is whole heads of nqb row blocks,
+// its j-th block is row block j / heads of head j % heads: the rows of every
+// pooled head in the order the logical numbering gives (longest first under
+// the causal mask), so the last claims are the shortest blocks.  -1 past the
+// pool's end.
+__device__ __forceinline__ int pool_block(int c, int total, int stat, int nqb) {
+    constexpr int kXcd = 8;
+    const int per = total / kXcd, rem = total % kXcd;
+    const int base = per - stat;
+    int x, j;
+    if (c < kXcd * base) {
+        x = c % kXcd;
+        j = c / kXcd;
+    } else {
+        x = c - kXcd * base;
+        if (x >= rem) return -1;
+        j = base;
+    }
+    const int start = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+    const int lo = start + stat;
+    const int rest = (x < rem ? per + 1 : per) - stat;
+    if (lo % nqb == 0 && rest % nqb == 0) {
+        const int heads = rest / nqb;
+        return lo + (j % heads) * nqb + j / heads;
+    }
+    return lo + j;
+}
+
 // Workgroups in a persistent grid of one workgroup per compute unit of the
 // current device, rounded down to a multiple of the 8 XCDs (0 if unknown).
 // The compute-unit count is cached per device in relaxed atomics: threads that

@@ -29,6 +29,31 @@ namespace fa355 {
 
 FA355_CLOCK_PROBE_ARRAY(fa355_clock_fwd)
 
+// Counters of the persistent forward's shared tail: a ring of 64-byte slots
+// (a claim counter and a done counter each), one slot per launch, chosen
+// round-robin on the host.  A launch leaves its slot at zero when it ends, so
+// launches that overlap in time (other streams) stay apart as long as fewer
+// than kPoolSlots of them are in flight on one device at once.
+constexpr int kPoolSlots = 64;
+__device__ __attribute__((aligned(64))) unsigned fa355_fwd_pool[kPoolSlots * 16];
+
+// This launch's slot on the current device (nullptr if the symbol's address
+// cannot be had: the kernel then keeps its static schedule).
+unsigned* fwd_pool_slot() {
+    static std::atomic<unsigned*> base[64];
+    static std::atomic<unsigned> seq{0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    unsigned* p = base[dev].load(std::memory_order_acquire);
+    if (!p) {
+        void* a = nullptr;
+        if (hipGetSymbolAddress(&a, HIP_SYMBOL(fa355_fwd_pool)) != hipSuccess || !a) return nullptr;
+        p = static_cast<unsigned*>(a);
+        base[dev].store(p, std::memory_order_release);
+    }
+    return p + 16 * (seq.fetch_add(1, std::memory_order_relaxed) % kPoolSlots);
+}
+
 namespace {
 
 // Sixth-generation 16-bit forward kernel: NW waves of 32 query rows, tiles of
@@ -84,7 +109,8 @@ template <typename T, int D, bool CAUSAL, int NW, int BC, bool PERSIST = false, 
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-               int B, int Hq, int Hkv, int N, float cl2, DropParams dp, SparseParams sp) {
+               int B, int Hq, int Hkv, int N, float cl2, DropParams dp, SparseParams sp,
+               unsigned* __restrict__ pool) {
     FA355_CLOCK_BEGIN
     static_assert(BC == 64 || BC == 128, "tiles of one or two 64-key sub-tiles");
     static_assert(D == 64 || D == 128, "head dimensions with a K tile swizzle");
@@ -203,14 +229,59 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         }
     };
     int p0 = 0;   // QL: buffer of the current block's tile 0
+    // Shared tail (QL, with a pool slot): the XCDs of the chip run at clocks
+    // that differ by up to ~10% under this kernel, so equal static shares end
+    // when the slowest XCD does.  Every workgroup walks its first rs rounds of
+    // persist_block statically; the blocks past them in every XCD's range (at
+    // least two rounds' worth, an eighth of the work on long walks) form one
+    // pool that any workgroup claims from, one block at a time, through an
+    // atomic counter in pool[0].  A workgroup whose claim fails counts itself
+    // in pool[1]; the last one resets both counters for the next launch that
+    // takes this slot.  Without a slot every round is static, and so is every
+    // round without the causal mask: its blocks are all as long as the longest
+    // causal ones, too coarse to even out the XCDs' ends.
+    constexpr bool TAIL = QL && CAUSAL;
+    const int gxd = (int)gridDim.x / 8;
+    const int rounds_x = gxd > 0 ? (total / 8) / gxd : 0;
+    const int rs = (TAIL && pool) ? max(0, rounds_x - max(2, rounds_x / 8)) : 0x7fffffff;
     // One block per workgroup, or (PERSIST) a grid of one workgroup per compute
     // unit that walks its blocks in rounds.
     for (int round = 0;; ++round) {
         int logical, nxt = -1;
+        bool fresh = round == 0;   // QL: nothing of this block is in flight yet
         if constexpr (PERSIST) {
-            logical = persist_block((int)blockIdx.x, (int)gridDim.x, total, round);
-            if (logical < 0) break;
-            nxt = persist_block((int)blockIdx.x, (int)gridDim.x, total, round + 1);
+            if (round < rs) {
+                logical = persist_block((int)blockIdx.x, (int)gridDim.x, total, round);
+                if (logical < 0) break;
+                nxt = round + 1 < rs ? persist_block((int)blockIdx.x, (int)gridDim.x, total, round + 1) : -1;
+            } else {
+                if constexpr (TAIL) {
+                    // the word goes through the spare staging region, which the
+                    // previous block's epilogue is done with after this barrier
+                    // and this block's epilogue writes only after later ones
+                    int* const word = reinterpret_cast<int*>(smem + 2 * STAGE + QTILE);
+                    __syncthreads();
+                    if (tid == 0) {
+                        const unsigned pooled = (unsigned)(total - 8 * rs * gxd);
+                        const unsigned c = atomicAdd(&pool[0], 1u);
+                        int lg = c < pooled ? pool_block((int)c, total, rs * gxd, nqb) : -1;
+                        if (lg < 0) {
+                            if (atomicAdd(&pool[1], 1u) == gridDim.x - 1) {
+                                atomicExch(&pool[0], 0u);
+                                atomicExch(&pool[1], 0u);
+                            }
+                        }
+                        *word = lg;
+                    }
+                    __syncthreads();
+                    logical = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile int*>(word));
+                    if (logical < 0) break;
+                    fresh = true;
+                    p0 = 0;
+                } else {
+                    break;
+                }
+            }
         } else {
             if (round > 0) break;
             logical = xcd_remap((int)blockIdx.x, total);
@@ -247,7 +318,7 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         if constexpr (QL) {
             // the first block's copies are issued here, the others' during the
             // previous block
-            if (round == 0) {
+            if (fresh) {
                 issue_q(logical);
                 issue_kv0(logical, smem);
             }
@@ -834,13 +905,14 @@ hipError_t launch16v6(const FwdArgs& a) {
             hipLaunchKernelGGL((fwd16v6_kernel<T, D, CAUSAL, NW, BC, true, DROP, SPARSE, GS>), dim3((unsigned)grid),
                                dim3(NW * 64), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                                (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.dp,
-                               a.sp);
+                               a.sp, fwd_pool_slot());
             return hipGetLastError();
         }
     }
     hipLaunchKernelGGL((fwd16v6_kernel<T, D, CAUSAL, NW, BC, false, DROP, SPARSE, GS>), dim3((unsigned)total),
                        dim3(NW * 64), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                       (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.dp, a.sp);
+                       (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.N, a.cl2, a.dp, a.sp,
+                       nullptr);
     return hipGetLastError();
 }
 

@@ -179,3 +179,31 @@ def test_many_short_heads_other_groups(hkv, causal):
     err = (o.to(torch.float64) - ref).abs()
     assert err.max().item() <= TOL["bf16"]["o_max"], err.max().item()
     assert err.mean().item() <= TOL["bf16"]["o_mean"], err.mean().item()
+
+
+def test_shared_tail_repeats_and_streams():
+    """The persistent forward hands the last rounds' blocks out through counters
+    that each launch takes from a ring of slots and resets when it ends: 80
+    launches in a row (more than the ring holds) and launches on two streams
+    without waits between them all give bitwise the same output and lse."""
+    d, causal = 128, True
+    print("case repeats", flush=True)
+    scale = 1.0 / math.sqrt(d)
+    q, k, v, _ = workloads.make_inputs(B, HQ, HKV, N, d, "bf16", 4500)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o0, l0 = fa_fwd(qd, kd, vd, causal, scale)
+    torch.cuda.synchronize()
+    O, L = oracle.attention_forward(f64(q[3:4, 9:10]), f64(k[3:4, 2:3]), f64(v[3:4, 2:3]), scale, causal)
+    check_fwd(o0[3:4, 9:10], l0[3:4, 9:10], O, L, "bf16", "b=3 h=9")
+    o, lse = torch.empty_like(o0), torch.empty_like(l0)
+    for i in range(80):
+        fa_fwd(qd, kd, vd, causal, scale, o=o, lse=lse)
+        assert torch.equal(o, o0) and torch.equal(lse, l0), f"launch {i}"
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [(torch.empty_like(o0), torch.empty_like(l0)) for _ in range(8)]
+    torch.cuda.synchronize()
+    for i, (oi, li) in enumerate(outs):
+        fa_fwd(qd, kd, vd, causal, scale, o=oi, lse=li, stream=streams[i % 2])
+    torch.cuda.synchronize()
+    for i, (oi, li) in enumerate(outs):
+        assert torch.equal(oi, o0) and torch.equal(li, l0), f"stream launch {i}"
