@@ -32,6 +32,31 @@ namespace fa355 {
 
 FA355_CLOCK_PROBE_ARRAY(fa355_clock_bwd)
 
+// Counters of the persistent dK/dV pass's shared tail: a ring of 64-byte slots
+// (a claim counter and a done counter each), one slot per launch, chosen
+// round-robin on the host; a launch leaves its slot at zero when it ends, so
+// launches on other streams stay apart while fewer than kPoolSlots of them
+// are in flight on one device at once.
+constexpr int kPoolSlots = 64;
+__device__ __attribute__((aligned(64))) unsigned fa355_dkdv_pool[kPoolSlots * 16];
+
+// This launch's slot on the current device (nullptr if the symbol's address
+// cannot be had: the kernel then keeps its static schedule).
+unsigned* dkdv_pool_slot() {
+    static std::atomic<unsigned*> base[64];
+    static std::atomic<unsigned> seq{0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    unsigned* p = base[dev].load(std::memory_order_acquire);
+    if (!p) {
+        void* a = nullptr;
+        if (hipGetSymbolAddress(&a, HIP_SYMBOL(fa355_dkdv_pool)) != hipSuccess || !a) return nullptr;
+        p = static_cast<unsigned*>(a);
+        base[dev].store(p, std::memory_order_release);
+    }
+    return p + 16 * (seq.fetch_add(1, std::memory_order_relaxed) % kPoolSlots);
+}
+
 namespace {
 
 // ---------------------------------------------------------------------------
@@ -140,7 +165,7 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                 const float* __restrict__ LSE, const float* __restrict__ Delta,
                 uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int B, int Hq, int Hkv, int N,
-                float cl2, float scale, DropParams dp, SparseParams sp) {
+                float cl2, float scale, DropParams dp, SparseParams sp, unsigned* __restrict__ pool) {
     FA355_CLOCK_BEGIN
     static_assert(!(DROP && MASKED), "dropout runs on the dense walk");
     constexpr int NW = 4;
@@ -183,13 +208,48 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
     const int nkb = (N + BKV - 1) / BKV;
     const int total = nkb * Hkv * B;
+    // Shared tail (dense causal walk, with a pool slot), as in the forward: the
+    // first rs rounds are static, the key blocks past them in every XCD's range
+    // are claimed one at a time from one pool (the longest first: key block 0
+    // of a head meets every query row), so XCDs at lower clocks take fewer.
+    // The claimed index passes through the row-term area of buffer kvbuf
+    // (below), which no copy of the block reaches before its K and V rows are
+    // read, after every wave has read the index.
+    constexpr bool TAIL = PERSIST && CAUSAL && !DROP && !SPARSE;
+    const int gxd = (int)gridDim.x / 8;
+    const int rounds_x = gxd > 0 ? (total / 8) / gxd : 0;
+    const int rs = (TAIL && pool) ? max(0, rounds_x - max(2, rounds_x / 8)) : 0x7fffffff;
     // One key block per workgroup, or (PERSIST) a grid of one workgroup per
     // compute unit that walks its key blocks in rounds.
     for (int round = 0;; ++round) {
         int logical;
         if constexpr (PERSIST) {
-            logical = persist_block((int)blockIdx.x, (int)gridDim.x, total, round);
-            if (logical < 0) break;
+            if (round < rs) {
+                logical = persist_block((int)blockIdx.x, (int)gridDim.x, total, round);
+                if (logical < 0) break;
+            } else {
+                if constexpr (TAIL) {
+                    int* const word = reinterpret_cast<int*>(smem + (((Hq / Hkv) & 1) ^ 1) * STAGE + OFF_LSE);
+                    __syncthreads();
+                    if (tid == 0) {
+                        const unsigned pooled = (unsigned)(total - 8 * rs * gxd);
+                        const unsigned c = atomicAdd(&pool[0], 1u);
+                        int lg = c < pooled ? pool_block((int)c, total, rs * gxd, nkb) : -1;
+                        if (lg < 0) {
+                            if (atomicAdd(&pool[1], 1u) == gridDim.x - 1) {
+                                atomicExch(&pool[0], 0u);
+                                atomicExch(&pool[1], 0u);
+                            }
+                        }
+                        *word = lg;
+                    }
+                    __syncthreads();
+                    logical = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile int*>(word));
+                    if (logical < 0) break;
+                } else {
+                    break;
+                }
+            }
         } else {
             if (round > 0) break;
             logical = xcd_remap((int)blockIdx.x, total);
@@ -1197,7 +1257,7 @@ hipError_t dkdv16(const BwdArgs& a) {
         hipLaunchKernelGGL(kern, dim3((unsigned)(pers ? grid : total)), dim3(256), 0, a.stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                            (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.B,
-                           a.Hq, a.Hkv, a.N, a.cl2, a.scale, a.dp, a.sp);
+                           a.Hq, a.Hkv, a.N, a.cl2, a.scale, a.dp, a.sp, pers ? dkdv_pool_slot() : nullptr);
         return hipGetLastError();
     };
     if (a.sparse)
