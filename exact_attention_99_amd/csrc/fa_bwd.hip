@@ -33,8 +33,8 @@ namespace fa355 {
 FA355_CLOCK_PROBE_ARRAY(fa355_clock_bwd)
 
 // Counters of the persistent dK/dV pass's shared tail: a ring of 64-byte slots
-// (a claim counter and a done counter each), one slot per launch, chosen
-// round-robin on the host; a launch leaves its slot at zero when it ends, so
+// (a claim counter per XCD and a done counter each), one slot per launch,
+// chosen round-robin on the host; a launch leaves its slot at zero when it ends, so
 // launches on other streams stay apart while fewer than kPoolSlots of them
 // are in flight on one device at once.
 constexpr int kPoolSlots = 64;
@@ -209,16 +209,22 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int nkb = (N + BKV - 1) / BKV;
     const int total = nkb * Hkv * B;
     // Shared tail (dense causal walk, with a pool slot), as in the forward: the
-    // first rs rounds are static, the key blocks past them in every XCD's range
-    // are claimed one at a time from one pool (the longest first: key block 0
-    // of a head meets every query row), so XCDs at lower clocks take fewer.
+    // first rs rounds are static, the key blocks past them in each XCD's range
+    // are claimed one at a time (claim_pooled: own XCD's pool first, the
+    // longest first: key block 0 of a head meets every query row), so XCDs at
+    // lower clocks take fewer.
     // The claimed index passes through the row-term area of buffer kvbuf
     // (below), which no copy of the block reaches before its K and V rows are
     // read, after every wave has read the index.
     constexpr bool TAIL = PERSIST && CAUSAL && !DROP && !SPARSE;
     const int gxd = (int)gridDim.x / 8;
     const int rounds_x = gxd > 0 ? (total / 8) / gxd : 0;
-    const int rs = (TAIL && pool) ? max(0, rounds_x - max(2, rounds_x / 8)) : 0x7fffffff;
+    const int tail_rounds = max(2, rounds_x / 8);
+    // (the 16-bit pool counters: each pool holds at most (tail_rounds + 1) G/8
+    // blocks, its back counter counts at most all pooled claims and one failed
+    // claim per workgroup)
+    const bool fits16 = 9 * (tail_rounds + 1) * gxd + (int)gridDim.x < (1 << 16);
+    const int rs = (TAIL && pool && fits16) ? max(0, rounds_x - tail_rounds) : 0x7fffffff;
     // One key block per workgroup, or (PERSIST) a grid of one workgroup per
     // compute unit that walks its key blocks in rounds.
     for (int round = 0;; ++round) {
@@ -231,18 +237,8 @@ dkdv16v3_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 if constexpr (TAIL) {
                     int* const word = reinterpret_cast<int*>(smem + (((Hq / Hkv) & 1) ^ 1) * STAGE + OFF_LSE);
                     __syncthreads();
-                    if (tid == 0) {
-                        const unsigned pooled = (unsigned)(total - 8 * rs * gxd);
-                        const unsigned c = atomicAdd(&pool[0], 1u);
-                        int lg = c < pooled ? pool_block((int)c, total, rs * gxd, nkb) : -1;
-                        if (lg < 0) {
-                            if (atomicAdd(&pool[1], 1u) == gridDim.x - 1) {
-                                atomicExch(&pool[0], 0u);
-                                atomicExch(&pool[1], 0u);
-                            }
-                        }
-                        *word = lg;
-                    }
+                    if (tid == 0)
+                        *word = claim_pooled(pool, (int)blockIdx.x % 8, total, rs * gxd, nkb, gridDim.x);
                     __syncthreads();
                     logical = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile int*>(word));
                     if (logical < 0) break;

@@ -222,34 +222,42 @@ __device__ __forceinline__ int persist_block(int p, int G, int total, int round)
 
 // The shared tail of that schedule: once every workgroup has walked its first
 // rs rounds (stat = rs * G/8 blocks of each XCD's range), the blocks left in
-// all ranges form one pool, numbered XCD by XCD in turn (c % 8 is the XCD, c / 8
-// the j-th block of its rest) and, past 8 times the shortest rest, the ranges'
-// one extra block each.  Where an XCD's rest is whole heads of nqb row blocks,
-// its j-th block is row block j / heads of head j % heads: the rows of every
-// pooled head in the order the logical numbering gives (longest first under
-// the causal mask), so the last claims are the shortest blocks.  -1 past the
-// pool's end.
-__device__ __forceinline__ int pool_block(int c, int total, int stat, int nqb) {
+// XCD y's range form its pool, ordered longest first where the pool is whole
+// heads of nqb row (or key) blocks (position c is block c / heads of head
+// c % heads; under the causal mask the logical numbering puts a head's longest
+// block first).  pool[y] packs two counters: the low 16 bits count claims from
+// the front, the high 16 from the back.  A workgroup on XCD x takes pool x's
+// front (the longest block left, its heads in its own L2); once that pool is
+// empty it takes the back (the shortest block left) of x + 1, x + 2, ...  A
+// claim is valid while front + back < the pool's size, so no position is
+// handed out twice.  A workgroup that finds every pool empty counts itself in
+// pool[8]; the last of the grid resets the counters for the next launch that
+// takes this slot.  Returns the block, or -1.  (The caller keeps the schedule
+// static where a counter could pass 16 bits.)
+__device__ __forceinline__ int claim_pooled(unsigned* pool, int x, int total, int stat, int nqb,
+                                            unsigned grid) {
     constexpr int kXcd = 8;
     const int per = total / kXcd, rem = total % kXcd;
-    const int base = per - stat;
-    int x, j;
-    if (c < kXcd * base) {
-        x = c % kXcd;
-        j = c / kXcd;
-    } else {
-        x = c - kXcd * base;
-        if (x >= rem) return -1;
-        j = base;
+    for (int t = 0; t < kXcd; ++t) {
+        const int y = (x + t) % kXcd;
+        const int rest = (y < rem ? per + 1 : per) - stat;
+        if (rest <= 0) continue;
+        const unsigned old = atomicAdd(&pool[y], t == 0 ? 1u : 0x10000u);
+        const int f = (int)(old & 0xffffu), bk = (int)(old >> 16);
+        if (f + bk < rest) {
+            const int c = t == 0 ? f : rest - 1 - bk;
+            const int start = y < rem ? y * (per + 1) : rem * (per + 1) + (y - rem) * per;
+            const int lo = start + stat;
+            if (lo % nqb == 0 && rest % nqb == 0) {
+                const int heads = rest / nqb;
+                return lo + (c % heads) * nqb + c / heads;
+            }
+            return lo + c;
+        }
     }
-    const int start = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
-    const int lo = start + stat;
-    const int rest = (x < rem ? per + 1 : per) - stat;
-    if (lo % nqb == 0 && rest % nqb == 0) {
-        const int heads = rest / nqb;
-        return lo + (j % heads) * nqb + j / heads;
-    }
-    return lo + j;
+    if (atomicAdd(&pool[kXcd], 1u) == grid - 1)
+        for (int y = 0; y <= kXcd; ++y) atomicExch(&pool[y], 0u);
+    return -1;
 }
 
 // Workgroups in a persistent grid of one workgroup per compute unit of the

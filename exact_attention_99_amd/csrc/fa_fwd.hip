@@ -30,8 +30,8 @@ namespace fa355 {
 FA355_CLOCK_PROBE_ARRAY(fa355_clock_fwd)
 
 // Counters of the persistent forward's shared tail: a ring of 64-byte slots
-// (a claim counter and a done counter each), one slot per launch, chosen
-// round-robin on the host.  A launch leaves its slot at zero when it ends, so
+// (a claim counter per XCD and a done counter each), one slot per launch,
+// chosen round-robin on the host.  A launch leaves its slot at zero when it ends, so
 // launches that overlap in time (other streams) stay apart as long as fewer
 // than kPoolSlots of them are in flight on one device at once.
 constexpr int kPoolSlots = 64;
@@ -232,18 +232,22 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     // Shared tail (QL, with a pool slot): the XCDs of the chip run at clocks
     // that differ by up to ~10% under this kernel, so equal static shares end
     // when the slowest XCD does.  Every workgroup walks its first rs rounds of
-    // persist_block statically; the blocks past them in every XCD's range (at
-    // least two rounds' worth, an eighth of the work on long walks) form one
-    // pool that any workgroup claims from, one block at a time, through an
-    // atomic counter in pool[0].  A workgroup whose claim fails counts itself
-    // in pool[1]; the last one resets both counters for the next launch that
-    // takes this slot.  Without a slot every round is static, and so is every
-    // round without the causal mask: its blocks are all as long as the longest
-    // causal ones, too coarse to even out the XCDs' ends.
+    // persist_block statically; the blocks past them in each XCD's range (at
+    // least two rounds' worth, an eighth of the work on long walks) are
+    // claimed one at a time (claim_pooled: the workgroup's own XCD's pool
+    // first, then the others'), so a faster XCD takes more of them.  Without a
+    // slot every round is static, and so is every round without the causal
+    // mask: its blocks are all as long as the longest causal ones, too coarse
+    // to even out the XCDs' ends.
     constexpr bool TAIL = QL && CAUSAL;
     const int gxd = (int)gridDim.x / 8;
     const int rounds_x = gxd > 0 ? (total / 8) / gxd : 0;
-    const int rs = (TAIL && pool) ? max(0, rounds_x - max(2, rounds_x / 8)) : 0x7fffffff;
+    const int tail_rounds = max(2, rounds_x / 8);
+    // (the 16-bit pool counters: each pool holds at most (tail_rounds + 1) G/8
+    // blocks, its back counter counts at most all pooled claims and one failed
+    // claim per workgroup)
+    const bool fits16 = 9 * (tail_rounds + 1) * gxd + (int)gridDim.x < (1 << 16);
+    const int rs = (TAIL && pool && fits16) ? max(0, rounds_x - tail_rounds) : 0x7fffffff;
     // One block per workgroup, or (PERSIST) a grid of one workgroup per compute
     // unit that walks its blocks in rounds.
     for (int round = 0;; ++round) {
@@ -261,18 +265,8 @@ fwd16v6_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                     // and this block's epilogue writes only after later ones
                     int* const word = reinterpret_cast<int*>(smem + 2 * STAGE + QTILE);
                     __syncthreads();
-                    if (tid == 0) {
-                        const unsigned pooled = (unsigned)(total - 8 * rs * gxd);
-                        const unsigned c = atomicAdd(&pool[0], 1u);
-                        int lg = c < pooled ? pool_block((int)c, total, rs * gxd, nqb) : -1;
-                        if (lg < 0) {
-                            if (atomicAdd(&pool[1], 1u) == gridDim.x - 1) {
-                                atomicExch(&pool[0], 0u);
-                                atomicExch(&pool[1], 0u);
-                            }
-                        }
-                        *word = lg;
-                    }
+                    if (tid == 0)
+                        *word = claim_pooled(pool, (int)blockIdx.x % 8, total, rs * gxd, nqb, gridDim.x);
                     __syncthreads();
                     logical = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile int*>(word));
                     if (logical < 0) break;
