@@ -29,9 +29,14 @@
  * library allocates no device memory and keeps no pointer after a call
  * returns.  Inputs are only read.  Outputs must not overlap inputs or each
  * other.  Every buffer must be 16-byte aligned.  The library's only state is
- * a per-device cache of the compute-unit count and, for fa_bwd_noalloc, one
- * fixed scratch array per device (see there), each initialised once in a
- * thread-safe way.
+ * a per-device cache of the compute-unit count, for fa_bwd_noalloc one fixed
+ * scratch array per device (see there), and two rings of 64 small counter
+ * slots per device (part of the code object, not allocated) through which the
+ * causal forward and dK/dV kernels hand out their last blocks at run time, so
+ * that the chip's faster XCDs take more of them.  Each launch takes the next
+ * slot (host-side atomic) and leaves it at zero when it ends; at most 64
+ * launches of one of these kernels may be in flight on one device at once.
+ * Every cache is initialised once in a thread-safe way.
  *
  * Timing and errors: calls enqueue work on `stream` and return without
  * synchronising.  Argument errors are reported synchronously and nothing is
